@@ -1,0 +1,312 @@
+"""FP64 CPU oracle for the KDA token mixer -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this module. It shares no code with the HIP library
+and never imports it.
+
+Sources (the pages this follows):
+
+* [flozi-KDA] "Ling-3.1-flash: Grouped Routing and Two Different MLA Caches"
+  (flozi.net), section "KDA replaces a token list with a recurrent matrix":
+  q/k/v projections of width 64x128, one causal short convolution of width four
+  with SiLU per projection, reshape to [B,T,64,128], q/k normalisation,
+  channel-dependent retention, a delta-rule write, a read of the per-head
+  matrix, then an output normalisation and a sigmoid gate before the projection
+  back to width 4096; safe forget gate with log-retention lower bound -5.
+* [satyajit-Eq] "Ling-3.1-flash: a 560B hybrid-attention MoE, counted from its
+  safetensors headers", section "How KDA and MLA split the work": the decay
+  comes from f_proj and A_log, the write strength from b_proj (one scalar per
+  head), full-rank 4096->8192 decay and gate projections (no_kda_lora).
+* [asivanadi-Memory] "Ling-3.1-flash: What 63 Linear-Attention Layers Do to the
+  KV Budget", section "The memory math": FP32 state of 64x128x128 per layer,
+  kernel size 4 short convolution.
+
+Readings where the pages are silent (each is a choice, listed with its reason in
+the design notes): delta-rule write (not the additive form printed in
+[satyajit-Eq]); retention before the write, read after it; state rows are key
+channels; readout scale is an argument (1.0 by default); g is a natural-log
+retention clamped at ``lower_bound`` on use; conv taps run oldest -> newest with
+the last tap on the current token, no bias; q/k L2-normalised per head with
+eps 1e-6 inside the square root; per-head RMSNorm over dv with eps 1e-6;
+g = max(-exp(A_log[h]) * softplus(f), -5); beta = sigmoid(b); W stored
+[out, in] with y = x W^T.
+
+The token-serial recurrence is in C (``kda_oracle.c``) for speed; everything
+else is numpy float64. The chunked form here is the oracle's own cross-check of
+the chunk reorganisation (an exact rewrite of the recurrence) and is checked
+against the serial form in the tests.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        path = _build.build(force=False)
+        lib = ctypes.CDLL(path)
+        f = lib.oracle_kda_serial
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                              ctypes.c_double, ctypes.c_double,
+                                              ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_int]
+        _LIB = lib
+    return _LIB
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+# --------------------------------------------------------------------------
+# KDA core: token-serial recurrence (the definition) -- [flozi-KDA]
+# --------------------------------------------------------------------------
+def kda_serial(q, k, v, g, beta, cu_seqlens=None, initial_state=None, scale=1.0,
+               lower_bound=-5.0, nthreads=None):
+    """Token-serial FP64 KDA recurrence.
+
+    q, k, g: [T, H, dk]; v: [T, H, dv]; beta: [T, H] (any float dtype; values are
+    taken as given, i.e. already bf16-rounded where the inputs are bf16).
+    cu_seqlens: int [N+1] packed sequence boundaries, or None for one sequence.
+    initial_state: [N, H, dk, dv] or None (zeros).
+    Returns (o [T, H, dv] float64, final_state [N, H, dk, dv] float64).
+    """
+    q, k, v, g, beta = (_f32(x) for x in (q, k, v, g, beta))
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    assert k.shape == (T, H, dk) and g.shape == (T, H, dk)
+    assert v.shape == (T, H, dv) and beta.shape == (T, H)
+    if cu_seqlens is None:
+        cu = np.array([0, T], dtype=np.int64)
+    else:
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+    N = cu.shape[0] - 1
+    s0 = None
+    if initial_state is not None:
+        s0 = np.ascontiguousarray(initial_state, dtype=np.float64)
+        assert s0.shape == (N, H, dk, dv)
+    o = np.empty((T, H, dv), dtype=np.float64)
+    sT = np.empty((N, H, dk, dv), dtype=np.float64)
+    rc = _lib().oracle_kda_serial(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), T, H, dk, dv,
+                                  _ptr(cu), N, float(scale), float(lower_bound), _ptr(s0),
+                                  _ptr(o), _ptr(sT), int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle_kda_serial failed with code %d" % rc)
+    return o, sT
+
+
+# --------------------------------------------------------------------------
+# KDA core: chunked reorganisation, FP64 numpy (cross-check of the serial form)
+# --------------------------------------------------------------------------
+def kda_chunked_one(q, k, v, g, beta, S0=None, chunk=64, scale=1.0, lower_bound=-5.0):
+    """One (sequence, head): the recurrence reorganised over chunks of ``chunk``.
+
+    Inside a chunk with start state S0 and tokens r = 1..n (b_r = cumulative
+    log-retention, per key channel):
+      A[r,i] = beta_r sum_c k_rc k_ic exp(b_rc - b_ic)      (i < r)
+      T      = (I + A)^-1
+      U      = T diag(beta) (V - (K o e^B) S0)              corrected writes
+      P[r,i] = sum_c q_rc k_ic exp(b_rc - b_ic)             (i <= r)
+      O      = scale ((Q o e^B) S0 + P U)
+      S_n    = Diag(e^{b_n}) S0 + (K o e^{b_n - B})^T U
+    Arrays are [T, dk] / [T, dv] / [T]; returns (o [T, dv], S [dk, dv]).
+    """
+    q, k, v, g, beta = (np.asarray(x, dtype=np.float64) for x in (q, k, v, g, beta))
+    T, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    o = np.zeros((T, dv))
+    g = np.maximum(g, lower_bound)
+    for s in range(0, T, chunk):
+        e = min(s + chunk, T)
+        n = e - s
+        Q, K, V, B = q[s:e], k[s:e], v[s:e], beta[s:e]
+        b = np.cumsum(g[s:e], axis=0)                       # [n, dk]
+        diff = b[:, None, :] - b[None, :, :]                # [r, i, c] = b_r - b_i
+        lower_incl = np.tril(np.ones((n, n), dtype=bool))
+        dec = np.exp(np.where(lower_incl[:, :, None], diff, -np.inf))
+        KK = np.einsum("rc,ic,ric->ri", K, K, dec)
+        A = B[:, None] * np.tril(KK, -1)
+        Tm = np.linalg.inv(np.eye(n) + A)
+        eB = np.exp(b)
+        U = Tm @ (B[:, None] * (V - (K * eB) @ S))
+        P = np.einsum("rc,ic,ric->ri", Q, K, dec)
+        o[s:e] = scale * ((Q * eB) @ S + P @ U)
+        Kbar = K * np.exp(b[-1][None, :] - b)
+        S = np.exp(b[-1])[:, None] * S + Kbar.T @ U
+    return o, S
+
+
+def kda_chunked_segment_map(k, g, beta, lower_bound=-5.0):
+    """Affine map of one chunk on the state: S_out = M S_in + N_v (for v given).
+
+    Returns M [dk, dk] and the matrix K_bar^T T diag(beta) [dk, n] so that
+    N = K_bar^T T diag(beta) V. Used to pin linearity of the chunk in S_in.
+    """
+    k, g, beta = (np.asarray(x, dtype=np.float64) for x in (k, g, beta))
+    n, dk = k.shape
+    g = np.maximum(g, lower_bound)
+    b = np.cumsum(g, axis=0)
+    diff = b[:, None, :] - b[None, :, :]
+    lower = np.tril(np.ones((n, n), dtype=bool), -1)
+    dec = np.exp(np.where(lower[:, :, None], diff, -np.inf))
+    A = beta[:, None] * np.einsum("rc,ic,ric->ri", k, k, dec)
+    Tm = np.linalg.inv(np.eye(n) + A)
+    W = Tm @ (beta[:, None] * (k * np.exp(b)))
+    Kbar = k * np.exp(b[-1][None, :] - b)
+    M = np.diag(np.exp(b[-1])) - Kbar.T @ W
+    Nmat = Kbar.T @ Tm @ np.diag(beta)
+    return M, Nmat
+
+
+# --------------------------------------------------------------------------
+# Prologue / epilogue pieces (numpy float64)
+# --------------------------------------------------------------------------
+def round_bf16(x):
+    """Round float64 values to the nearest bfloat16 (ties to even), return float64.
+
+    bfloat16 keeps 8 significant bits and the float32 exponent range. Values are
+    split as m * 2^e with m in [0.5, 1); m is rounded to 8 bits with numpy's
+    round-half-even. Below 2^-126 the spacing is fixed at 2^-133 (subnormals);
+    beyond the largest finite bfloat16 the result is +-inf.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    m, e = np.frexp(x)
+    normal = np.abs(x) >= 2.0 ** -126
+    out[normal] = np.ldexp(np.rint(m[normal] * 256.0) / 256.0, e[normal])
+    sub = ~normal
+    out[sub] = np.rint(x[sub] * 2.0 ** 133) * 2.0 ** -133
+    big = np.abs(out) > 3.3895313892515355e38
+    out[big] = np.sign(out[big]) * np.inf
+    return out
+
+
+def silu(x):
+    x = np.asarray(x, dtype=np.float64)
+    return x / (1.0 + np.exp(-x))
+
+
+def sigmoid(x):
+    x = np.asarray(x, dtype=np.float64)
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def softplus(x):
+    return np.logaddexp(0.0, np.asarray(x, dtype=np.float64))
+
+
+def conv_causal(x, w, cu_seqlens=None, state_in=None, apply_silu=True):
+    """Depthwise causal convolution of width W per sequence, then SiLU.
+
+    [flozi-KDA]: one causal short convolution of width four with SiLU per stream.
+    x: [T, C]; w: [C, W] with w[:, W-1] applied to the current token and
+    w[:, 0] to the token W-1 steps back; state_in: [N, W-1, C] (oldest first) or
+    None for zero history. Returns (y [T, C] float64, state_out [N, W-1, C]): the
+    last W-1 inputs of each sequence, including history when it is shorter.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    T, C = x.shape
+    W = w.shape[1]
+    cu = np.array([0, T]) if cu_seqlens is None else np.asarray(cu_seqlens, dtype=np.int64)
+    N = len(cu) - 1
+    y = np.empty((T, C))
+    state_out = np.empty((N, W - 1, C))
+    for n in range(N):
+        s, e = int(cu[n]), int(cu[n + 1])
+        hist = np.zeros((W - 1, C)) if state_in is None else np.asarray(state_in[n], np.float64)
+        ext = np.concatenate([hist, x[s:e]], axis=0)      # [W-1 + L, C]
+        L = e - s
+        acc = np.zeros((L, C))
+        for j in range(W):                                 # tap j sees token t - (W-1-j)
+            acc += w[None, :, j] * ext[j:j + L]
+        y[s:e] = silu(acc) if apply_silu else acc
+        state_out[n] = ext[L:L + W - 1]
+    return y, state_out
+
+
+def l2norm_groups(y, group=128, eps=1e-6):
+    """Per-group (per-head) L2 normalisation: y / sqrt(sum(y^2) + eps)."""
+    y = np.asarray(y, dtype=np.float64)
+    shp = y.shape
+    z = y.reshape(shp[:-1] + (shp[-1] // group, group))
+    z = z / np.sqrt(np.sum(z * z, axis=-1, keepdims=True) + eps)
+    return z.reshape(shp)
+
+
+def gate_prologue(f, b, A_log, lower_bound=-5.0):
+    """Log-retention and write strength from the raw projections.
+
+    f: [T, H, dk] (f_proj output); b: [T, H] (b_proj output); A_log: [H].
+    g = max(-exp(A_log[h]) * softplus(f), lower_bound); beta = sigmoid(b).
+    """
+    f = np.asarray(f, dtype=np.float64)
+    A = np.exp(np.asarray(A_log, dtype=np.float64))
+    g = np.maximum(-A[None, :, None] * softplus(f), lower_bound)
+    return g, sigmoid(b)
+
+
+def output_norm_gate(o, gate, w, eps=1e-6):
+    """Per-head RMSNorm over dv, times weight, times sigmoid(gate).
+
+    o: [T, H, dv]; gate: [T, H*dv] or [T, H, dv]; w: [dv]. Returns [T, H, dv].
+    """
+    o = np.asarray(o, dtype=np.float64)
+    gate = np.asarray(gate, dtype=np.float64).reshape(o.shape)
+    r = o / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    return r * np.asarray(w, dtype=np.float64)[None, None, :] * sigmoid(gate)
+
+
+def layer_forward(x, Wq, Wk, Wv, Wf, Wg, Wb, Wo, conv_q, conv_k, conv_v, A_log, norm_w,
+                  H, d=128, scale=1.0, lower_bound=-5.0, l2_eps=1e-6, rms_eps=1e-6,
+                  nthreads=None, return_parts=False):
+    """Whole KDA token mixer on one sequence, FP64, rounding to bfloat16 exactly
+    where the library stores bfloat16 (projection outputs, conv outputs, gate
+    outputs, epilogue output).
+
+    x: [T, hidden]; W*: [out, in] (y = x W^T); conv_*: [H*d, 4].
+    Returns out [T, hidden] float64 (and a dict of intermediates if asked).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    T = x.shape[0]
+    mm = lambda a, W: a @ np.asarray(W, dtype=np.float64).T
+    q_pre = round_bf16(mm(x, Wq))
+    k_pre = round_bf16(mm(x, Wk))
+    v_pre = round_bf16(mm(x, Wv))
+    f_pre = round_bf16(mm(x, Wf))
+    g_pre = round_bf16(mm(x, Wg))
+    b_pre = round_bf16(mm(x, Wb))
+    q = round_bf16(l2norm_groups(conv_causal(q_pre, conv_q)[0], d, l2_eps))
+    k = round_bf16(l2norm_groups(conv_causal(k_pre, conv_k)[0], d, l2_eps))
+    v = round_bf16(conv_causal(v_pre, conv_v)[0])
+    g, beta = gate_prologue(f_pre.reshape(T, H, d), b_pre, A_log, lower_bound)
+    g, beta = round_bf16(g), round_bf16(beta)
+    o, S = kda_serial(q.reshape(T, H, d), k.reshape(T, H, d), v.reshape(T, H, d), g, beta,
+                      scale=scale, lower_bound=lower_bound, nthreads=nthreads)
+    y = round_bf16(output_norm_gate(o, g_pre, norm_w, rms_eps)).reshape(T, H * d)
+    out = mm(y, Wo)
+    if return_parts:
+        return out, dict(q=q, k=k, v=v, g=g, beta=beta, o=o, S=S, y=y, gate=g_pre)
+    return out
