@@ -1,0 +1,331 @@
+// kda_api.cpp -- the C ABI (include/kda.h): host-side validation and launches.
+//
+// Every entry point validates all of its arguments before touching the HIP
+// runtime, so a rejected call launches nothing and writes nothing. Messages
+// for rejected calls are kept per thread and returned by kda_last_error().
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "../../include/kda.h"
+#include "kda_internal.h"
+
+using namespace kda;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok()
+{
+    g_err.clear();
+    return KDA_OK;
+}
+
+int hip_status(hipError_t e, const char* what)
+{
+    if (e == hipSuccess) return ok();
+    return fail(KDA_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool valid_dtype(kda_dtype d) { return d == KDA_F32 || d == KDA_BF16; }
+size_t esize(kda_dtype d) { return d == KDA_F32 ? 4 : 2; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Byte range [p, p + n) of a tensor, for overlap checks.
+struct Range {
+    const char* p;
+    size_t n;
+};
+Range rng(const void* p, size_t n) { return Range{static_cast<const char*>(p), n}; }
+bool overlap(Range a, Range b)
+{
+    if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+    return a.p < b.p + b.n && b.p < a.p + a.n;
+}
+
+#define REQUIRE(cond, code, ...)                \
+    do {                                        \
+        if (!(cond)) return fail(code, __VA_ARGS__); \
+    } while (0)
+
+// cu_seqlens on the host: cu[0] = 0, non-decreasing, cu[N] = T.
+int check_cu(const int32_t* cu_dev, const int32_t* cu_host, int num_seqs, int64_t T, int64_t* seq_len)
+{
+    REQUIRE(num_seqs >= 1, KDA_ERR_INVALID_ARG, "num_seqs must be >= 1 (got %d)", num_seqs);
+    REQUIRE((cu_dev == nullptr) == (cu_host == nullptr), KDA_ERR_INVALID_ARG,
+            "cu_seqlens_dev and cu_seqlens_host must both be given or both be NULL");
+    *seq_len = 0;
+    if (!cu_host) {
+        REQUIRE(T % num_seqs == 0, KDA_ERR_INVALID_ARG,
+                "without cu_seqlens, num_tokens (%lld) must be a multiple of num_seqs (%d)",
+                (long long)T, num_seqs);
+        *seq_len = T / num_seqs;
+        return KDA_OK;
+    }
+    REQUIRE(aligned16(cu_dev), KDA_ERR_INVALID_ARG, "cu_seqlens_dev must be 16-byte aligned");
+    REQUIRE(cu_host[0] == 0, KDA_ERR_INVALID_ARG, "cu_seqlens[0] must be 0 (got %d)", cu_host[0]);
+    for (int n = 0; n < num_seqs; ++n)
+        REQUIRE(cu_host[n + 1] >= cu_host[n], KDA_ERR_INVALID_ARG,
+                "cu_seqlens must be non-decreasing (cu[%d]=%d > cu[%d]=%d)", n, cu_host[n], n + 1,
+                cu_host[n + 1]);
+    REQUIRE((int64_t)cu_host[num_seqs] == T, KDA_ERR_INVALID_ARG,
+            "cu_seqlens[num_seqs] (%d) must equal num_tokens (%lld)", cu_host[num_seqs], (long long)T);
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_last_error(void) { return g_err.c_str(); }
+
+int kda_version(void) { return KDA_VERSION; }
+
+size_t kda_state_bytes(int H, int dk, int dv, kda_dtype dtype)
+{
+    if (H <= 0 || dk <= 0 || dv <= 0 || !valid_dtype(dtype)) return 0;
+    return (size_t)H * dk * dv * esize(dtype);
+}
+
+size_t kda_conv_state_bytes(int streams, int W, int C, kda_dtype dtype)
+{
+    if (streams <= 0 || W <= 1 || C <= 0 || !valid_dtype(dtype)) return 0;
+    return (size_t)streams * (W - 1) * C * esize(dtype);
+}
+
+// ---------------------------------------------------------------- decode
+int kda_decode_step(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                    kda_dtype in_dtype, int B, int H, int dk, int dv, float scale,
+                    float lower_bound, float* state, void* o, kda_dtype out_dtype,
+                    void* hip_stream)
+{
+    REQUIRE(q && k && v && g && beta && state && o, KDA_ERR_INVALID_ARG,
+            "kda_decode_step: null tensor pointer");
+    REQUIRE(valid_dtype(in_dtype) && valid_dtype(out_dtype), KDA_ERR_INVALID_ARG,
+            "kda_decode_step: bad dtype");
+    REQUIRE(B >= 1 && H >= 1, KDA_ERR_INVALID_ARG, "kda_decode_step: B and H must be >= 1");
+    REQUIRE(dk == 128 && dv == 128, KDA_ERR_UNSUPPORTED,
+            "kda_decode_step: only dk = dv = 128 is supported (got %d, %d)", dk, dv);
+    REQUIRE((int64_t)B * H <= 0x7fffffff, KDA_ERR_INVALID_ARG, "kda_decode_step: B*H too large");
+    for (const void* p : {q, k, v, g, beta, (const void*)state, (const void*)o})
+        REQUIRE(aligned16(p), KDA_ERR_INVALID_ARG, "kda_decode_step: pointers must be 16-byte aligned");
+    const size_t rows = (size_t)B * H;
+    const Range rs = rng(state, rows * 128 * 128 * 4), ro = rng(o, rows * 128 * esize(out_dtype));
+    for (Range r : {rng(q, rows * 128 * esize(in_dtype)), rng(k, rows * 128 * esize(in_dtype)),
+                    rng(v, rows * 128 * esize(in_dtype)), rng(g, rows * 128 * esize(in_dtype)),
+                    rng(beta, rows * esize(in_dtype))}) {
+        REQUIRE(!overlap(r, rs), KDA_ERR_INVALID_ARG, "kda_decode_step: state overlaps an input");
+        REQUIRE(!overlap(r, ro), KDA_ERR_INVALID_ARG, "kda_decode_step: o overlaps an input");
+    }
+    REQUIRE(!overlap(rs, ro), KDA_ERR_INVALID_ARG, "kda_decode_step: o overlaps state");
+
+    DecodeArgs a{q, k, v, g, beta, state, o, B, H, scale, lower_bound, (DType)in_dtype, (DType)out_dtype};
+    return hip_status(launch_decode(a, static_cast<hipStream_t>(hip_stream)), "kda_decode_step");
+}
+
+// ---------------------------------------------------------------- conv
+int kda_conv_state_update(const void* x, void* conv_state, const void* weight, const void* bias,
+                          kda_dtype dtype, int B, int C, int W, int apply_silu,
+                          int l2norm_group, float l2norm_eps, void* y, void* hip_stream)
+{
+    REQUIRE(x && conv_state && weight && y, KDA_ERR_INVALID_ARG, "kda_conv_state_update: null pointer");
+    REQUIRE(valid_dtype(dtype), KDA_ERR_INVALID_ARG, "kda_conv_state_update: bad dtype");
+    REQUIRE(B >= 1 && C >= 2, KDA_ERR_INVALID_ARG, "kda_conv_state_update: bad B or C");
+    REQUIRE(W >= 2 && W <= 8, KDA_ERR_UNSUPPORTED, "kda_conv_state_update: W must be in [2, 8] (got %d)", W);
+    REQUIRE(C % 128 == 0, KDA_ERR_UNSUPPORTED, "kda_conv_state_update: C must be a multiple of 128 (got %d)", C);
+    REQUIRE(l2norm_group == 0 || l2norm_group == 128, KDA_ERR_UNSUPPORTED,
+            "kda_conv_state_update: l2norm_group must be 0 or 128 (got %d)", l2norm_group);
+    for (const void* p : {x, (const void*)conv_state, weight, bias, (const void*)y})
+        REQUIRE(!p || aligned16(p), KDA_ERR_INVALID_ARG, "kda_conv_state_update: pointers must be 16-byte aligned");
+    const size_t es = esize(dtype);
+    const Range ry = rng(y, (size_t)B * C * es), rs = rng(conv_state, (size_t)B * (W - 1) * C * es);
+    const Range rx = rng(x, (size_t)B * C * es), rw = rng(weight, (size_t)C * W * es),
+                rb = rng(bias, bias ? (size_t)C * es : 0);
+    REQUIRE(!overlap(ry, rx) && !overlap(ry, rs) && !overlap(ry, rw) && !overlap(ry, rb),
+            KDA_ERR_INVALID_ARG, "kda_conv_state_update: y overlaps another tensor");
+    REQUIRE(!overlap(rs, rx) && !overlap(rs, rw) && !overlap(rs, rb), KDA_ERR_INVALID_ARG,
+            "kda_conv_state_update: conv_state overlaps an input");
+
+    ConvUpdateArgs a{x, conv_state, weight, bias, y, B, C, W, apply_silu ? 1 : 0, l2norm_group,
+                     l2norm_eps, (DType)dtype};
+    return hip_status(launch_conv_update(a, static_cast<hipStream_t>(hip_stream)), "kda_conv_state_update");
+}
+
+int kda_conv_prefill(const void* x, int64_t x_ld, int64_t num_tokens, int C, int W,
+                     const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int num_seqs,
+                     const void* weight, const void* bias, const void* conv_state_in,
+                     void* conv_state_out, int apply_silu, int l2norm_group, float l2norm_eps,
+                     void* y, int64_t y_ld, kda_dtype dtype, void* hip_stream)
+{
+    REQUIRE(x && weight && y, KDA_ERR_INVALID_ARG, "kda_conv_prefill: null pointer");
+    REQUIRE(valid_dtype(dtype), KDA_ERR_INVALID_ARG, "kda_conv_prefill: bad dtype");
+    REQUIRE(num_tokens >= 0 && C >= 2, KDA_ERR_INVALID_ARG, "kda_conv_prefill: bad num_tokens or C");
+    REQUIRE(W >= 2 && W <= 8, KDA_ERR_UNSUPPORTED, "kda_conv_prefill: W must be in [2, 8] (got %d)", W);
+    REQUIRE(C % 128 == 0, KDA_ERR_UNSUPPORTED, "kda_conv_prefill: C must be a multiple of 128 (got %d)", C);
+    REQUIRE(l2norm_group == 0 || l2norm_group == 128, KDA_ERR_UNSUPPORTED,
+            "kda_conv_prefill: l2norm_group must be 0 or 128 (got %d)", l2norm_group);
+    REQUIRE(x_ld >= C && y_ld >= C && x_ld % 8 == 0 && y_ld % 8 == 0, KDA_ERR_INVALID_ARG,
+            "kda_conv_prefill: x_ld and y_ld must be >= C and multiples of 8");
+    for (const void* p : {x, weight, bias, conv_state_in, (const void*)conv_state_out, (const void*)y})
+        REQUIRE(!p || aligned16(p), KDA_ERR_INVALID_ARG, "kda_conv_prefill: pointers must be 16-byte aligned");
+    int64_t seq_len = 0;
+    int rc = check_cu(cu_seqlens_dev, cu_seqlens_host, num_seqs, num_tokens, &seq_len);
+    if (rc != KDA_OK) return rc;
+    const size_t es = esize(dtype);
+    const size_t rows_bytes_y = num_tokens > 0 ? ((size_t)(num_tokens - 1) * y_ld + C) * es : 0;
+    const size_t rows_bytes_x = num_tokens > 0 ? ((size_t)(num_tokens - 1) * x_ld + C) * es : 0;
+    const size_t sbytes = (size_t)num_seqs * (W - 1) * C * es;
+    const Range ry = rng(y, rows_bytes_y), rx = rng(x, rows_bytes_x), rso = rng(conv_state_out, conv_state_out ? sbytes : 0),
+                rsi = rng(conv_state_in, conv_state_in ? sbytes : 0);
+    REQUIRE(!overlap(ry, rx) && !overlap(ry, rsi) && !overlap(ry, rso), KDA_ERR_INVALID_ARG,
+            "kda_conv_prefill: y overlaps an input or the output state");
+    REQUIRE(!overlap(rso, rx) && !overlap(rso, rsi), KDA_ERR_INVALID_ARG,
+            "kda_conv_prefill: conv_state_out overlaps x or conv_state_in");
+
+    ConvPrefillArgs a{};
+    a.x = x; a.x_ld = x_ld; a.y_ld = y_ld; a.num_tokens = num_tokens; a.C = C; a.W = W;
+    a.num_seqs = num_seqs; a.apply_silu = apply_silu ? 1 : 0; a.l2_group = l2norm_group;
+    a.seq_len = seq_len; a.cu_seqlens = cu_seqlens_dev; a.weight = weight; a.bias = bias;
+    a.state_in = conv_state_in; a.state_out = conv_state_out; a.y = y; a.l2_eps = l2norm_eps;
+    a.dtype = (DType)dtype;
+    return hip_status(launch_conv_prefill(a, static_cast<hipStream_t>(hip_stream)), "kda_conv_prefill");
+}
+
+// ---------------------------------------------------------------- gate / epilogue
+int kda_gate_prologue(const void* f, int64_t f_ld, const void* b, int64_t b_ld,
+                      const float* A_log, int64_t num_tokens, int H, int dk, float lower_bound,
+                      kda_dtype in_dtype, void* g_out, void* beta_out, kda_dtype out_dtype,
+                      void* hip_stream)
+{
+    REQUIRE(f && b && A_log && g_out && beta_out, KDA_ERR_INVALID_ARG, "kda_gate_prologue: null pointer");
+    REQUIRE(valid_dtype(in_dtype) && valid_dtype(out_dtype), KDA_ERR_INVALID_ARG, "kda_gate_prologue: bad dtype");
+    REQUIRE(num_tokens >= 0 && H >= 1, KDA_ERR_INVALID_ARG, "kda_gate_prologue: bad sizes");
+    REQUIRE(dk == 128, KDA_ERR_UNSUPPORTED, "kda_gate_prologue: only dk = 128 is supported");
+    REQUIRE(f_ld >= (int64_t)H * dk && f_ld % 8 == 0 && b_ld >= H, KDA_ERR_INVALID_ARG,
+            "kda_gate_prologue: f_ld must be >= H*dk and a multiple of 8; b_ld >= H");
+    for (const void* p : {f, b, (const void*)A_log, (const void*)g_out, (const void*)beta_out})
+        REQUIRE(aligned16(p), KDA_ERR_INVALID_ARG, "kda_gate_prologue: pointers must be 16-byte aligned");
+    const size_t ei = esize(in_dtype), eo = esize(out_dtype);
+    const Range rg = rng(g_out, (size_t)num_tokens * H * dk * eo), rb = rng(beta_out, (size_t)num_tokens * H * eo);
+    const Range rf = rng(f, num_tokens ? ((size_t)(num_tokens - 1) * f_ld + (size_t)H * dk) * ei : 0);
+    const Range rbi = rng(b, num_tokens ? ((size_t)(num_tokens - 1) * b_ld + H) * ei : 0);
+    REQUIRE(!overlap(rg, rf) && !overlap(rg, rbi) && !overlap(rb, rf) && !overlap(rb, rbi) && !overlap(rg, rb),
+            KDA_ERR_INVALID_ARG, "kda_gate_prologue: outputs overlap inputs or each other");
+    GateArgs a{f, b, f_ld, b_ld, num_tokens, A_log, g_out, beta_out, H, dk, lower_bound,
+               (DType)in_dtype, (DType)out_dtype};
+    return hip_status(launch_gate(a, static_cast<hipStream_t>(hip_stream)), "kda_gate_prologue");
+}
+
+int kda_output_norm_gate(const void* o, kda_dtype o_dtype, const void* gate, int64_t gate_ld,
+                         const float* norm_weight, int64_t num_tokens, int H, int dv, float eps,
+                         void* y, kda_dtype y_dtype, void* hip_stream)
+{
+    REQUIRE(o && gate && norm_weight && y, KDA_ERR_INVALID_ARG, "kda_output_norm_gate: null pointer");
+    REQUIRE(valid_dtype(o_dtype) && valid_dtype(y_dtype), KDA_ERR_INVALID_ARG, "kda_output_norm_gate: bad dtype");
+    REQUIRE(num_tokens >= 0 && H >= 1, KDA_ERR_INVALID_ARG, "kda_output_norm_gate: bad sizes");
+    REQUIRE(dv == 128, KDA_ERR_UNSUPPORTED, "kda_output_norm_gate: only dv = 128 is supported");
+    REQUIRE(gate_ld >= (int64_t)H * dv && gate_ld % 8 == 0, KDA_ERR_INVALID_ARG,
+            "kda_output_norm_gate: gate_ld must be >= H*dv and a multiple of 8");
+    for (const void* p : {o, gate, (const void*)norm_weight, (const void*)y})
+        REQUIRE(aligned16(p), KDA_ERR_INVALID_ARG, "kda_output_norm_gate: pointers must be 16-byte aligned");
+    const Range ry = rng(y, (size_t)num_tokens * H * dv * esize(y_dtype));
+    const Range ro = rng(o, (size_t)num_tokens * H * dv * esize(o_dtype));
+    const Range rgt = rng(gate, num_tokens ? ((size_t)(num_tokens - 1) * gate_ld + (size_t)H * dv) * esize(y_dtype) : 0);
+    REQUIRE(!overlap(ry, ro) && !overlap(ry, rgt), KDA_ERR_INVALID_ARG, "kda_output_norm_gate: y overlaps an input");
+    NormGateArgs a{o, gate, gate_ld, num_tokens, norm_weight, y, H, dv, eps, (DType)o_dtype, (DType)y_dtype};
+    return hip_status(launch_norm_gate(a, static_cast<hipStream_t>(hip_stream)), "kda_output_norm_gate");
+}
+
+// ---------------------------------------------------------------- prefill
+size_t kda_prefill_workspace_bytes(int64_t num_tokens, int num_seqs, int H, int dk, int dv,
+                                   kda_dtype in_dtype)
+{
+    (void)num_tokens; (void)num_seqs; (void)H; (void)dk; (void)dv; (void)in_dtype;
+    return 0;
+}
+
+int kda_prefill(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                kda_dtype in_dtype, int64_t num_tokens, int H, int dk, int dv,
+                const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int num_seqs,
+                float scale, float lower_bound, const float* initial_state, float* final_state,
+                void* o, kda_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                void* hip_stream)
+{
+    REQUIRE(valid_dtype(in_dtype) && valid_dtype(out_dtype), KDA_ERR_INVALID_ARG, "kda_prefill: bad dtype");
+    REQUIRE(num_tokens >= 0 && H >= 1, KDA_ERR_INVALID_ARG, "kda_prefill: bad num_tokens or H");
+    REQUIRE(dk == 128 && dv == 128, KDA_ERR_UNSUPPORTED,
+            "kda_prefill: only dk = dv = 128 is supported (got %d, %d)", dk, dv);
+    REQUIRE(num_tokens == 0 || (q && k && v && g && beta && o), KDA_ERR_INVALID_ARG,
+            "kda_prefill: null tensor pointer");
+    for (const void* p : {q, k, v, g, beta, (const void*)initial_state, (const void*)final_state, (const void*)o})
+        REQUIRE(!p || aligned16(p), KDA_ERR_INVALID_ARG, "kda_prefill: pointers must be 16-byte aligned");
+    int64_t seq_len = 0;
+    int rc = check_cu(cu_seqlens_dev, cu_seqlens_host, num_seqs, num_tokens, &seq_len);
+    if (rc != KDA_OK) return rc;
+    REQUIRE((int64_t)num_seqs * H * 2 <= 0x7fffffff, KDA_ERR_INVALID_ARG, "kda_prefill: num_seqs*H too large");
+    const size_t need = kda_prefill_workspace_bytes(num_tokens, num_seqs, H, dk, dv, in_dtype);
+    REQUIRE(workspace_bytes >= need && (need == 0 || workspace), KDA_ERR_WORKSPACE,
+            "kda_prefill: workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+
+    const size_t ei = esize(in_dtype), T = (size_t)num_tokens;
+    const size_t sbytes = (size_t)num_seqs * H * 128 * 128 * 4;
+    const Range ro = rng(o, T * H * 128 * esize(out_dtype));
+    const Range rs0 = rng(initial_state, initial_state ? sbytes : 0), rsT = rng(final_state, final_state ? sbytes : 0);
+    const Range ins[] = {rng(q, T * H * 128 * ei), rng(k, T * H * 128 * ei), rng(v, T * H * 128 * ei),
+                         rng(g, T * H * 128 * ei), rng(beta, T * H * ei), rs0};
+    for (const Range& r : ins) {
+        REQUIRE(!overlap(r, ro), KDA_ERR_INVALID_ARG, "kda_prefill: o overlaps an input");
+        if (r.p != rs0.p) REQUIRE(!overlap(r, rsT), KDA_ERR_INVALID_ARG, "kda_prefill: final_state overlaps an input");
+    }
+    REQUIRE(!overlap(ro, rsT), KDA_ERR_INVALID_ARG, "kda_prefill: o overlaps final_state");
+    REQUIRE(!overlap(rs0, rsT) || (initial_state == final_state), KDA_ERR_INVALID_ARG,
+            "kda_prefill: initial_state and final_state overlap without being the same buffer");
+
+    PrefillArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.cu_seqlens = cu_seqlens_dev; a.seq_len = seq_len;
+    a.s0 = initial_state; a.sT = final_state; a.o = o;
+    a.num_seqs = num_seqs; a.H = H; a.scale = scale; a.lower_bound = lower_bound;
+    a.in_dtype = (DType)in_dtype; a.out_dtype = (DType)out_dtype;
+    (void)workspace;
+    return hip_status(launch_prefill(a, static_cast<hipStream_t>(hip_stream)), "kda_prefill");
+}
+
+// ---------------------------------------------------------------- GEMM
+int kda_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+             int64_t M, int64_t N, int64_t K, kda_dtype ab_dtype, kda_dtype c_dtype,
+             void* hip_stream)
+{
+    REQUIRE(A && B && C, KDA_ERR_INVALID_ARG, "kda_gemm: null pointer");
+    REQUIRE(valid_dtype(ab_dtype) && valid_dtype(c_dtype), KDA_ERR_INVALID_ARG, "kda_gemm: bad dtype");
+    REQUIRE(ab_dtype == KDA_BF16, KDA_ERR_UNSUPPORTED, "kda_gemm: only bfloat16 A and B are supported");
+    REQUIRE(M >= 1 && N >= 1 && K >= 8, KDA_ERR_INVALID_ARG, "kda_gemm: bad sizes");
+    REQUIRE(K % 8 == 0, KDA_ERR_UNSUPPORTED, "kda_gemm: K must be a multiple of 8");
+    REQUIRE(lda >= K && ldb >= K && ldc >= N && lda % 8 == 0 && ldb % 8 == 0 && ldc % 4 == 0,
+            KDA_ERR_INVALID_ARG, "kda_gemm: lda, ldb >= K (multiples of 8), ldc >= N (multiple of 4)");
+    for (const void* p : {A, B, (const void*)C})
+        REQUIRE(aligned16(p), KDA_ERR_INVALID_ARG, "kda_gemm: pointers must be 16-byte aligned");
+    const Range rc = rng(C, ((size_t)(M - 1) * ldc + N) * esize(c_dtype));
+    REQUIRE(!overlap(rc, rng(A, ((size_t)(M - 1) * lda + K) * 2)) && !overlap(rc, rng(B, ((size_t)(N - 1) * ldb + K) * 2)),
+            KDA_ERR_INVALID_ARG, "kda_gemm: C overlaps A or B");
+    GemmArgs a{A, B, C, lda, ldb, ldc, M, N, K, (DType)c_dtype};
+    return hip_status(launch_gemm(a, static_cast<hipStream_t>(hip_stream)), "kda_gemm");
+}
+
+}  // extern "C"

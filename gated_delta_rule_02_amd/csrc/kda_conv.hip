@@ -1,0 +1,237 @@
+// kda_conv.hip -- causal depthwise short convolution (+SiLU, + per-group L2).
+//
+// "Ling-3.1-flash: Grouped Routing and Two Different MLA Caches" (flozi.net),
+// section "KDA replaces a token list with a recurrent matrix": each of the q,
+// k and v projections passes through its own causal convolution of width four
+// with SiLU; the same section has q and k normalised. Taps run oldest to
+// newest: weight[c, W-1] multiplies the current token, weight[c, 0] the token
+// W-1 steps back. Tokens before a sequence's first come from its conv state
+// (oldest first) or are zero.
+//
+// Both kernels are memory-bound elementwise passes. A wavefront owns one group
+// of 128 channels (two per lane, 4- or 8-byte accesses) so that the per-head L2
+// norm is a single wavefront reduction.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int kMaxW = 8;
+constexpr int kGroup = 128;     // channels per wavefront
+constexpr int kWaves = 4;       // wavefronts per workgroup
+constexpr int kTokTile = 16;    // tokens per workgroup (prefill)
+
+template <typename T>
+__device__ __forceinline__ void st2(T* p, float a, float b);
+template <>
+__device__ __forceinline__ void st2<float>(float* p, float a, float b)
+{
+    *reinterpret_cast<f32x2*>(p) = f32x2{a, b};
+}
+template <>
+__device__ __forceinline__ void st2<bf16_t>(bf16_t* p, float a, float b)
+{
+    *reinterpret_cast<uint32_t*>(p) = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+// Finish one output pair: activation, optional L2 over the wavefront's group.
+__device__ __forceinline__ f32x2 finish(f32x2 acc, int apply_silu, int l2, float eps)
+{
+    if (apply_silu) {
+        acc.x = siluf_(acc.x);
+        acc.y = siluf_(acc.y);
+    }
+    if (l2) {
+        const float ss = wave_sum(acc.x * acc.x + acc.y * acc.y);
+        const float r = rsqrtf(ss + eps);
+        acc.x *= r;
+        acc.y *= r;
+    }
+    return acc;
+}
+
+// ---------------------------------------------------------------- decode step
+template <typename T>
+__global__ __launch_bounds__(kWaves * 64) void conv_update_kernel(ConvUpdateArgs a)
+{
+    const int b = blockIdx.x;
+    const int grp = blockIdx.y * kWaves + (threadIdx.x >> 6);
+    if (grp * kGroup >= a.C) return;  // whole wavefront leaves together
+    const int c = grp * kGroup + 2 * (threadIdx.x & 63);
+    const int W = a.W;
+    const T* x = static_cast<const T*>(a.x) + (size_t)b * a.C;
+    T* st = static_cast<T*>(a.conv_state) + (size_t)b * (W - 1) * a.C;
+    const T* w = static_cast<const T*>(a.weight);
+
+    // window[j] = input j steps after the oldest kept one; window[W-1] = new x
+    f32x2 win[kMaxW];
+    const f32x2 xn = ld2(x + c);
+#pragma unroll
+    for (int j = 0; j < kMaxW; ++j) {
+        if (j < W - 1) win[j] = ld2(st + (size_t)j * a.C + c);
+        else if (j == W - 1) win[j] = xn;
+    }
+
+    f32x2 acc = {0.f, 0.f};
+    if (a.bias) acc = ld2(static_cast<const T*>(a.bias) + c);
+#pragma unroll
+    for (int j = 0; j < kMaxW; ++j)
+        if (j < W) {
+            acc.x += ld(w + (size_t)c * W + j) * win[j].x;
+            acc.y += ld(w + (size_t)(c + 1) * W + j) * win[j].y;
+        }
+    acc = finish(acc, a.apply_silu, a.l2_group != 0, a.l2_eps);
+    st2(static_cast<T*>(a.y) + (size_t)b * a.C + c, acc.x, acc.y);
+
+    // shift the window left by one and append the new input (values are
+    // exactly representable in T, so the stored bits are unchanged copies)
+#pragma unroll
+    for (int j = 0; j < kMaxW - 1; ++j)
+        if (j < W - 1) st2(st + (size_t)j * a.C + c, win[j + 1].x, win[j + 1].y);
+}
+
+// ---------------------------------------------------------------- prefill
+__device__ __forceinline__ int find_seq(const int32_t* cu, int num_seqs, int64_t t)
+{
+    // largest n with cu[n] <= t and cu[n+1] > t (skips empty sequences)
+    int lo = 0, hi = num_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((int64_t)cu[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kWaves * 64) void conv_prefill_kernel(ConvPrefillArgs a)
+{
+    const int grp = blockIdx.y * kWaves + (threadIdx.x >> 6);
+    if (grp * kGroup >= a.C) return;
+    const int c = grp * kGroup + 2 * (threadIdx.x & 63);
+    const int W = a.W;
+    const T* x = static_cast<const T*>(a.x);
+    const T* w = static_cast<const T*>(a.weight);
+    const T* sin = static_cast<const T*>(a.state_in);
+
+    float wc0[kMaxW], wc1[kMaxW];
+#pragma unroll
+    for (int j = 0; j < kMaxW; ++j)
+        if (j < W) {
+            wc0[j] = ld(w + (size_t)c * W + j);
+            wc1[j] = ld(w + (size_t)(c + 1) * W + j);
+        }
+    f32x2 bias = {0.f, 0.f};
+    if (a.bias) bias = ld2(static_cast<const T*>(a.bias) + c);
+
+    const int64_t t0 = (int64_t)blockIdx.x * kTokTile;
+    for (int i = 0; i < kTokTile; ++i) {
+        const int64_t t = t0 + i;
+        if (t >= a.num_tokens) break;
+        int n;
+        int64_t s;
+        if (a.cu_seqlens) {
+            n = find_seq(a.cu_seqlens, a.num_seqs, t);
+            s = a.cu_seqlens[n];
+        } else {
+            n = (int)(t / a.seq_len);
+            s = (int64_t)n * a.seq_len;
+        }
+        f32x2 acc = bias;
+#pragma unroll
+        for (int j = 0; j < kMaxW; ++j)
+            if (j < W) {
+                const int64_t p = t - (W - 1) + j;  // input position of tap j
+                f32x2 xv;
+                if (p >= s) {
+                    xv = ld2(x + p * a.x_ld + c);
+                } else if (sin) {
+                    // history row (W-1) - (s - p), oldest first
+                    xv = ld2(sin + ((size_t)n * (W - 1) + (size_t)((W - 1) - (s - p))) * a.C + c);
+                } else {
+                    xv = f32x2{0.f, 0.f};
+                }
+                acc.x += wc0[j] * xv.x;
+                acc.y += wc1[j] * xv.y;
+            }
+        acc = finish(acc, a.apply_silu, a.l2_group != 0, a.l2_eps);
+        st2(static_cast<T*>(a.y) + t * a.y_ld + c, acc.x, acc.y);
+    }
+}
+
+// Bit copies of two consecutive elements.
+__device__ __forceinline__ void copy2(float* d, const float* p) { *reinterpret_cast<uint2*>(d) = *reinterpret_cast<const uint2*>(p); }
+__device__ __forceinline__ void copy2(bf16_t* d, const bf16_t* p) { *reinterpret_cast<uint32_t*>(d) = *reinterpret_cast<const uint32_t*>(p); }
+__device__ __forceinline__ void zero2(float* d) { *reinterpret_cast<uint2*>(d) = make_uint2(0u, 0u); }
+__device__ __forceinline__ void zero2(bf16_t* d) { *reinterpret_cast<uint32_t*>(d) = 0u; }
+
+// Last W-1 inputs of each sequence (history included for short sequences).
+template <typename T>
+__global__ void conv_state_out_kernel(ConvPrefillArgs a)
+{
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // over N*(W-1)*C/2
+    const int W = a.W;
+    const int64_t pairs = (int64_t)a.C / 2;
+    const int64_t total = (int64_t)a.num_seqs * (W - 1) * pairs;
+    if (idx >= total) return;
+    const int c = (int)(idx % pairs) * 2;
+    const int j = (int)((idx / pairs) % (W - 1));
+    const int n = (int)(idx / (pairs * (W - 1)));
+    int64_t s, e;
+    if (a.cu_seqlens) {
+        s = a.cu_seqlens[n];
+        e = a.cu_seqlens[n + 1];
+    } else {
+        s = (int64_t)n * a.seq_len;
+        e = s + a.seq_len;
+    }
+    const int64_t p = e - (W - 1) + j;  // position of the j-th kept input
+    const T* x = static_cast<const T*>(a.x);
+    const T* sin = static_cast<const T*>(a.state_in);
+    T* so = static_cast<T*>(a.state_out) + ((size_t)n * (W - 1) + j) * a.C + c;
+    if (p >= s)
+        copy2(so, x + p * a.x_ld + c);
+    else if (sin)
+        copy2(so, sin + ((size_t)n * (W - 1) + (size_t)((W - 1) - (s - p))) * a.C + c);
+    else
+        zero2(so);
+}
+
+}  // namespace
+
+hipError_t launch_conv_update(const ConvUpdateArgs& a, hipStream_t s)
+{
+    dim3 grid((unsigned)a.B, (unsigned)((a.C + kGroup * kWaves - 1) / (kGroup * kWaves))), block(kWaves * 64);
+    if (a.dtype == F32)
+        hipLaunchKernelGGL(conv_update_kernel<float>, grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL(conv_update_kernel<bf16_t>, grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_conv_prefill(const ConvPrefillArgs& a, hipStream_t s)
+{
+    if (a.num_tokens > 0) {
+        dim3 grid((unsigned)((a.num_tokens + kTokTile - 1) / kTokTile),
+                  (unsigned)((a.C + kGroup * kWaves - 1) / (kGroup * kWaves))),
+            block(kWaves * 64);
+        if (a.dtype == F32)
+            hipLaunchKernelGGL(conv_prefill_kernel<float>, grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL(conv_prefill_kernel<bf16_t>, grid, block, 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (a.state_out) {
+        const int64_t total = (int64_t)a.num_seqs * (a.W - 1) * (a.C / 2);
+        dim3 grid((unsigned)((total + 255) / 256)), block(256);
+        if (a.dtype == F32)
+            hipLaunchKernelGGL(conv_state_out_kernel<float>, grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL(conv_state_out_kernel<bf16_t>, grid, block, 0, s, a);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+}  // namespace kda

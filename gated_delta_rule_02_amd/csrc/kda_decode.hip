@@ -1,0 +1,122 @@
+// kda_decode.hip -- one KDA decode step for a batch of sequences (gfx950).
+//
+// Per (sequence, head) the step is the recurrence of "Ling-3.1-flash: Grouped
+// Routing and Two Different MLA Caches" (flozi.net), section "KDA replaces a
+// token list with a recurrent matrix", for a single token:
+//   S' = Diag(alpha) S,   u = beta (v - S'^T k),   S = S' + k u^T,
+//   o  = scale S^T q = scale (S'^T q + u (k . q)).
+// The 128 x 128 float32 state (64 KiB) is the only large operand, so the kernel
+// is bound by HBM: it reads every state once into registers with 16-byte
+// coalesced loads, reduces the two column sums S'^T k and S'^T q across the
+// workgroup, and writes the state back once from the same registers.
+//
+// Workgroup = 256 threads = one (sequence, head). Thread t owns the 4 columns
+// 4*(t%32) .. +3 of the 16 rows r = t/32 + 8*i (i = 0..15): a wavefront's 64
+// lanes cover two whole rows, i.e. 1 KiB of contiguous state per load.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int D = 128;
+constexpr int kThreads = 256;
+constexpr int kRowsPerThread = 16;
+
+template <typename TIN, typename TOUT>
+__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a)
+{
+    const int bh = blockIdx.x;  // b * H + h
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = t >> 6;
+
+    __shared__ float s_alpha[D], s_k[D], s_q[D];
+    __shared__ float s_part[4][2][D];  // per-wave partial column sums (S'^T k, S'^T q)
+    __shared__ float s_u[D];
+    __shared__ float s_kq[2];
+
+    const TIN* q = static_cast<const TIN*>(a.q) + (size_t)bh * D;
+    const TIN* k = static_cast<const TIN*>(a.k) + (size_t)bh * D;
+    const TIN* g = static_cast<const TIN*>(a.g) + (size_t)bh * D;
+
+    // Issue the state loads first: they are the long-latency stream.
+    const int cg = t & 31;
+    const int rg = t >> 5;
+    float* Sp = a.state + (size_t)bh * D * D;
+    f32x4 s[kRowsPerThread];
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i)
+        s[i] = *reinterpret_cast<const f32x4*>(Sp + (size_t)(rg + 8 * i) * D + 4 * cg);
+
+    if (t < D) {
+        const float kv = ld(k + t), qv = ld(q + t);
+        s_k[t] = kv;
+        s_q[t] = qv;
+        s_alpha[t] = __expf(fmaxf(ld(g + t), a.lower_bound));
+        const float kq = wave_sum(kv * qv);
+        if (lane == 0) s_kq[wave] = kq;
+    }
+    __syncthreads();
+
+    // Retention on rows, then the two column sums over this thread's rows.
+    f32x4 pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i) {
+        const int r = rg + 8 * i;
+        s[i] *= s_alpha[r];
+        pk += s[i] * s_k[r];
+        pq += s[i] * s_q[r];
+    }
+    // lanes l and l^32 hold the same columns for adjacent row groups
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        pk[j] += __shfl_xor(pk[j], 32, 64);
+        pq[j] += __shfl_xor(pq[j], 32, 64);
+    }
+    if (lane < 32) {
+        *reinterpret_cast<f32x4*>(&s_part[wave][0][4 * cg]) = pk;
+        *reinterpret_cast<f32x4*>(&s_part[wave][1][4 * cg]) = pq;
+    }
+    __syncthreads();
+
+    if (t < D) {
+        const int j = t;
+        const float sk = (s_part[0][0][j] + s_part[1][0][j]) + (s_part[2][0][j] + s_part[3][0][j]);
+        const float sq = (s_part[0][1][j] + s_part[1][1][j]) + (s_part[2][1][j] + s_part[3][1][j]);
+        const float beta = ld(static_cast<const TIN*>(a.beta) + bh);
+        const float vj = ld(static_cast<const TIN*>(a.v) + (size_t)bh * D + j);
+        const float u = beta * (vj - sk);
+        s_u[j] = u;
+        const float kq = s_kq[0] + s_kq[1];
+        st(static_cast<TOUT*>(a.o) + (size_t)bh * D + j, a.scale * (sq + u * kq));
+    }
+    __syncthreads();
+
+    const f32x4 u4 = *reinterpret_cast<const f32x4*>(&s_u[4 * cg]);
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i) {
+        const int r = rg + 8 * i;
+        *reinterpret_cast<f32x4*>(Sp + (size_t)r * D + 4 * cg) = s[i] + s_k[r] * u4;
+    }
+}
+
+template <typename TIN>
+hipError_t launch_t(const DecodeArgs& a, hipStream_t s)
+{
+    dim3 grid((unsigned)((int64_t)a.B * a.H)), block(kThreads);
+    if (a.out_dtype == F32)
+        hipLaunchKernelGGL((decode_kernel<TIN, float>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((decode_kernel<TIN, bf16_t>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s)
+{
+    return a.in_dtype == F32 ? launch_t<float>(a, s) : launch_t<bf16_t>(a, s);
+}
+
+}  // namespace kda

@@ -1,0 +1,90 @@
+// kda_internal.h -- argument blocks and launchers shared by the host API and
+// the kernel translation units. Host validation happens in kda_api.cpp before
+// any launcher is called; launchers assume valid arguments.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+enum DType : int { F32 = 0, BF16 = 1 };
+
+struct DecodeArgs {
+    const void *q, *k, *v, *g, *beta;
+    float* state;  // [B, H, 128, 128] in place
+    void* o;
+    int B, H;
+    float scale, lower_bound;
+    DType in_dtype, out_dtype;
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+struct ConvUpdateArgs {
+    const void* x;
+    void* conv_state;
+    const void *weight, *bias;
+    void* y;
+    int B, C, W, apply_silu, l2_group;
+    float l2_eps;
+    DType dtype;
+};
+hipError_t launch_conv_update(const ConvUpdateArgs& a, hipStream_t s);
+
+struct ConvPrefillArgs {
+    const void* x;
+    int64_t x_ld, y_ld, num_tokens;
+    int C, W, num_seqs, apply_silu, l2_group;
+    int64_t seq_len;  // used when cu_seqlens is null: equal-length sequences
+    const int32_t* cu_seqlens;
+    const void *weight, *bias, *state_in;
+    void *state_out, *y;
+    float l2_eps;
+    DType dtype;
+};
+hipError_t launch_conv_prefill(const ConvPrefillArgs& a, hipStream_t s);
+
+struct GateArgs {
+    const void *f, *b;
+    int64_t f_ld, b_ld, num_tokens;
+    const float* A_log;
+    void *g_out, *beta_out;
+    int H, dk;
+    float lower_bound;
+    DType in_dtype, out_dtype;
+};
+hipError_t launch_gate(const GateArgs& a, hipStream_t s);
+
+struct NormGateArgs {
+    const void *o, *gate;
+    int64_t gate_ld, num_tokens;
+    const float* w;
+    void* y;
+    int H, dv;
+    float eps;
+    DType o_dtype, y_dtype;
+};
+hipError_t launch_norm_gate(const NormGateArgs& a, hipStream_t s);
+
+struct PrefillArgs {
+    const void *q, *k, *v, *g, *beta;
+    const int32_t* cu_seqlens;  // device, or null => equal lengths of seq_len
+    int64_t seq_len;
+    const float* s0;  // [N, H, 128, 128] or null
+    float* sT;        // [N, H, 128, 128] or null
+    void* o;
+    int num_seqs, H;
+    float scale, lower_bound;
+    DType in_dtype, out_dtype;
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+
+struct GemmArgs {
+    const void *A, *B;
+    void* C;
+    int64_t lda, ldb, ldc, M, N, K;
+    DType c_dtype;
+};
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+
+}  // namespace kda

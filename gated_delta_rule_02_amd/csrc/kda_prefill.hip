@@ -1,0 +1,439 @@
+// kda_prefill.hip -- chunked KDA prefill over packed sequences on gfx950 MFMA.
+//
+// Computes, per (sequence, head), the recurrence of "Ling-3.1-flash: Grouped
+// Routing and Two Different MLA Caches" (flozi.net), section "KDA replaces a
+// token list with a recurrent matrix" (retention per key channel, delta-rule
+// write, read after the write), reorganised exactly over chunks of C tokens.
+//
+// The chunk form. For a chunk with start state S0 (dk x dv) and tokens
+// r = 0..C-1, let b_r = sum_{j<=r} g_j (per key channel, here in base 2). Then
+//   A[r,i] = beta_r sum_c k_rc k_ic 2^(b_rc - b_ic)   (i < r)
+//   U      = (I + A)^-1 X,    X = diag(beta) (V - (K o 2^B) S0)
+//   P[r,i] = sum_c q_rc k_ic 2^(b_rc - b_ic)           (i <= r)
+//   O      = scale ((Q o 2^B) S0 + P U)
+//   S_C    = Diag(2^b_C) S0 + (K o 2^(b_C - B))^T U
+// U are the corrected writes u_r = beta_r (v_r - S'_r^T k_r) of all tokens of
+// the chunk; the triangular solve replaces the token-serial dependency.
+//
+// Overflow-safe factorisation. The chunk is cut into NB = C/16 blocks of 16
+// tokens. With rho_R the cumulative log-retention before block R, l_r the
+// inclusive prefix sum inside r's block, s_i the sum over the tokens after i in
+// i's block, and G_R the block total:
+//   b_r - b_i = l_r + (rho_R - rho_{I+1}) + s_i   (i in block I < R: all <= 0)
+//   b_r - b_i = l_r + s_i - G_R                   (i, r in the same block R)
+// Every factor 2^x of a block product then lies in [2^-116, 2^116] because the
+// log-retention is clamped at -5 ("safe forget gate ... lower bound -5" in the
+// flozi.net section above): 15 tokens x 5 x log2(e) < 116 < 127.
+//
+// Work split. A workgroup (4 wavefronts) owns one (sequence, head, 64 value
+// columns); wavefront w owns 16 columns and keeps its 128 x 16 float32 slice
+// of the state in registers for the whole sequence (value columns of the state
+// evolve independently). Per chunk the workgroup stages the key-side operands
+// in LDS, each wavefront computes some of the 16 x 16 blocks of A and P and
+// one diagonal block inverse, then every wavefront runs its own value-side
+// chain (X, block forward substitution, O, state update) on MFMA without
+// further synchronisation.
+//
+// Precision (bfloat16 inputs): the key-side operands are staged in LDS as
+// float32 and rounded once per use. Off-diagonal blocks and the whole value
+// side run float16 MFMA (their operands are bounded by 1 or by the state and
+// value magnitudes, so float16's range suffices and its 11-bit significand
+// keeps the error well inside the bound); A's diagonal blocks use bfloat16
+// (their right operand reaches 2^116); P's diagonal blocks use a hi+lo
+// bfloat16 split (3 MFMAs) because they dominate the output error otherwise.
+// Accumulation, the state and all exponents are float32. Float32 inputs run a
+// float32-MFMA variant with 32-token chunks.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int D = 128;        // dk = dv
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kDvBlock = 16 * kWaves;  // value columns per workgroup
+constexpr int kDvBlocks = D / kDvBlock;
+
+// ---------------------------------------------------------------- MFMA ops
+// One K16 slab: lane (m = lane%16, q = lane/16) holds A[m][4q..4q+3] and
+// B[4q..4q+3][n = lane%16]; the 16 x 16 result holds C[4q+i][n] in element i.
+__device__ __forceinline__ f32x4 mma16_f16(f16x4 a, f16x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16_bf16(i16x4 a, i16x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16_f32(f32x4 a, f32x4 b, f32x4 c)
+{
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, c, 0, 0, 0);
+    return c;
+}
+
+__device__ __forceinline__ i16x4 to_bf16x4(f32x4 x)
+{
+    return i16x4{(short)f32_to_bf16(x.x), (short)f32_to_bf16(x.y), (short)f32_to_bf16(x.z),
+                 (short)f32_to_bf16(x.w)};
+}
+__device__ __forceinline__ f32x4 from_bf16x4(i16x4 x)
+{
+    return f32x4{bf16_to_f32((bf16_t)x.x), bf16_to_f32((bf16_t)x.y), bf16_to_f32((bf16_t)x.z),
+                 bf16_to_f32((bf16_t)x.w)};
+}
+
+template <bool F32P> struct Ops;
+
+template <> struct Ops<false> {  // bfloat16 inputs
+    using OT = _Float16;
+    using frag = f16x4;
+    static constexpr int C = 64;
+    static constexpr int PAD = 8;
+    __device__ static frag cvt(f32x4 x)
+    {
+        return f16x4{(_Float16)x.x, (_Float16)x.y, (_Float16)x.z, (_Float16)x.w};
+    }
+    __device__ static f32x4 unpack(frag x) { return f32x4{(float)x.x, (float)x.y, (float)x.z, (float)x.w}; }
+    __device__ static frag lda(const OT* p) { return *reinterpret_cast<const f16x4*>(p); }
+    __device__ static f32x4 mma(frag a, frag b, f32x4 c) { return mma16_f16(a, b, c); }
+    // diagonal blocks: A single bfloat16, P hi+lo bfloat16 split
+    __device__ static f32x4 diagA(f32x4 a, f32x4 b, f32x4 c) { return mma16_bf16(to_bf16x4(a), to_bf16x4(b), c); }
+    __device__ static f32x4 diagP(f32x4 a, f32x4 b, f32x4 c)
+    {
+        const i16x4 ah = to_bf16x4(a), bh = to_bf16x4(b);
+        const i16x4 al = to_bf16x4(a - from_bf16x4(ah)), bl = to_bf16x4(b - from_bf16x4(bh));
+        c = mma16_bf16(ah, bh, c);
+        c = mma16_bf16(ah, bl, c);
+        c = mma16_bf16(al, bh, c);
+        return c;
+    }
+};
+
+template <> struct Ops<true> {  // float32 inputs
+    using OT = float;
+    using frag = f32x4;
+    static constexpr int C = 32;
+    static constexpr int PAD = 4;
+    __device__ static frag cvt(f32x4 x) { return x; }
+    __device__ static f32x4 unpack(frag x) { return x; }
+    __device__ static frag lda(const OT* p) { return *reinterpret_cast<const f32x4*>(p); }
+    __device__ static f32x4 mma(frag a, frag b, f32x4 c) { return mma16_f32(a, b, c); }
+    __device__ static f32x4 diagA(f32x4 a, f32x4 b, f32x4 c) { return mma16_f32(a, b, c); }
+    __device__ static f32x4 diagP(f32x4 a, f32x4 b, f32x4 c) { return mma16_f32(a, b, c); }
+};
+
+__device__ __forceinline__ f32x4 ld4f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+// index of the off-diagonal block pair (R, I), I < R
+__host__ __device__ constexpr int pair_id(int R, int I) { return R * (R - 1) / 2 + I; }
+// index of the lower-triangle block (R, I), I <= R
+__host__ __device__ constexpr int tri_id(int R, int I) { return R * (R + 1) / 2 + I; }
+
+template <bool F32P, typename TIN>
+struct __attribute__((aligned(16))) Smem {
+    using OT = typename Ops<F32P>::OT;
+    static constexpr int C = Ops<F32P>::C;
+    static constexpr int NB = C / 16;
+    static constexpr int NPAIR = NB * (NB - 1) / 2;
+    static constexpr int LDK = D + 4;               // row stride of the float [C][128] arrays
+    static constexpr int LDT = C + Ops<F32P>::PAD;  // row stride of [128][C]
+    static constexpr int LDV = kDvBlock + 8;
+    // Key-side operands stay float32: their factors span 2^-116 .. 1 and the
+    // diagonal blocks rescale them by up to 2^116, beyond float16's range.
+    // Each use rounds once to the MFMA operand type.
+    float KL[C][LDK];  // k o 2^l         (left operand of A; X)
+    float QL[C][LDK];  // q o 2^l         (left operand of P; O)
+    float KS[C][LDK];  // k o 2^s         (right operand of A and P)
+    OT KbT[D][LDT];    // (k o 2^(b_C - b))^T   (state update)
+    OT Nd[NB][16][16];          // -A diagonal blocks (strictly lower, beta-scaled)
+    OT Tb[NB][16][16];          // (I + A_RR)^-1
+    OT An[NPAIR > 0 ? NPAIR : 1][16][16];  // -A off-diagonal blocks
+    OT Pb[NB * (NB + 1) / 2][16][16];      // P lower-triangle blocks
+    TIN V[C][LDV];              // values of this workgroup's 64 columns (as stored)
+    float Dr[NB][D];            // 2^rho_R
+    float Fd[NB][D];            // 2^-G_R
+    float Fo[NPAIR > 0 ? NPAIR : 1][D];    // 2^(rho_R - rho_{I+1})
+    float Gt[NB][D];            // block totals (exchange)
+    float bC[D];                // 2^b_C
+    float beta[C];
+};
+
+template <bool F32P, typename TIN, typename TOUT>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
+{
+    using O = Ops<F32P>;
+    using OT = typename O::OT;
+    using frag = typename O::frag;
+    using SM = Smem<F32P, TIN>;
+    constexpr int C = SM::C;
+    constexpr int NB = SM::NB;
+    constexpr int NPAIR = SM::NPAIR;
+
+    __shared__ SM sm;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int m16 = lane & 15;
+    const int q4 = lane >> 4;
+
+    int bid = blockIdx.x;
+    const int dvblk = bid % kDvBlocks;
+    bid /= kDvBlocks;
+    const int h = bid % a.H;
+    const int n = bid / a.H;
+    const int jcol = dvblk * kDvBlock + wave * 16 + m16;  // this lane's value column
+
+    int64_t seq_s, seq_e;
+    if (a.cu_seqlens) {
+        seq_s = a.cu_seqlens[n];
+        seq_e = a.cu_seqlens[n + 1];
+    } else {
+        seq_s = (int64_t)n * a.seq_len;
+        seq_e = seq_s + a.seq_len;
+    }
+
+    // state slice: S[t][i] = S[16t + 4q + i][jcol]
+    f32x4 S[8];
+    const size_t sbase = ((size_t)n * a.H + h) * D * D;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            S[t][i] = a.s0 ? a.s0[sbase + (size_t)(16 * t + 4 * q4 + i) * D + jcol] : 0.0f;
+
+    const int64_t tok_stride = (int64_t)a.H * D;
+    const TIN* qg = static_cast<const TIN*>(a.q) + (int64_t)h * D;
+    const TIN* kg = static_cast<const TIN*>(a.k) + (int64_t)h * D;
+    const TIN* gg = static_cast<const TIN*>(a.g) + (int64_t)h * D;
+    const TIN* vg = static_cast<const TIN*>(a.v) + (int64_t)h * D + dvblk * kDvBlock;
+    const TIN* bg = static_cast<const TIN*>(a.beta) + h;
+    TOUT* og = static_cast<TOUT*>(a.o) + (int64_t)h * D + jcol;
+    const float lb = a.lower_bound;
+
+    for (int64_t cs = seq_s; cs < seq_e; cs += C) {
+        const int ntok = (int)min<int64_t>(C, seq_e - cs);
+
+        // ---------------- phase 1a: per-block prefix/suffix sums and operands
+        // thread = (channel pair c0, c0+1; block R = wave)
+        const int R = wave;
+        const int c0 = 2 * lane;
+        f32x2 ks[16];  // k o 2^s, kept for the transposed state-update operand
+        if (R < NB) {
+            f32x2 kk[16], qq[16], g2[16];
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const int r = 16 * R + rr;
+                if (r < ntok) {
+                    const int64_t off = (cs + r) * tok_stride + c0;
+                    kk[rr] = ld2(kg + off);
+                    qq[rr] = ld2(qg + off);
+                    const f32x2 gv = ld2(gg + off);
+                    g2[rr] = f32x2{fmaxf(gv.x, lb) * kLog2e, fmaxf(gv.y, lb) * kLog2e};
+                } else {
+                    kk[rr] = qq[rr] = g2[rr] = f32x2{0.f, 0.f};
+                }
+            }
+            f32x2 l = {0.f, 0.f};
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                l += g2[rr];
+                const f32x2 e = {exp2_fast(l.x), exp2_fast(l.y)};
+                const int r = 16 * R + rr;
+                *reinterpret_cast<f32x2*>(&sm.KL[r][c0]) = kk[rr] * e;
+                *reinterpret_cast<f32x2*>(&sm.QL[r][c0]) = qq[rr] * e;
+            }
+            sm.Gt[R][c0] = l.x;
+            sm.Gt[R][c0 + 1] = l.y;
+            f32x2 s = {0.f, 0.f};  // sum over tokens after rr in the block
+#pragma unroll
+            for (int rr = 15; rr >= 0; --rr) {
+                ks[rr] = f32x2{kk[rr].x * exp2_fast(s.x), kk[rr].y * exp2_fast(s.y)};
+                const int r = 16 * R + rr;
+                *reinterpret_cast<f32x2*>(&sm.KS[r][c0]) = ks[rr];
+                s += g2[rr];
+            }
+        }
+        if (tid < C) sm.beta[tid] = tid < ntok ? ld(bg + (cs + tid) * a.H) : 0.0f;
+        {   // values of the 64 columns: thread -> column pair cp, rows t/32 + 8i
+            const int cp = tid & 31;
+#pragma unroll
+            for (int i = 0; i < C / 8; ++i) {
+                const int r = (tid >> 5) + 8 * i;
+                if (r < ntok) {
+                    sm.V[r][2 * cp] = vg[(cs + r) * tok_stride + 2 * cp];
+                    sm.V[r][2 * cp + 1] = vg[(cs + r) * tok_stride + 2 * cp + 1];
+                } else {
+                    sm.V[r][2 * cp] = sm.V[r][2 * cp + 1] = TIN(0);
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---------------- phase 1b: cross-block factors, transposed K-bar
+        if (R < NB) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int c = c0 + e;
+                float rho[NB + 1];
+                rho[0] = 0.f;
+#pragma unroll
+                for (int J = 0; J < NB; ++J) rho[J + 1] = rho[J] + sm.Gt[J][c];
+                sm.Dr[R][c] = exp2_fast(rho[R]);
+                sm.Fd[R][c] = exp2_fast(-sm.Gt[R][c]);
+#pragma unroll
+                for (int I = 0; I < NB; ++I)
+                    if (I < R) sm.Fo[pair_id(R, I)][c] = exp2_fast(rho[R] - rho[I + 1]);
+                if (R == 0) sm.bC[c] = exp2_fast(rho[NB]);
+                const float fb = exp2_fast(rho[NB] - rho[R + 1]);
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr)
+                    sm.KbT[c][16 * R + rr] = (OT)((e == 0 ? ks[rr].x : ks[rr].y) * fb);
+            }
+        }
+        __syncthreads();
+
+        // ---------------- phase 2: blocks of A and P; diagonal inverses
+        if (wave < NB) {
+            const int Rd = wave;
+            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int c = 16 * t + 4 * q4;
+                const f32x4 kl = ld4f(&sm.KL[16 * Rd + m16][c]);
+                const f32x4 ql = ld4f(&sm.QL[16 * Rd + m16][c]);
+                const f32x4 x = ld4f(&sm.KS[16 * Rd + m16][c]) * ld4f(&sm.Fd[Rd][c]);
+                accA = O::diagA(kl, x, accA);
+                accP = O::diagP(ql, x, accP);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 4 * q4 + i;  // row in block, column m16
+                const float b = sm.beta[16 * Rd + row];
+                sm.Nd[Rd][row][m16] = (OT)(row > m16 ? -accA[i] * b : 0.0f);
+                sm.Pb[tri_id(Rd, Rd)][row][m16] = (OT)(row >= m16 ? accP[i] : 0.0f);
+            }
+            // wavefront-local: the inverse below reads what this wavefront wrote
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            // (I + N)^-1 = sum_{j<16} (-N)^j  (N strictly lower, N^16 = 0), Horner form
+            const frag nA = O::lda(&sm.Nd[Rd][m16][4 * q4]);
+            f32x4 eye;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) eye[i] = (4 * q4 + i == m16) ? 1.0f : 0.0f;
+            f32x4 Y = eye;
+#pragma unroll
+            for (int it = 0; it < 15; ++it) Y = O::mma(nA, O::cvt(Y), eye);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm.Tb[Rd][4 * q4 + i][m16] = (OT)Y[i];
+        }
+        // off-diagonal pairs, spread over the wavefronts
+#pragma unroll
+        for (int Rr = 1; Rr < NB; ++Rr)
+#pragma unroll
+            for (int I = 0; I < Rr; ++I) {
+                if (pair_id(Rr, I) % kWaves != wave) continue;
+                const int pid = pair_id(Rr, I);
+                f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const int c = 16 * t + 4 * q4;
+                    const frag kl = O::cvt(ld4f(&sm.KL[16 * Rr + m16][c]));
+                    const frag ql = O::cvt(ld4f(&sm.QL[16 * Rr + m16][c]));
+                    const frag b = O::cvt(ld4f(&sm.KS[16 * I + m16][c]) * ld4f(&sm.Fo[pid][c]));
+                    accA = O::mma(kl, b, accA);
+                    accP = O::mma(ql, b, accP);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 4 * q4 + i;
+                    sm.An[pid][row][m16] = (OT)(-accA[i] * sm.beta[16 * Rr + row]);
+                    sm.Pb[tri_id(Rr, I)][row][m16] = (OT)accP[i];
+                }
+            }
+        __syncthreads();
+
+        // ---------------- phase 3: value side, one 16-column tile per wavefront
+        f32x4 X[NB], O1[NB], U[NB];
+        frag UB[NB];
+#pragma unroll
+        for (int Rr = 0; Rr < NB; ++Rr) {
+            f32x4 accX = {0.f, 0.f, 0.f, 0.f}, accO = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int c = 16 * t + 4 * q4;
+                const frag sb = O::cvt(S[t] * ld4f(&sm.Dr[Rr][c]));
+                accX = O::mma(O::cvt(ld4f(&sm.KL[16 * Rr + m16][c])), sb, accX);
+                accO = O::mma(O::cvt(ld4f(&sm.QL[16 * Rr + m16][c])), sb, accO);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * Rr + 4 * q4 + i;
+                X[Rr][i] = sm.beta[r] * (ld(&sm.V[r][wave * 16 + m16]) - accX[i]);
+            }
+            O1[Rr] = accO;
+        }
+        // block forward substitution: U_R = T_RR (X_R - sum_{I<R} A_RI U_I)
+#pragma unroll
+        for (int Rr = 0; Rr < NB; ++Rr) {
+            f32x4 Y = X[Rr];
+#pragma unroll
+            for (int I = 0; I < Rr; ++I) Y = O::mma(O::lda(&sm.An[pair_id(Rr, I)][m16][4 * q4]), UB[I], Y);
+            U[Rr] = O::mma(O::lda(&sm.Tb[Rr][m16][4 * q4]), O::cvt(Y), f32x4{0.f, 0.f, 0.f, 0.f});
+            UB[Rr] = O::cvt(U[Rr]);
+        }
+        // outputs O_R = scale (O1_R + sum_{I<=R} P_RI U_I)
+#pragma unroll
+        for (int Rr = 0; Rr < NB; ++Rr) {
+            f32x4 acc = O1[Rr];
+#pragma unroll
+            for (int I = 0; I <= Rr; ++I) acc = O::mma(O::lda(&sm.Pb[tri_id(Rr, I)][m16][4 * q4]), UB[I], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * Rr + 4 * q4 + i;
+                if (r < ntok) st(og + (cs + r) * tok_stride, a.scale * acc[i]);
+            }
+        }
+        // state: S <- Diag(2^b_C) S + Kbar^T U
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            f32x4 acc = S[t] * ld4f(&sm.bC[16 * t + 4 * q4]);
+#pragma unroll
+            for (int Rr = 0; Rr < NB; ++Rr) acc = O::mma(O::lda(&sm.KbT[16 * t + m16][16 * Rr + 4 * q4]), UB[Rr], acc);
+            S[t] = acc;
+        }
+        __syncthreads();
+    }
+
+    if (a.sT) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a.sT[sbase + (size_t)(16 * t + 4 * q4 + i) * D + jcol] = S[t][i];
+    }
+}
+
+template <bool F32P, typename TIN>
+hipError_t launch_t(const PrefillArgs& a, hipStream_t s)
+{
+    dim3 grid((unsigned)((int64_t)a.num_seqs * a.H * kDvBlocks)), block(kThreads);
+    if (a.out_dtype == F32)
+        hipLaunchKernelGGL((prefill_kernel<F32P, TIN, float>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((prefill_kernel<F32P, TIN, bf16_t>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s)
+{
+    return a.in_dtype == F32 ? launch_t<true, float>(a, s) : launch_t<false, bf16_t>(a, s);
+}
+
+}  // namespace kda

@@ -1,0 +1,231 @@
+"""Thin Python binding of the C ABI in ``include/kda.h`` (ctypes).
+
+Each function has the name of the C entry point it calls and only marshals
+arguments: torch tensors become device pointers and sizes, the current HIP
+stream is passed through, and a non-OK status raises ``KDAError`` with the
+library's message. All computation happens in ``libkda.so``; if the library is
+not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = 0, -1, -2, -3, -4
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+_SIGS = {
+    "kda_prefill": (_I, [_P] * 5 + [_I, _I64, _I, _I, _I, _P, _P, _I, _F, _F, _P, _P, _P, _I, _P, _SZ, _P]),
+    "kda_prefill_workspace_bytes": (_SZ, [_I64, _I, _I, _I, _I, _I]),
+    "kda_decode_step": (_I, [_P] * 5 + [_I, _I, _I, _I, _I, _F, _F, _P, _P, _I, _P]),
+    "kda_conv_state_update": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P]),
+    "kda_conv_prefill": (_I, [_P, _I64, _I64, _I, _I, _P, _P, _I, _P, _P, _P, _P, _I, _I, _F, _P, _I64, _I, _P]),
+    "kda_gate_prologue": (_I, [_P, _I64, _P, _I64, _P, _I64, _I, _I, _F, _I, _P, _P, _I, _P]),
+    "kda_output_norm_gate": (_I, [_P, _I, _P, _I64, _P, _I64, _I, _I, _F, _P, _I, _P]),
+    "kda_gemm": (_I, [_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _I, _I, _P]),
+    "kda_state_bytes": (_SZ, [_I, _I, _I, _I]),
+    "kda_conv_state_bytes": (_SZ, [_I, _I, _I, _I]),
+    "kda_last_error": (ctypes.c_char_p, []),
+    "kda_version": (_I, []),
+}
+EXPORTED = tuple(_SIGS)
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    def __init__(self, name, status, message):
+        super().__init__("%s failed with status %d: %s" % (name, status, message))
+        self.status = status
+
+
+def lib():
+    """Load libkda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libkda.so is not built (expected at %s); run __graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _call(name, *args):
+    rc = getattr(lib(), name)(*args)
+    if rc != KDA_OK:
+        raise KDAError(name, rc, lib().kda_last_error().decode())
+    return rc
+
+
+def _dt(t):
+    if t.dtype == torch.float32:
+        return KDA_F32
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    raise TypeError("unsupported dtype %s (float32 or bfloat16 expected)" % t.dtype)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on a GPU device")
+    return t.data_ptr()
+
+
+def _dense(t, name):
+    if t is not None and not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _cu(cu_seqlens, cu_seqlens_host):
+    if cu_seqlens is None:
+        return None, None, None
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    host = cu_seqlens_host
+    if host is None:
+        host = cu_seqlens.cpu()  # one device->host copy when no mirror is given
+    host = host.to(torch.int32).contiguous()
+    return _ptr(_dense(cu_seqlens, "cu_seqlens")), host.data_ptr(), host
+
+
+# --------------------------------------------------------------------------
+def kda_prefill(q, k, v, g, beta, o, cu_seqlens=None, cu_seqlens_host=None, num_seqs=None,
+                initial_state=None, final_state=None, scale=1.0, lower_bound=-5.0,
+                workspace=None, stream=None):
+    """KDA core over packed sequences. q,k,g [T,H,128], v [T,H,128], beta [T,H]
+    (one dtype), o [T,H,128] (float32 or bfloat16), states float32 [N,H,128,128]."""
+    for n_, t_ in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("o", o),
+                   ("initial_state", initial_state), ("final_state", final_state)):
+        _dense(t_, n_)
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    cu_dev, cu_host, keep = _cu(cu_seqlens, cu_seqlens_host)
+    if num_seqs is None:
+        num_seqs = (keep.numel() - 1) if keep is not None else 1
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _call("kda_prefill", _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dt(q), T, H, dk, dv,
+          cu_dev, cu_host, num_seqs, scale, lower_bound, _ptr(initial_state), _ptr(final_state),
+          _ptr(o), _dt(o), _ptr(workspace), ws_bytes, _stream(stream))
+    return o
+
+
+def kda_prefill_workspace_bytes(num_tokens, num_seqs, H, dk=128, dv=128, in_dtype=KDA_BF16):
+    return lib().kda_prefill_workspace_bytes(num_tokens, num_seqs, H, dk, dv, in_dtype)
+
+
+def kda_decode_step(q, k, v, g, beta, state, o, scale=1.0, lower_bound=-5.0, stream=None):
+    """One token per sequence. q,k,g,v [B,H,128], beta [B,H]; state float32
+    [B,H,128,128] updated in place; o [B,H,128]."""
+    for n_, t_ in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("state", state), ("o", o)):
+        _dense(t_, n_)
+    B, H, dk = q.shape
+    dv = v.shape[2]
+    _call("kda_decode_step", _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dt(q), B, H, dk, dv,
+          scale, lower_bound, _ptr(state), _ptr(o), _dt(o), _stream(stream))
+    return o
+
+
+def kda_conv_state_update(x, conv_state, weight, y, bias=None, apply_silu=True, l2norm_group=0,
+                          l2norm_eps=1e-6, stream=None):
+    """x [B,C], conv_state [B,W-1,C] (in place), weight [C,W], y [B,C]."""
+    for n_, t_ in (("x", x), ("conv_state", conv_state), ("weight", weight), ("y", y), ("bias", bias)):
+        _dense(t_, n_)
+    B, C = x.shape
+    W = weight.shape[1]
+    _call("kda_conv_state_update", _ptr(x), _ptr(conv_state), _ptr(weight), _ptr(bias), _dt(x), B, C, W,
+          int(bool(apply_silu)), l2norm_group, l2norm_eps, _ptr(y), _stream(stream))
+    return y
+
+
+def kda_conv_prefill(x, weight, y, cu_seqlens=None, cu_seqlens_host=None, num_seqs=None, bias=None,
+                     conv_state_in=None, conv_state_out=None, apply_silu=True, l2norm_group=0,
+                     l2norm_eps=1e-6, stream=None):
+    """x rows [T, >=C] (row stride x.stride(0)), weight [C,W], y rows [T, >=C]."""
+    for n_, t_ in (("weight", weight), ("bias", bias), ("conv_state_in", conv_state_in),
+                   ("conv_state_out", conv_state_out)):
+        _dense(t_, n_)
+    if x.stride(1) != 1 or y.stride(1) != 1:
+        raise ValueError("x and y rows must be contiguous")
+    T = x.shape[0]
+    C, W = weight.shape
+    cu_dev, cu_host, keep = _cu(cu_seqlens, cu_seqlens_host)
+    if num_seqs is None:
+        num_seqs = (keep.numel() - 1) if keep is not None else 1
+    _call("kda_conv_prefill", _ptr(x), x.stride(0), T, C, W, cu_dev, cu_host, num_seqs, _ptr(weight),
+          _ptr(bias), _ptr(conv_state_in), _ptr(conv_state_out), int(bool(apply_silu)), l2norm_group,
+          l2norm_eps, _ptr(y), y.stride(0), _dt(x), _stream(stream))
+    return y
+
+
+def kda_gate_prologue(f, b, A_log, g_out, beta_out, H, dk=128, lower_bound=-5.0, stream=None):
+    """f rows [T, >=H*dk], b rows [T, >=H], A_log float32 [H]; g_out [T,H,dk], beta_out [T,H]."""
+    _dense(A_log, "A_log"); _dense(g_out, "g_out"); _dense(beta_out, "beta_out")
+    if f.stride(-1) != 1 or b.stride(-1) != 1:
+        raise ValueError("f and b rows must be contiguous")
+    T = f.shape[0]
+    _call("kda_gate_prologue", _ptr(f), f.stride(0), _ptr(b), b.stride(0), _ptr(A_log), T, H, dk,
+          lower_bound, _dt(f), _ptr(g_out), _ptr(beta_out), _dt(g_out), _stream(stream))
+    return g_out, beta_out
+
+
+def kda_output_norm_gate(o, gate, norm_weight, y, eps=1e-6, stream=None):
+    """o [T,H,dv], gate rows [T, >=H*dv] (dtype of y), norm_weight float32 [dv], y [T,H*dv]."""
+    _dense(o, "o"); _dense(norm_weight, "norm_weight"); _dense(y, "y")
+    if gate.stride(-1) != 1:
+        raise ValueError("gate rows must be contiguous")
+    T, H, dv = o.shape
+    _call("kda_output_norm_gate", _ptr(o), _dt(o), _ptr(gate), gate.stride(0), _ptr(norm_weight), T, H,
+          dv, eps, _ptr(y), _dt(y), _stream(stream))
+    return y
+
+
+def kda_gemm(A, B, C, stream=None):
+    """C[M,N] = A[M,K] B[N,K]^T (rows may be strided; last dims contiguous)."""
+    for n_, t_ in (("A", A), ("B", B), ("C", C)):
+        if t_.stride(-1) != 1:
+            raise ValueError("%s rows must be contiguous" % n_)
+    M, K = A.shape
+    N = B.shape[0]
+    _call("kda_gemm", _ptr(A), A.stride(0), _ptr(B), B.stride(0), _ptr(C), C.stride(0), M, N, K,
+          _dt(A), _dt(C), _stream(stream))
+    return C
+
+
+def kda_state_bytes(H, dk=128, dv=128, dtype=KDA_F32):
+    return lib().kda_state_bytes(H, dk, dv, dtype)
+
+
+def kda_conv_state_bytes(streams, W, C, dtype=KDA_BF16):
+    return lib().kda_conv_state_bytes(streams, W, C, dtype)
+
+
+def kda_last_error():
+    return lib().kda_last_error().decode()
+
+
+def kda_version():
+    return lib().kda_version()

@@ -1,0 +1,236 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention token-mixer library.
+ *
+ * What the library computes is the KDA mixer described on
+ *   "Ling-3.1-flash: Grouped Routing and Two Different MLA Caches" (flozi.net),
+ *   section "KDA replaces a token list with a recurrent matrix":
+ * q/k/v projections of width 64 x 128, a causal width-4 short convolution with
+ * SiLU per stream, normalised q and k, channel-dependent retention and a
+ * delta-rule write into a per-head recurrent matrix, a read with the query, and
+ * an output normalisation times a sigmoid gate before the output projection.
+ * Per head, with the state S of shape dk x dv (rows are key channels):
+ *
+ *   S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ *   o_t = scale * S_t^T q_t,          alpha_t = exp(max(g_t, lower_bound)).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers are caller-owned DEVICE pointers (allocated by the caller, e.g. by
+ *   PyTorch), except those named *_host. The library allocates no memory.
+ * - Tensors are dense, row-major, last dimension fastest, unless a leading
+ *   dimension ("ld", in elements) is given for the row stride.
+ * - Work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL is the
+ *   null stream). Nothing synchronises the host.
+ * - The return value is a kda_status. All arguments are validated on the host
+ *   before anything is enqueued: on any error nothing is launched, no output
+ *   is touched, and kda_last_error() returns a message. No exception crosses
+ *   the ABI.
+ * - Base pointers must be 16-byte aligned.
+ * - Results are deterministic: no atomics, fixed reduction orders.
+ * - kda_dtype selects float32 or bfloat16 storage; bfloat16 values are stored
+ *   as their 16-bit patterns, rounded to nearest even by the library.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = -1, /* null pointer, bad size, inconsistent cu_seqlens, misalignment, aliasing */
+    KDA_ERR_UNSUPPORTED = -2, /* valid but not implemented here (e.g. dk != 128) */
+    KDA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+    KDA_ERR_HIP = -4          /* the HIP runtime reported an error on launch */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+#define KDA_VERSION 100 /* 1.0.0 */
+
+/* ------------------------------------------------------------------------
+ * kda_prefill -- the KDA core over packed variable-length sequences.
+ *
+ * Defined by the recurrence above (flozi.net page, section "KDA replaces a
+ * token list with a recurrent matrix"; the per-layer state of 64 x 128 x 128
+ * FP32 and the -5 log-retention bound are from the same section). Computed
+ * chunk-wise (64 tokens for bfloat16 inputs, 32 for float32) with an exact
+ * reorganisation of the recurrence; results equal the token-serial recurrence
+ * up to rounding.
+ *
+ * q, k, g    [num_tokens, H, dk]   in_dtype. g is the natural-log retention
+ *                                  (<= 0); it is clamped at lower_bound on use.
+ *                                  q and k are expected unit-norm per head (the
+ *                                  prologue produces them); the core does not
+ *                                  normalise.
+ * v          [num_tokens, H, dv]   in_dtype
+ * beta       [num_tokens, H]       in_dtype, write strength in [0, 1]
+ * cu_seqlens_dev / cu_seqlens_host  int32 [num_seqs + 1], the same values on
+ *            device and host: cu[0] = 0, non-decreasing, cu[num_seqs] =
+ *            num_tokens. Sequence n is tokens [cu[n], cu[n+1]); empty
+ *            sequences are allowed (final state = initial state). Both NULL:
+ *            num_seqs sequences of num_tokens / num_seqs tokens back to back
+ *            (num_tokens must then be a multiple of num_seqs).
+ * initial_state  float32 [num_seqs, H, dk, dv] or NULL (zero state).
+ * final_state    float32 [num_seqs, H, dk, dv] or NULL (not written). May be
+ *            the same pointer as initial_state (in-place update); any other
+ *            overlap is rejected.
+ * o          [num_tokens, H, dv]   out_dtype (float32 keeps full precision).
+ * scale      read-out multiplier (1.0 for the plain S^T q read).
+ * lower_bound  log-retention floor, -5 for the safe forget gate.
+ * workspace / workspace_bytes  device scratch of at least
+ *            kda_prefill_workspace_bytes(...) bytes (may be NULL when that is 0).
+ * Supported: dk = dv = 128, H >= 1, in_dtype F32 or BF16.
+ * ---------------------------------------------------------------------- */
+int kda_prefill(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                kda_dtype in_dtype, int64_t num_tokens, int H, int dk, int dv,
+                const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int num_seqs,
+                float scale, float lower_bound, const float* initial_state, float* final_state,
+                void* o, kda_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                void* hip_stream);
+
+size_t kda_prefill_workspace_bytes(int64_t num_tokens, int num_seqs, int H, int dk, int dv,
+                                   kda_dtype in_dtype);
+
+/* ------------------------------------------------------------------------
+ * kda_decode_step -- one new token for each of B sequences, state in place.
+ *
+ * The same recurrence with T = 1 (retention, corrected write, read after the
+ * write), as in "Ling-3.1-flash: Grouped Routing and Two Different MLA Caches",
+ * section "KDA replaces a token list with a recurrent matrix". Each step reads
+ * and writes every sequence's [H, dk, dv] float32 state exactly once.
+ *
+ * q, k, g [B, H, dk], v [B, H, dv], beta [B, H]: in_dtype.
+ * state   float32 [B, H, dk, dv], read and overwritten with the new state.
+ * o       [B, H, dv] out_dtype.
+ * Supported: dk = dv = 128, B >= 1, H >= 1.
+ * ---------------------------------------------------------------------- */
+int kda_decode_step(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                    kda_dtype in_dtype, int B, int H, int dk, int dv, float scale,
+                    float lower_bound, float* state, void* o, kda_dtype out_dtype,
+                    void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * kda_conv_state_update -- decode-time causal short convolution.
+ *
+ * One causal depthwise convolution of width W (4 in the model) per projection
+ * stream, followed by SiLU ("Ling-3.1-flash: Grouped Routing and Two Different
+ * MLA Caches", section "KDA replaces a token list with a recurrent matrix";
+ * the convolution tails are counted in "Ling-3.1-flash: What 63 Linear-
+ * Attention Layers Do to the KV Budget", section "The memory math").
+ *
+ * x          [B, C]          new input token per sequence
+ * conv_state [B, W-1, C]     the previous W-1 inputs, oldest first; updated in
+ *                            place to the last W-1 inputs (shift left, append x)
+ * weight     [C, W]          weight[:, W-1] multiplies the current input
+ * bias       [C] or NULL
+ * y          [B, C]          y = act(sum_j weight[c, j] * window[j] + bias[c]),
+ *                            act = SiLU if apply_silu else identity, then, if
+ *                            l2norm_group = 128, each group of 128 channels is
+ *                            scaled by 1 / sqrt(sum(y^2) + l2norm_eps) (the
+ *                            per-head q/k normalisation of the same section).
+ * All in `dtype`. y must not overlap x or conv_state; conv_state must not
+ * overlap x. The kept history is copied bit for bit. Supported: 2 <= W <= 8,
+ * C a multiple of 128, l2norm_group 0 or 128.
+ * ---------------------------------------------------------------------- */
+int kda_conv_state_update(const void* x, void* conv_state, const void* weight, const void* bias,
+                          kda_dtype dtype, int B, int C, int W, int apply_silu,
+                          int l2norm_group, float l2norm_eps, void* y, void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * kda_conv_prefill -- the prologue convolution over packed sequences.
+ *
+ * Causal depthwise convolution of width W per sequence (no leakage across
+ * cu_seqlens boundaries), optional SiLU, then optional L2 normalisation over
+ * each group of `l2norm_group` channels (the per-head q/k normalisation of the
+ * same flozi.net section): y <- y / sqrt(sum(y^2) + l2norm_eps).
+ *
+ * x           rows of C channels, row r at x + r * x_ld (in_dtype = dtype)
+ * cu_seqlens_*  as for kda_prefill
+ * weight [C, W], bias [C] or NULL
+ * conv_state_in  [num_seqs, W-1, C] history before each sequence, or NULL (zeros)
+ * conv_state_out [num_seqs, W-1, C] last W-1 inputs of each sequence (taking
+ *             history into account for short sequences), or NULL. Must not
+ *             overlap conv_state_in.
+ * l2norm_group  0 (off) or 128 (per-head normalisation); C a multiple of 128
+ * y           rows of C channels at y + r * y_ld; must not overlap x
+ * ---------------------------------------------------------------------- */
+int kda_conv_prefill(const void* x, int64_t x_ld, int64_t num_tokens, int C, int W,
+                     const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int num_seqs,
+                     const void* weight, const void* bias, const void* conv_state_in,
+                     void* conv_state_out, int apply_silu, int l2norm_group, float l2norm_eps,
+                     void* y, int64_t y_ld, kda_dtype dtype, void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * kda_gate_prologue -- log-retention and write strength from projections.
+ *
+ * "Ling-3.1-flash: a 560B hybrid-attention MoE, counted from its safetensors
+ * headers", section "How KDA and MLA split the work": the per-channel decay
+ * comes from f_proj and A_log, the write strength from b_proj (one scalar per
+ * head). Here
+ *   g    = max(-exp(A_log[h]) * softplus(f), lower_bound)      [T, H, dk]
+ *   beta = sigmoid(b)                                            [T, H]
+ * f rows of H*dk at f + t * f_ld; b rows of H at b + t * b_ld (in_dtype);
+ * A_log float32 [H]; g_out [T, H, dk] and beta_out [T, H] in out_dtype.
+ * ---------------------------------------------------------------------- */
+int kda_gate_prologue(const void* f, int64_t f_ld, const void* b, int64_t b_ld,
+                      const float* A_log, int64_t num_tokens, int H, int dk, float lower_bound,
+                      kda_dtype in_dtype, void* g_out, void* beta_out, kda_dtype out_dtype,
+                      void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * kda_output_norm_gate -- epilogue: per-head RMSNorm times sigmoid gate.
+ *
+ * "An output normalization and sigmoid gate precede the projection back to
+ * width 4,096" (flozi.net page, section "KDA replaces a token list with a
+ * recurrent matrix"). Per token and head:
+ *   y = o / sqrt(mean(o^2) + eps) * norm_weight * sigmoid(gate)
+ * o [T, H, dv] (o_dtype); gate rows of H*dv at gate + t * gate_ld (stored in
+ * y_dtype); norm_weight float32 [dv]; y [T, H*dv] (y_dtype), must not overlap o.
+ * ---------------------------------------------------------------------- */
+int kda_output_norm_gate(const void* o, kda_dtype o_dtype, const void* gate, int64_t gate_ld,
+                         const float* norm_weight, int64_t num_tokens, int H, int dv, float eps,
+                         void* y, kda_dtype y_dtype, void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * kda_gemm -- C[M, N] = A[M, K] * B[N, K]^T on MFMA, float32 accumulation.
+ *
+ * The layer's dense projections: q, k, v, decay and gate are 4096 -> 8192,
+ * the output projection 8192 -> 4096 ("Ling-3.1-flash: a 560B hybrid-attention
+ * MoE ...", section "How KDA and MLA split the work": six 8192 x 4096 matrices
+ * per KDA layer). Weights are stored [out, in].
+ * A rows at A + m * lda, B rows at B + n * ldb (ab_dtype = KDA_BF16),
+ * C rows at C + m * ldc (c_dtype). K must be a multiple of 8; lda, ldb
+ * multiples of 8, ldc a multiple of 4. C must not overlap A or B.
+ * ---------------------------------------------------------------------- */
+int kda_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+             int64_t M, int64_t N, int64_t K, kda_dtype ab_dtype, kda_dtype c_dtype,
+             void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * Size helpers. kda_state_bytes(64, 128, 128, KDA_F32) = 4,194,304: one
+ * [64,128,128] FP32 matrix per layer, 252 MiB over 63 layers (flozi.net page,
+ * section "KDA replaces a token list with a recurrent matrix").
+ * kda_conv_state_bytes(3, 4, 8192, KDA_BF16) = 147,456 bytes per layer for
+ * the q/k/v convolution tails (width-4 convolution of "Ling-3.1-flash: What
+ * 63 Linear-Attention Layers Do to the KV Budget", section "The memory math").
+ * Both return 0 for non-positive sizes.
+ * ---------------------------------------------------------------------- */
+size_t kda_state_bytes(int H, int dk, int dv, kda_dtype dtype);
+size_t kda_conv_state_bytes(int streams, int W, int C, kda_dtype dtype);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* kda_last_error(void);
+
+/* KDA_VERSION of the built library. */
+int kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -217,14 +217,16 @@ def softplus(x):
     return np.logaddexp(0.0, np.asarray(x, dtype=np.float64))
 
 
-def conv_causal(x, w, cu_seqlens=None, state_in=None, apply_silu=True):
+def conv_causal(x, w, cu_seqlens=None, state_in=None, apply_silu=True, bias=None):
     """Depthwise causal convolution of width W per sequence, then SiLU.
 
     [flozi-KDA]: one causal short convolution of width four with SiLU per stream.
     x: [T, C]; w: [C, W] with w[:, W-1] applied to the current token and
     w[:, 0] to the token W-1 steps back; state_in: [N, W-1, C] (oldest first) or
-    None for zero history. Returns (y [T, C] float64, state_out [N, W-1, C]): the
-    last W-1 inputs of each sequence, including history when it is shorter.
+    None for zero history; bias: [C] added before the activation (the model
+    uses none; the library accepts one). Returns (y [T, C] float64,
+    state_out [N, W-1, C]): the last W-1 inputs of each sequence, including
+    history when it is shorter.
     """
     x = np.asarray(x, dtype=np.float64)
     w = np.asarray(w, dtype=np.float64)
@@ -240,6 +242,8 @@ def conv_causal(x, w, cu_seqlens=None, state_in=None, apply_silu=True):
         ext = np.concatenate([hist, x[s:e]], axis=0)      # [W-1 + L, C]
         L = e - s
         acc = np.zeros((L, C))
+        if bias is not None:
+            acc += np.asarray(bias, dtype=np.float64)[None, :]
         for j in range(W):                                 # tap j sees token t - (W-1-j)
             acc += w[None, :, j] * ext[j:j + L]
         y[s:e] = silu(acc) if apply_silu else acc

@@ -1,0 +1,154 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/kda.h, its size helpers reproduce the pages' figures, and
+host-side validation rejects bad arguments before anything reaches the device
+(every call below fails validation, so no kernel is launched)."""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+from gated_delta_rule_02_amd import kda as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = K.lib()
+    declared = header_functions()
+    assert declared, "no declarations parsed"
+    for name in declared:
+        assert hasattr(L, name), name
+    assert sorted(K.EXPORTED) == declared
+
+
+def test_version_and_sizes_match_page_figures():
+    fig = json.load(open(os.path.join(ROOT, "tests", "golden", "page_figures.json")))
+    assert K.kda_version() == 100
+    per_layer = K.kda_state_bytes(64, 128, 128, K.KDA_F32)
+    assert per_layer == 4 * 2 ** 20
+    assert 63 * per_layer == fig["state_per_sequence_63_layers_mib"]["value"] * 2 ** 20
+    assert 63 * K.kda_state_bytes(64, 128, 128, K.KDA_BF16) == fig["state_per_sequence_bf16_mib"]["value"] * 2 ** 20
+    conv = K.kda_conv_state_bytes(3, 4, 8192, K.KDA_BF16)
+    assert conv == 147456
+    total = 63 * conv
+    assert total < fig["conv_tails_per_sequence"]["under_mib"] * 2 ** 20
+    assert round(total / 1e6) == fig["conv_tails_per_sequence"]["about_mb"]
+    # crossover vs an all-MLA cache: 252 MiB / (63 layers x 1152 B per token)
+    mla = fig["mla_bytes_per_token_all_9_layers"]["per_layer"]
+    assert abs(63 * per_layer / (63 * mla) - fig["kda_vs_all_mla_crossover_tokens"]["fp32_about"]) < 50
+    assert K.kda_state_bytes(0, 128, 128, K.KDA_F32) == 0
+
+
+# ---- validation: fake, aligned, never-dereferenced device addresses -----------
+BASE = 1 << 40
+
+
+def fake(i, size=1 << 30):
+    return BASE + i * size
+
+
+def call(name, *args):
+    fn = getattr(K.lib(), name)
+    return fn(*args), K.kda_last_error()
+
+
+def cu_host(values):
+    arr = (ctypes.c_int32 * len(values))(*values)
+    return arr
+
+
+def prefill(**over):
+    a = dict(q=fake(1), k=fake(2), v=fake(3), g=fake(4), beta=fake(5), in_dtype=K.KDA_BF16,
+             T=256, H=4, dk=128, dv=128, cu_dev=None, cu_host=None, N=1, scale=1.0, lb=-5.0,
+             s0=None, sT=None, o=fake(6), out_dtype=K.KDA_F32, ws=None, ws_bytes=0, stream=None)
+    a.update(over)
+    return call("kda_prefill", a["q"], a["k"], a["v"], a["g"], a["beta"], a["in_dtype"], a["T"], a["H"],
+                a["dk"], a["dv"], a["cu_dev"], a["cu_host"], a["N"], a["scale"], a["lb"], a["s0"], a["sT"],
+                a["o"], a["out_dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_prefill_validation():
+    assert prefill(q=None)[0] == K.KDA_ERR_INVALID_ARG
+    rc, msg = prefill(dk=64)
+    assert rc == K.KDA_ERR_UNSUPPORTED and "dk = dv = 128" in msg
+    assert prefill(in_dtype=7)[0] == K.KDA_ERR_INVALID_ARG
+    assert prefill(q=fake(1) + 8)[0] == K.KDA_ERR_INVALID_ARG          # misaligned
+    assert prefill(N=3)[0] == K.KDA_ERR_INVALID_ARG                    # 256 % 3 != 0
+    h = cu_host([0, 100, 50, 256])
+    rc, msg = prefill(cu_dev=fake(7), cu_host=h, N=3)
+    assert rc == K.KDA_ERR_INVALID_ARG and "non-decreasing" in msg
+    h = cu_host([0, 100, 200])
+    rc, msg = prefill(cu_dev=fake(7), cu_host=h, N=2)
+    assert rc == K.KDA_ERR_INVALID_ARG and "must equal num_tokens" in msg
+    h = cu_host([1, 100, 256])
+    assert prefill(cu_dev=fake(7), cu_host=h, N=2)[0] == K.KDA_ERR_INVALID_ARG
+    assert prefill(cu_dev=fake(7), cu_host=None)[0] == K.KDA_ERR_INVALID_ARG
+    # o overlapping an input
+    assert prefill(o=fake(1) + 4096)[0] == K.KDA_ERR_INVALID_ARG
+    # partial overlap of the two state buffers
+    rc, msg = prefill(s0=fake(8), sT=fake(8) + 1024)
+    assert rc == K.KDA_ERR_INVALID_ARG and "overlap" in msg
+    # final_state overlapping q
+    assert prefill(sT=fake(1) + 64)[0] == K.KDA_ERR_INVALID_ARG
+
+
+def test_decode_validation():
+    args = [fake(1), fake(2), fake(3), fake(4), fake(5), K.KDA_BF16, 256, 64, 128, 128, 1.0, -5.0,
+            fake(6, 1 << 34), fake(9), K.KDA_F32, None]
+    a = list(args); a[0] = None
+    assert call("kda_decode_step", *a)[0] == K.KDA_ERR_INVALID_ARG
+    a = list(args); a[8] = 96
+    assert call("kda_decode_step", *a)[0] == K.KDA_ERR_UNSUPPORTED
+    a = list(args); a[13] = fake(6, 1 << 34) + 256          # o inside the state
+    rc, msg = call("kda_decode_step", *a)
+    assert rc == K.KDA_ERR_INVALID_ARG and "overlap" in msg
+    a = list(args); a[6] = 0
+    assert call("kda_decode_step", *a)[0] == K.KDA_ERR_INVALID_ARG
+
+
+def test_conv_and_misc_validation():
+    # conv update: W out of range, C not a multiple of 128, y aliasing the state
+    base = [fake(1), fake(2), fake(3), None, K.KDA_BF16, 256, 8192, 4, 1, 0, 1e-6, fake(4), None]
+    a = list(base); a[7] = 9
+    assert call("kda_conv_state_update", *a)[0] == K.KDA_ERR_UNSUPPORTED
+    a = list(base); a[6] = 100
+    assert call("kda_conv_state_update", *a)[0] == K.KDA_ERR_UNSUPPORTED
+    a = list(base); a[11] = fake(2)
+    assert call("kda_conv_state_update", *a)[0] == K.KDA_ERR_INVALID_ARG
+    a = list(base); a[9] = 64
+    assert call("kda_conv_state_update", *a)[0] == K.KDA_ERR_UNSUPPORTED
+    # conv prefill: y aliasing x; bad cu_seqlens
+    h = cu_host([0, 10, 5])
+    rc, _ = call("kda_conv_prefill", fake(1), 8192, 10, 8192, 4, fake(2), h, 2, fake(3), None, None, None,
+                 1, 0, 1e-6, fake(4), 8192, K.KDA_BF16, None)
+    assert rc == K.KDA_ERR_INVALID_ARG
+    rc, _ = call("kda_conv_prefill", fake(1), 8192, 10, 8192, 4, None, None, 1, fake(3), None, None, None,
+                 1, 0, 1e-6, fake(1), 8192, K.KDA_BF16, None)
+    assert rc == K.KDA_ERR_INVALID_ARG
+    # gemm: unsupported fp32 operands, misaligned ld
+    rc, _ = call("kda_gemm", fake(1), 4096, fake(2), 4096, fake(3), 8192, 64, 8192, 4096, K.KDA_F32, K.KDA_F32, None)
+    assert rc == K.KDA_ERR_UNSUPPORTED
+    rc, _ = call("kda_gemm", fake(1), 4095, fake(2), 4096, fake(3), 8192, 64, 8192, 4095, K.KDA_BF16, K.KDA_F32, None)
+    assert rc != K.KDA_OK
+    # gate and epilogue: dk != 128
+    rc, _ = call("kda_gate_prologue", fake(1), 8192, fake(2), 64, fake(3), 8, 64, 64, -5.0, K.KDA_BF16,
+                 fake(4), fake(5), K.KDA_BF16, None)
+    assert rc == K.KDA_ERR_UNSUPPORTED
+    rc, _ = call("kda_output_norm_gate", fake(1), K.KDA_F32, fake(2), 8192, fake(3), 8, 64, 128, 1e-6,
+                 fake(1), K.KDA_BF16, None)
+    assert rc == K.KDA_ERR_INVALID_ARG
+
+
+def test_error_message_cleared_on_success_path_helpers():
+    prefill(q=None)
+    assert K.kda_last_error() != ""

@@ -412,3 +412,11 @@ def test_layer_composition_identity():
     y = R.round_bf16(R.output_norm_gate(parts["o"], parts["gate"], np.ones(d))).reshape(T, W)
     np.testing.assert_array_equal(parts["y"], y)
     np.testing.assert_allclose(out, y @ Wo.T, rtol=1e-13)
+
+
+def test_conv_bias_shifts_preactivation():
+    """A per-channel bias adds to the pre-activation: with zero taps the output
+    is SiLU(bias)."""
+    b = np.array([0.0, 1.0, -2.0])
+    y, _ = R.conv_causal(np.ones((2, 3)), np.zeros((3, 4)), bias=b)
+    np.testing.assert_allclose(y[0], b / (1 + np.exp(-b)), rtol=1e-15)
