@@ -1,0 +1,204 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA token-mixer hot path on one MI355X (gfx950).
+
+A step is one KDA prefill of one layer over the single-sequence workload
+(B=1, T=4096, H=64, dk=dv=128, bfloat16 q/k/v/g/beta, float32 state in and
+out, float32 output, 64-token chunks): ``value`` is tokens per second for that
+layer. The same run also times the batched decode step (B=256 sequences x 64
+heads, 1 GiB float32 state updated in place) and reports its state bandwidth,
+the decode-time convolution update, and (unless --skip-layer) the whole
+token-mixer layer at T=8192.
+
+Timing: W untimed warm-up steps, then exactly K steps bracketed by
+torch.cuda.synchronize() on both sides, with HIP events recorded on the stream
+the kernels are launched on. Inputs are resident in device memory before the
+timed region starts. Prints one JSON line.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16/fp16 MFMA, TFLOP/s
+
+# algorithmic bytes per token-layer of the prefill: q,k,v,g bf16 (4 x 64 x 128 x 2)
+# + beta (64 x 2) + o float32 (64 x 128 x 4) + state in and out amortised over
+# 4096 tokens (2 x 4 MiB / 4096)
+PREFILL_BYTES_PER_TOKEN = 4 * 64 * 128 * 2 + 64 * 2 + 64 * 128 * 4 + 2 * 64 * 128 * 128 * 4 // 4096
+# algorithmic flops per token-layer (chunk 64, triangles only): 4,468,736 MAC per
+# chunk-head -> x2 / 64 tokens x 64 heads
+PREFILL_FLOPS_PER_TOKEN = 2 * 4468736 * 64 // 64
+# decode step: state read + write (2 x 1 GiB) + q,k,v,g bf16 + beta bf16 + o float32
+DECODE_BYTES = 2 * 256 * 64 * 128 * 128 * 4 + 4 * 256 * 64 * 128 * 2 + 256 * 64 * 2 + 256 * 64 * 128 * 4
+# conv update: x + state in + state out (shift) + weight + y, bf16
+CONV_BYTES = (256 * 8192 + 2 * 256 * 3 * 8192 + 8192 * 4 + 256 * 8192) * 2
+
+COUNTERS = os.path.join(ROOT, "profiles", "kda_prefill_t4096_h64_counters.json")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("kda_prefill.hip", "kda_device.h"):
+        h.update(open(os.path.join(ROOT, "gated_delta_rule_02_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def dev(t, torch):
+    import numpy as np
+    if t.bits is not None:
+        return torch.from_numpy(np.ascontiguousarray(t.bits).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(t.vals)).cuda()
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def timed(torch, fn, steps, warmup):
+    """Average ms per call over `steps` calls after `warmup` untimed ones."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / steps, wall
+
+
+def bench_prefill(torch, K, steps, warmup):
+    from gated_delta_rule_02_amd import synth
+    d = synth.workload_prefill()
+    q, k, v, g, b = (dev(d[x], torch) for x in ("q", "k", "v", "g", "beta"))
+    T, H, D = q.shape
+    s0 = torch.zeros((1, H, D, D), dtype=torch.float32, device="cuda")
+    sT = torch.empty_like(s0)
+    o = torch.empty((T, H, D), dtype=torch.float32, device="cuda")
+    fn = lambda: K.kda_prefill(q, k, v, g, b, o, initial_state=s0, final_state=sT)
+    ms, wall = timed(torch, fn, steps, warmup)
+    return ms, wall, d
+
+
+def bench_decode(torch, K, steps, warmup):
+    from gated_delta_rule_02_amd import synth
+    d = synth.workload_decode()
+    q, k, v, g, b = (dev(d[x], torch) for x in ("q", "k", "v", "g", "beta"))
+    st = torch.from_numpy(d["state"]).cuda()
+    o = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    ms, _ = timed(torch, lambda: K.kda_decode_step(q, k, v, g, b, st, o), steps, warmup)
+    x, cst, w = dev(d["conv_x"], torch), dev(d["conv_state"], torch), dev(d["conv_w"], torch)
+    y = torch.empty_like(x)
+    ms_conv, _ = timed(torch, lambda: K.kda_conv_state_update(x, cst, w, y), steps, warmup)
+    return ms, ms_conv
+
+
+def bench_layer(torch, steps, warmup):
+    from gated_delta_rule_02_amd import layer, synth
+    d = synth.workload_layer()
+    mixer = layer.KDAMixer.from_host(d)
+    x = dev(d["x"], torch)
+    fn = lambda: mixer.forward(x)
+    ms, _ = timed(torch, fn, max(1, steps // 4), max(1, warmup // 2))
+    return ms, mixer.flops_per_token() * x.shape[0]
+
+
+def cpu_baseline(d):
+    """The FP64 oracle (token-serial, threads over heads) on the whole prefill
+    workload, timed on this host."""
+    from oracle import reference as R
+    threads = R.default_threads()
+    t0 = time.perf_counter()
+    R.kda_serial(d["q"].vals, d["k"].vals, d["v"].vals, d["g"].vals, d["beta"].vals, nthreads=threads)
+    t = time.perf_counter() - t0
+    T = d["q"].shape[0]
+    return {"value": T / t, "unit": "tokens/s/layer", "cores": threads, "kind": "oracle",
+            "sample": "whole prefill workload (4096 tokens x 64 heads, d=128), fp64 token-serial, "
+                      "%.2f s wall on %d threads" % (t, threads)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--skip-layer", action="store_true")
+    ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "layer"], default=None,
+                    help="time one path only (for profiler runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (requested --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_delta_rule_02_amd import kda as K
+    K.lib()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    out = {}
+    if args.only in (None, "prefill"):
+        log("prefill T=4096 H=64")
+        ms, wall, d = bench_prefill(torch, K, args.steps, args.warmup)
+        log("prefill %.3f ms/step" % ms)
+        T = 4096
+        achieved = PREFILL_BYTES_PER_TOKEN * T / (ms * 1e-3) / 1e9
+        traffic = None
+        if os.path.exists(COUNTERS):
+            c = json.load(open(COUNTERS))
+            if c.get("source_hash") == kernel_source_hash():
+                traffic = c.get("hbm_bytes_per_launch")
+        out.update({
+            "metric": "KDA prefill tokens/s/layer (T=4096,H=64,d=128); decode state GB/s",
+            "value": T / (ms * 1e-3), "unit": "tokens/s/layer", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": "KDA prefill, one layer: B=1 T=4096 H=64 dk=dv=128, bf16 q/k/v/g/beta, "
+                                   "fp32 state in/out, fp32 o, chunk 64",
+                       "global_batch": 1, "seq_len": T, "heads": 64, "head_dim": 128, "chunk": 64},
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                         "kernel": "prefill_kernel<bf16>", "algorithmic_bytes_per_launch": PREFILL_BYTES_PER_TOKEN * T,
+                         "mfma_tflops": PREFILL_FLOPS_PER_TOKEN * T / (ms * 1e-3) / 1e12,
+                         "mfma_frac_of_bf16_peak": PREFILL_FLOPS_PER_TOKEN * T / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+        })
+        if not args.skip_cpu:
+            log("cpu baseline (fp64 oracle)")
+            out["cpu_baseline"] = cpu_baseline(d)
+    if args.only in (None, "decode"):
+        log("decode B=256 H=64")
+        ms, ms_conv = bench_decode(torch, K, args.steps, args.warmup)
+        log("decode %.3f ms/step, conv %.3f ms" % (ms, ms_conv))
+        out["decode"] = {"workload": "decode step B=256 H=64 dk=dv=128, bf16 inputs, fp32 state [256,64,128,128] in place, fp32 o",
+                         "ms_per_step": ms, "GB/s": DECODE_BYTES / (ms * 1e-3) / 1e9,
+                         "frac_of_hbm_peak": DECODE_BYTES / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "bytes_per_step": DECODE_BYTES, "state_GB/s": 2 * 2 ** 30 / (ms * 1e-3) / 1e9}
+        out["conv_update"] = {"workload": "x [256,8192] bf16, state [256,3,8192] bf16 in place",
+                              "ms_per_step": ms_conv, "GB/s": CONV_BYTES / (ms_conv * 1e-3) / 1e9}
+    if args.only == "layer" or (args.only is None and not args.skip_layer):
+        log("layer T=8192 hidden=4096")
+        ms, flops = bench_layer(torch, args.steps, args.warmup)
+        log("layer %.3f ms/step" % ms)
+        out["layer"] = {"workload": "full token-mixer layer T=8192 hidden=4096 H=64: projections, conv, gate, "
+                                    "KDA core, norm x gate, output projection",
+                        "ms_per_step": ms, "tokens/s": 8192 / (ms * 1e-3), "TFLOP/s": flops / (ms * 1e-3) / 1e12}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

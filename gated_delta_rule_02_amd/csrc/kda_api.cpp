@@ -140,7 +140,7 @@ int kda_decode_step(const void* q, const void* k, const void* v, const void* g, 
 }
 
 // ---------------------------------------------------------------- conv
-int kda_conv_state_update(const void* x, void* conv_state, const void* weight, const void* bias,
+int kda_conv_state_update(const void* x, int64_t x_ld, void* conv_state, const void* weight, const void* bias,
                           kda_dtype dtype, int B, int C, int W, int apply_silu,
                           int l2norm_group, float l2norm_eps, void* y, void* hip_stream)
 {
@@ -151,18 +151,20 @@ int kda_conv_state_update(const void* x, void* conv_state, const void* weight, c
     REQUIRE(C % 128 == 0, KDA_ERR_UNSUPPORTED, "kda_conv_state_update: C must be a multiple of 128 (got %d)", C);
     REQUIRE(l2norm_group == 0 || l2norm_group == 128, KDA_ERR_UNSUPPORTED,
             "kda_conv_state_update: l2norm_group must be 0 or 128 (got %d)", l2norm_group);
+    REQUIRE(x_ld >= C && x_ld % 8 == 0, KDA_ERR_INVALID_ARG,
+            "kda_conv_state_update: x_ld must be >= C and a multiple of 8");
     for (const void* p : {x, (const void*)conv_state, weight, bias, (const void*)y})
         REQUIRE(!p || aligned16(p), KDA_ERR_INVALID_ARG, "kda_conv_state_update: pointers must be 16-byte aligned");
     const size_t es = esize(dtype);
     const Range ry = rng(y, (size_t)B * C * es), rs = rng(conv_state, (size_t)B * (W - 1) * C * es);
-    const Range rx = rng(x, (size_t)B * C * es), rw = rng(weight, (size_t)C * W * es),
+    const Range rx = rng(x, ((size_t)(B - 1) * x_ld + C) * es), rw = rng(weight, (size_t)C * W * es),
                 rb = rng(bias, bias ? (size_t)C * es : 0);
     REQUIRE(!overlap(ry, rx) && !overlap(ry, rs) && !overlap(ry, rw) && !overlap(ry, rb),
             KDA_ERR_INVALID_ARG, "kda_conv_state_update: y overlaps another tensor");
     REQUIRE(!overlap(rs, rx) && !overlap(rs, rw) && !overlap(rs, rb), KDA_ERR_INVALID_ARG,
             "kda_conv_state_update: conv_state overlaps an input");
 
-    ConvUpdateArgs a{x, conv_state, weight, bias, y, B, C, W, apply_silu ? 1 : 0, l2norm_group,
+    ConvUpdateArgs a{x, x_ld, conv_state, weight, bias, y, B, C, W, apply_silu ? 1 : 0, l2norm_group,
                      l2norm_eps, (DType)dtype};
     return hip_status(launch_conv_update(a, static_cast<hipStream_t>(hip_stream)), "kda_conv_state_update");
 }

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kWaves * 64) void conv_update_kernel(ConvUpdateArgs
     if (grp * kGroup >= a.C) return;  // whole wavefront leaves together
     const int c = grp * kGroup + 2 * (threadIdx.x & 63);
     const int W = a.W;
-    const T* x = static_cast<const T*>(a.x) + (size_t)b * a.C;
+    const T* x = static_cast<const T*>(a.x) + (size_t)b * a.x_ld;
     T* st = static_cast<T*>(a.conv_state) + (size_t)b * (W - 1) * a.C;
     const T* w = static_cast<const T*>(a.weight);
 

@@ -22,6 +22,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
 struct ConvUpdateArgs {
     const void* x;
+    int64_t x_ld;
     void* conv_state;
     const void *weight, *bias;
     void* y;

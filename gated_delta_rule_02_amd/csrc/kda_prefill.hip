@@ -128,6 +128,25 @@ template <> struct Ops<true> {  // float32 inputs
 
 __device__ __forceinline__ f32x4 ld4f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
+// Two consecutive input elements kept raw in registers between load and use.
+template <typename T> struct Pair;
+template <> struct Pair<bf16_t> {
+    using type = uint32_t;
+    __device__ static f32x2 unpack(uint32_t u) { return f32x2{__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u)}; }
+};
+template <> struct Pair<float> {
+    using type = uint2;
+    __device__ static f32x2 unpack(uint2 u) { return f32x2{__uint_as_float(u.x), __uint_as_float(u.y)}; }
+};
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return bf16_to_f32(x); }
+
+template <typename T>
+__device__ __forceinline__ typename Pair<T>::type ldpair(const T* p)
+{
+    return *reinterpret_cast<const typename Pair<T>::type*>(p);
+}
+
 // index of the off-diagonal block pair (R, I), I < R
 __host__ __device__ constexpr int pair_id(int R, int I) { return R * (R - 1) / 2 + I; }
 // index of the lower-triangle block (R, I), I <= R
@@ -200,11 +219,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
     // state slice: S[t][i] = S[16t + 4q + i][jcol]
     f32x4 S[8];
     const size_t sbase = ((size_t)n * a.H + h) * D * D;
+    if (a.s0) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+        for (int t = 0; t < 8; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            S[t][i] = a.s0 ? a.s0[sbase + (size_t)(16 * t + 4 * q4 + i) * D + jcol] : 0.0f;
+            for (int i = 0; i < 4; ++i) S[t][i] = a.s0[sbase + (size_t)(16 * t + 4 * q4 + i) * D + jcol];
+    } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     const int64_t tok_stride = (int64_t)a.H * D;
     const TIN* qg = static_cast<const TIN*>(a.q) + (int64_t)h * D;
@@ -215,28 +238,48 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
     TOUT* og = static_cast<TOUT*>(a.o) + (int64_t)h * D + jcol;
     const float lb = a.lower_bound;
 
+    // Raw inputs of one chunk, loaded one chunk ahead. Rows past the end of
+    // the sequence load a valid row (clamped) and are zeroed on use, so every
+    // load is unconditional and all of them are in flight together.
+    using PT = typename Pair<TIN>::type;
+    const int R = wave;         // phase 1 block of 16 tokens
+    const int c0 = 2 * lane;    // phase 1 channel pair
+    const int cp = tid & 31;    // value column pair for the V copy
+    PT rk[16], rq[16], rgt[16], rv[C / 8];
+    TIN rb = TIN(0);
+    auto load_chunk = [&](int64_t c_s, int nt) {
+        if (R < NB) {
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const int64_t off = (c_s + min(16 * R + rr, nt - 1)) * tok_stride + c0;
+                rk[rr] = ldpair(kg + off);
+                rq[rr] = ldpair(qg + off);
+                rgt[rr] = ldpair(gg + off);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < C / 8; ++i)
+            rv[i] = ldpair(vg + (c_s + min((tid >> 5) + 8 * i, nt - 1)) * tok_stride + 2 * cp);
+        if (tid < C) rb = bg[(c_s + min(tid, nt - 1)) * a.H];
+    };
+    if (seq_s < seq_e) load_chunk(seq_s, (int)min<int64_t>(C, seq_e - seq_s));
+
     for (int64_t cs = seq_s; cs < seq_e; cs += C) {
         const int ntok = (int)min<int64_t>(C, seq_e - cs);
 
         // ---------------- phase 1a: per-block prefix/suffix sums and operands
         // thread = (channel pair c0, c0+1; block R = wave)
-        const int R = wave;
-        const int c0 = 2 * lane;
         f32x2 ks[16];  // k o 2^s, kept for the transposed state-update operand
         if (R < NB) {
             f32x2 kk[16], qq[16], g2[16];
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
-                const int r = 16 * R + rr;
-                if (r < ntok) {
-                    const int64_t off = (cs + r) * tok_stride + c0;
-                    kk[rr] = ld2(kg + off);
-                    qq[rr] = ld2(qg + off);
-                    const f32x2 gv = ld2(gg + off);
-                    g2[rr] = f32x2{fmaxf(gv.x, lb) * kLog2e, fmaxf(gv.y, lb) * kLog2e};
-                } else {
-                    kk[rr] = qq[rr] = g2[rr] = f32x2{0.f, 0.f};
-                }
+                const bool valid = 16 * R + rr < ntok;
+                const f32x2 kv = Pair<TIN>::unpack(rk[rr]), qv = Pair<TIN>::unpack(rq[rr]);
+                const f32x2 gv = Pair<TIN>::unpack(rgt[rr]);
+                kk[rr] = valid ? kv : f32x2{0.f, 0.f};
+                qq[rr] = valid ? qv : f32x2{0.f, 0.f};
+                g2[rr] = valid ? f32x2{fmaxf(gv.x, lb) * kLog2e, fmaxf(gv.y, lb) * kLog2e} : f32x2{0.f, 0.f};
             }
             f32x2 l = {0.f, 0.f};
 #pragma unroll
@@ -258,20 +301,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
                 s += g2[rr];
             }
         }
-        if (tid < C) sm.beta[tid] = tid < ntok ? ld(bg + (cs + tid) * a.H) : 0.0f;
-        {   // values of the 64 columns: thread -> column pair cp, rows t/32 + 8i
-            const int cp = tid & 31;
+        if (tid < C) sm.beta[tid] = tid < ntok ? to_f32(rb) : 0.0f;
 #pragma unroll
-            for (int i = 0; i < C / 8; ++i) {
-                const int r = (tid >> 5) + 8 * i;
-                if (r < ntok) {
-                    sm.V[r][2 * cp] = vg[(cs + r) * tok_stride + 2 * cp];
-                    sm.V[r][2 * cp + 1] = vg[(cs + r) * tok_stride + 2 * cp + 1];
-                } else {
-                    sm.V[r][2 * cp] = sm.V[r][2 * cp + 1] = TIN(0);
-                }
-            }
+        for (int i = 0; i < C / 8; ++i) {  // values: column pair cp, rows tid/32 + 8i
+            const int r = (tid >> 5) + 8 * i;
+            *reinterpret_cast<PT*>(&sm.V[r][2 * cp]) = r < ntok ? rv[i] : PT{};
         }
+        // next chunk's inputs stream in while this chunk computes
+        if (cs + C < seq_e) load_chunk(cs + C, (int)min<int64_t>(C, seq_e - cs - C));
         __syncthreads();
 
         // ---------------- phase 1b: cross-block factors, transposed K-bar

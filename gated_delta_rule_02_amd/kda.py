@@ -29,7 +29,7 @@ _SIGS = {
     "kda_prefill": (_I, [_P] * 5 + [_I, _I64, _I, _I, _I, _P, _P, _I, _F, _F, _P, _P, _P, _I, _P, _SZ, _P]),
     "kda_prefill_workspace_bytes": (_SZ, [_I64, _I, _I, _I, _I, _I]),
     "kda_decode_step": (_I, [_P] * 5 + [_I, _I, _I, _I, _I, _F, _F, _P, _P, _I, _P]),
-    "kda_conv_state_update": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P]),
+    "kda_conv_state_update": (_I, [_P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P]),
     "kda_conv_prefill": (_I, [_P, _I64, _I64, _I, _I, _P, _P, _I, _P, _P, _P, _P, _I, _I, _F, _P, _I64, _I, _P]),
     "kda_gate_prologue": (_I, [_P, _I64, _P, _I64, _P, _I64, _I, _I, _F, _I, _P, _P, _I, _P]),
     "kda_output_norm_gate": (_I, [_P, _I, _P, _I64, _P, _I64, _I, _I, _F, _P, _I, _P]),
@@ -151,12 +151,15 @@ def kda_decode_step(q, k, v, g, beta, state, o, scale=1.0, lower_bound=-5.0, str
 
 def kda_conv_state_update(x, conv_state, weight, y, bias=None, apply_silu=True, l2norm_group=0,
                           l2norm_eps=1e-6, stream=None):
-    """x [B,C], conv_state [B,W-1,C] (in place), weight [C,W], y [B,C]."""
-    for n_, t_ in (("x", x), ("conv_state", conv_state), ("weight", weight), ("y", y), ("bias", bias)):
+    """x rows [B, >=C] (row stride x.stride(0)), conv_state [B,W-1,C] (in place),
+    weight [C,W], y [B,C]."""
+    for n_, t_ in (("conv_state", conv_state), ("weight", weight), ("y", y), ("bias", bias)):
         _dense(t_, n_)
-    B, C = x.shape
-    W = weight.shape[1]
-    _call("kda_conv_state_update", _ptr(x), _ptr(conv_state), _ptr(weight), _ptr(bias), _dt(x), B, C, W,
+    if x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous")
+    B = x.shape[0]
+    C, W = weight.shape
+    _call("kda_conv_state_update", _ptr(x), x.stride(0), _ptr(conv_state), _ptr(weight), _ptr(bias), _dt(x), B, C, W,
           int(bool(apply_silu)), l2norm_group, l2norm_eps, _ptr(y), _stream(stream))
     return y
 

@@ -28,11 +28,14 @@ CORE_D = 128
 def bf16_round(x):
     """float32 -> nearest-even bfloat16, returned as (float32 values, uint16 bits)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    bits = (u >> 16).astype(np.uint16)
-    vals = u.astype(np.uint32).view(np.float32)
-    return vals, bits
+    u = x.view(np.uint32)
+    # finite inputs cannot overflow 32 bits here: 0xff7fffff + 0x8000 < 2^32
+    r = (u >> np.uint32(16)) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r &= np.uint32(0xFFFF0000)
+    bits = (r >> np.uint32(16)).astype(np.uint16)
+    return r.view(np.float32), bits
 
 
 class Tensor:

@@ -123,7 +123,7 @@ int kda_decode_step(const void* q, const void* k, const void* v, const void* g, 
  * the convolution tails are counted in "Ling-3.1-flash: What 63 Linear-
  * Attention Layers Do to the KV Budget", section "The memory math").
  *
- * x          [B, C]          new input token per sequence
+ * x          B rows of C     new input token per sequence, row b at x + b * x_ld
  * conv_state [B, W-1, C]     the previous W-1 inputs, oldest first; updated in
  *                            place to the last W-1 inputs (shift left, append x)
  * weight     [C, W]          weight[:, W-1] multiplies the current input
@@ -137,7 +137,7 @@ int kda_decode_step(const void* q, const void* k, const void* v, const void* g, 
  * overlap x. The kept history is copied bit for bit. Supported: 2 <= W <= 8,
  * C a multiple of 128, l2norm_group 0 or 128.
  * ---------------------------------------------------------------------- */
-int kda_conv_state_update(const void* x, void* conv_state, const void* weight, const void* bias,
+int kda_conv_state_update(const void* x, int64_t x_ld, void* conv_state, const void* weight, const void* bias,
                           kda_dtype dtype, int B, int C, int W, int apply_silu,
                           int l2norm_group, float l2norm_eps, void* y, void* hip_stream);
 

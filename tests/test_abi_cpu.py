@@ -118,15 +118,17 @@ def test_decode_validation():
 
 def test_conv_and_misc_validation():
     # conv update: W out of range, C not a multiple of 128, y aliasing the state
-    base = [fake(1), fake(2), fake(3), None, K.KDA_BF16, 256, 8192, 4, 1, 0, 1e-6, fake(4), None]
-    a = list(base); a[7] = 9
+    base = [fake(1), 8192, fake(2), fake(3), None, K.KDA_BF16, 256, 8192, 4, 1, 0, 1e-6, fake(4), None]
+    a = list(base); a[8] = 9
     assert call("kda_conv_state_update", *a)[0] == K.KDA_ERR_UNSUPPORTED
-    a = list(base); a[6] = 100
+    a = list(base); a[7] = 100
     assert call("kda_conv_state_update", *a)[0] == K.KDA_ERR_UNSUPPORTED
-    a = list(base); a[11] = fake(2)
+    a = list(base); a[12] = fake(2)
     assert call("kda_conv_state_update", *a)[0] == K.KDA_ERR_INVALID_ARG
-    a = list(base); a[9] = 64
+    a = list(base); a[10] = 64
     assert call("kda_conv_state_update", *a)[0] == K.KDA_ERR_UNSUPPORTED
+    a = list(base); a[1] = 100
+    assert call("kda_conv_state_update", *a)[0] == K.KDA_ERR_INVALID_ARG
     # conv prefill: y aliasing x; bad cu_seqlens
     h = cu_host([0, 10, 5])
     rc, _ = call("kda_conv_prefill", fake(1), 8192, 10, 8192, 4, fake(2), h, 2, fake(3), None, None, None,

@@ -1,0 +1,104 @@
+"""Whole token-mixer layer (projections, conv, gate, core, norm x gate,
+output projection) on the GPU vs the FP64 oracle's layer."""
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_02_amd import layer, synth
+from gated_delta_rule_02_amd import kda as K
+from oracle import reference as R
+from tests.gpu_util import TOL_BF16, announce, dev, host64, relerr
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_layer(d, T=None):
+    x = d["x"].vals if T is None else d["x"].vals[:T]
+    return R.layer_forward(x, d["Wq"].vals, d["Wk"].vals, d["Wv"].vals, d["Wf"].vals, d["Wg"].vals,
+                           d["Wb"].vals, d["Wo"].vals, d["conv_q"].vals, d["conv_k"].vals,
+                           d["conv_v"].vals, d["A_log"], d["norm_w"], d["H"], return_parts=True)
+
+
+def test_layer_small():
+    announce("layer small T=150 hidden=256 H=2")
+    d = synth.workload_layer(T=150, hidden=256, H=2, seed=11)
+    mixer = layer.KDAMixer.from_host(d)
+    out, parts = mixer.forward(dev(d["x"]), return_parts=True)
+    torch.cuda.synchronize()
+    ref, rp = oracle_layer(d)
+    e_o = relerr(host64(parts["o"]), rp["o"])
+    e_out = relerr(host64(out), ref)
+    print("  core o %.2e  out %.2e" % (e_o, e_out))
+    assert e_o < TOL_BF16 and e_out < TOL_BF16
+
+
+def test_layer_varlen_and_states_small():
+    """Two packed sequences with conv and KDA state carried in and out equal
+    running them one by one."""
+    announce("layer varlen small")
+    d = synth.workload_layer(T=100, hidden=256, H=2, seed=12)
+    mixer = layer.KDAMixer.from_host(d)
+    x = dev(d["x"])
+    cu = torch.tensor([0, 37, 100], dtype=torch.int32, device="cuda")
+    cu_h = cu.cpu()
+    H, W = 2, 256
+    st_out = torch.zeros((2, H, 128, 128), device="cuda")
+    cs_out = torch.zeros((3, 2, 3, W), dtype=torch.bfloat16, device="cuda")
+    out = mixer.forward(x, cu_seqlens=cu, cu_seqlens_host=cu_h, final_state=st_out,
+                        conv_state_out=cs_out).clone()
+    for n, (s, e) in enumerate(((0, 37), (37, 100))):
+        stn = torch.zeros((1, H, 128, 128), device="cuda")
+        csn = torch.zeros((3, 1, 3, W), dtype=torch.bfloat16, device="cuda")
+        on = mixer.forward(x[s:e].contiguous(), final_state=stn, conv_state_out=csn)
+        torch.cuda.synchronize()
+        assert relerr(host64(out[s:e]), host64(on)) < 1e-6
+        assert relerr(host64(st_out[n]), host64(stn[0])) < 1e-6
+        assert torch.equal(cs_out[:, n], csn[:, 0])
+
+
+def test_layer_decode_continues_prefill():
+    """prefill(T) then mixer.decode of token T == prefill(T+1) at the last token."""
+    announce("layer decode continuation")
+    d = synth.workload_layer(T=65, hidden=256, H=2, seed=13)
+    mixer = layer.KDAMixer.from_host(d)
+    x = dev(d["x"])
+    H, W = 2, 256
+    st = torch.zeros((1, H, 128, 128), device="cuda")
+    cs = torch.zeros((3, 1, 3, W), dtype=torch.bfloat16, device="cuda")
+    mixer.forward(x[:64].contiguous(), final_state=st, conv_state_out=cs)
+    od = mixer.decode(x[64:65].contiguous(), st, cs).clone()
+    torch.cuda.synchronize()
+    ref, _ = oracle_layer(d)
+    assert relerr(host64(od[0]), ref[64]) < TOL_BF16 * 2
+
+
+def test_layer_workload_full_size_sampled():
+    """hidden [8192, 4096], H=64: final output on the first 256 tokens (exact
+    causal prefix) and the core output of two heads over all 8192 tokens."""
+    announce("layer full size sampled")
+    d = synth.workload_layer()
+    mixer = layer.KDAMixer.from_host(d)
+    out, parts = mixer.forward(dev(d["x"]), return_parts=True)
+    torch.cuda.synchronize()
+    out = host64(out[:256])
+    o_core = parts["o"]
+    ref, _ = oracle_layer(d, T=256)
+    e_out = relerr(out, ref)
+    # two heads over the whole sequence: the oracle layer restricted to those heads
+    errs = []
+    for h in (0, 41):
+        cols = slice(h * 128, (h + 1) * 128)
+        sub = dict(d)
+        for n in ("Wq", "Wk", "Wv", "Wf", "Wg", "conv_q", "conv_k", "conv_v"):
+            t = d[n]
+            sub[n] = synth.Tensor(t.vals[cols], t.bits[cols])
+        sub["Wb"] = synth.Tensor(d["Wb"].vals[h:h + 1], d["Wb"].bits[h:h + 1])
+        sub["A_log"] = d["A_log"][h:h + 1]
+        sub["H"] = 1
+        _, rp = R.layer_forward(d["x"].vals, sub["Wq"].vals, sub["Wk"].vals, sub["Wv"].vals, sub["Wf"].vals,
+                                sub["Wg"].vals, sub["Wb"].vals, np.zeros((1, 128)), sub["conv_q"].vals,
+                                sub["conv_k"].vals, sub["conv_v"].vals, sub["A_log"], d["norm_w"], 1,
+                                return_parts=True)
+        errs.append(relerr(host64(o_core[:, h]), rp["o"][:, 0]))
+    print("  out[:256] %.2e  core heads %s" % (e_out, ["%.2e" % e for e in errs]))
+    assert e_out < TOL_BF16 and max(errs) < TOL_BF16
