@@ -155,9 +155,19 @@ def test_outputs_stay_in_bounds():
 
 
 def test_bf16_output():
+    """bfloat16 output equals the float32 output of the same kernel rounded to
+    bfloat16 (same arithmetic, only the store differs)."""
     announce("prefill bf16 out")
     rng = np.random.default_rng(7)
     d = synth.core_inputs(rng, 128, 2, bf16=True)
-    o, _ = gpu_prefill(d, out_dtype=torch.bfloat16)
+    o16, s16 = gpu_prefill(d, out_dtype=torch.bfloat16)
+    o32, s32 = gpu_prefill(d, out_dtype=torch.float32)
+    diff = (o16.float() - o32.to(torch.bfloat16).float()).abs()
+    if diff.max() > 0:
+        idx = np.unravel_index(int(torch.argmax(diff).item()), tuple(diff.shape))
+        print("  max diff at", idx, "bf16", o16[idx].item(), "fp32", o32[idx].item(),
+              "mismatches", int((diff > 0).sum().item()), flush=True)
+    assert torch.equal(o16.float(), o32.to(torch.bfloat16).float())
+    assert torch.equal(s16, s32)
     ro, _ = oracle(d)
-    assert relerr(host64(o), ro) < 6e-3
+    assert relerr(host64(o16), ro) < 6e-3
