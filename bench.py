@@ -114,18 +114,35 @@ def bench_layer(torch, steps, warmup):
     return ms, mixer.flops_per_token() * x.shape[0]
 
 
-def cpu_baseline(d):
-    """The FP64 oracle (token-serial, threads over heads) on the whole prefill
-    workload, timed on this host."""
+def cpu_baseline(d, min_seconds=10.0):
+    """The FP64 oracle (token-serial, threads over heads) on the prefill
+    workload, timed on this host: the whole 4096-token sequence is run again
+    until at least `min_seconds` of wall time have passed."""
     from oracle import reference as R
     threads = R.default_threads()
-    t0 = time.perf_counter()
-    R.kda_serial(d["q"].vals, d["k"].vals, d["v"].vals, d["g"].vals, d["beta"].vals, nthreads=threads)
-    t = time.perf_counter() - t0
     T = d["q"].shape[0]
-    return {"value": T / t, "unit": "tokens/s/layer", "cores": threads, "kind": "oracle",
-            "sample": "whole prefill workload (4096 tokens x 64 heads, d=128), fp64 token-serial, "
-                      "%.2f s wall on %d threads" % (t, threads)}
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        R.kda_serial(d["q"].vals, d["k"].vals, d["v"].vals, d["g"].vals, d["beta"].vals, nthreads=threads)
+        reps += 1
+        t = time.perf_counter() - t0
+        if t >= min_seconds:
+            break
+    return {"value": reps * T / t, "unit": "tokens/s/layer", "cores": threads, "kind": "oracle",
+            "sample": "the prefill workload (4096 tokens x 64 heads, d=128, zero initial state) run %d times "
+                      "back to back, fp64 token-serial, %.1f s wall on %d threads" % (reps, t, threads)}
+
+
+def bench_copy(torch, steps, warmup):
+    """A plain device-to-device copy of 256 MiB: the known-size kernel that
+    calibrates the HBM byte counters."""
+    n = 64 << 20
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    ms, _ = timed(torch, lambda: dst.copy_(src), steps, warmup)
+    return {"workload": "torch copy_ of 256 MiB float32", "read_bytes_per_launch": n * 4,
+            "write_bytes_per_launch": n * 4, "ms_per_step": ms, "GB/s": 2 * n * 4 / (ms * 1e-3) / 1e9}
 
 
 def main():
@@ -135,8 +152,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--skip-layer", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "layer"], default=None,
-                    help="time one path only (for profiler runs)")
+    ap.add_argument("--only", choices=["prefill", "decode", "layer", "copy"], default=None,
+                    help="time one path only (for profiler runs); 'copy' times the plain copy that calibrates byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (requested --gpus %d)" % args.gpus,
@@ -197,6 +214,9 @@ def main():
         out["layer"] = {"workload": "full token-mixer layer T=8192 hidden=4096 H=64: projections, conv, gate, "
                                     "KDA core, norm x gate, output projection",
                         "ms_per_step": ms, "tokens/s": 8192 / (ms * 1e-3), "TFLOP/s": flops / (ms * 1e-3) / 1e12}
+    if args.only == "copy":
+        log("copy 256 MiB")
+        out["copy"] = bench_copy(torch, args.steps, args.warmup)
     print(json.dumps(out), flush=True)
 
 

@@ -25,25 +25,27 @@
 // log-retention is clamped at -5 ("safe forget gate ... lower bound -5" in the
 // flozi.net section above): 15 tokens x 5 x log2(e) < 116 < 127.
 //
-// Work split. A workgroup (4 wavefronts) owns one (sequence, head, 64 value
-// columns); wavefront w owns 16 columns and keeps its 128 x 16 float32 slice
-// of the state in registers for the whole sequence (value columns of the state
-// evolve independently). Per chunk:
-//   P0  each thread (2 key channels, one 16-token block) sums its block's
-//       log-retention; the block totals are exchanged through LDS.
-//   P1  the same thread forms the decay factors by running products of
-//       alpha = 2^g and writes the key-side operands k o 2^l, q o 2^l, k o 2^s
-//       (float32) and the transposed K-bar (float16); it keeps k o 2^b and
-//       q o 2^b (float16) in registers.
-//   P2  each wavefront computes some 16 x 16 blocks of A and P on MFMA and
-//       one diagonal-block inverse.
+// Work split. A workgroup of 8 wavefronts (2 per SIMD, so one wavefront's
+// latency hides behind the other's work) owns one (sequence, head); wavefront
+// w owns value columns 16w..16w+15 and keeps its 128 x 16 float32 slice of the
+// state in registers for the whole sequence (value columns of the state evolve
+// independently). Per chunk:
+//   P0  each producer thread (2 key channels, half of a 16-token block) sums
+//       its 8 log-retentions; the partial sums are exchanged through LDS.
+//   P1  it forms the decay factors by running products of alpha = 2^g and
+//       writes the key-side operands k o 2^l, q o 2^l, k o 2^s (float32) and
+//       the transposed K-bar (float16); it keeps k o 2^b and q o 2^b (float16)
+//       in registers.
+//   P2  wavefronts 0..NB-1 compute the diagonal blocks of A and P and the
+//       diagonal inverses; the others compute the off-diagonal blocks.
 //   P2b the float32 region is dead: k o 2^b and q o 2^b are written over it.
 //   P3  every wavefront runs its own value-side chain (X, block forward
 //       substitution, O, state update) on MFMA with no further barrier.
-// The next chunk's inputs are loaded into registers while a chunk computes.
-// Workgroups of one head are mapped to the same XCD so that the second one
-// finds q, k, g in that XCD's L2.
-//
+// Global accesses go through buffer descriptors whose byte range ends at the
+// chunk's last valid row: loads past it return zero and stores are dropped,
+// so ragged chunks need no masks or branches. The next chunk's inputs are
+// loaded into registers while a chunk computes.
+
 // Precision (bfloat16 inputs): the key-side operands are staged in LDS as
 // float32 and rounded once per use. Off-diagonal blocks and the whole value
 // side run float16 MFMA (their operands are bounded by 1 or by the state and
@@ -59,16 +61,52 @@
 namespace kda {
 namespace {
 
-constexpr int D = 128;        // dk = dv
-constexpr int kWaves = 4;
+constexpr int D = 128;  // dk = dv
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kDvBlock = 16 * kWaves;  // value columns per workgroup
-constexpr int kDvBlocks = D / kDvBlock;
 
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef __bf16 b4 __attribute__((ext_vector_type(4)));
 typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// ---------------------------------------------------------------- buffers
+// Raw buffer over [base, base + bytes): loads beyond return 0, stores beyond
+// are dropped (the descriptor's range check).
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes)
+{
+    const uint32_t nr = bytes <= 0 ? 0u : (bytes >= 0xffffffffll ? 0xffffffffu : (uint32_t)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nr, 0x00020000);
+}
+template <typename T> struct Io;
+template <> struct Io<bf16_t> {
+    using pair_t = uint32_t;
+    __device__ static pair_t ld_pair(rsrc_t r, int off, int soff) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0); }
+    __device__ static f32x2 unpack(pair_t u) { return f32x2{__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u)}; }
+    __device__ static uint32_t ld_one(rsrc_t r, int off, int soff) { return __builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0); }
+    __device__ static float one(uint32_t u) { return __uint_as_float(u << 16); }
+    __device__ static void st(rsrc_t r, int off, int soff, float v)
+    {
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)v), r, off, soff, 0);
+    }
+};
+template <> struct Io<float> {
+    using pair_t = uint2;
+    __device__ static pair_t ld_pair(rsrc_t r, int off, int soff)
+    {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0);
+        return make_uint2(v[0], v[1]);
+    }
+    __device__ static f32x2 unpack(pair_t u) { return f32x2{__uint_as_float(u.x), __uint_as_float(u.y)}; }
+    __device__ static uint32_t ld_one(rsrc_t r, int off, int soff) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0); }
+    __device__ static float one(uint32_t u) { return __uint_as_float(u); }
+    __device__ static void st(rsrc_t r, int off, int soff, float v)
+    {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, soff, 0);
+    }
+};
 
 // ---------------------------------------------------------------- MFMA ops
 // Operand layout of the 16 x 16 MFMAs used here. A K16 slab: lane
@@ -114,9 +152,9 @@ template <> struct Ops<false> {
     __device__ static F4 cvt(f32x4 x) { return to_h4(x); }
     __device__ static F8 cat2(F4 a, F4 b) { return cat(a, b); }
     __device__ static F4 lds(const OT* p) { return *reinterpret_cast<const h4*>(p); }
-    // A K16 step runs as the K32 instruction with a zero second half: dependent
-    // chains that mixed the 16x16x16 and 16x16x32 forms returned stale
-    // accumulator elements on gfx950, so only the K32 form is used.
+    // Only the 16x16x32 instruction form is used: dependent chains that mixed
+    // the 16x16x16 and 16x16x32 forms returned stale accumulator elements on
+    // gfx950, so a K16 step is the K32 instruction with a zero second half.
     __device__ static f32x4 mma16(F4 a, F4 b, f32x4 c)
     {
         const F4 z = {(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
@@ -139,6 +177,15 @@ template <> struct Ops<false> {
         c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, c, 0, 0, 0);
         c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, c, 0, 0, 0);
         return c;
+    }
+    // two operand-type values of channels c, c+1 packed for one LDS store
+    using P2 = h2;
+    __device__ static P2 pack2(float x, float y) { return h2{(_Float16)x, (_Float16)y}; }
+    // 8 consecutive tokens of one channel for the transposed K-bar
+    __device__ static void store8(OT* p, const float* v)
+    {
+        *reinterpret_cast<h8*>(p) = h8{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3],
+                                       (_Float16)v[4], (_Float16)v[5], (_Float16)v[6], (_Float16)v[7]};
     }
 };
 
@@ -165,25 +212,14 @@ template <> struct Ops<true> {
     {
         return mma_f32_k16(a1, b1, mma_f32_k16(a0, b0, c));
     }
+    using P2 = f32x2;
+    __device__ static P2 pack2(float x, float y) { return f32x2{x, y}; }
+    __device__ static void store8(OT* p, const float* v)
+    {
+        *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    }
 };
-
-// Two consecutive input elements kept raw in a register between load and use.
-template <typename T> struct Pair;
-template <> struct Pair<bf16_t> {
-    using type = uint32_t;
-    __device__ static f32x2 unpack(uint32_t u) { return f32x2{__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u)}; }
-};
-template <> struct Pair<float> {
-    using type = uint2;
-    __device__ static f32x2 unpack(uint2 u) { return f32x2{__uint_as_float(u.x), __uint_as_float(u.y)}; }
-};
-template <typename T>
-__device__ __forceinline__ typename Pair<T>::type ldpair(const T* p)
-{
-    return *reinterpret_cast<const typename Pair<T>::type*>(p);
-}
-__device__ __forceinline__ float to_f32(float x) { return x; }
-__device__ __forceinline__ float to_f32(bf16_t x) { return bf16_to_f32(x); }
 
 // index of the off-diagonal block pair (R, I), I < R
 __host__ __device__ constexpr int pair_id(int R, int I) { return R * (R - 1) / 2 + I; }
@@ -221,7 +257,7 @@ struct __attribute__((aligned(16))) Smem {
     OT Pb[NB * (NB + 1) / 2][16][16];       // P lower-triangle blocks
     float Fd[NB][D];                        // 2^-G_R
     float Fo[NPAIR > 0 ? NPAIR : 1][D];     // 2^(rho_R - rho_{I+1})
-    float Gt[NB][D];                        // block totals of the log-retention (base 2)
+    float Gp[NB][2][D];                     // half-block sums of the log-retention (base 2)
     float bC[D];                            // 2^b_C
     float beta[C];
 };
@@ -234,8 +270,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
     using F4 = typename O::F4;
     using F8 = typename O::F8;
     using SM = Smem<F32P>;
+    using IN = Io<TIN>;
+    using PT = typename IN::pair_t;
     constexpr int C = SM::C;
     constexpr int NB = SM::NB;
+    constexpr int NPAIR = SM::NPAIR;
+    constexpr int ES = sizeof(TIN);
 
     __shared__ SM sm;
 
@@ -245,15 +285,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
     const int m16 = lane & 15;
     const int q4 = lane >> 4;
 
-    // XCD-aware order: consecutive logical ids (the value blocks of one head)
-    // land on the same XCD (workgroups are dealt round-robin over 8 XCDs).
-    int bid = blockIdx.x;
-    if ((gridDim.x & 7) == 0) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
-    const int dvblk = bid % kDvBlocks;
-    bid /= kDvBlocks;
+    const int bid = blockIdx.x;
     const int h = bid % a.H;
     const int n = bid / a.H;
-    const int jcol = dvblk * kDvBlock + wave * 16 + m16;  // this lane's value column
+    const int jcol = wave * 16 + m16;  // this lane's value column
 
     int64_t seq_s, seq_e;
     if (a.cu_seqlens) {
@@ -277,45 +312,49 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
         for (int t = 0; t < 8; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    const int64_t tok_stride = (int64_t)a.H * D;
-    const TIN* qg = static_cast<const TIN*>(a.q) + (int64_t)h * D;
-    const TIN* kg = static_cast<const TIN*>(a.k) + (int64_t)h * D;
-    const TIN* gg = static_cast<const TIN*>(a.g) + (int64_t)h * D;
-    const TIN* vg = static_cast<const TIN*>(a.v) + (int64_t)h * D + jcol;
-    const TIN* bg = static_cast<const TIN*>(a.beta) + h;
-    TOUT* og = static_cast<TOUT*>(a.o) + (int64_t)h * D + jcol;
+    const int ts = a.H * D;  // token stride in elements
+    const TIN* qg = static_cast<const TIN*>(a.q);
+    const TIN* kg = static_cast<const TIN*>(a.k);
+    const TIN* gg = static_cast<const TIN*>(a.g);
+    const TIN* vg = static_cast<const TIN*>(a.v);
+    const TIN* bg = static_cast<const TIN*>(a.beta);
+    TOUT* og = static_cast<TOUT*>(a.o);
     const float lbl = a.lower_bound * kLog2e;
 
-    // Raw inputs of one chunk, loaded one chunk ahead. Rows past the end of
-    // the sequence load a valid row (clamped) and are zeroed on use, so every
-    // load is unconditional and all of them are in flight together.
-    using PT = typename Pair<TIN>::type;
-    const int R = wave;       // P0/P1 token block of this thread
-    const int c0 = 2 * lane;  // P0/P1 key channels c0, c0 + 1
-    PT rk[16], rq[16], rg[16];
-    TIN rv[NB][4];            // v[16R' + 4q + i][jcol]
-    TIN rb = TIN(0);
-    const int ts32 = a.H * D;  // token stride in elements (fits 32 bits)
+    // producer role (P0, P1, P2b): channels c0, c0+1 of tokens 8 hh .. 8 hh + 7
+    // of block R; wavefronts 0 .. 2 NB - 1
+    const bool prod = wave < 2 * NB;
+    const int R = wave % NB;
+    const int hh = wave / NB;
+    const int c0 = 2 * lane;
+    const int rbase = 16 * R + 8 * hh;
+
+    PT rk[8], rq[8], rg[8];  // next chunk's k, q, g for this producer
+    uint32_t rv[NB][4];      // v[16R' + 4q + i][jcol] (raw bits)
+    uint32_t rb = 0;         // beta[tid]
     auto load_kqg = [&](int64_t c_s, int nt) {  // consumed in P0/P1
-        const int64_t base = c_s * tok_stride;
-        if (R < NB) {
-            const TIN *kb_ = kg + base, *qb_ = qg + base, *gb_ = gg + base;
+        const int64_t bytes = (int64_t)nt * ts * ES;
+        const rsrc_t rk_ = make_rsrc(kg + c_s * ts, bytes), rq_ = make_rsrc(qg + c_s * ts, bytes),
+                     rg_ = make_rsrc(gg + c_s * ts, bytes);
+        if (prod) {
+            const int voff = (c0 + h * D) * ES;        // per lane
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                const int off = min(16 * R + rr, nt - 1) * ts32 + c0;
-                rk[rr] = ldpair(kb_ + off);
-                rq[rr] = ldpair(qb_ + off);
-                rg[rr] = ldpair(gb_ + off);
+            for (int t = 0; t < 8; ++t) {
+                const int soff = (rbase + t) * ts * ES;  // wave-uniform row term
+                rk[t] = IN::ld_pair(rk_, voff, soff);
+                rq[t] = IN::ld_pair(rq_, voff, soff);
+                rg[t] = IN::ld_pair(rg_, voff, soff);
             }
         }
-        if (tid < C) rb = bg[(c_s + min(tid, nt - 1)) * a.H];
+        if (tid < C) rb = IN::ld_one(make_rsrc(bg + c_s * a.H, (int64_t)nt * a.H * ES), (tid * a.H + h) * ES, 0);
     };
     auto load_v = [&](int64_t c_s, int nt) {  // consumed in P3
-        const TIN* vb_ = vg + c_s * tok_stride;
+        const rsrc_t rv_ = make_rsrc(vg + c_s * ts, (int64_t)nt * ts * ES);
+        const int voff = (4 * q4 * ts + h * D + jcol) * ES;
 #pragma unroll
         for (int Rr = 0; Rr < NB; ++Rr)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) rv[Rr][i] = vb_[min(16 * Rr + 4 * q4 + i, nt - 1) * ts32];
+            for (int i = 0; i < 4; ++i) rv[Rr][i] = IN::ld_one(rv_, voff, (16 * Rr + i) * ts * ES);
     };
     if (seq_s < seq_e) {
         load_kqg(seq_s, (int)min<int64_t>(C, seq_e - seq_s));
@@ -325,95 +364,80 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
     for (int64_t cs = seq_s; cs < seq_e; cs += C) {
         const int ntok = (int)min<int64_t>(C, seq_e - cs);
 
-        // ---------------- P0: block totals of the log-retention (base 2)
-        f32x2 g2[16];
-        if (R < NB) {
+        // ---------------- P0: half-block sums of the log-retention (base 2)
+        f32x2 g2[8];
+        if (prod) {
             f32x2 G = {0.f, 0.f};
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                const f32x2 gv = Pair<TIN>::unpack(rg[rr]);
-                const bool valid = 16 * R + rr < ntok;
-                g2[rr] = valid ? f32x2{fmaxf(gv.x * kLog2e, lbl), fmaxf(gv.y * kLog2e, lbl)} : f32x2{0.f, 0.f};
-                G += g2[rr];
+            for (int t = 0; t < 8; ++t) {
+                const f32x2 gv = IN::unpack(rg[t]);  // rows past the chunk read as 0
+                g2[t] = f32x2{fmaxf(gv.x * kLog2e, lbl), fmaxf(gv.y * kLog2e, lbl)};
+                G += g2[t];
             }
-            *reinterpret_cast<f32x2*>(&sm.Gt[R][c0]) = G;
+            *reinterpret_cast<f32x2*>(&sm.Gp[R][hh][c0]) = G;
         }
-        if (tid < C) sm.beta[tid] = tid < ntok ? to_f32(rb) : 0.0f;
+        if (tid < C) sm.beta[tid] = IN::one(rb);
         __syncthreads();
 
         // ---------------- P1: decay factors and key-side operands
-        // kt/qt: k o 2^b and q o 2^b in the operand type, written in P2b
-        F4 kt[8], qt[8];
-        if (R < NB) {
-            f32x2 rho_R = {0.f, 0.f}, rho_R1, bCv = {0.f, 0.f};
+        typename O::P2 kt2[8], qt2[8];  // k o 2^b, q o 2^b of this thread's 8 tokens
+        if (prod) {
+            f32x2 rho_R = {0.f, 0.f}, bCv = {0.f, 0.f};
 #pragma unroll
             for (int J = 0; J < NB; ++J) {
-                const f32x2 gJ = *reinterpret_cast<const f32x2*>(&sm.Gt[J][c0]);
+                const f32x2 gJ = *reinterpret_cast<const f32x2*>(&sm.Gp[J][0][c0]) +
+                                 *reinterpret_cast<const f32x2*>(&sm.Gp[J][1][c0]);
                 if (J < R) rho_R += gJ;
                 bCv += gJ;
             }
-            const f32x2 GR = *reinterpret_cast<const f32x2*>(&sm.Gt[R][c0]);
-            rho_R1 = rho_R + GR;
-            // factor tables for P2 and P3 (this thread's two channels)
-            *reinterpret_cast<f32x2*>(&sm.Fd[R][c0]) = f32x2{exp2_fast(-GR.x), exp2_fast(-GR.y)};
-            {
+            const f32x2 G0 = *reinterpret_cast<const f32x2*>(&sm.Gp[R][0][c0]);
+            const f32x2 G1 = *reinterpret_cast<const f32x2*>(&sm.Gp[R][1][c0]);
+            const f32x2 GR = G0 + G1;
+            if (hh == 0) {
+                // factor tables for P2 and P3 (this thread's two channels)
+                *reinterpret_cast<f32x2*>(&sm.Fd[R][c0]) = f32x2{exp2_fast(-GR.x), exp2_fast(-GR.y)};
                 f32x2 rho_I1 = {0.f, 0.f};
 #pragma unroll
                 for (int I = 0; I < NB - 1; ++I) {
-                    rho_I1 += *reinterpret_cast<const f32x2*>(&sm.Gt[I][c0]);
+                    rho_I1 += *reinterpret_cast<const f32x2*>(&sm.Gp[I][0][c0]) +
+                              *reinterpret_cast<const f32x2*>(&sm.Gp[I][1][c0]);
                     if (I < R)  // pair (R, I): index R (R - 1) / 2 + I
                         *reinterpret_cast<f32x2*>(&sm.Fo[R * (R - 1) / 2 + I][c0]) =
                             f32x2{exp2_fast(rho_R.x - rho_I1.x), exp2_fast(rho_R.y - rho_I1.y)};
                 }
+                if (R == 0) *reinterpret_cast<f32x2*>(&sm.bC[c0]) = f32x2{exp2_fast(bCv.x), exp2_fast(bCv.y)};
             }
-            if (R == 0) *reinterpret_cast<f32x2*>(&sm.bC[c0]) = f32x2{exp2_fast(bCv.x), exp2_fast(bCv.y)};
             const f32x2 DR = {exp2_fast(rho_R.x), exp2_fast(rho_R.y)};
-            const f32x2 fb = {exp2_fast(bCv.x - rho_R1.x), exp2_fast(bCv.y - rho_R1.y)};
+            const f32x2 fb = {exp2_fast(bCv.x - rho_R.x - GR.x), exp2_fast(bCv.y - rho_R.y - GR.y)};
 
-            // forward: e_l = prod_{j<=r} alpha_j ; reverse: e_s = prod_{j>r} alpha_j
-            f32x2 al[16];
+            // forward: e_l = prod_{j<=r} alpha_j over the block (starts after half 0)
+            f32x2 al[8];
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) al[rr] = f32x2{exp2_fast(g2[rr].x), exp2_fast(g2[rr].y)};
-            f32x2 el = {1.f, 1.f};
-            f32x4 k4[2], q4v[2];  // 4 tokens of k o 2^b / q o 2^b per channel
+            for (int t = 0; t < 8; ++t) al[t] = f32x2{exp2_fast(g2[t].x), exp2_fast(g2[t].y)};
+            f32x2 el = hh ? f32x2{exp2_fast(G0.x), exp2_fast(G0.y)} : f32x2{1.f, 1.f};
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                const bool valid = 16 * R + rr < ntok;
-                el *= al[rr];
-                f32x2 kv = Pair<TIN>::unpack(rk[rr]), qv = Pair<TIN>::unpack(rq[rr]);
-                kv = valid ? kv : f32x2{0.f, 0.f};
-                qv = valid ? qv : f32x2{0.f, 0.f};
-                const int r = 16 * R + rr;
+            for (int t = 0; t < 8; ++t) {
+                el *= al[t];
+                const f32x2 kv = IN::unpack(rk[t]), qv = IN::unpack(rq[t]);
                 const f32x2 klv = kv * el, qlv = qv * el;
-                *reinterpret_cast<f32x2*>(&sm.key.f.KL[r][c0]) = klv;
-                *reinterpret_cast<f32x2*>(&sm.key.f.QL[r][c0]) = qlv;
-                const f32x2 ktt = klv * DR, qtt = qlv * DR;
-                k4[0][rr & 3] = ktt.x; k4[1][rr & 3] = ktt.y;
-                q4v[0][rr & 3] = qtt.x; q4v[1][rr & 3] = qtt.y;
-                if ((rr & 3) == 3) {  // kt[4e + j]: channel c0 + e, tokens 16R + 4j .. +3
-                    kt[rr >> 2] = O::cvt(k4[0]);
-                    kt[4 + (rr >> 2)] = O::cvt(k4[1]);
-                    qt[rr >> 2] = O::cvt(q4v[0]);
-                    qt[4 + (rr >> 2)] = O::cvt(q4v[1]);
-                }
+                *reinterpret_cast<f32x2*>(&sm.key.f.KL[rbase + t][c0]) = klv;
+                *reinterpret_cast<f32x2*>(&sm.key.f.QL[rbase + t][c0]) = qlv;
+                kt2[t] = O::pack2(klv.x * DR.x, klv.y * DR.y);
+                qt2[t] = O::pack2(qlv.x * DR.x, qlv.y * DR.y);
             }
-            f32x2 es = {1.f, 1.f};
-            f32x4 kb4[2];
+            // reverse: e_s = prod_{j>r} alpha_j over the block (starts before half 1)
+            f32x2 es = hh ? f32x2{1.f, 1.f} : f32x2{exp2_fast(G1.x), exp2_fast(G1.y)};
+            float kb0[8], kb1[8];
 #pragma unroll
-            for (int rr = 15; rr >= 0; --rr) {
-                const bool valid = 16 * R + rr < ntok;
-                f32x2 kv = Pair<TIN>::unpack(rk[rr]);
-                kv = valid ? kv : f32x2{0.f, 0.f};
-                const f32x2 ksv = kv * es;
-                *reinterpret_cast<f32x2*>(&sm.key.f.KS[16 * R + rr][c0]) = ksv;
-                kb4[0][rr & 3] = ksv.x * fb.x;
-                kb4[1][rr & 3] = ksv.y * fb.y;
-                if ((rr & 3) == 0) {  // transposed K-bar: row = channel, tokens 16R + rr .. +3
-                    *reinterpret_cast<F4*>(&sm.KbT[c0][16 * R + rr]) = O::cvt(kb4[0]);
-                    *reinterpret_cast<F4*>(&sm.KbT[c0 + 1][16 * R + rr]) = O::cvt(kb4[1]);
-                }
-                es *= al[rr];
+            for (int t = 7; t >= 0; --t) {
+                const f32x2 ksv = IN::unpack(rk[t]) * es;
+                *reinterpret_cast<f32x2*>(&sm.key.f.KS[rbase + t][c0]) = ksv;
+                kb0[t] = ksv.x * fb.x;
+                kb1[t] = ksv.y * fb.y;
+                es *= al[t];
             }
+            O::store8(&sm.KbT[c0][rbase], kb0);
+            O::store8(&sm.KbT[c0 + 1][rbase], kb1);
         }
         // the next chunk's key-side inputs stream in while this chunk computes
         if (cs + C < seq_e) load_kqg(cs + C, (int)min<int64_t>(C, seq_e - cs - C));
@@ -455,47 +479,43 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
             for (int it = 0; it < 15; ++it) Y = O::mma16(nA, O::cvt(Y), eye);
 #pragma unroll
             for (int i = 0; i < 4; ++i) sm.Tb[Rd][4 * q4 + i][m16] = (OT)Y[i];
+        } else {
+            // off-diagonal pairs on the remaining wavefronts
+#pragma unroll
+            for (int Rr = 1; Rr < NB; ++Rr)
+#pragma unroll
+                for (int I = 0; I < Rr; ++I) {
+                    const int pid = pair_id(Rr, I);
+                    if (NB + pid % (kWaves - NB) != wave) continue;
+                    f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const int c = 32 * s + 4 * q4;
+                        const float* kl = &sm.key.f.KL[16 * Rr + m16][c];
+                        const float* ql = &sm.key.f.QL[16 * Rr + m16][c];
+                        const float* ks = &sm.key.f.KS[16 * I + m16][c];
+                        const F8 b = O::cat2(O::cvt(ld4f(ks) * ld4f(&sm.Fo[pid][c])),
+                                             O::cvt(ld4f(ks + 16) * ld4f(&sm.Fo[pid][c + 16])));
+                        accA = O::mma32(O::cat2(O::cvt(ld4f(kl)), O::cvt(ld4f(kl + 16))), b, accA);
+                        accP = O::mma32(O::cat2(O::cvt(ld4f(ql)), O::cvt(ld4f(ql + 16))), b, accP);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = 4 * q4 + i;
+                        sm.An[pid][row][m16] = (OT)(-accA[i] * sm.beta[16 * Rr + row]);
+                        sm.Pb[tri_id(Rr, I)][row][m16] = (OT)accP[i];
+                    }
+                }
         }
-        // off-diagonal pairs, spread over the wavefronts
-#pragma unroll
-        for (int Rr = 1; Rr < NB; ++Rr)
-#pragma unroll
-            for (int I = 0; I < Rr; ++I) {
-                const int pid = pair_id(Rr, I);
-                if (pid % kWaves != wave) continue;
-                f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int c = 32 * s + 4 * q4;
-                    const float* kl = &sm.key.f.KL[16 * Rr + m16][c];
-                    const float* ql = &sm.key.f.QL[16 * Rr + m16][c];
-                    const float* ks = &sm.key.f.KS[16 * I + m16][c];
-                    const F8 b = O::cat2(O::cvt(ld4f(ks) * ld4f(&sm.Fo[pid][c])),
-                                         O::cvt(ld4f(ks + 16) * ld4f(&sm.Fo[pid][c + 16])));
-                    accA = O::mma32(O::cat2(O::cvt(ld4f(kl)), O::cvt(ld4f(kl + 16))), b, accA);
-                    accP = O::mma32(O::cat2(O::cvt(ld4f(ql)), O::cvt(ld4f(ql + 16))), b, accP);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 4 * q4 + i;
-                    sm.An[pid][row][m16] = (OT)(-accA[i] * sm.beta[16 * Rr + row]);
-                    sm.Pb[tri_id(Rr, I)][row][m16] = (OT)accP[i];
-                }
-            }
         __syncthreads();
 
         // ---------------- P2b: k o 2^b, q o 2^b over the dead float32 region
-        if (R < NB) {
+        if (prod) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * R + 4 * j + i;
-                    sm.key.h.Kt[r][c0] = kt[j][i];
-                    sm.key.h.Kt[r][c0 + 1] = kt[4 + j][i];
-                    sm.key.h.Qt[r][c0] = qt[j][i];
-                    sm.key.h.Qt[r][c0 + 1] = qt[4 + j][i];
-                }
+            for (int t = 0; t < 8; ++t) {
+                *reinterpret_cast<typename O::P2*>(&sm.key.h.Kt[rbase + t][c0]) = kt2[t];
+                *reinterpret_cast<typename O::P2*>(&sm.key.h.Qt[rbase + t][c0]) = qt2[t];
+            }
         }
         __syncthreads();
 
@@ -517,11 +537,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = 16 * Rr + 4 * q4 + i;
-                const float vv = r < ntok ? to_f32(rv[Rr][i]) : 0.0f;
-                X[Rr][i] = sm.beta[r] * (vv - accX[i]);
+                const int r = 16 * Rr + 4 * q4 + i;  // rows past the chunk: v = beta = 0
+                X[Rr][i] = sm.beta[r] * (IN::one(rv[Rr][i]) - accX[i]);
             }
             O1[Rr] = accO;
+            __builtin_amdgcn_sched_barrier(0);  // bound the scheduler's look-ahead (register pressure)
         }
         // block forward substitution: U_R = T_RR (X_R - sum_{I<R} A_RI U_I)
 #pragma unroll
@@ -535,7 +555,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
             const f32x4 U = O::mma16(O::lds(&sm.Tb[Rr][m16][4 * q4]), O::cvt(Y), f32x4{0.f, 0.f, 0.f, 0.f});
             UB[Rr] = O::cvt(U);
         }
-        // outputs O_R = scale (O1_R + sum_{I<=R} P_RI U_I)
+        // outputs O_R = scale (O1_R + sum_{I<=R} P_RI U_I); rows past the chunk are dropped
+        const rsrc_t ro_ = make_rsrc(og + cs * ts, (int64_t)ntok * ts * (int64_t)sizeof(TOUT));
 #pragma unroll
         for (int Rr = 0; Rr < NB; ++Rr) {
             f32x4 acc = O1[Rr];
@@ -545,10 +566,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
                                O::cat2(UB[I], UB[I + 1]), acc);
             if (!(Rr & 1)) acc = O::mma16(O::lds(&sm.Pb[tri_id(Rr, Rr)][m16][4 * q4]), UB[Rr], acc);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * Rr + 4 * q4 + i;
-                if (r < ntok) st(og + (cs + r) * tok_stride, a.scale * acc[i]);
-            }
+            for (int i = 0; i < 4; ++i)
+                Io<TOUT>::st(ro_, (4 * q4 * ts + h * D + jcol) * (int)sizeof(TOUT), (16 * Rr + i) * ts * (int)sizeof(TOUT),
+                             a.scale * acc[i]);
         }
         // state: S <- Diag(2^b_C) S + Kbar^T U
 #pragma unroll
@@ -565,17 +585,22 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
     }
 
     if (a.sT) {
+        // the empty asm keeps the compiler from computing these addresses before
+        // the chunk loop and holding them in registers across it
+        int off = 4 * q4 * D + jcol;
+        asm volatile("" : "+v"(off));
+        float* sT = a.sT + sbase + off;
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a.sT[sbase + (size_t)(16 * t + 4 * q4 + i) * D + jcol] = S[t][i];
+            for (int i = 0; i < 4; ++i) sT[(16 * t + i) * D] = S[t][i];
     }
 }
 
 template <bool F32P, typename TIN>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t s)
 {
-    dim3 grid((unsigned)((int64_t)a.num_seqs * a.H * kDvBlocks)), block(kThreads);
+    dim3 grid((unsigned)((int64_t)a.num_seqs * a.H)), block(kThreads);
     if (a.out_dtype == F32)
         hipLaunchKernelGGL((prefill_kernel<F32P, TIN, float>), grid, block, 0, s, a);
     else
