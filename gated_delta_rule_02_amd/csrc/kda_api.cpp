@@ -255,11 +255,22 @@ int kda_output_norm_gate(const void* o, kda_dtype o_dtype, const void* gate, int
 }
 
 // ---------------------------------------------------------------- prefill
+namespace {
+constexpr int64_t kChunk = 64;          // chunk of the bfloat16 forms
+constexpr int64_t kWindowChunks = 16;   // recommended window of the two-pass form
+size_t state_carry_bytes(int64_t units) { return (size_t)units * 128 * 128 * sizeof(float); }
+}  // namespace
+
 size_t kda_prefill_workspace_bytes(int64_t num_tokens, int num_seqs, int H, int dk, int dv,
                                    kda_dtype in_dtype)
 {
-    (void)num_tokens; (void)num_seqs; (void)H; (void)dk; (void)dv; (void)in_dtype;
-    return 0;
+    if (in_dtype != KDA_BF16 || num_tokens <= 0 || num_seqs < 1 || H < 1 || dk != 128 || dv != 128) return 0;
+    const int64_t units = (int64_t)num_seqs * H;
+    const int64_t max_chunks = (num_tokens + kChunk - 1) / kChunk;  // bounds every sequence's chunk count
+    const int64_t nwin = std::min(max_chunks, kWindowChunks);
+    size_t bytes = (size_t)(units * nwin) * prefill_split_slot_bytes();
+    if (nwin < max_chunks) bytes += state_carry_bytes(units);
+    return bytes;
 }
 
 int kda_prefill(const void* q, const void* k, const void* v, const void* g, const void* beta,
@@ -275,27 +286,46 @@ int kda_prefill(const void* q, const void* k, const void* v, const void* g, cons
             "kda_prefill: only dk = dv = 128 is supported (got %d, %d)", dk, dv);
     REQUIRE(num_tokens == 0 || (q && k && v && g && beta && o), KDA_ERR_INVALID_ARG,
             "kda_prefill: null tensor pointer");
-    for (const void* p : {q, k, v, g, beta, (const void*)initial_state, (const void*)final_state, (const void*)o})
+    for (const void* p : {q, k, v, g, beta, (const void*)initial_state, (const void*)final_state, (const void*)o,
+                          (const void*)workspace})
         REQUIRE(!p || aligned16(p), KDA_ERR_INVALID_ARG, "kda_prefill: pointers must be 16-byte aligned");
     int64_t seq_len = 0;
     int rc = check_cu(cu_seqlens_dev, cu_seqlens_host, num_seqs, num_tokens, &seq_len);
     if (rc != KDA_OK) return rc;
     REQUIRE((int64_t)num_seqs * H * 2 <= 0x7fffffff, KDA_ERR_INVALID_ARG, "kda_prefill: num_seqs*H too large");
-    const size_t need = kda_prefill_workspace_bytes(num_tokens, num_seqs, H, dk, dv, in_dtype);
-    REQUIRE(workspace_bytes >= need && (need == 0 || workspace), KDA_ERR_WORKSPACE,
-            "kda_prefill: workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+
+    // the two-pass form runs for bfloat16 inputs when a workspace is given
+    const bool split = in_dtype == KDA_BF16 && workspace != nullptr;
+    const int64_t units = (int64_t)num_seqs * H;
+    int64_t max_len = seq_len;
+    if (cu_seqlens_host)
+        for (int n = 0; n < num_seqs; ++n)
+            max_len = std::max<int64_t>(max_len, (int64_t)cu_seqlens_host[n + 1] - cu_seqlens_host[n]);
+    const int64_t max_chunks = (max_len + kChunk - 1) / kChunk;
+    if (split) {
+        const size_t slot = prefill_split_slot_bytes();
+        const size_t whole = (size_t)(units * std::max<int64_t>(max_chunks, 1)) * slot;
+        const size_t least = (size_t)units * slot + state_carry_bytes(units);
+        REQUIRE(workspace_bytes >= std::min(whole, least), KDA_ERR_WORKSPACE,
+                "kda_prefill: workspace of at least %zu bytes required (got %zu)", std::min(whole, least),
+                workspace_bytes);
+    }
 
     const size_t ei = esize(in_dtype), T = (size_t)num_tokens;
     const size_t sbytes = (size_t)num_seqs * H * 128 * 128 * 4;
     const Range ro = rng(o, T * H * 128 * esize(out_dtype));
     const Range rs0 = rng(initial_state, initial_state ? sbytes : 0), rsT = rng(final_state, final_state ? sbytes : 0);
+    const Range rws = rng(workspace, split ? workspace_bytes : 0);
     const Range ins[] = {rng(q, T * H * 128 * ei), rng(k, T * H * 128 * ei), rng(v, T * H * 128 * ei),
                          rng(g, T * H * 128 * ei), rng(beta, T * H * ei), rs0};
     for (const Range& r : ins) {
         REQUIRE(!overlap(r, ro), KDA_ERR_INVALID_ARG, "kda_prefill: o overlaps an input");
         if (r.p != rs0.p) REQUIRE(!overlap(r, rsT), KDA_ERR_INVALID_ARG, "kda_prefill: final_state overlaps an input");
+        REQUIRE(!overlap(r, rws), KDA_ERR_INVALID_ARG, "kda_prefill: workspace overlaps an input");
     }
     REQUIRE(!overlap(ro, rsT), KDA_ERR_INVALID_ARG, "kda_prefill: o overlaps final_state");
+    REQUIRE(!overlap(rws, ro) && !overlap(rws, rsT), KDA_ERR_INVALID_ARG,
+            "kda_prefill: workspace overlaps o or final_state");
     REQUIRE(!overlap(rs0, rsT) || (initial_state == final_state), KDA_ERR_INVALID_ARG,
             "kda_prefill: initial_state and final_state overlap without being the same buffer");
 
@@ -305,8 +335,10 @@ int kda_prefill(const void* q, const void* k, const void* v, const void* g, cons
     a.s0 = initial_state; a.sT = final_state; a.o = o;
     a.num_seqs = num_seqs; a.H = H; a.scale = scale; a.lower_bound = lower_bound;
     a.in_dtype = (DType)in_dtype; a.out_dtype = (DType)out_dtype;
-    (void)workspace;
-    return hip_status(launch_prefill(a, static_cast<hipStream_t>(hip_stream)), "kda_prefill");
+    const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    if (split)
+        return hip_status(launch_prefill_split(a, workspace, workspace_bytes, max_chunks, st), "kda_prefill");
+    return hip_status(launch_prefill(a, st), "kda_prefill");
 }
 
 // ---------------------------------------------------------------- GEMM

@@ -79,6 +79,12 @@ struct PrefillArgs {
     DType in_dtype, out_dtype;
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+// Two-pass form (bfloat16 inputs): per-chunk products in `ws`, then the state
+// recurrence. max_chunks = the largest number of 64-token chunks of one
+// sequence. ws_bytes must hold at least one chunk slot per (sequence, head),
+// plus the float32 state carry when the slots cannot hold every chunk.
+hipError_t launch_prefill_split(const PrefillArgs& a, void* ws, size_t ws_bytes, int64_t max_chunks, hipStream_t s);
+size_t prefill_split_slot_bytes();
 
 struct GemmArgs {
     const void *A, *B;

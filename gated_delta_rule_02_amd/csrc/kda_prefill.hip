@@ -1,280 +1,33 @@
-// kda_prefill.hip -- chunked KDA prefill over packed sequences on gfx950 MFMA.
+// kda_prefill.hip -- single-pass chunked KDA prefill over packed sequences.
 //
-// Computes, per (sequence, head), the recurrence of "Ling-3.1-flash: Grouped
-// Routing and Two Different MLA Caches" (flozi.net), section "KDA replaces a
-// token list with a recurrent matrix" (retention per key channel, delta-rule
-// write, read after the write), reorganised exactly over chunks of C tokens.
-//
-// The chunk form. For a chunk with start state S0 (dk x dv) and tokens
-// r = 0..C-1, let b_r = sum_{j<=r} g_j (per key channel, here in base 2). Then
-//   A[r,i] = beta_r sum_c k_rc k_ic 2^(b_rc - b_ic)   (i < r)
-//   U      = (I + A)^-1 X,    X = diag(beta) (V - (K o 2^B) S0)
-//   P[r,i] = sum_c q_rc k_ic 2^(b_rc - b_ic)           (i <= r)
-//   O      = scale ((Q o 2^B) S0 + P U)
-//   S_C    = Diag(2^b_C) S0 + (K o 2^(b_C - B))^T U
-// U are the corrected writes u_r = beta_r (v_r - S'_r^T k_r) of all tokens of
-// the chunk; the triangular solve replaces the token-serial dependency.
-//
-// Overflow-safe factorisation. The chunk is cut into NB = C/16 blocks of 16
-// tokens. With rho_R the cumulative log-retention before block R, l_r the
-// inclusive prefix sum inside r's block, s_i the sum over the tokens after i in
-// i's block, and G_R the block total:
-//   b_r - b_i = l_r + (rho_R - rho_{I+1}) + s_i   (i in block I < R: all <= 0)
-//   b_r - b_i = l_r + s_i - G_R                   (i, r in the same block R)
-// Every factor 2^x of a block product then lies in [2^-116, 2^116] because the
-// log-retention is clamped at -5 ("safe forget gate ... lower bound -5" in the
-// flozi.net section above): 15 tokens x 5 x log2(e) < 116 < 127.
-//
-// Work split. A workgroup of 8 wavefronts (2 per SIMD, so one wavefront's
-// latency hides behind the other's work) owns one (sequence, head); wavefront
-// w owns value columns 16w..16w+15 and keeps its 128 x 16 float32 slice of the
-// state in registers for the whole sequence (value columns of the state evolve
-// independently). Per chunk:
-//   P0  each producer thread (2 key channels, half of a 16-token block) sums
-//       its 8 log-retentions; the partial sums are exchanged through LDS.
-//   P1  it forms the decay factors by running products of alpha = 2^g and
-//       writes the key-side operands k o 2^l, q o 2^l, k o 2^s (float32) and
-//       the transposed K-bar (float16); it keeps k o 2^b and q o 2^b (float16)
-//       in registers.
-//   P2  wavefronts 0..NB-1 compute the diagonal blocks of A and P and the
-//       diagonal inverses; the others compute the off-diagonal blocks.
-//   P2b the float32 region is dead: k o 2^b and q o 2^b are written over it.
+// The chunk form, its overflow-safe factorisation and the chunk-local phases
+// P0 .. P2b are in kda_chunk.h. Here one workgroup of 8 wavefronts owns one
+// (sequence, head) for the whole sequence: wavefront w owns value columns
+// 16w .. 16w + 15 and keeps its 128 x 16 float32 slice of the state in
+// registers (value columns of the state evolve independently). After P2b,
 //   P3  every wavefront runs its own value-side chain (X, block forward
 //       substitution, O, state update) on MFMA with no further barrier.
 // Global accesses go through buffer descriptors whose byte range ends at the
 // chunk's last valid row: loads past it return zero and stores are dropped,
 // so ragged chunks need no masks or branches. The next chunk's inputs are
-// loaded into registers while a chunk computes.
-
-// Precision (bfloat16 inputs): the key-side operands are staged in LDS as
-// float32 and rounded once per use. Off-diagonal blocks and the whole value
-// side run float16 MFMA (their operands are bounded by 1 or by the state and
-// value magnitudes, so float16's range suffices and its 11-bit significand
-// keeps the error well inside the bound); A's diagonal blocks use bfloat16
-// (their right operand reaches 2^116); P's diagonal blocks use a hi+lo
-// bfloat16 split (3 MFMAs) because they dominate the output error otherwise.
-// Accumulation, the state and all exponents are float32. Float32 inputs run a
-// float32-MFMA variant with 32-token chunks.
-#include "kda_device.h"
-#include "kda_internal.h"
+// loaded into registers while a chunk computes. This path needs no workspace;
+// the two-pass path in kda_prefill_split.hip spreads the chunk-local work over
+// the whole GPU when a workspace is given.
+#include "kda_chunk.h"
 
 namespace kda {
 namespace {
-
-constexpr int D = 128;  // dk = dv
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
-
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef __bf16 b4 __attribute__((ext_vector_type(4)));
-typedef __bf16 b8 __attribute__((ext_vector_type(8)));
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-// ---------------------------------------------------------------- buffers
-// Raw buffer over [base, base + bytes): loads beyond return 0, stores beyond
-// are dropped (the descriptor's range check).
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes)
-{
-    const uint32_t nr = bytes <= 0 ? 0u : (bytes >= 0xffffffffll ? 0xffffffffu : (uint32_t)bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nr, 0x00020000);
-}
-template <typename T> struct Io;
-template <> struct Io<bf16_t> {
-    using pair_t = uint32_t;
-    __device__ static pair_t ld_pair(rsrc_t r, int off, int soff) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0); }
-    __device__ static f32x2 unpack(pair_t u) { return f32x2{__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u)}; }
-    __device__ static uint32_t ld_one(rsrc_t r, int off, int soff) { return __builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0); }
-    __device__ static float one(uint32_t u) { return __uint_as_float(u << 16); }
-    __device__ static void st(rsrc_t r, int off, int soff, float v)
-    {
-        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)v), r, off, soff, 0);
-    }
-};
-template <> struct Io<float> {
-    using pair_t = uint2;
-    __device__ static pair_t ld_pair(rsrc_t r, int off, int soff)
-    {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0);
-        return make_uint2(v[0], v[1]);
-    }
-    __device__ static f32x2 unpack(pair_t u) { return f32x2{__uint_as_float(u.x), __uint_as_float(u.y)}; }
-    __device__ static uint32_t ld_one(rsrc_t r, int off, int soff) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0); }
-    __device__ static float one(uint32_t u) { return __uint_as_float(u); }
-    __device__ static void st(rsrc_t r, int off, int soff, float v)
-    {
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, soff, 0);
-    }
-};
-
-// ---------------------------------------------------------------- MFMA ops
-// Operand layout of the 16 x 16 MFMAs used here. A K16 slab: lane
-// (m = lane % 16, q = lane / 16) holds A[m][4q..4q+3] and B[4q..4q+3][n = m];
-// the 16 x 16 result holds C[4q+i][n] in element i. A K32 step concatenates
-// two K16 slabs per lane (elements 0-3 from the first, 4-7 from the second);
-// A and B use the same assignment, so the product sums every k exactly once.
-__device__ __forceinline__ f32x4 ld4f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
-
-__device__ __forceinline__ h4 to_h4(f32x4 x)
-{
-    return h4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
-}
-__device__ __forceinline__ b4 to_b4(f32x4 x)
-{
-    return b4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
-}
-__device__ __forceinline__ f32x4 from_b4(b4 x)
-{
-    return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
-}
-__device__ __forceinline__ h8 cat(h4 a, h4 b) { return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7); }
-__device__ __forceinline__ b8 cat(b4 a, b4 b) { return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7); }
-
-__device__ __forceinline__ f32x4 mma_f32_k16(f32x4 a, f32x4 b, f32x4 c)
-{
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
-    return c;
-}
-
-template <bool F32P> struct Ops;
-
-// bfloat16 inputs: float16 operands (bfloat16 for the diagonal blocks)
-template <> struct Ops<false> {
-    using OT = _Float16;
-    using F4 = h4;
-    using F8 = h8;
-    static constexpr int C = 64;
-    static constexpr int PAD = 8;
-    __device__ static F4 cvt(f32x4 x) { return to_h4(x); }
-    __device__ static F8 cat2(F4 a, F4 b) { return cat(a, b); }
-    __device__ static F4 lds(const OT* p) { return *reinterpret_cast<const h4*>(p); }
-    // Only the 16x16x32 instruction form is used: dependent chains that mixed
-    // the 16x16x16 and 16x16x32 forms returned stale accumulator elements on
-    // gfx950, so a K16 step is the K32 instruction with a zero second half.
-    __device__ static f32x4 mma16(F4 a, F4 b, f32x4 c)
-    {
-        const F4 z = {(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(cat(a, z), cat(b, z), c, 0, 0, 0);
-    }
-    __device__ static f32x4 mma32(F8 a, F8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
-    // A's diagonal blocks: one bfloat16 product (operands up to 2^116)
-    __device__ static f32x4 diagA(f32x4 a0, f32x4 a1, f32x4 b0, f32x4 b1, f32x4 c)
-    {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(cat(to_b4(a0), to_b4(a1)), cat(to_b4(b0), to_b4(b1)), c, 0, 0, 0);
-    }
-    // P's diagonal blocks: hi + lo bfloat16 split of both operands (3 products)
-    __device__ static f32x4 diagP(f32x4 a0, f32x4 a1, f32x4 b0, f32x4 b1, f32x4 c)
-    {
-        const b4 ah0 = to_b4(a0), ah1 = to_b4(a1), bh0 = to_b4(b0), bh1 = to_b4(b1);
-        const b8 ah = cat(ah0, ah1), bh = cat(bh0, bh1);
-        const b8 al = cat(to_b4(a0 - from_b4(ah0)), to_b4(a1 - from_b4(ah1)));
-        const b8 bl = cat(to_b4(b0 - from_b4(bh0)), to_b4(b1 - from_b4(bh1)));
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, c, 0, 0, 0);
-        return c;
-    }
-    // two operand-type values of channels c, c+1 packed for one LDS store
-    using P2 = h2;
-    __device__ static P2 pack2(float x, float y) { return h2{(_Float16)x, (_Float16)y}; }
-    // 8 consecutive tokens of one channel for the transposed K-bar
-    __device__ static void store8(OT* p, const float* v)
-    {
-        *reinterpret_cast<h8*>(p) = h8{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3],
-                                       (_Float16)v[4], (_Float16)v[5], (_Float16)v[6], (_Float16)v[7]};
-    }
-};
-
-// float32 inputs: float32 MFMA throughout
-struct F32x8 {
-    f32x4 a, b;
-};
-template <> struct Ops<true> {
-    using OT = float;
-    using F4 = f32x4;
-    using F8 = F32x8;
-    static constexpr int C = 32;
-    static constexpr int PAD = 4;
-    __device__ static F4 cvt(f32x4 x) { return x; }
-    __device__ static F8 cat2(F4 a, F4 b) { return F8{a, b}; }
-    __device__ static F4 lds(const OT* p) { return *reinterpret_cast<const f32x4*>(p); }
-    __device__ static f32x4 mma16(F4 a, F4 b, f32x4 c) { return mma_f32_k16(a, b, c); }
-    __device__ static f32x4 mma32(F8 a, F8 b, f32x4 c) { return mma_f32_k16(a.b, b.b, mma_f32_k16(a.a, b.a, c)); }
-    __device__ static f32x4 diagA(f32x4 a0, f32x4 a1, f32x4 b0, f32x4 b1, f32x4 c)
-    {
-        return mma_f32_k16(a1, b1, mma_f32_k16(a0, b0, c));
-    }
-    __device__ static f32x4 diagP(f32x4 a0, f32x4 a1, f32x4 b0, f32x4 b1, f32x4 c)
-    {
-        return mma_f32_k16(a1, b1, mma_f32_k16(a0, b0, c));
-    }
-    using P2 = f32x2;
-    __device__ static P2 pack2(float x, float y) { return f32x2{x, y}; }
-    __device__ static void store8(OT* p, const float* v)
-    {
-        *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
-        *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
-    }
-};
-
-// index of the off-diagonal block pair (R, I), I < R
-__host__ __device__ constexpr int pair_id(int R, int I) { return R * (R - 1) / 2 + I; }
-// index of the lower-triangle block (R, I), I <= R
-__host__ __device__ constexpr int tri_id(int R, int I) { return R * (R + 1) / 2 + I; }
-
-template <bool F32P>
-struct __attribute__((aligned(16))) Smem {
-    using OT = typename Ops<F32P>::OT;
-    static constexpr int C = Ops<F32P>::C;
-    static constexpr int NB = C / 16;
-    static constexpr int NPAIR = NB * (NB - 1) / 2;
-    static constexpr int LDK = D + 4;               // row stride of the float32 [C][128] arrays
-    static constexpr int LDH = D + Ops<F32P>::PAD;  // row stride of the operand-type [C][128] arrays
-    static constexpr int LDT = C + Ops<F32P>::PAD;  // row stride of [128][C]
-    // P1 -> P2: key-side operands in float32. Their factors span 2^-116 .. 1
-    // and the diagonal blocks rescale them by up to 2^116, beyond float16's
-    // range, so each use rounds once to the MFMA operand type.
-    // P2b -> P3: the same bytes then hold k o 2^b and q o 2^b (operand type).
-    union Key {
-        struct {
-            float KL[C][LDK];  // k o 2^l   (left operand of A)
-            float QL[C][LDK];  // q o 2^l   (left operand of P)
-            float KS[C][LDK];  // k o 2^s   (right operand of A and P)
-        } f;
-        struct {
-            OT Kt[C][LDH];     // k o 2^b   (X = diag(beta)(V - Kt S))
-            OT Qt[C][LDH];     // q o 2^b   (O = Qt S + P U)
-        } h;
-    } key;
-    OT KbT[D][LDT];                         // (k o 2^(b_C - b))^T   (state update)
-    OT Nd[NB][16][16];                      // -A diagonal blocks (strictly lower, beta-scaled)
-    OT Tb[NB][16][16];                      // (I + A_RR)^-1
-    OT An[NPAIR > 0 ? NPAIR : 1][16][16];   // -A off-diagonal blocks (beta-scaled)
-    OT Pb[NB * (NB + 1) / 2][16][16];       // P lower-triangle blocks
-    float Fd[NB][D];                        // 2^-G_R
-    float Fo[NPAIR > 0 ? NPAIR : 1][D];     // 2^(rho_R - rho_{I+1})
-    float Gp[NB][2][D];                     // half-block sums of the log-retention (base 2)
-    float bC[D];                            // 2^b_C
-    float beta[C];
-};
 
 template <bool F32P, typename TIN, typename TOUT>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
 {
     using O = Ops<F32P>;
-    using OT = typename O::OT;
     using F4 = typename O::F4;
     using F8 = typename O::F8;
     using SM = Smem<F32P>;
     using IN = Io<TIN>;
-    using PT = typename IN::pair_t;
     constexpr int C = SM::C;
     constexpr int NB = SM::NB;
-    constexpr int NPAIR = SM::NPAIR;
     constexpr int ES = sizeof(TIN);
 
     __shared__ SM sm;
@@ -313,41 +66,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
     }
 
     const int ts = a.H * D;  // token stride in elements
-    const TIN* qg = static_cast<const TIN*>(a.q);
-    const TIN* kg = static_cast<const TIN*>(a.k);
-    const TIN* gg = static_cast<const TIN*>(a.g);
     const TIN* vg = static_cast<const TIN*>(a.v);
-    const TIN* bg = static_cast<const TIN*>(a.beta);
     TOUT* og = static_cast<TOUT*>(a.o);
-    const float lbl = a.lower_bound * kLog2e;
 
-    // producer role (P0, P1, P2b): channels c0, c0+1 of tokens 8 hh .. 8 hh + 7
-    // of block R; wavefronts 0 .. 2 NB - 1
-    const bool prod = wave < 2 * NB;
-    const int R = wave % NB;
-    const int hh = wave / NB;
-    const int c0 = 2 * lane;
-    const int rbase = 16 * R + 8 * hh;
-
-    PT rk[8], rq[8], rg[8];  // next chunk's k, q, g for this producer
-    uint32_t rv[NB][4];      // v[16R' + 4q + i][jcol] (raw bits)
-    uint32_t rb = 0;         // beta[tid]
-    auto load_kqg = [&](int64_t c_s, int nt) {  // consumed in P0/P1
-        const int64_t bytes = (int64_t)nt * ts * ES;
-        const rsrc_t rk_ = make_rsrc(kg + c_s * ts, bytes), rq_ = make_rsrc(qg + c_s * ts, bytes),
-                     rg_ = make_rsrc(gg + c_s * ts, bytes);
-        if (prod) {
-            const int voff = (c0 + h * D) * ES;        // per lane
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const int soff = (rbase + t) * ts * ES;  // wave-uniform row term
-                rk[t] = IN::ld_pair(rk_, voff, soff);
-                rq[t] = IN::ld_pair(rq_, voff, soff);
-                rg[t] = IN::ld_pair(rg_, voff, soff);
-            }
-        }
-        if (tid < C) rb = IN::ld_one(make_rsrc(bg + c_s * a.H, (int64_t)nt * a.H * ES), (tid * a.H + h) * ES, 0);
-    };
+    Front<F32P, TIN> fr(sm, a, h);
+    uint32_t rv[NB][4];  // v[16R + 4q + i][jcol] (raw bits)
     auto load_v = [&](int64_t c_s, int nt) {  // consumed in P3
         const rsrc_t rv_ = make_rsrc(vg + c_s * ts, (int64_t)nt * ts * ES);
         const int voff = (4 * q4 * ts + h * D + jcol) * ES;
@@ -357,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
             for (int i = 0; i < 4; ++i) rv[Rr][i] = IN::ld_one(rv_, voff, (16 * Rr + i) * ts * ES);
     };
     if (seq_s < seq_e) {
-        load_kqg(seq_s, (int)min<int64_t>(C, seq_e - seq_s));
+        fr.load(seq_s, (int)min<int64_t>(C, seq_e - seq_s));
         load_v(seq_s, (int)min<int64_t>(C, seq_e - seq_s));
     }
 
@@ -365,158 +88,21 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
         const int ntok = (int)min<int64_t>(C, seq_e - cs);
 
         // ---------------- P0: half-block sums of the log-retention (base 2)
-        f32x2 g2[8];
-        if (prod) {
-            f32x2 G = {0.f, 0.f};
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const f32x2 gv = IN::unpack(rg[t]);  // rows past the chunk read as 0
-                g2[t] = f32x2{fmaxf(gv.x * kLog2e, lbl), fmaxf(gv.y * kLog2e, lbl)};
-                G += g2[t];
-            }
-            *reinterpret_cast<f32x2*>(&sm.Gp[R][hh][c0]) = G;
-        }
-        if (tid < C) sm.beta[tid] = IN::one(rb);
+        fr.p0();
         __syncthreads();
 
         // ---------------- P1: decay factors and key-side operands
-        typename O::P2 kt2[8], qt2[8];  // k o 2^b, q o 2^b of this thread's 8 tokens
-        if (prod) {
-            f32x2 rho_R = {0.f, 0.f}, bCv = {0.f, 0.f};
-#pragma unroll
-            for (int J = 0; J < NB; ++J) {
-                const f32x2 gJ = *reinterpret_cast<const f32x2*>(&sm.Gp[J][0][c0]) +
-                                 *reinterpret_cast<const f32x2*>(&sm.Gp[J][1][c0]);
-                if (J < R) rho_R += gJ;
-                bCv += gJ;
-            }
-            const f32x2 G0 = *reinterpret_cast<const f32x2*>(&sm.Gp[R][0][c0]);
-            const f32x2 G1 = *reinterpret_cast<const f32x2*>(&sm.Gp[R][1][c0]);
-            const f32x2 GR = G0 + G1;
-            if (hh == 0) {
-                // factor tables for P2 and P3 (this thread's two channels)
-                *reinterpret_cast<f32x2*>(&sm.Fd[R][c0]) = f32x2{exp2_fast(-GR.x), exp2_fast(-GR.y)};
-                f32x2 rho_I1 = {0.f, 0.f};
-#pragma unroll
-                for (int I = 0; I < NB - 1; ++I) {
-                    rho_I1 += *reinterpret_cast<const f32x2*>(&sm.Gp[I][0][c0]) +
-                              *reinterpret_cast<const f32x2*>(&sm.Gp[I][1][c0]);
-                    if (I < R)  // pair (R, I): index R (R - 1) / 2 + I
-                        *reinterpret_cast<f32x2*>(&sm.Fo[R * (R - 1) / 2 + I][c0]) =
-                            f32x2{exp2_fast(rho_R.x - rho_I1.x), exp2_fast(rho_R.y - rho_I1.y)};
-                }
-                if (R == 0) *reinterpret_cast<f32x2*>(&sm.bC[c0]) = f32x2{exp2_fast(bCv.x), exp2_fast(bCv.y)};
-            }
-            const f32x2 DR = {exp2_fast(rho_R.x), exp2_fast(rho_R.y)};
-            const f32x2 fb = {exp2_fast(bCv.x - rho_R.x - GR.x), exp2_fast(bCv.y - rho_R.y - GR.y)};
-
-            // forward: e_l = prod_{j<=r} alpha_j over the block (starts after half 0)
-            f32x2 al[8];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) al[t] = f32x2{exp2_fast(g2[t].x), exp2_fast(g2[t].y)};
-            f32x2 el = hh ? f32x2{exp2_fast(G0.x), exp2_fast(G0.y)} : f32x2{1.f, 1.f};
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                el *= al[t];
-                const f32x2 kv = IN::unpack(rk[t]), qv = IN::unpack(rq[t]);
-                const f32x2 klv = kv * el, qlv = qv * el;
-                *reinterpret_cast<f32x2*>(&sm.key.f.KL[rbase + t][c0]) = klv;
-                *reinterpret_cast<f32x2*>(&sm.key.f.QL[rbase + t][c0]) = qlv;
-                kt2[t] = O::pack2(klv.x * DR.x, klv.y * DR.y);
-                qt2[t] = O::pack2(qlv.x * DR.x, qlv.y * DR.y);
-            }
-            // reverse: e_s = prod_{j>r} alpha_j over the block (starts before half 1)
-            f32x2 es = hh ? f32x2{1.f, 1.f} : f32x2{exp2_fast(G1.x), exp2_fast(G1.y)};
-            float kb0[8], kb1[8];
-#pragma unroll
-            for (int t = 7; t >= 0; --t) {
-                const f32x2 ksv = IN::unpack(rk[t]) * es;
-                *reinterpret_cast<f32x2*>(&sm.key.f.KS[rbase + t][c0]) = ksv;
-                kb0[t] = ksv.x * fb.x;
-                kb1[t] = ksv.y * fb.y;
-                es *= al[t];
-            }
-            O::store8(&sm.KbT[c0][rbase], kb0);
-            O::store8(&sm.KbT[c0 + 1][rbase], kb1);
-        }
+        fr.p1();
         // the next chunk's key-side inputs stream in while this chunk computes
-        if (cs + C < seq_e) load_kqg(cs + C, (int)min<int64_t>(C, seq_e - cs - C));
+        if (cs + C < seq_e) fr.load(cs + C, (int)min<int64_t>(C, seq_e - cs - C));
         __syncthreads();
 
         // ---------------- P2: blocks of A and P, diagonal inverses
-        if (wave < NB) {
-            const int Rd = wave;
-            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int c = 32 * s + 4 * q4;
-                const float* kl = &sm.key.f.KL[16 * Rd + m16][c];
-                const float* ql = &sm.key.f.QL[16 * Rd + m16][c];
-                const float* ks = &sm.key.f.KS[16 * Rd + m16][c];
-                const f32x4 x0 = ld4f(ks) * ld4f(&sm.Fd[Rd][c]);
-                const f32x4 x1 = ld4f(ks + 16) * ld4f(&sm.Fd[Rd][c + 16]);
-                accA = O::diagA(ld4f(kl), ld4f(kl + 16), x0, x1, accA);
-                accP = O::diagP(ld4f(ql), ld4f(ql + 16), x0, x1, accP);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 4 * q4 + i;  // row in block, column m16
-                const float b = sm.beta[16 * Rd + row];
-                sm.Nd[Rd][row][m16] = (OT)(row > m16 ? -accA[i] * b : 0.0f);
-                sm.Pb[tri_id(Rd, Rd)][row][m16] = (OT)(row >= m16 ? accP[i] : 0.0f);
-            }
-            // wavefront-local: the inverse below reads what this wavefront wrote
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-            // (I + N)^-1 = sum_{j<16} (-N)^j  (N strictly lower, N^16 = 0), Horner form
-            const F4 nA = O::lds(&sm.Nd[Rd][m16][4 * q4]);
-            f32x4 eye;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) eye[i] = (4 * q4 + i == m16) ? 1.0f : 0.0f;
-            f32x4 Y = eye;
-#pragma unroll
-            for (int it = 0; it < 15; ++it) Y = O::mma16(nA, O::cvt(Y), eye);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sm.Tb[Rd][4 * q4 + i][m16] = (OT)Y[i];
-        } else {
-            // off-diagonal pairs on the remaining wavefronts
-#pragma unroll
-            for (int Rr = 1; Rr < NB; ++Rr)
-#pragma unroll
-                for (int I = 0; I < Rr; ++I) {
-                    const int pid = pair_id(Rr, I);
-                    if (NB + pid % (kWaves - NB) != wave) continue;
-                    f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        const int c = 32 * s + 4 * q4;
-                        const float* kl = &sm.key.f.KL[16 * Rr + m16][c];
-                        const float* ql = &sm.key.f.QL[16 * Rr + m16][c];
-                        const float* ks = &sm.key.f.KS[16 * I + m16][c];
-                        const F8 b = O::cat2(O::cvt(ld4f(ks) * ld4f(&sm.Fo[pid][c])),
-                                             O::cvt(ld4f(ks + 16) * ld4f(&sm.Fo[pid][c + 16])));
-                        accA = O::mma32(O::cat2(O::cvt(ld4f(kl)), O::cvt(ld4f(kl + 16))), b, accA);
-                        accP = O::mma32(O::cat2(O::cvt(ld4f(ql)), O::cvt(ld4f(ql + 16))), b, accP);
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int row = 4 * q4 + i;
-                        sm.An[pid][row][m16] = (OT)(-accA[i] * sm.beta[16 * Rr + row]);
-                        sm.Pb[tri_id(Rr, I)][row][m16] = (OT)accP[i];
-                    }
-                }
-        }
+        fr.p2();
         __syncthreads();
 
         // ---------------- P2b: k o 2^b, q o 2^b over the dead float32 region
-        if (prod) {
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                *reinterpret_cast<typename O::P2*>(&sm.key.h.Kt[rbase + t][c0]) = kt2[t];
-                *reinterpret_cast<typename O::P2*>(&sm.key.h.Qt[rbase + t][c0]) = qt2[t];
-            }
-        }
+        fr.p2b();
         __syncthreads();
 
         // ---------------- P3: value side, one 16-column tile per wavefront

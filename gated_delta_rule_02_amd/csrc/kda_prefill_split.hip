@@ -1,0 +1,455 @@
+// kda_prefill_split.hip -- two-pass chunked KDA prefill (bfloat16 inputs).
+//
+// The single-pass kernel runs the whole chain of a (sequence, head) on one
+// compute unit, so a single long sequence with 64 heads occupies a quarter of
+// the GPU and every chunk pays the latency of its chunk-local phases. Here the
+// chunk-local work, which does not depend on the state, runs for all chunks at
+// once, and only the state recurrence stays sequential:
+//
+//   intra pass  (workgroup per (sequence, head, group of chunks); P0 .. P2b of
+//               kda_chunk.h, then a block forward substitution) writes, per
+//               chunk, in the operand layouts of the state pass:
+//                 -W = -(I + A)^-1 diag(beta) (K o 2^B)       tokens x dk
+//                 U' =  (I + A)^-1 diag(beta) V               tokens x dv
+//                 Q~ =  Q o 2^B                               tokens x dk
+//                 Kbar^T = (K o 2^(b_C - B))^T                dk x tokens
+//                 P (lower triangle incl. the diagonal)        tokens x tokens
+//                 2^b_C                                        dk
+//   state pass  (workgroup per (sequence, head, 32 value columns); the chunks
+//               of the sequence in order), from the identities of the chunk
+//               form in kda_chunk.h with U = U' + (-W) S0:
+//                 U   = U' + (-W) S
+//                 O   = scale (Q~ S + P U)
+//                 S  <- Diag(2^b_C) S + Kbar^T U
+//               four 64 x 128 x 16 or 128 x 64 x 16 MFMA products per chunk and
+//               wavefront, with no triangular solve left on the chain.
+//
+// The products are stored as float16 (their magnitudes are bounded by the
+// key, value and state magnitudes; entries that underflow are below 2^-24 of
+// the terms they multiply), which keeps the workspace at 72.5 KiB per chunk
+// and head. Chunks are processed in windows of up to `nwin` chunks per
+// sequence so that the workspace is bounded; between windows the state pass
+// carries the state through a float32 buffer in the workspace.
+#include <algorithm>
+
+#include "kda_chunk.h"
+
+namespace kda {
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Byte offsets inside one chunk slot. A-operand layout [t][s][lane][8 halves]:
+// for the 16-row tile t and the 32-wide K step s, lane (m = lane % 16,
+// qq = lane / 16) holds X[16t + m][32s + 4qq .. +3] followed by
+// X[16t + m][32s + 16 + 4qq .. +3].
+constexpr int kNegW = 0;        // -W       [4][4][64][8] f16
+constexpr int kQt = 16384;      // Q~       [4][4][64][8] f16
+constexpr int kKbT = 32768;     // Kbar^T   [8][2][64][8] f16
+constexpr int kPm = 49152;      // P        [4][2][64][8] f16
+constexpr int kDma = 57344;     // the four matrices above: copied to LDS as one block
+constexpr int kUp = 57344;      // U' in the accumulator layout [8 j][4 t][64][4] f16:
+                                // lane (n, q) of column tile j holds U'[16t + 4q + i][16j + n]
+constexpr int kDc = 73728;      // 2^b_C    [128] f32
+constexpr int kSlot = 74240;
+constexpr int kStateWaves = 2;  // one 16-column tile per wavefront
+constexpr int kStateThreads = 64 * kStateWaves;
+constexpr int kColGroups = D / (16 * kStateWaves);  // state-pass workgroups per (sequence, head)
+
+struct SplitArgs {
+    PrefillArgs p;
+    uint8_t* ws;      // slots [num_seqs][H][nwin]
+    float* carry;     // [num_seqs][H][128][128] between windows, or null
+    int64_t chunk0;   // first chunk (of each sequence) in this window
+    int nwin;         // chunk slots per (sequence, head)
+    int groups;       // intra-pass workgroups per (sequence, head)
+};
+
+__device__ __forceinline__ void seq_bounds(const PrefillArgs& a, int n, int64_t& s, int64_t& e)
+{
+    if (a.cu_seqlens) {
+        s = a.cu_seqlens[n];
+        e = a.cu_seqlens[n + 1];
+    } else {
+        s = (int64_t)n * a.seq_len;
+        e = s + a.seq_len;
+    }
+}
+
+// ------------------------------------------------------------- intra pass
+template <typename TIN>
+__global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
+{
+    using O = Ops<false>;
+    using OT = _Float16;
+    using F4 = typename O::F4;
+    using F8 = typename O::F8;
+    using SM = Smem<false>;
+    using IN = Io<TIN>;
+    constexpr int C = SM::C;
+    constexpr int NB = SM::NB;
+    constexpr int ES = sizeof(TIN);
+    static_assert(C == 64 && NB == 4, "slot layout assumes 64-token chunks");
+
+    __shared__ SM sm;
+    const PrefillArgs& a = sa.p;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int m16 = lane & 15;
+    const int q4 = lane >> 4;
+    const int jcol = 16 * wave + m16;  // this lane's column of the K~ and V tiles
+
+    const int grp = blockIdx.x % sa.groups;
+    const int u = blockIdx.x / sa.groups;  // n * H + h
+    const int h = u % a.H;
+    const int n = u / a.H;
+    int64_t seq_s, seq_e;
+    seq_bounds(a, n, seq_s, seq_e);
+    const int64_t nchunks = (seq_e - seq_s + C - 1) / C;
+    const int64_t c_end = min<int64_t>(nchunks, sa.chunk0 + sa.nwin);
+    const int64_t c_first = sa.chunk0 + grp;
+    if (c_first >= c_end) return;
+
+    const int ts = a.H * D;
+    const TIN* vg = static_cast<const TIN*>(a.v);
+    uint8_t* slots = sa.ws + (size_t)u * sa.nwin * kSlot;
+
+    Front<false, TIN> fr(sm, a, h);
+    uint32_t rv[NB][4];  // v[16R + 4q + i][jcol] (raw bits)
+    auto load_v = [&](int64_t c_s, int nt) {
+        const rsrc_t rv_ = make_rsrc(vg + c_s * ts, (int64_t)nt * ts * ES);
+        const int voff = (4 * q4 * ts + h * D + jcol) * ES;
+#pragma unroll
+        for (int Rr = 0; Rr < NB; ++Rr)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rv[Rr][i] = IN::ld_one(rv_, voff, (16 * Rr + i) * ts * ES);
+    };
+    {
+        const int64_t cs = seq_s + c_first * C;
+        fr.load(cs, (int)min<int64_t>(C, seq_e - cs));
+        load_v(cs, (int)min<int64_t>(C, seq_e - cs));
+    }
+
+    for (int64_t c = c_first; c < c_end; c += sa.groups) {
+        const int64_t cs = seq_s + c * C;
+        const int64_t cn = c + sa.groups;  // this workgroup's next chunk
+        const int64_t csn = seq_s + cn * C;
+        const bool more = cn < c_end;
+
+        fr.p0();
+        __syncthreads();
+        fr.p1();
+        if (more) fr.load(csn, (int)min<int64_t>(C, seq_e - csn));
+        __syncthreads();
+        fr.p2();
+        __syncthreads();
+        fr.p2b();
+        __syncthreads();
+
+        // ---- -W and U' by block forward substitution, one K~ tile and one V
+        // tile per wavefront: Z_R = T_RR (X_R + sum_{I<R} (-A_RI) Z_I)
+        uint8_t* slot = slots + (size_t)(c - sa.chunk0) * kSlot;
+        F4 ZW[NB], ZU[NB];
+#pragma unroll
+        for (int Rr = 0; Rr < NB; ++Rr) {
+            f32x4 yw, yu;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * Rr + 4 * q4 + i;  // rows past the chunk: k = v = beta = 0
+                const float b = sm.beta[r];
+                yw[i] = -b * (float)sm.key.h.Kt[r][jcol];
+                yu[i] = b * IN::one(rv[Rr][i]);
+            }
+#pragma unroll
+            for (int I = 0; I + 1 < Rr; I += 2) {
+                const F8 an = O::cat2(O::lds(&sm.An[pair_id(Rr, I)][m16][4 * q4]),
+                                       O::lds(&sm.An[pair_id(Rr, I + 1)][m16][4 * q4]));
+                yw = O::mma32(an, O::cat2(ZW[I], ZW[I + 1]), yw);
+                yu = O::mma32(an, O::cat2(ZU[I], ZU[I + 1]), yu);
+            }
+            if (Rr & 1) {
+                const F4 an = O::lds(&sm.An[pair_id(Rr, Rr - 1)][m16][4 * q4]);
+                yw = O::mma16(an, ZW[Rr - 1], yw);
+                yu = O::mma16(an, ZU[Rr - 1], yu);
+            }
+            const F4 tb = O::lds(&sm.Tb[Rr][m16][4 * q4]);
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            ZW[Rr] = O::cvt(O::mma16(tb, O::cvt(yw), z));
+            ZU[Rr] = O::cvt(O::mma16(tb, O::cvt(yu), z));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // U' straight to the slot (its accumulator layout); -W to LDS for the
+        // transposed store below
+#pragma unroll
+        for (int Rr = 0; Rr < NB; ++Rr) {
+            *reinterpret_cast<F4*>(slot + kUp + ((wave * 4 + Rr) * 64 + lane) * 8) = ZU[Rr];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm.key.h.Wst[16 * Rr + 4 * q4 + i][jcol] = ZW[Rr][i];
+        }
+        if (more) load_v(csn, (int)min<int64_t>(C, seq_e - csn));
+        __syncthreads();
+
+        // ---- the operand matrices in the A-operand layout, 16 bytes per lane
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const int idx = tid + kThreads * k2;  // [t 4][s 4][lane 64]
+            const int t = idx >> 8, s = (idx >> 6) & 3, l = idx & 63;
+            const int row = 16 * t + (l & 15), col = 32 * s + 4 * (l >> 4);
+            *reinterpret_cast<h8*>(slot + kNegW + idx * 16) =
+                cat(*reinterpret_cast<const h4*>(&sm.key.h.Wst[row][col]), *reinterpret_cast<const h4*>(&sm.key.h.Wst[row][col + 16]));
+            *reinterpret_cast<h8*>(slot + kQt + idx * 16) =
+                cat(*reinterpret_cast<const h4*>(&sm.key.h.Qt[row][col]), *reinterpret_cast<const h4*>(&sm.key.h.Qt[row][col + 16]));
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const int idx = tid + kThreads * k2;  // [t 8][s 2][lane 64]
+            const int t = idx >> 7, s = (idx >> 6) & 1, l = idx & 63;
+            const int row = 16 * t + (l & 15), col = 32 * s + 4 * (l >> 4);
+            *reinterpret_cast<h8*>(slot + kKbT + idx * 16) =
+                cat(*reinterpret_cast<const h4*>(&sm.KbT[row][col]), *reinterpret_cast<const h4*>(&sm.KbT[row][col + 16]));
+        }
+        {
+            const int idx = tid;  // [t 4][s 2][lane 64]
+            const int t = idx >> 7, s = (idx >> 6) & 1, l = idx & 63;
+            const int m = l & 15, cq = 4 * (l >> 4);
+            const h4 zero = {(OT)0.f, (OT)0.f, (OT)0.f, (OT)0.f};
+            const h4 lo = (2 * s <= t) ? *reinterpret_cast<const h4*>(&sm.Pb[tri_id(t, 2 * s)][m][cq]) : zero;
+            const h4 hi = (2 * s + 1 <= t) ? *reinterpret_cast<const h4*>(&sm.Pb[tri_id(t, 2 * s + 1)][m][cq]) : zero;
+            *reinterpret_cast<h8*>(slot + kPm + idx * 16) = cat(lo, hi);
+        }
+        if (tid < D / 4) *reinterpret_cast<f32x4*>(slot + kDc + tid * 16) = ld4f(&sm.bC[4 * tid]);
+        // the next P0 writes only Gp and beta, which nothing above reads; its
+        // barrier orders these LDS reads before P1 reuses the region
+    }
+}
+
+// ------------------------------------------------------------- state pass
+// The output is formed transposed, O^T = S^T Q~^T + U^T P^T: the 16 x 16 x 32
+// MFMA takes the same lane layout for its two operands, so the registers that
+// hold S (or U) as a B operand serve as the A operand of the transposed
+// product, and the stored A-operand layouts of Q~ and P serve as B operands.
+// The result then holds four consecutive output columns of one token per lane
+// (16-byte stores) instead of four tokens of one column.
+template <typename TOUT>
+__global__ __launch_bounds__(kStateThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void state_kernel(SplitArgs sa)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t buf[2][kDma];
+    const PrefillArgs& a = sa.p;
+    constexpr int C = 64;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int m16 = lane & 15;
+    const int q4 = lane >> 4;
+
+    // Workgroup ids are dealt to the 8 XCDs round robin; the kColGroups
+    // workgroups of one (sequence, head) get ids congruent mod 8, so they read
+    // the chunk products through the same L2.
+    const int bid = blockIdx.x;
+    const int jq = (bid >> 3) % kColGroups;
+    const int u = (bid & 7) + 8 * ((bid >> 3) / kColGroups);  // n * H + h
+    if (u >= a.num_seqs * a.H) return;
+    const int h = u % a.H;
+    const int n = u / a.H;
+    int64_t seq_s, seq_e;
+    seq_bounds(a, n, seq_s, seq_e);
+    const int64_t nchunks = (seq_e - seq_s + C - 1) / C;
+    const int64_t c_end = min<int64_t>(nchunks, sa.chunk0 + sa.nwin);
+    const int nch = (int)max<int64_t>(0, c_end - sa.chunk0);
+    const int j = kStateWaves * jq + wave;  // 16-column tile
+    const int jcol = 16 * j + m16;
+    const size_t sbase = (size_t)u * D * D;
+
+    if (nch == 0) {
+        // an empty sequence still has a final state: the initial one
+        if (sa.chunk0 == 0 && a.sT) {
+            int off = 4 * q4 * D + jcol;
+            asm volatile("" : "+v"(off));
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const size_t e = sbase + off + (size_t)(16 * t + i) * D;
+                    a.sT[e] = a.s0 ? a.s0[e] : 0.0f;
+                }
+        }
+        return;
+    }
+    const float* sin = sa.chunk0 == 0 ? a.s0 : sa.carry;
+    float* sout = c_end >= nchunks ? a.sT : sa.carry;
+
+    f32x4 S[8];  // S[t][i] = S[16t + 4q + i][jcol]
+    if (sin) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[t][i] = sin[sbase + (size_t)(16 * t + 4 * q4 + i) * D + jcol];
+    } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // this (sequence, head)'s slots through one descriptor; the wave-uniform
+    // parts of every address are scalar
+    const uint8_t* slots = sa.ws + (size_t)u * sa.nwin * kSlot;
+    const rsrc_t rs = make_rsrc(slots, (int64_t)nch * kSlot);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)&buf[0][0];
+    const int half = __builtin_amdgcn_readfirstlane(wave * (kDma / kStateWaves));
+    // each wavefront copies half of a chunk's operand block into LDS, 1 KiB
+    // per instruction (lane l moves bytes 16 l .. 16 l + 15)
+    auto dma = [&](int c, int b) {
+#pragma unroll
+        for (int i = 0; i < kDma / kStateWaves / 1024; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(uintptr_t)(lds0 + b * kDma + half + i * 1024), 16,
+                                                     lane * 16, c * kSlot + half + i * 1024, 0, 0);
+    };
+    h4 up[4];    // U' of this lane (accumulator layout)
+    f32x4 dc[8]; // 2^b_C of this lane's state rows
+    auto load_ud = [&](int c) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            up[t] = __builtin_bit_cast(h4, __builtin_amdgcn_raw_buffer_load_b64(rs, ((j * 4 + t) * 64 + lane) * 8, c * kSlot + kUp, 0));
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            dc[t] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (16 * t + 4 * q4) * 4, c * kSlot + kDc, 0));
+    };
+
+    const int ts = a.H * D;
+    TOUT* og = static_cast<TOUT*>(a.o);
+    // outputs of chunk c: lane (token m16 of tile t, q4) holds columns
+    // 16j + 4 q4 .. +3; rows past the sequence are dropped by the descriptor
+    auto store_o = [&](int c, const f32x4 (&Ot)[4]) {
+        const int64_t cs = seq_s + (sa.chunk0 + c) * C;
+        const int ntok = (int)min<int64_t>(C, seq_e - cs);
+        const rsrc_t ro_ = make_rsrc(og + cs * ts, (int64_t)ntok * ts * (int64_t)sizeof(TOUT));
+        const int voff = (m16 * ts + h * D + 16 * j + 4 * q4) * (int)sizeof(TOUT);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const f32x4 v = a.scale * Ot[t];
+            if constexpr (sizeof(TOUT) == 4) {
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), ro_, voff, 16 * t * ts * 4, 0);
+            } else {
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, to_b4(v)), ro_, voff, 16 * t * ts * 2, 0);
+            }
+        }
+    };
+
+    // Per chunk: the loads of chunk c + 1 and the stores of chunk c - 1 are
+    // issued right after the barrier and complete while chunk c computes; the
+    // wait at the next barrier covers all of them (a compiler-visible wait, so
+    // no further waits are placed on the register copies below).
+    dma(0, 0);
+    load_ud(0);
+    f32x4 Ot[4];  // O^T of the previous chunk, stored one iteration later
+    for (int c = 0; c < nch; ++c) {
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+        __syncthreads();
+        if (c > 0) store_o(c - 1, Ot);
+        h4 upc[4];
+        f32x4 dcc[8];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) upc[t] = up[t];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) dcc[t] = dc[t];
+        if (c + 1 < nch) {
+            load_ud(c + 1);
+            dma(c + 1, (c + 1) & 1);
+        }
+
+        const h8* nw = reinterpret_cast<const h8*>(&buf[c & 1][kNegW]);
+        const h8* qt = reinterpret_cast<const h8*>(&buf[c & 1][kQt]);
+        const h8* kb = reinterpret_cast<const h8*>(&buf[c & 1][kKbT]);
+        const h8* pm = reinterpret_cast<const h8*>(&buf[c & 1][kPm]);
+
+        h8 sb[4];  // S as the B operand (and S^T as the A operand) of a K step over dk
+#pragma unroll
+        for (int s = 0; s < 4; ++s) sb[s] = cat(to_h4(S[2 * s]), to_h4(S[2 * s + 1]));
+        f32x4 U[4];  // U[t]: tokens 16t.. x this tile; Ot[t]: this tile x tokens 16t..
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            U[t] = f32x4{(float)upc[t][0], (float)upc[t][1], (float)upc[t][2], (float)upc[t][3]};
+            Ot[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                U[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(nw[(t * 4 + s) * 64 + lane], sb[s], U[t], 0, 0, 0);
+                Ot[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sb[s], qt[(t * 4 + s) * 64 + lane], Ot[t], 0, 0, 0);
+            }
+        h8 ub[2];  // U as the B operand (U^T as the A operand) of a K step over tokens
+#pragma unroll
+        for (int s = 0; s < 2; ++s) ub[s] = cat(to_h4(U[2 * s]), to_h4(U[2 * s + 1]));
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                if (2 * s <= t) Ot[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ub[s], pm[(t * 2 + s) * 64 + lane], Ot[t], 0, 0, 0);
+        // state: S <- Diag(2^b_C) S + Kbar^T U
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            f32x4 acc = S[t] * dcc[t];
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb[(t * 2 + s) * 64 + lane], ub[s], acc, 0, 0, 0);
+            S[t] = acc;
+        }
+    }
+    store_o(nch - 1, Ot);
+
+    if (sout) {
+        int off = 4 * q4 * D + jcol;
+        asm volatile("" : "+v"(off));
+        float* so = sout + sbase + off;
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) so[(16 * t + i) * D] = S[t][i];
+    }
+}
+
+}  // namespace
+
+size_t prefill_split_slot_bytes() { return kSlot; }
+
+hipError_t launch_prefill_split(const PrefillArgs& a, void* ws, size_t ws_bytes, int64_t max_chunks, hipStream_t s)
+{
+    const int64_t U = (int64_t)a.num_seqs * a.H;
+    SplitArgs sa{};
+    sa.p = a;
+    sa.ws = static_cast<uint8_t*>(ws);
+    if (max_chunks <= 0) {
+        // every sequence is empty: the state pass only copies the states
+        sa.nwin = 1;
+    } else if (ws_bytes >= (size_t)(U * max_chunks) * kSlot) {
+        sa.nwin = (int)max_chunks;
+    } else {
+        const size_t carry = (size_t)U * D * D * sizeof(float);
+        sa.nwin = (int)std::min<int64_t>(max_chunks, (int64_t)((ws_bytes - carry) / ((size_t)U * kSlot)));
+        sa.carry = reinterpret_cast<float*>(sa.ws + (size_t)U * sa.nwin * kSlot);
+    }
+    // about one intra-pass workgroup per compute unit, each taking every
+    // groups-th chunk of the window with its next chunk prefetched
+    sa.groups = (int)std::max<int64_t>(1, std::min<int64_t>(sa.nwin, (256 + U - 1) / U));
+    const dim3 gi((unsigned)(U * sa.groups)), bi(kThreads);
+    const dim3 gs((unsigned)(kColGroups * 8 * ((U + 7) / 8))), bs(kStateThreads);
+    for (int64_t c0 = 0; c0 < std::max<int64_t>(max_chunks, 1); c0 += sa.nwin) {
+        sa.chunk0 = c0;
+        if (max_chunks > 0) hipLaunchKernelGGL(intra_kernel<bf16_t>, gi, bi, 0, s, sa);
+        if (a.out_dtype == F32)
+            hipLaunchKernelGGL(state_kernel<float>, gs, bs, 0, s, sa);
+        else
+            hipLaunchKernelGGL(state_kernel<bf16_t>, gs, bs, 0, s, sa);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace kda

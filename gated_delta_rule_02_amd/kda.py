@@ -113,11 +113,29 @@ def _cu(cu_seqlens, cu_seqlens_host):
 
 
 # --------------------------------------------------------------------------
+_workspaces = {}
+
+
+def _workspace(device, nbytes):
+    """A cached device buffer of at least nbytes (one per device; grows on demand)."""
+    key = torch.device(device).index
+    buf = _workspaces.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _workspaces[key] = buf
+    return buf
+
+
 def kda_prefill(q, k, v, g, beta, o, cu_seqlens=None, cu_seqlens_host=None, num_seqs=None,
                 initial_state=None, final_state=None, scale=1.0, lower_bound=-5.0,
-                workspace=None, stream=None):
+                workspace="auto", stream=None):
     """KDA core over packed sequences. q,k,g [T,H,128], v [T,H,128], beta [T,H]
-    (one dtype), o [T,H,128] (float32 or bfloat16), states float32 [N,H,128,128]."""
+    (one dtype), o [T,H,128] (float32 or bfloat16), states float32 [N,H,128,128].
+
+    workspace: "auto" (a cached buffer of kda_prefill_workspace_bytes bytes, so
+    bfloat16 inputs take the two-pass form), None (no workspace: single-pass
+    form), or a caller-owned uint8 device tensor. Calls sharing the cached
+    buffer must be ordered on one stream."""
     for n_, t_ in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("o", o),
                    ("initial_state", initial_state), ("final_state", final_state)):
         _dense(t_, n_)
@@ -126,6 +144,11 @@ def kda_prefill(q, k, v, g, beta, o, cu_seqlens=None, cu_seqlens_host=None, num_
     cu_dev, cu_host, keep = _cu(cu_seqlens, cu_seqlens_host)
     if num_seqs is None:
         num_seqs = (keep.numel() - 1) if keep is not None else 1
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a tensor")
+        need = lib().kda_prefill_workspace_bytes(T, num_seqs, H, dk, dv, _dt(q))
+        workspace = _workspace(q.device, need) if need else None
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _call("kda_prefill", _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dt(q), T, H, dk, dv,
           cu_dev, cu_host, num_seqs, scale, lower_bound, _ptr(initial_state), _ptr(final_state),

@@ -82,8 +82,23 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  * o          [num_tokens, H, dv]   out_dtype (float32 keeps full precision).
  * scale      read-out multiplier (1.0 for the plain S^T q read).
  * lower_bound  log-retention floor, -5 for the safe forget gate.
- * workspace / workspace_bytes  device scratch of at least
- *            kda_prefill_workspace_bytes(...) bytes (may be NULL when that is 0).
+ * workspace / workspace_bytes  device scratch, caller-owned, not touching
+ *            any tensor above. NULL: the single-pass form runs (one workgroup
+ *            per (sequence, head) carries the state through all chunks; no
+ *            scratch). With BF16 inputs and a workspace, the two-pass form runs:
+ *            the chunk-local products of every chunk are computed in parallel
+ *            and stored in the workspace (72.5 KiB per chunk and head, float16),
+ *            then a sequential pass over the chunks carries the state. The
+ *            chunks of each sequence are taken in windows of as many as the
+ *            workspace holds; with more than one window a float32 state carry
+ *            of num_seqs*H*64 KiB is kept at the end of the workspace. The
+ *            minimum is one chunk slot per (sequence, head) plus that carry
+ *            (or a slot for every chunk, if smaller); less returns
+ *            KDA_ERR_WORKSPACE. kda_prefill_workspace_bytes() gives the
+ *            recommended size (windows of 16 chunks; 0 for F32 inputs, which
+ *            always run the single-pass form and ignore the workspace). The
+ *            contents need no initialisation and are garbage afterwards; calls
+ *            that share a workspace must be ordered on one stream.
  * Supported: dk = dv = 128, H >= 1, in_dtype F32 or BF16.
  * ---------------------------------------------------------------------- */
 int kda_prefill(const void* q, const void* k, const void* v, const void* g, const void* beta,

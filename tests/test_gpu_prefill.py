@@ -1,4 +1,8 @@
-"""Chunked prefill on the GPU vs the FP64 token-serial oracle."""
+"""Chunked prefill on the GPU vs the FP64 token-serial oracle.
+
+bfloat16 cases run both forms of the library: the two-pass form (a workspace
+is given: per-chunk products for all chunks, then the state pass) and the
+single-pass form (no workspace)."""
 import numpy as np
 import pytest
 import torch
@@ -11,7 +15,11 @@ from tests.gpu_util import TOL_BF16, TOL_F32, announce, dev, host64, relerr
 pytestmark = pytest.mark.gpu
 
 
-def gpu_prefill(d, cu=None, s0=None, out_dtype=torch.float32, final=True, in_place=False):
+PATHS = ["split", "single"]
+
+
+def gpu_prefill(d, cu=None, s0=None, out_dtype=torch.float32, final=True, in_place=False, path="split",
+                workspace=None):
     q, k, v, g, b = (dev(d[x]) for x in ("q", "k", "v", "g", "beta"))
     T, H, _ = q.shape
     o = torch.empty((T, H, 128), dtype=out_dtype, device="cuda")
@@ -22,8 +30,9 @@ def gpu_prefill(d, cu=None, s0=None, out_dtype=torch.float32, final=True, in_pla
     sT = None
     if final:
         sT = s0_d if in_place else torch.empty((N, H, 128, 128), dtype=torch.float32, device="cuda")
+    ws = workspace if workspace is not None else ("auto" if path == "split" else None)
     K.kda_prefill(q, k, v, g, b, o, cu_seqlens=cu_d, cu_seqlens_host=cu_h, num_seqs=N,
-                  initial_state=s0_d, final_state=sT)
+                  initial_state=s0_d, final_state=sT, workspace=ws)
     torch.cuda.synchronize()
     return o, sT
 
@@ -49,27 +58,30 @@ def test_core_fp32_workload():
     check(o, sT, ro, rS, TOL_F32)
 
 
-@pytest.mark.parametrize("T,H,bf16", [(1, 2, True), (15, 1, True), (64, 2, True), (200, 3, True),
-                                      (77, 2, False), (333, 1, False)])
-def test_ragged_lengths_with_state(T, H, bf16):
-    announce("prefill ragged T=%d H=%d bf16=%s" % (T, H, bf16))
+@pytest.mark.parametrize("T,H,bf16,path", [(1, 2, True, "split"), (15, 1, True, "split"), (64, 2, True, "split"),
+                                           (200, 3, True, "split"), (1, 2, True, "single"), (15, 1, True, "single"),
+                                           (64, 2, True, "single"), (200, 3, True, "single"),
+                                           (77, 2, False, "single"), (333, 1, False, "single")])
+def test_ragged_lengths_with_state(T, H, bf16, path):
+    announce("prefill ragged T=%d H=%d bf16=%s %s" % (T, H, bf16, path))
     rng = np.random.default_rng(1000 + T)
     d = synth.core_inputs(rng, T, H, bf16=bf16)
     s0 = synth.states(rng, 1, H, std=0.3)
-    o, sT = gpu_prefill(d, s0=s0)
+    o, sT = gpu_prefill(d, s0=s0, path=path)
     ro, rS = oracle(d, s0=s0)
     check(o, sT, ro, rS, TOL_BF16 if bf16 else TOL_F32)
 
 
-def test_varlen_small_with_empty_sequences():
-    announce("prefill varlen small")
+@pytest.mark.parametrize("path", PATHS)
+def test_varlen_small_with_empty_sequences(path):
+    announce("prefill varlen small %s" % path)
     lens = [1, 63, 64, 65, 0, 130, 7, 0]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     rng = np.random.default_rng(42)
     H = 2
     d = synth.core_inputs(rng, int(cu[-1]), H, bf16=True)
     s0 = synth.states(rng, len(lens), H, std=0.1)
-    o, sT = gpu_prefill(d, cu=cu, s0=s0)
+    o, sT = gpu_prefill(d, cu=cu, s0=s0, path=path)
     ro, rS = oracle(d, cu=cu, s0=s0)
     check(o, sT, ro, rS, TOL_BF16)
     # empty sequences return their initial state unchanged
@@ -77,11 +89,12 @@ def test_varlen_small_with_empty_sequences():
         np.testing.assert_array_equal(sT[n].cpu().numpy(), s0[n])
 
 
-def test_prefill_workload_full_size():
+@pytest.mark.parametrize("path", PATHS)
+def test_prefill_workload_full_size(path):
     """B=1, T=4096, H=64, bf16 inputs, chunk 64, zero state."""
-    announce("prefill full T=4096 H=64")
+    announce("prefill full T=4096 H=64 %s" % path)
     d = synth.workload_prefill()
-    o, sT = gpu_prefill(d)
+    o, sT = gpu_prefill(d, path=path)
     ro, rS = oracle(d)
     check(o, sT, ro, rS, TOL_BF16)
 
@@ -98,19 +111,20 @@ def test_read_after_write_identity():
     assert np.max(np.abs(host64(o) - v)) < 1e-4 * np.max(np.abs(v))
 
 
-def test_split_invariance_and_decode_continuation():
+@pytest.mark.parametrize("path", PATHS)
+def test_split_invariance_and_decode_continuation(path):
     """prefill(T) then prefill(rest) from its state == prefill(all), and
     prefill(T) + one decode step == prefill(T+1)."""
-    announce("prefill split + decode continuation")
+    announce("prefill split + decode continuation %s" % path)
     rng = np.random.default_rng(4)
     T, H = 300, 2
     d = synth.core_inputs(rng, T + 1, H, bf16=True)
     head = {k_: synth.Tensor(v_.vals[:100], None if v_.bits is None else v_.bits[:100]) for k_, v_ in d.items()}
     tail = {k_: synth.Tensor(v_.vals[100:T], None if v_.bits is None else v_.bits[100:T]) for k_, v_ in d.items()}
     first = {k_: synth.Tensor(v_.vals[:T], None if v_.bits is None else v_.bits[:T]) for k_, v_ in d.items()}
-    o_all, s_all = gpu_prefill(first)
-    o1, s1 = gpu_prefill(head)
-    o2, s2 = gpu_prefill(tail, s0=s1.cpu().numpy())
+    o_all, s_all = gpu_prefill(first, path=path)
+    o1, s1 = gpu_prefill(head, path=path)
+    o2, s2 = gpu_prefill(tail, s0=s1.cpu().numpy(), path=path)
     ref = host64(o_all)
     assert relerr(host64(torch.cat([o1, o2])), ref) < 1e-3
     assert relerr(host64(s2), host64(s_all)) < 1e-3
@@ -125,20 +139,22 @@ def test_split_invariance_and_decode_continuation():
     assert relerr(host64(st[0]), rS[0]) < TOL_BF16
 
 
-def test_in_place_state_and_determinism():
-    announce("prefill in-place + determinism")
+@pytest.mark.parametrize("path", PATHS)
+def test_in_place_state_and_determinism(path):
+    announce("prefill in-place + determinism %s" % path)
     rng = np.random.default_rng(5)
     T, H = 257, 3
     d = synth.core_inputs(rng, T, H, bf16=True)
     s0 = synth.states(rng, 1, H, std=0.2)
-    o1, s1 = gpu_prefill(d, s0=s0)
-    o2, s2 = gpu_prefill(d, s0=s0, in_place=True)
+    o1, s1 = gpu_prefill(d, s0=s0, path=path)
+    o2, s2 = gpu_prefill(d, s0=s0, in_place=True, path=path)
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
 
 
-def test_outputs_stay_in_bounds():
+@pytest.mark.parametrize("path", PATHS)
+def test_outputs_stay_in_bounds(path):
     """Guard bands around o and the final state are left untouched."""
-    announce("prefill guard bands")
+    announce("prefill guard bands %s" % path)
     rng = np.random.default_rng(6)
     T, H = 70, 2
     d = synth.core_inputs(rng, T, H, bf16=True)
@@ -148,20 +164,21 @@ def test_outputs_stay_in_bounds():
     sbuf = torch.full((H * 128 * 128 + 2 * pad,), 7.0, device="cuda")
     o = obuf[pad:pad + T * H * 128].view(T, H, 128)
     sT = sbuf[pad:pad + H * 128 * 128].view(1, H, 128, 128)
-    K.kda_prefill(q, k, v, g, b, o, final_state=sT)
+    K.kda_prefill(q, k, v, g, b, o, final_state=sT, workspace="auto" if path == "split" else None)
     torch.cuda.synchronize()
     for buf in (obuf, sbuf):
         assert torch.all(buf[:pad] == 7.0) and torch.all(buf[-pad:] == 7.0)
 
 
-def test_bf16_output():
+@pytest.mark.parametrize("path", PATHS)
+def test_bf16_output(path):
     """bfloat16 output equals the float32 output of the same kernel rounded to
     bfloat16 (same arithmetic, only the store differs)."""
-    announce("prefill bf16 out")
+    announce("prefill bf16 out %s" % path)
     rng = np.random.default_rng(7)
     d = synth.core_inputs(rng, 128, 2, bf16=True)
-    o16, s16 = gpu_prefill(d, out_dtype=torch.bfloat16)
-    o32, s32 = gpu_prefill(d, out_dtype=torch.float32)
+    o16, s16 = gpu_prefill(d, out_dtype=torch.bfloat16, path=path)
+    o32, s32 = gpu_prefill(d, out_dtype=torch.float32, path=path)
     diff = (o16.float() - o32.to(torch.bfloat16).float()).abs()
     if diff.max() > 0:
         idx = np.unravel_index(int(torch.argmax(diff).item()), tuple(diff.shape))
@@ -171,3 +188,26 @@ def test_bf16_output():
     assert torch.equal(s16, s32)
     ro, _ = oracle(d)
     assert relerr(host64(o16), ro) < 6e-3
+
+
+@pytest.mark.parametrize("lens", [[333], [1, 63, 64, 65, 0, 130, 7, 0, 200]])
+def test_split_windows_match_one_window(lens):
+    """A workspace of one chunk slot per (sequence, head) plus the state carry
+    forces one-chunk windows; outputs and states equal the one-window run bit
+    for bit (the windows change only where the state waits between chunks)
+    and match the oracle. Sequences end in different windows."""
+    announce("prefill split windows lens=%s" % lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    rng = np.random.default_rng(11)
+    H = 2
+    N = len(lens)
+    d = synth.core_inputs(rng, int(cu[-1]), H, bf16=True)
+    s0 = synth.states(rng, N, H, std=0.2)
+    U = N * H
+    small = torch.empty(U * 74240 + U * 128 * 128 * 4, dtype=torch.uint8, device="cuda")
+    big = torch.empty(U * 74240 * ((max(lens) + 63) // 64), dtype=torch.uint8, device="cuda")
+    o1, s1 = gpu_prefill(d, cu=cu, s0=s0, workspace=small)
+    o2, s2 = gpu_prefill(d, cu=cu, s0=s0, workspace=big)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    ro, rS = oracle(d, cu=cu, s0=s0)
+    check(o1, s1, ro, rS, TOL_BF16)
