@@ -28,8 +28,8 @@
 // flozi.net section above): 15 tokens x 5 x log2(e) < 116 < 127.
 //
 // Work split. A workgroup of 8 wavefronts handles one chunk at a time:
-//   P0  each producer thread (2 key channels, half of a 16-token block) sums
-//       its 8 log-retentions; the partial sums are exchanged through LDS.
+//   P0  each producer thread (2 key channels, a row group of a 16-token
+//       block) sums its log-retentions; the partial sums go through LDS.
 //   P1  it forms the decay factors by running products of alpha = 2^g and
 //       writes the key-side operands k o 2^l, q o 2^l, k o 2^s (float32) and
 //       the transposed K-bar (operand type); it keeps k o 2^b and q o 2^b
@@ -70,10 +70,17 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 // ---------------------------------------------------------------- buffers
 // Raw buffer over [base, base + bytes): loads beyond return 0, stores beyond
 // are dropped (the descriptor's range check).
+// Every descriptor built here is wave-uniform; readfirstlane states that to
+// the compiler, which otherwise may build it in vector registers and wrap
+// each load in a loop over the distinct values.
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes)
 {
     const uint32_t nr = bytes <= 0 ? 0u : (bytes >= 0xffffffffll ? 0xffffffffu : (uint32_t)bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nr, 0x00020000);
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint64_t bu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(bu), (short)0,
+                                             __builtin_amdgcn_readfirstlane((int)nr), 0x00020000);
 }
 template <typename T> struct Io;
 template <> struct Io<bf16_t> {
@@ -176,11 +183,16 @@ template <> struct Ops<false> {
     // two operand-type values of channels c, c+1 packed for one LDS store
     using P2 = h2;
     __device__ static P2 pack2(float x, float y) { return h2{(_Float16)x, (_Float16)y}; }
-    // 8 consecutive tokens of one channel for the transposed K-bar
-    __device__ static void store8(OT* p, const float* v)
+    // N consecutive tokens of one channel for the transposed K-bar
+    template <int N>
+    __device__ static void store_n(OT* p, const float* v)
     {
-        *reinterpret_cast<h8*>(p) = h8{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3],
-                                       (_Float16)v[4], (_Float16)v[5], (_Float16)v[6], (_Float16)v[7]};
+        static_assert(N == 4 || N == 8, "4 or 8 tokens");
+        if constexpr (N == 8)
+            *reinterpret_cast<h8*>(p) = h8{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3],
+                                           (_Float16)v[4], (_Float16)v[5], (_Float16)v[6], (_Float16)v[7]};
+        else
+            *reinterpret_cast<h4*>(p) = h4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
     }
 };
 
@@ -209,10 +221,12 @@ template <> struct Ops<true> {
     }
     using P2 = f32x2;
     __device__ static P2 pack2(float x, float y) { return f32x2{x, y}; }
-    __device__ static void store8(OT* p, const float* v)
+    template <int N>
+    __device__ static void store_n(OT* p, const float* v)
     {
+        static_assert(N == 4 || N == 8, "4 or 8 tokens");
         *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
-        *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+        if constexpr (N == 8) *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
     }
 };
 
@@ -221,7 +235,8 @@ __host__ __device__ constexpr int pair_id(int R, int I) { return R * (R - 1) / 2
 // index of the lower-triangle block (R, I), I <= R
 __host__ __device__ constexpr int tri_id(int R, int I) { return R * (R + 1) / 2 + I; }
 
-template <bool F32P>
+// NQ: producer row groups per 16-token block (16 / NQ tokens per producer thread)
+template <bool F32P, int NQ = 2>
 struct __attribute__((aligned(16))) Smem {
     using OT = typename Ops<F32P>::OT;
     static constexpr int C = Ops<F32P>::C;
@@ -230,10 +245,22 @@ struct __attribute__((aligned(16))) Smem {
     static constexpr int LDK = D + 4;               // row stride of the float32 [C][128] arrays
     static constexpr int LDH = D + Ops<F32P>::PAD;  // row stride of the operand-type [C][128] arrays
     static constexpr int LDT = C + Ops<F32P>::PAD;  // row stride of [128][C]
+    OT Nd[NB][16][16];                      // -A diagonal blocks (strictly lower, beta-scaled)
+    OT Tb[NB][16][16];                      // (I + A_RR)^-1
+    OT An[NPAIR > 0 ? NPAIR : 1][16][16];   // -A off-diagonal blocks (beta-scaled)
+    OT Pb[NB * (NB + 1) / 2][16][16];       // P lower-triangle blocks
+    float Fd[NB][D];                        // 2^-G_R
+    float Fo[NPAIR > 0 ? NPAIR : 1][D];     // 2^(rho_R - rho_{I+1})
+    float Gp[NB][NQ][D];                    // row-group sums of the log-retention (base 2)
+    float bC[D];                            // 2^b_C
+    float beta[C];
+    OT KbT[D][LDT];                         // (k o 2^(b_C - b))^T   (state update)
     // P1 -> P2: key-side operands in float32. Their factors span 2^-116 .. 1
     // and the diagonal blocks rescale them by up to 2^116, beyond float16's
     // range, so each use rounds once to the MFMA operand type.
     // P2b -> P3: the same bytes then hold k o 2^b and q o 2^b (operand type).
+    // The small tables come first so that their LDS offsets fit the
+    // instructions' immediate offset field.
     union Key {
         struct {
             float KL[C][LDK];  // k o 2^l   (left operand of A)
@@ -244,37 +271,30 @@ struct __attribute__((aligned(16))) Smem {
             OT Kt[C][LDH];     // k o 2^b   (X = diag(beta)(V - Kt S))
             OT Qt[C][LDH];     // q o 2^b   (O = Qt S + P U)
             OT Wst[C][LDH];    // -W staged for its transposed store (two-pass form)
+            uint16_t Vst[C][LDH];  // v (input storage bits), staged by the producers (two-pass form)
         } h;
     } key;
-    OT KbT[D][LDT];                         // (k o 2^(b_C - b))^T   (state update)
-    OT Nd[NB][16][16];                      // -A diagonal blocks (strictly lower, beta-scaled)
-    OT Tb[NB][16][16];                      // (I + A_RR)^-1
-    OT An[NPAIR > 0 ? NPAIR : 1][16][16];   // -A off-diagonal blocks (beta-scaled)
-    OT Pb[NB * (NB + 1) / 2][16][16];       // P lower-triangle blocks
-    float Fd[NB][D];                        // 2^-G_R
-    float Fo[NPAIR > 0 ? NPAIR : 1][D];     // 2^(rho_R - rho_{I+1})
-    float Gp[NB][2][D];                     // half-block sums of the log-retention (base 2)
-    float bC[D];                            // 2^b_C
-    float beta[C];
 };
 
 
 // ---------------------------------------------------------------- P0 .. P2b
-// The chunk-local phases. Producer threads (wavefronts 0 .. 2 NB - 1) own
-// channels c0, c0 + 1 of tokens rbase .. rbase + 7 (half hh of block R); the
-// next chunk's k, q, g of those tokens and beta stream into registers while
-// the current chunk computes. The caller separates the phases with barriers.
-template <bool F32P, typename TIN>
+// The chunk-local phases. Producer threads (wavefronts 0 .. NQ NB - 1) own
+// channels c0, c0 + 1 of the RP = 16 / NQ tokens rbase .. rbase + RP - 1 (row
+// group hh of block R); the next chunk's k, q, g of those tokens and beta
+// stream into registers while the current chunk computes. The caller
+// separates the phases with barriers.
+template <bool F32P, typename TIN, int NQ = 2, bool StageV = false>
 struct Front {
     using O = Ops<F32P>;
     using OT = typename O::OT;
     using F4 = typename O::F4;
     using F8 = typename O::F8;
-    using SM = Smem<F32P>;
+    using SM = Smem<F32P, NQ>;
     using IN = Io<TIN>;
     using PT = typename IN::pair_t;
     static constexpr int C = SM::C;
     static constexpr int NB = SM::NB;
+    static constexpr int RP = 16 / NQ;  // tokens per producer thread
     static constexpr int ES = sizeof(TIN);
 
     SM& sm;
@@ -285,24 +305,26 @@ struct Front {
     const float lbl;
     const TIN *qg, *kg, *gg, *bg;
 
-    PT rk[8], rq[8], rg[8];     // k, q, g of this producer's tokens
+    PT rk[RP], rq[RP], rg[RP];  // k, q, g of this producer's tokens
+    PT rvv[StageV ? RP : 1];    // v of this producer's tokens (StageV)
     uint32_t rb = 0;            // beta[tid] (threads < C)
-    f32x2 g2[8];                // clamped base-2 log-retention
-    typename O::P2 kt2[8], qt2[8];  // k o 2^b, q o 2^b of this producer's tokens
+    f32x2 g2[RP];               // clamped base-2 log-retention
+    typename O::P2 kt2[RP], qt2[RP];  // k o 2^b, q o 2^b of this producer's tokens
 
     // the wavefront index is read through readfirstlane so that the compiler
     // knows every quantity derived from it is wave-uniform (scalar offsets)
     __device__ __forceinline__ Front(SM& s, const PrefillArgs& a, int head)
         : sm(s), tid(threadIdx.x), wave(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)), lane(threadIdx.x & 63),
-          m16(threadIdx.x & 15), q4((threadIdx.x & 63) >> 4), prod(wave < 2 * NB), R(wave % NB), hh(wave / NB),
-          c0(2 * (threadIdx.x & 63)), rbase(16 * (wave % NB) + 8 * (wave / NB)), h(head), H(a.H), ts(a.H * D),
+          m16(threadIdx.x & 15), q4((threadIdx.x & 63) >> 4), prod(wave < NQ * NB), R(wave % NB), hh(wave / NB),
+          c0(2 * (threadIdx.x & 63)), rbase(16 * (wave % NB) + RP * (wave / NB)), h(head), H(a.H), ts(a.H * D),
           lbl(a.lower_bound * kLog2e), qg(static_cast<const TIN*>(a.q)), kg(static_cast<const TIN*>(a.k)),
           gg(static_cast<const TIN*>(a.g)), bg(static_cast<const TIN*>(a.beta))
     {
     }
 
     // k, q, g, beta of the nt tokens starting at c_s (rows past nt read as 0)
-    __device__ __forceinline__ void load(int64_t c_s, int nt)
+    // (and v with StageV)
+    __device__ __forceinline__ void load(int64_t c_s, int nt, const TIN* vg = nullptr)
     {
         const int64_t bytes = (int64_t)nt * ts * ES;
         const rsrc_t rk_ = make_rsrc(kg + c_s * ts, bytes), rq_ = make_rsrc(qg + c_s * ts, bytes),
@@ -310,23 +332,29 @@ struct Front {
         if (prod) {
             const int voff = (c0 + h * D) * ES;  // per lane
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
+            for (int t = 0; t < RP; ++t) {
                 const int soff = (rbase + t) * ts * ES;  // wave-uniform row term
                 rk[t] = IN::ld_pair(rk_, voff, soff);
                 rq[t] = IN::ld_pair(rq_, voff, soff);
                 rg[t] = IN::ld_pair(rg_, voff, soff);
             }
+            if constexpr (StageV) {
+                const rsrc_t rv_ = make_rsrc(vg + c_s * ts, bytes);
+#pragma unroll
+                for (int t = 0; t < RP; ++t) rvv[t] = IN::ld_pair(rv_, voff, (rbase + t) * ts * ES);
+            }
         }
-        if (tid < C) rb = IN::ld_one(make_rsrc(bg + c_s * H, (int64_t)nt * H * ES), (tid * H + h) * ES, 0);
+        const rsrc_t rb_ = make_rsrc(bg + c_s * H, (int64_t)nt * H * ES);  // uniform: built outside the branch
+        if (tid < C) rb = IN::ld_one(rb_, (tid * H + h) * ES, 0);
     }
 
-    // P0: half-block sums of the log-retention (base 2), beta to LDS
+    // P0: row-group sums of the log-retention (base 2), beta to LDS
     __device__ __forceinline__ void p0()
     {
         if (prod) {
             f32x2 G = {0.f, 0.f};
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
+            for (int t = 0; t < RP; ++t) {
                 const f32x2 gv = IN::unpack(rg[t]);  // rows past the chunk read as 0
                 g2[t] = f32x2{fmaxf(gv.x * kLog2e, lbl), fmaxf(gv.y * kLog2e, lbl)};
                 G += g2[t];
@@ -336,29 +364,41 @@ struct Front {
         if (tid < C) sm.beta[tid] = IN::one(rb);
     }
 
+    __device__ __forceinline__ f32x2 block_sum(int J) const
+    {
+        f32x2 g = {0.f, 0.f};
+#pragma unroll
+        for (int qq = 0; qq < NQ; ++qq) g += *reinterpret_cast<const f32x2*>(&sm.Gp[J][qq][c0]);
+        return g;
+    }
+
     // P1: decay factors and key-side operands
     __device__ __forceinline__ void p1()
     {
         if (!prod) return;
-        f32x2 rho_R = {0.f, 0.f}, bCv = {0.f, 0.f};
+        f32x2 rho_R = {0.f, 0.f}, bCv = {0.f, 0.f}, GR = {0.f, 0.f};
 #pragma unroll
         for (int J = 0; J < NB; ++J) {
-            const f32x2 gJ = *reinterpret_cast<const f32x2*>(&sm.Gp[J][0][c0]) +
-                             *reinterpret_cast<const f32x2*>(&sm.Gp[J][1][c0]);
+            const f32x2 gJ = block_sum(J);
             if (J < R) rho_R += gJ;
+            if (J == R) GR = gJ;
             bCv += gJ;
         }
-        const f32x2 G0 = *reinterpret_cast<const f32x2*>(&sm.Gp[R][0][c0]);
-        const f32x2 G1 = *reinterpret_cast<const f32x2*>(&sm.Gp[R][1][c0]);
-        const f32x2 GR = G0 + G1;
+        // sums of the row groups before / after this thread's inside the block
+        f32x2 pre = {0.f, 0.f}, suf = {0.f, 0.f};
+#pragma unroll
+        for (int qq = 0; qq < NQ; ++qq) {
+            const f32x2 x = *reinterpret_cast<const f32x2*>(&sm.Gp[R][qq][c0]);
+            if (qq < hh) pre += x;
+            if (qq > hh) suf += x;
+        }
         if (hh == 0) {
             // factor tables for P2 and the value side (this thread's two channels)
             *reinterpret_cast<f32x2*>(&sm.Fd[R][c0]) = f32x2{exp2_fast(-GR.x), exp2_fast(-GR.y)};
             f32x2 rho_I1 = {0.f, 0.f};
 #pragma unroll
             for (int I = 0; I < NB - 1; ++I) {
-                rho_I1 += *reinterpret_cast<const f32x2*>(&sm.Gp[I][0][c0]) +
-                          *reinterpret_cast<const f32x2*>(&sm.Gp[I][1][c0]);
+                rho_I1 += block_sum(I);
                 if (I < R)  // pair (R, I): index R (R - 1) / 2 + I
                     *reinterpret_cast<f32x2*>(&sm.Fo[R * (R - 1) / 2 + I][c0]) =
                         f32x2{exp2_fast(rho_R.x - rho_I1.x), exp2_fast(rho_R.y - rho_I1.y)};
@@ -368,13 +408,13 @@ struct Front {
         const f32x2 DR = {exp2_fast(rho_R.x), exp2_fast(rho_R.y)};
         const f32x2 fb = {exp2_fast(bCv.x - rho_R.x - GR.x), exp2_fast(bCv.y - rho_R.y - GR.y)};
 
-        // forward: e_l = prod_{j<=r} alpha_j over the block (starts after half 0)
-        f32x2 al[8];
+        // forward: e_l = prod_{j<=r} alpha_j over the block (starts after the earlier row groups)
+        f32x2 al[RP];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) al[t] = f32x2{exp2_fast(g2[t].x), exp2_fast(g2[t].y)};
-        f32x2 el = hh ? f32x2{exp2_fast(G0.x), exp2_fast(G0.y)} : f32x2{1.f, 1.f};
+        for (int t = 0; t < RP; ++t) al[t] = f32x2{exp2_fast(g2[t].x), exp2_fast(g2[t].y)};
+        f32x2 el = {exp2_fast(pre.x), exp2_fast(pre.y)};
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
+        for (int t = 0; t < RP; ++t) {
             el *= al[t];
             const f32x2 kv = IN::unpack(rk[t]), qv = IN::unpack(rq[t]);
             const f32x2 klv = kv * el, qlv = qv * el;
@@ -383,87 +423,100 @@ struct Front {
             kt2[t] = O::pack2(klv.x * DR.x, klv.y * DR.y);
             qt2[t] = O::pack2(qlv.x * DR.x, qlv.y * DR.y);
         }
-        // reverse: e_s = prod_{j>r} alpha_j over the block (starts before half 1)
-        f32x2 es = hh ? f32x2{1.f, 1.f} : f32x2{exp2_fast(G1.x), exp2_fast(G1.y)};
-        float kb0[8], kb1[8];
+        // reverse: e_s = prod_{j>r} alpha_j over the block (starts before the later row groups)
+        f32x2 es = {exp2_fast(suf.x), exp2_fast(suf.y)};
+        float kb0[RP], kb1[RP];
 #pragma unroll
-        for (int t = 7; t >= 0; --t) {
+        for (int t = RP - 1; t >= 0; --t) {
             const f32x2 ksv = IN::unpack(rk[t]) * es;
             *reinterpret_cast<f32x2*>(&sm.key.f.KS[rbase + t][c0]) = ksv;
             kb0[t] = ksv.x * fb.x;
             kb1[t] = ksv.y * fb.y;
             es *= al[t];
         }
-        O::store8(&sm.KbT[c0][rbase], kb0);
-        O::store8(&sm.KbT[c0 + 1][rbase], kb1);
+        O::template store_n<RP>(&sm.KbT[c0][rbase], kb0);
+        O::template store_n<RP>(&sm.KbT[c0 + 1][rbase], kb1);
     }
 
-    // P2: blocks of A and P, diagonal inverses
+    // P2 pieces. Diagonal block Rd: A (bfloat16) and P (hi+lo split), the
+    // beta-scaled strict lower part N and (I + N)^-1 by a Horner product.
+    __device__ __forceinline__ void p2_diag(int Rd)
+    {
+        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int c = 32 * s + 4 * q4;
+            const float* kl = &sm.key.f.KL[16 * Rd + m16][c];
+            const float* ql = &sm.key.f.QL[16 * Rd + m16][c];
+            const float* ks = &sm.key.f.KS[16 * Rd + m16][c];
+            const f32x4 x0 = ld4f(ks) * ld4f(&sm.Fd[Rd][c]);
+            const f32x4 x1 = ld4f(ks + 16) * ld4f(&sm.Fd[Rd][c + 16]);
+            accA = O::diagA(ld4f(kl), ld4f(kl + 16), x0, x1, accA);
+            accP = O::diagP(ld4f(ql), ld4f(ql + 16), x0, x1, accP);
+            __builtin_amdgcn_sched_barrier(0);  // one K step at a time (register pressure)
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 4 * q4 + i;  // row in block, column m16
+            const float b = sm.beta[16 * Rd + row];
+            sm.Nd[Rd][row][m16] = (OT)(row > m16 ? -accA[i] * b : 0.0f);
+            sm.Pb[tri_id(Rd, Rd)][row][m16] = (OT)(row >= m16 ? accP[i] : 0.0f);
+        }
+        // wavefront-local: the inverse below reads what this wavefront wrote
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        // (I + N)^-1 = sum_{j<16} (-N)^j  (N strictly lower, N^16 = 0), Horner form
+        const F4 nA = O::lds(&sm.Nd[Rd][m16][4 * q4]);
+        f32x4 eye;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) eye[i] = (4 * q4 + i == m16) ? 1.0f : 0.0f;
+        f32x4 Y = eye;
+#pragma unroll
+        for (int it = 0; it < 15; ++it) Y = O::mma16(nA, O::cvt(Y), eye);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.Tb[Rd][4 * q4 + i][m16] = (OT)Y[i];
+    }
+
+    // Off-diagonal block (Rr, I), I < Rr: -A (beta-scaled) and / or P
+    template <bool DoA, bool DoP>
+    __device__ __forceinline__ void p2_pair(int Rr, int I)
+    {
+        const int pid = pair_id(Rr, I);
+        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int c = 32 * s + 4 * q4;
+            const float* kl = &sm.key.f.KL[16 * Rr + m16][c];
+            const float* ql = &sm.key.f.QL[16 * Rr + m16][c];
+            const float* ks = &sm.key.f.KS[16 * I + m16][c];
+            const F8 b = O::cat2(O::cvt(ld4f(ks) * ld4f(&sm.Fo[pid][c])),
+                                 O::cvt(ld4f(ks + 16) * ld4f(&sm.Fo[pid][c + 16])));
+            if (DoA) accA = O::mma32(O::cat2(O::cvt(ld4f(kl)), O::cvt(ld4f(kl + 16))), b, accA);
+            if (DoP) accP = O::mma32(O::cat2(O::cvt(ld4f(ql)), O::cvt(ld4f(ql + 16))), b, accP);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 4 * q4 + i;
+            if (DoA) sm.An[pid][row][m16] = (OT)(-accA[i] * sm.beta[16 * Rr + row]);
+            if (DoP) sm.Pb[tri_id(Rr, I)][row][m16] = (OT)accP[i];
+        }
+    }
+
+    // P2 with 8 wavefronts: 0 .. NB-1 the diagonal blocks, the rest the
+    // off-diagonal pairs (A and P together)
     __device__ __forceinline__ void p2()
     {
         constexpr int kW = kWaves;
         if (wave < NB) {
-            const int Rd = wave;
-            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int c = 32 * s + 4 * q4;
-                const float* kl = &sm.key.f.KL[16 * Rd + m16][c];
-                const float* ql = &sm.key.f.QL[16 * Rd + m16][c];
-                const float* ks = &sm.key.f.KS[16 * Rd + m16][c];
-                const f32x4 x0 = ld4f(ks) * ld4f(&sm.Fd[Rd][c]);
-                const f32x4 x1 = ld4f(ks + 16) * ld4f(&sm.Fd[Rd][c + 16]);
-                accA = O::diagA(ld4f(kl), ld4f(kl + 16), x0, x1, accA);
-                accP = O::diagP(ld4f(ql), ld4f(ql + 16), x0, x1, accP);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 4 * q4 + i;  // row in block, column m16
-                const float b = sm.beta[16 * Rd + row];
-                sm.Nd[Rd][row][m16] = (OT)(row > m16 ? -accA[i] * b : 0.0f);
-                sm.Pb[tri_id(Rd, Rd)][row][m16] = (OT)(row >= m16 ? accP[i] : 0.0f);
-            }
-            // wavefront-local: the inverse below reads what this wavefront wrote
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-            // (I + N)^-1 = sum_{j<16} (-N)^j  (N strictly lower, N^16 = 0), Horner form
-            const F4 nA = O::lds(&sm.Nd[Rd][m16][4 * q4]);
-            f32x4 eye;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) eye[i] = (4 * q4 + i == m16) ? 1.0f : 0.0f;
-            f32x4 Y = eye;
-#pragma unroll
-            for (int it = 0; it < 15; ++it) Y = O::mma16(nA, O::cvt(Y), eye);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sm.Tb[Rd][4 * q4 + i][m16] = (OT)Y[i];
+            p2_diag(wave);
         } else {
-            // off-diagonal pairs on the remaining wavefronts
 #pragma unroll
             for (int Rr = 1; Rr < NB; ++Rr)
 #pragma unroll
-                for (int I = 0; I < Rr; ++I) {
-                    const int pid = pair_id(Rr, I);
-                    if (NB + pid % (kW - NB) != wave) continue;
-                    f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        const int c = 32 * s + 4 * q4;
-                        const float* kl = &sm.key.f.KL[16 * Rr + m16][c];
-                        const float* ql = &sm.key.f.QL[16 * Rr + m16][c];
-                        const float* ks = &sm.key.f.KS[16 * I + m16][c];
-                        const F8 b = O::cat2(O::cvt(ld4f(ks) * ld4f(&sm.Fo[pid][c])),
-                                             O::cvt(ld4f(ks + 16) * ld4f(&sm.Fo[pid][c + 16])));
-                        accA = O::mma32(O::cat2(O::cvt(ld4f(kl)), O::cvt(ld4f(kl + 16))), b, accA);
-                        accP = O::mma32(O::cat2(O::cvt(ld4f(ql)), O::cvt(ld4f(ql + 16))), b, accP);
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int row = 4 * q4 + i;
-                        sm.An[pid][row][m16] = (OT)(-accA[i] * sm.beta[16 * Rr + row]);
-                        sm.Pb[tri_id(Rr, I)][row][m16] = (OT)accP[i];
-                    }
-                }
+                for (int I = 0; I < Rr; ++I)
+                    if (NB + pair_id(Rr, I) % (kW - NB) == wave) p2_pair<true, true>(Rr, I);
         }
     }
 
@@ -472,9 +525,10 @@ struct Front {
     {
         if (!prod) return;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
+        for (int t = 0; t < RP; ++t) {
             *reinterpret_cast<typename O::P2*>(&sm.key.h.Kt[rbase + t][c0]) = kt2[t];
             *reinterpret_cast<typename O::P2*>(&sm.key.h.Qt[rbase + t][c0]) = qt2[t];
+            if constexpr (StageV) *reinterpret_cast<uint32_t*>(&sm.key.h.Vst[rbase + t][c0]) = rvv[t];
         }
     }
 };

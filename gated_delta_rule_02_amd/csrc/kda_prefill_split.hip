@@ -54,9 +54,13 @@ constexpr int kUp = 57344;      // U' in the accumulator layout [8 j][4 t][64][4
                                 // lane (n, q) of column tile j holds U'[16t + 4q + i][16j + n]
 constexpr int kDc = 73728;      // 2^b_C    [128] f32
 constexpr int kSlot = 74240;
-constexpr int kStateWaves = 2;  // one 16-column tile per wavefront
-constexpr int kStateThreads = 64 * kStateWaves;
+constexpr int kStateWaves = 2;  // compute wavefronts of the state pass, one 16-column tile each
+constexpr int kStateThreads = 64 * (kStateWaves + 2);  // + a loader and a prefetcher wavefront
 constexpr int kColGroups = D / (16 * kStateWaves);  // state-pass workgroups per (sequence, head)
+constexpr int kStage = 62464;   // LDS stage: operand block, U' of the workgroup's tiles, 2^b_C (+ pad)
+constexpr int kStUp = kDma;     // offset of U' (the workgroup's two tiles, 4 KiB) in a stage
+constexpr int kStDc = kDma + 4096;  // offset of 2^b_C in a stage
+constexpr int kPrefetchAhead = 3;   // chunks the prefetcher runs ahead of the loader
 
 struct SplitArgs {
     PrefillArgs p;
@@ -228,6 +232,13 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
 }
 
 // ------------------------------------------------------------- state pass
+// Four wavefronts: two compute wavefronts (one 16-column tile of the state
+// each), a loader that copies each chunk's operands into an LDS stage with
+// buffer-to-LDS loads (two stages, one chunk ahead), and a prefetcher that
+// touches the chunks further ahead so the loader's copies hit L2. Each role
+// waits only on its own memory counter; one barrier per chunk hands a stage
+// from the loader to the compute wavefronts.
+//
 // The output is formed transposed, O^T = S^T Q~^T + U^T P^T: the 16 x 16 x 32
 // MFMA takes the same lane layout for its two operands, so the registers that
 // hold S (or U) as a B operand serve as the A operand of the transposed
@@ -238,15 +249,18 @@ template <typename TOUT>
 __global__ __launch_bounds__(kStateThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void state_kernel(SplitArgs sa)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t buf[2][kDma];
+    __shared__ __attribute__((aligned(16))) uint8_t buf[2][kStage];
+    __shared__ __attribute__((aligned(16))) uint32_t sink[64];  // target of the prefetcher's loads
     const PrefillArgs& a = sa.p;
     constexpr int C = 64;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int m16 = lane & 15;
     const int q4 = lane >> 4;
+    const bool compute = wave < kStateWaves;
+    const bool loader = wave == kStateWaves;
 
     // Workgroup ids are dealt to the 8 XCDs round robin; the kColGroups
     // workgroups of one (sequence, head) get ids congruent mod 8, so they read
@@ -262,13 +276,14 @@ void state_kernel(SplitArgs sa)
     const int64_t nchunks = (seq_e - seq_s + C - 1) / C;
     const int64_t c_end = min<int64_t>(nchunks, sa.chunk0 + sa.nwin);
     const int nch = (int)max<int64_t>(0, c_end - sa.chunk0);
-    const int j = kStateWaves * jq + wave;  // 16-column tile
+    const int jl = compute ? wave : 0;       // this wavefront's tile within the workgroup
+    const int j = kStateWaves * jq + jl;     // 16-column tile
     const int jcol = 16 * j + m16;
     const size_t sbase = (size_t)u * D * D;
 
     if (nch == 0) {
         // an empty sequence still has a final state: the initial one
-        if (sa.chunk0 == 0 && a.sT) {
+        if (compute && sa.chunk0 == 0 && a.sT) {
             int off = 4 * q4 * D + jcol;
             asm volatile("" : "+v"(off));
 #pragma unroll
@@ -284,96 +299,85 @@ void state_kernel(SplitArgs sa)
     const float* sin = sa.chunk0 == 0 ? a.s0 : sa.carry;
     float* sout = c_end >= nchunks ? a.sT : sa.carry;
 
-    f32x4 S[8];  // S[t][i] = S[16t + 4q + i][jcol]
-    if (sin) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) S[t][i] = sin[sbase + (size_t)(16 * t + 4 * q4 + i) * D + jcol];
-    } else {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
     // this (sequence, head)'s slots through one descriptor; the wave-uniform
     // parts of every address are scalar
     const uint8_t* slots = sa.ws + (size_t)u * sa.nwin * kSlot;
     const rsrc_t rs = make_rsrc(slots, (int64_t)nch * kSlot);
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)&buf[0][0];
-    const int half = __builtin_amdgcn_readfirstlane(wave * (kDma / kStateWaves));
-    // each wavefront copies half of a chunk's operand block into LDS, 1 KiB
-    // per instruction (lane l moves bytes 16 l .. 16 l + 15)
+    // loader: chunk c into stage b, 1 KiB per instruction (lane l moves bytes
+    // 16 l .. 16 l + 15): the operand block, then U' of this workgroup's two
+    // tiles, then 2^b_C (the instruction moves 1 KiB; the tail is padding)
     auto dma = [&](int c, int b) {
+        const uint32_t st = lds0 + b * kStage;
 #pragma unroll
-        for (int i = 0; i < kDma / kStateWaves / 1024; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(uintptr_t)(lds0 + b * kDma + half + i * 1024), 16,
-                                                     lane * 16, c * kSlot + half + i * 1024, 0, 0);
+        for (int i = 0; i < kDma / 1024; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(uintptr_t)(st + i * 1024), 16, lane * 16,
+                                                     c * kSlot + i * 1024, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(uintptr_t)(st + kStUp + i * 1024), 16, lane * 16,
+                                                     c * kSlot + kUp + jq * 4096 + i * 1024, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(uintptr_t)(st + kStDc), 16, lane * 16,
+                                                 c * kSlot + kDc, 0, 0);
     };
-    h4 up[4];    // U' of this lane (accumulator layout)
-    f32x4 dc[8]; // 2^b_C of this lane's state rows
-    auto load_ud = [&](int c) {
+    // prefetcher: one 4-byte read per 128-byte line of what the loader will copy
+    const uint32_t sink0 = (uint32_t)(uintptr_t)(lds_void*)&sink[0];
+    auto prefetch = [&](int c) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-            up[t] = __builtin_bit_cast(h4, __builtin_amdgcn_raw_buffer_load_b64(rs, ((j * 4 + t) * 64 + lane) * 8, c * kSlot + kUp, 0));
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-            dc[t] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (16 * t + 4 * q4) * 4, c * kSlot + kDc, 0));
+        for (int i = 0; i < kDma / 8192; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(uintptr_t)sink0, 4, lane * 128, c * kSlot + i * 8192, 0, 0);
+        if (lane < 36)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(uintptr_t)sink0, 4,
+                                                     lane < 32 ? lane * 128 : kDc - kUp - jq * 4096 + (lane - 32) * 128,
+                                                     c * kSlot + kUp + jq * 4096, 0, 0);
     };
+
+    f32x4 S[8];  // S[t][i] = S[16t + 4q + i][jcol]
+    if (compute) {
+        if (sin) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[t][i] = sin[sbase + (size_t)(16 * t + 4 * q4 + i) * D + jcol];
+        } else {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    if (loader) {
+        dma(0, 0);
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    } else if (!compute) {
+        for (int p = 1; p <= kPrefetchAhead && p < nch; ++p) prefetch(p);
+    }
 
     const int ts = a.H * D;
     TOUT* og = static_cast<TOUT*>(a.o);
-    // outputs of chunk c: lane (token m16 of tile t, q4) holds columns
-    // 16j + 4 q4 .. +3; rows past the sequence are dropped by the descriptor
-    auto store_o = [&](int c, const f32x4 (&Ot)[4]) {
-        const int64_t cs = seq_s + (sa.chunk0 + c) * C;
-        const int ntok = (int)min<int64_t>(C, seq_e - cs);
-        const rsrc_t ro_ = make_rsrc(og + cs * ts, (int64_t)ntok * ts * (int64_t)sizeof(TOUT));
-        const int voff = (m16 * ts + h * D + 16 * j + 4 * q4) * (int)sizeof(TOUT);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const f32x4 v = a.scale * Ot[t];
-            if constexpr (sizeof(TOUT) == 4) {
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), ro_, voff, 16 * t * ts * 4, 0);
-            } else {
-                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, to_b4(v)), ro_, voff, 16 * t * ts * 2, 0);
-            }
-        }
-    };
-
-    // Per chunk: the loads of chunk c + 1 and the stores of chunk c - 1 are
-    // issued right after the barrier and complete while chunk c computes; the
-    // wait at the next barrier covers all of them (a compiler-visible wait, so
-    // no further waits are placed on the register copies below).
-    dma(0, 0);
-    load_ud(0);
-    f32x4 Ot[4];  // O^T of the previous chunk, stored one iteration later
     for (int c = 0; c < nch; ++c) {
-        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-        __syncthreads();
-        if (c > 0) store_o(c - 1, Ot);
-        h4 upc[4];
-        f32x4 dcc[8];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) upc[t] = up[t];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) dcc[t] = dc[t];
-        if (c + 1 < nch) {
-            load_ud(c + 1);
-            dma(c + 1, (c + 1) & 1);
+        __syncthreads();  // stage c & 1 holds chunk c
+        if (loader) {
+            if (c + 1 < nch) dma(c + 1, (c + 1) & 1);
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the stage is complete before the next barrier
+            continue;
         }
-
-        const h8* nw = reinterpret_cast<const h8*>(&buf[c & 1][kNegW]);
-        const h8* qt = reinterpret_cast<const h8*>(&buf[c & 1][kQt]);
-        const h8* kb = reinterpret_cast<const h8*>(&buf[c & 1][kKbT]);
-        const h8* pm = reinterpret_cast<const h8*>(&buf[c & 1][kPm]);
+        if (!compute) {
+            if (c + 1 + kPrefetchAhead < nch) prefetch(c + 1 + kPrefetchAhead);
+            continue;
+        }
+        const uint8_t* st = &buf[c & 1][0];
+        const h8* nw = reinterpret_cast<const h8*>(st + kNegW);
+        const h8* qt = reinterpret_cast<const h8*>(st + kQt);
+        const h8* kb = reinterpret_cast<const h8*>(st + kKbT);
+        const h8* pm = reinterpret_cast<const h8*>(st + kPm);
 
         h8 sb[4];  // S as the B operand (and S^T as the A operand) of a K step over dk
 #pragma unroll
         for (int s = 0; s < 4; ++s) sb[s] = cat(to_h4(S[2 * s]), to_h4(S[2 * s + 1]));
-        f32x4 U[4];  // U[t]: tokens 16t.. x this tile; Ot[t]: this tile x tokens 16t..
+        f32x4 U[4], Ot[4];  // U[t]: tokens 16t.. x this tile; Ot[t]: this tile x tokens 16t..
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            U[t] = f32x4{(float)upc[t][0], (float)upc[t][1], (float)upc[t][2], (float)upc[t][3]};
+            const h4 up = *reinterpret_cast<const h4*>(st + kStUp + ((jl * 4 + t) * 64 + lane) * 8);
+            U[t] = f32x4{(float)up[0], (float)up[1], (float)up[2], (float)up[3]};
             Ot[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
@@ -394,15 +398,33 @@ void state_kernel(SplitArgs sa)
         // state: S <- Diag(2^b_C) S + Kbar^T U
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            f32x4 acc = S[t] * dcc[t];
+            f32x4 acc = S[t] * *reinterpret_cast<const f32x4*>(st + kStDc + (16 * t + 4 * q4) * 4);
 #pragma unroll
             for (int s = 0; s < 2; ++s)
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb[(t * 2 + s) * 64 + lane], ub[s], acc, 0, 0, 0);
             S[t] = acc;
         }
+        // outputs: lane (token m16 of tile t, q4) holds columns 16j + 4 q4 .. +3;
+        // rows past the sequence are dropped by the descriptor range
+        const int64_t cs = seq_s + (sa.chunk0 + c) * C;
+        const int ntok = (int)min<int64_t>(C, seq_e - cs);
+        const rsrc_t ro_ = make_rsrc(og + cs * ts, (int64_t)ntok * ts * (int64_t)sizeof(TOUT));
+        const int voff = (m16 * ts + h * D + 16 * j + 4 * q4) * (int)sizeof(TOUT);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const f32x4 v = a.scale * Ot[t];
+            if constexpr (sizeof(TOUT) == 4) {
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), ro_, voff, 16 * t * ts * 4, 0);
+            } else {
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, to_b4(v)), ro_, voff, 16 * t * ts * 2, 0);
+            }
+        }
     }
-    store_o(nch - 1, Ot);
-
+    if (!compute) {
+        // no load may still be writing LDS when the workgroup ends
+        __builtin_amdgcn_s_waitcnt(0x0f70);
+        return;
+    }
     if (sout) {
         int off = 4 * q4 * D + jcol;
         asm volatile("" : "+v"(off));
