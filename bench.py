@@ -101,7 +101,10 @@ def bench_decode(torch, K, steps, warmup):
     x, cst, w = dev(d["conv_x"], torch), dev(d["conv_state"], torch), dev(d["conv_w"], torch)
     y = torch.empty_like(x)
     ms_conv, _ = timed(torch, lambda: K.kda_conv_state_update(x, cst, w, y), steps, warmup)
-    return ms, ms_conv
+    # reference: a plain in-place read-modify-write of a buffer the size of the
+    # state (torch's elementwise kernel), the access pattern decode cannot avoid
+    ms_ref, _ = timed(torch, lambda: st.mul_(1.0), max(5, steps // 2), 2)
+    return ms, ms_conv, ms_ref
 
 
 def bench_layer(torch, steps, warmup):
@@ -200,12 +203,15 @@ def main():
             out["cpu_baseline"] = cpu_baseline(d)
     if args.only in (None, "decode"):
         log("decode B=256 H=64")
-        ms, ms_conv = bench_decode(torch, K, args.steps, args.warmup)
-        log("decode %.3f ms/step, conv %.3f ms" % (ms, ms_conv))
+        ms, ms_conv, ms_ref = bench_decode(torch, K, args.steps, args.warmup)
+        log("decode %.3f ms/step, conv %.3f ms, in-place stream %.3f ms" % (ms, ms_conv, ms_ref))
+        ref_gbs = 2 * 2 ** 30 / (ms_ref * 1e-3) / 1e9
         out["decode"] = {"workload": "decode step B=256 H=64 dk=dv=128, bf16 inputs, fp32 state [256,64,128,128] in place, fp32 o",
                          "ms_per_step": ms, "GB/s": DECODE_BYTES / (ms * 1e-3) / 1e9,
                          "frac_of_hbm_peak": DECODE_BYTES / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                         "bytes_per_step": DECODE_BYTES, "state_GB/s": 2 * 2 ** 30 / (ms * 1e-3) / 1e9}
+                         "bytes_per_step": DECODE_BYTES, "state_GB/s": 2 * 2 ** 30 / (ms * 1e-3) / 1e9,
+                         "inplace_stream_reference_GB/s": ref_gbs,
+                         "inplace_stream_reference": "torch mul_ in place on the 1 GiB state buffer (read + write)"}
         out["conv_update"] = {"workload": "x [256,8192] bf16, state [256,3,8192] bf16 in place",
                               "ms_per_step": ms_conv, "GB/s": CONV_BYTES / (ms_conv * 1e-3) / 1e9}
     if args.only == "layer" or (args.only is None and not args.skip_layer):

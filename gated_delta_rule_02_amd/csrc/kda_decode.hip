@@ -10,18 +10,39 @@
 // coalesced loads, reduces the two column sums S'^T k and S'^T q across the
 // workgroup, and writes the state back once from the same registers.
 //
-// Workgroup = 256 threads = one (sequence, head). Thread t owns the 4 columns
-// 4*(t%32) .. +3 of the 16 rows r = t/32 + 8*i (i = 0..15): a wavefront's 64
+// Workgroup = 1024 threads = one (sequence, head). Thread t owns the 4 columns
+// 4*(t%32) .. +3 of the 4 rows r = t/32 + 32*i (i = 0..3): a wavefront's 64
 // lanes cover two whole rows, i.e. 1 KiB of contiguous state per load.
+// Measured on the 1 GiB decode workload: 256 threads x 16 rows 410 us,
+// 512 x 8 410 us, 1024 x 4 386 us (the in-place stream of the state is the
+// whole cost; the wider workgroup keeps more of it in flight).
 #include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
 namespace {
 
+#ifndef KDA_DECODE_NT
+#define KDA_DECODE_NT 1
+#endif
+#if KDA_DECODE_NT
+// the state is streamed exactly once per step: non-temporal accesses keep it
+// from displacing the small per-step inputs in the caches
+#define KDA_NT_LOAD(p) __builtin_nontemporal_load(p)
+#define KDA_NT_STORE(v, p) __builtin_nontemporal_store(v, p)
+#else
+#define KDA_NT_LOAD(p) (*(p))
+#define KDA_NT_STORE(v, p) (*(p) = (v))
+#endif
+
 constexpr int D = 128;
-constexpr int kThreads = 256;
-constexpr int kRowsPerThread = 16;
+#ifndef KDA_DECODE_THREADS
+#define KDA_DECODE_THREADS 1024
+#endif
+constexpr int kThreads = KDA_DECODE_THREADS;   // per (sequence, head)
+constexpr int kWaves = kThreads / 64;
+constexpr int kRowGroups = kThreads / 32;      // 32 lanes cover one 128-float row
+constexpr int kRowsPerThread = D / kRowGroups;
 
 template <typename TIN, typename TOUT>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a)
@@ -32,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a)
     const int wave = t >> 6;
 
     __shared__ float s_alpha[D], s_k[D], s_q[D];
-    __shared__ float s_part[4][2][D];  // per-wave partial column sums (S'^T k, S'^T q)
+    __shared__ float s_part[kWaves][2][D];  // per-wave partial column sums (S'^T k, S'^T q)
     __shared__ float s_u[D];
     __shared__ float s_kq[2];
 
@@ -40,14 +61,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a)
     const TIN* k = static_cast<const TIN*>(a.k) + (size_t)bh * D;
     const TIN* g = static_cast<const TIN*>(a.g) + (size_t)bh * D;
 
-    // Issue the state loads first: they are the long-latency stream.
+    // Issue the state loads first: they are the long-latency stream. Thread t
+    // owns columns 4 (t % 32) .. +3 of the rows t / 32 + kRowGroups i.
     const int cg = t & 31;
     const int rg = t >> 5;
     float* Sp = a.state + (size_t)bh * D * D;
     f32x4 s[kRowsPerThread];
 #pragma unroll
     for (int i = 0; i < kRowsPerThread; ++i)
-        s[i] = *reinterpret_cast<const f32x4*>(Sp + (size_t)(rg + 8 * i) * D + 4 * cg);
+        s[i] = KDA_NT_LOAD(reinterpret_cast<const f32x4*>(Sp + (size_t)(rg + kRowGroups * i) * D + 4 * cg));
 
     if (t < D) {
         const float kv = ld(k + t), qv = ld(q + t);
@@ -63,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a)
     f32x4 pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < kRowsPerThread; ++i) {
-        const int r = rg + 8 * i;
+        const int r = rg + kRowGroups * i;
         s[i] *= s_alpha[r];
         pk += s[i] * s_k[r];
         pq += s[i] * s_q[r];
@@ -82,8 +104,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a)
 
     if (t < D) {
         const int j = t;
-        const float sk = (s_part[0][0][j] + s_part[1][0][j]) + (s_part[2][0][j] + s_part[3][0][j]);
-        const float sq = (s_part[0][1][j] + s_part[1][1][j]) + (s_part[2][1][j] + s_part[3][1][j]);
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            sk += s_part[w][0][j];
+            sq += s_part[w][1][j];
+        }
         const float beta = ld(static_cast<const TIN*>(a.beta) + bh);
         const float vj = ld(static_cast<const TIN*>(a.v) + (size_t)bh * D + j);
         const float u = beta * (vj - sk);
@@ -96,8 +122,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a)
     const f32x4 u4 = *reinterpret_cast<const f32x4*>(&s_u[4 * cg]);
 #pragma unroll
     for (int i = 0; i < kRowsPerThread; ++i) {
-        const int r = rg + 8 * i;
-        *reinterpret_cast<f32x4*>(Sp + (size_t)r * D + 4 * cg) = s[i] + s_k[r] * u4;
+        const int r = rg + kRowGroups * i;
+        KDA_NT_STORE(s[i] + s_k[r] * u4, reinterpret_cast<f32x4*>(Sp + (size_t)r * D + 4 * cg));
     }
 }
 

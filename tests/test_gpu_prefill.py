@@ -211,3 +211,37 @@ def test_split_windows_match_one_window(lens):
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
     ro, rS = oracle(d, cu=cu, s0=s0)
     check(o1, s1, ro, rS, TOL_BF16)
+
+
+def test_varlen_workload_full_size_sampled():
+    """Packed varlen workload at full size: 8 sequences (123,444 tokens, up to
+    447 chunks each), H = 64, bf16 inputs, random fp32 initial states, final
+    states returned; default two-pass form with 16-chunk windows. The GPU runs
+    every head; the oracle checks heads 0 and 41 of every sequence (o and
+    final state), and every other head's final state must be finite."""
+    announce("prefill varlen full size (sampled heads)")
+    d = synth.workload_varlen()
+    cu = d["cu_seqlens"]
+    q, k, v, g, b = (dev(d[x]) for x in ("q", "k", "v", "g", "beta"))
+    T, H, _ = q.shape
+    N = len(cu) - 1
+    s0 = torch.from_numpy(d["initial_state"]).cuda()
+    sT = torch.empty_like(s0)
+    o = torch.empty((T, H, 128), dtype=torch.float32, device="cuda")
+    cu_d = torch.from_numpy(cu).cuda()
+    K.kda_prefill(q, k, v, g, b, o, cu_seqlens=cu_d, cu_seqlens_host=torch.from_numpy(cu), num_seqs=N,
+                  initial_state=s0, final_state=sT)
+    torch.cuda.synchronize()
+    assert torch.isfinite(sT).all()
+    del q, k, v, g, b
+    for h in (0, 41):
+        ro, rS = R.kda_serial(d["q"].vals[:, h:h + 1], d["k"].vals[:, h:h + 1], d["v"].vals[:, h:h + 1],
+                              d["g"].vals[:, h:h + 1], d["beta"].vals[:, h:h + 1], cu_seqlens=cu,
+                              initial_state=d["initial_state"][:, h:h + 1].astype(np.float64))
+        oh = o[:, h:h + 1].cpu().numpy().astype(np.float64)
+        for n in range(N):
+            a_, e_ = int(cu[n]), int(cu[n + 1])
+            eo = relerr(oh[a_:e_], ro[a_:e_])
+            es = relerr(host64(sT[n, h]), rS[n, 0])
+            print("  head %d seq %d (T=%d): o err %.3e  state err %.3e" % (h, n, e_ - a_, eo, es), flush=True)
+            assert eo < TOL_BF16 and es < TOL_BF16
