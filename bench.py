@@ -44,7 +44,7 @@ COUNTERS = os.path.join(ROOT, "profiles", "kda_prefill_t4096_h64_counters.json")
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("kda_prefill_split.hip", "kda_chunk.h", "kda_device.h"):
+    for f in ("kda_prefill_split.hip", "kda_chunk.h", "kda_device.h", "kda_api.cpp"):
         h.update(open(os.path.join(ROOT, "gated_delta_rule_02_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -193,7 +193,7 @@ def main():
                        "global_batch": 1, "seq_len": T, "heads": 64, "head_dim": 128, "chunk": 64},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                         "kernel": "kda_prefill call (two-pass form: intra_kernel + state_kernel per 16-chunk window)",
+                         "kernel": "kda_prefill call (two-pass form: intra_kernel + state_kernel per window of 24 chunks, 3 windows)",
                          "algorithmic_bytes_per_launch": PREFILL_BYTES_PER_TOKEN * T,
                          "mfma_tflops": PREFILL_FLOPS_PER_TOKEN * T / (ms * 1e-3) / 1e12,
                          "mfma_frac_of_bf16_peak": PREFILL_FLOPS_PER_TOKEN * T / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},

@@ -306,7 +306,9 @@ void state_kernel(SplitArgs sa)
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)&buf[0][0];
     // loader: chunk c into stage b, 1 KiB per instruction (lane l moves bytes
     // 16 l .. 16 l + 15): the operand block, then U' of this workgroup's two
-    // tiles, then 2^b_C (the instruction moves 1 KiB; the tail is padding)
+    // tiles, then 2^b_C (the instruction moves 1 KiB; the tail is padding).
+    // Measured alternatives moved the same ~61 KiB per chunk and compute unit
+    // no faster: two loader wavefronts, or loads through registers + LDS stores.
     auto dma = [&](int c, int b) {
         const uint32_t st = lds0 + b * kStage;
 #pragma unroll
@@ -370,6 +372,8 @@ void state_kernel(SplitArgs sa)
         const h8* kb = reinterpret_cast<const h8*>(st + kKbT);
         const h8* pm = reinterpret_cast<const h8*>(st + kPm);
 
+        // The operand reads run one group ahead of the MFMAs that consume them
+        // (LDS latency is otherwise exposed on every product).
         h8 sb[4];  // S as the B operand (and S^T as the A operand) of a K step over dk
 #pragma unroll
         for (int s = 0; s < 4; ++s) sb[s] = cat(to_h4(S[2 * s]), to_h4(S[2 * s + 1]));
@@ -380,28 +384,51 @@ void state_kernel(SplitArgs sa)
             U[t] = f32x4{(float)up[0], (float)up[1], (float)up[2], (float)up[3]};
             Ot[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        h8 an[2][4], aq[2][4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int t = 0; t < 4; ++t) {
+            an[0][t] = nw[(t * 4 + 0) * 64 + lane];
+            aq[0][t] = qt[(t * 4 + 0) * 64 + lane];
+        }
+        h8 ap[6], ak[16];  // P and Kbar^T operands, read during the first products
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int cur = s & 1, nxt = cur ^ 1;
+            if (s < 3) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    an[nxt][t] = nw[(t * 4 + s + 1) * 64 + lane];
+                    aq[nxt][t] = qt[(t * 4 + s + 1) * 64 + lane];
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 6; ++i) {
+                    const int t = i < 2 ? i : 2 + (i - 2) / 2, s2 = i < 2 ? 0 : (i - 2) % 2;  // (t, s) with 2s <= t
+                    ap[i] = pm[(t * 2 + s2) * 64 + lane];
+                }
+            }
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                U[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(nw[(t * 4 + s) * 64 + lane], sb[s], U[t], 0, 0, 0);
-                Ot[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sb[s], qt[(t * 4 + s) * 64 + lane], Ot[t], 0, 0, 0);
+                U[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(an[cur][t], sb[s], U[t], 0, 0, 0);
+                Ot[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sb[s], aq[cur][t], Ot[t], 0, 0, 0);
             }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ak[i] = kb[i * 64 + lane];  // [t][s] = index t * 2 + s
         h8 ub[2];  // U as the B operand (U^T as the A operand) of a K step over tokens
 #pragma unroll
         for (int s = 0; s < 2; ++s) ub[s] = cat(to_h4(U[2 * s]), to_h4(U[2 * s + 1]));
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-                if (2 * s <= t) Ot[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ub[s], pm[(t * 2 + s) * 64 + lane], Ot[t], 0, 0, 0);
+        for (int i = 0; i < 6; ++i) {
+            const int t = i < 2 ? i : 2 + (i - 2) / 2, s2 = i < 2 ? 0 : (i - 2) % 2;
+            Ot[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ub[s2], ap[i], Ot[t], 0, 0, 0);
+        }
         // state: S <- Diag(2^b_C) S + Kbar^T U
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             f32x4 acc = S[t] * *reinterpret_cast<const f32x4*>(st + kStDc + (16 * t + 4 * q4) * 4);
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb[(t * 2 + s) * 64 + lane], ub[s], acc, 0, 0, 0);
+            for (int s = 0; s < 2; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak[t * 2 + s], ub[s], acc, 0, 0, 0);
             S[t] = acc;
         }
         // outputs: lane (token m16 of tile t, q4) holds columns 16j + 4 q4 .. +3;
