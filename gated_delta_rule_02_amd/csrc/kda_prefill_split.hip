@@ -55,12 +55,11 @@ constexpr int kUp = 57344;      // U' in the accumulator layout [8 j][4 t][64][4
 constexpr int kDc = 73728;      // 2^b_C    [128] f32
 constexpr int kSlot = 74240;
 constexpr int kStateWaves = 2;  // compute wavefronts of the state pass, one 16-column tile each
-constexpr int kStateThreads = 64 * (kStateWaves + 2);  // + a loader and a prefetcher wavefront
+constexpr int kStateThreads = 64 * (kStateWaves + 1);  // + a loader wavefront
 constexpr int kColGroups = D / (16 * kStateWaves);  // state-pass workgroups per (sequence, head)
 constexpr int kStage = 62464;   // LDS stage: operand block, U' of the workgroup's tiles, 2^b_C (+ pad)
 constexpr int kStUp = kDma;     // offset of U' (the workgroup's two tiles, 4 KiB) in a stage
 constexpr int kStDc = kDma + 4096;  // offset of 2^b_C in a stage
-constexpr int kPrefetchAhead = 3;   // chunks the prefetcher runs ahead of the loader
 
 struct SplitArgs {
     PrefillArgs p;
@@ -232,12 +231,14 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
 }
 
 // ------------------------------------------------------------- state pass
-// Four wavefronts: two compute wavefronts (one 16-column tile of the state
-// each), a loader that copies each chunk's operands into an LDS stage with
-// buffer-to-LDS loads (two stages, one chunk ahead), and a prefetcher that
-// touches the chunks further ahead so the loader's copies hit L2. Each role
-// waits only on its own memory counter; one barrier per chunk hands a stage
-// from the loader to the compute wavefronts.
+// Three wavefronts: two compute wavefronts (one 16-column tile of the state
+// each) and a loader that copies each chunk's operands into an LDS stage with
+// buffer-to-LDS loads (two stages, one chunk ahead). Each role waits only on
+// its own memory counter; one barrier per chunk hands a stage from the loader
+// to the compute wavefronts. (A fourth wavefront that touched the chunks two
+// to four ahead, to pull them into L2 early, made the pass slower: its reads
+// competed with the loader's, and lines it fetched were evicted before use,
+// so the pass fetched 1.65x the workspace instead of 1.04x.)
 //
 // The output is formed transposed, O^T = S^T Q~^T + U^T P^T: the 16 x 16 x 32
 // MFMA takes the same lane layout for its two operands, so the registers that
@@ -250,7 +251,6 @@ __global__ __launch_bounds__(kStateThreads) __attribute__((amdgpu_waves_per_eu(1
 void state_kernel(SplitArgs sa)
 {
     __shared__ __attribute__((aligned(16))) uint8_t buf[2][kStage];
-    __shared__ __attribute__((aligned(16))) uint32_t sink[64];  // target of the prefetcher's loads
     const PrefillArgs& a = sa.p;
     constexpr int C = 64;
 
@@ -322,17 +322,6 @@ void state_kernel(SplitArgs sa)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(uintptr_t)(st + kStDc), 16, lane * 16,
                                                  c * kSlot + kDc, 0, 0);
     };
-    // prefetcher: one 4-byte read per 128-byte line of what the loader will copy
-    const uint32_t sink0 = (uint32_t)(uintptr_t)(lds_void*)&sink[0];
-    auto prefetch = [&](int c) {
-#pragma unroll
-        for (int i = 0; i < kDma / 8192; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(uintptr_t)sink0, 4, lane * 128, c * kSlot + i * 8192, 0, 0);
-        if (lane < 36)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(uintptr_t)sink0, 4,
-                                                     lane < 32 ? lane * 128 : kDc - kUp - jq * 4096 + (lane - 32) * 128,
-                                                     c * kSlot + kUp + jq * 4096, 0, 0);
-    };
 
     f32x4 S[8];  // S[t][i] = S[16t + 4q + i][jcol]
     if (compute) {
@@ -349,8 +338,6 @@ void state_kernel(SplitArgs sa)
     if (loader) {
         dma(0, 0);
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-    } else if (!compute) {
-        for (int p = 1; p <= kPrefetchAhead && p < nch; ++p) prefetch(p);
     }
 
     const int ts = a.H * D;
@@ -360,10 +347,6 @@ void state_kernel(SplitArgs sa)
         if (loader) {
             if (c + 1 < nch) dma(c + 1, (c + 1) & 1);
             __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the stage is complete before the next barrier
-            continue;
-        }
-        if (!compute) {
-            if (c + 1 + kPrefetchAhead < nch) prefetch(c + 1 + kPrefetchAhead);
             continue;
         }
         const uint8_t* st = &buf[c & 1][0];
