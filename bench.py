@@ -6,8 +6,9 @@ A step is one KDA prefill of one layer over the single-sequence workload
 out, float32 output, 64-token chunks): ``value`` is tokens per second for that
 layer. The same run also times the batched decode step (B=256 sequences x 64
 heads, 1 GiB float32 state updated in place) and reports its state bandwidth,
-the decode-time convolution update, and (unless --skip-layer) the whole
-token-mixer layer at T=8192.
+the decode-time convolution update, the packed variable-length prefill (8
+sequences, ~135K tokens), the prefill with caches flushed before each call, and
+(unless --skip-layer) the whole token-mixer layer at T=8192.
 
 Timing: W untimed warm-up steps, then exactly K steps bracketed by
 torch.cuda.synchronize() on both sides, with HIP events recorded on the stream
@@ -78,6 +79,27 @@ def timed(torch, fn, steps, warmup):
     return start.elapsed_time(end) / steps, wall
 
 
+def timed_cold(torch, fn, steps, warmup, flush_bytes=512 << 20):
+    """Average ms per call when, before every call, a 512 MiB buffer is
+    written so that the 256 MB last-level cache (MALL) and L2 hold none of the
+    call's inputs. Each call is bracketed by its own events; the flush is not
+    timed."""
+    stream = torch.cuda.current_stream()
+    buf = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+    for i in range(warmup):
+        buf.fill_(float(i))
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        buf.fill_(float(i))
+        ev[i][0].record(stream)
+        fn()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / steps
+
+
 def bench_prefill(torch, K, steps, warmup):
     from gated_delta_rule_02_amd import synth
     d = synth.workload_prefill()
@@ -88,7 +110,43 @@ def bench_prefill(torch, K, steps, warmup):
     o = torch.empty((T, H, D), dtype=torch.float32, device="cuda")
     fn = lambda: K.kda_prefill(q, k, v, g, b, o, initial_state=s0, final_state=sT)
     ms, wall = timed(torch, fn, steps, warmup)
-    return ms, wall, d
+    ms_cold = timed_cold(torch, fn, max(5, steps // 2), 2)
+    snaps = torch.empty((1, 4, H, D, D), dtype=torch.float32, device="cuda")
+    fs = lambda: K.kda_prefill(q, k, v, g, b, o, initial_state=s0, final_state=sT, snapshots=snaps,
+                               snapshot_interval=1024)
+    ms_snap, _ = timed(torch, fs, max(5, steps // 2), 2)
+    return ms, wall, d, ms_cold, ms_snap
+
+
+def bench_varlen(torch, K, steps, warmup):
+    """The packed variable-length prefill: 8 sequences whose lengths are the
+    seeded draw U[1024, 32768] of the varlen parity workload, H=64, bf16
+    inputs with that workload's distributions (drawn on the device here: the
+    kernels' timing does not depend on the values), random fp32 initial
+    states, final states written."""
+    import numpy as np
+    from gated_delta_rule_02_amd import synth
+    lengths = synth.varlen_lengths(np.random.default_rng(1003), 8, 1024, 32768)
+    cu = synth.cu_from_lengths(lengths)
+    T, H, D = int(cu[-1]), 64, 128
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1003)
+    rn = lambda *shape: torch.randn(*shape, device="cuda", generator=gen, dtype=torch.float32)
+    unit = lambda x: x / x.norm(dim=-1, keepdim=True)
+    q = unit(rn(T, H, D)).to(torch.bfloat16)
+    k = unit(rn(T, H, D)).to(torch.bfloat16)
+    v = rn(T, H, D).to(torch.bfloat16)
+    g = torch.clamp(-torch.nn.functional.softplus(rn(T, H, D)), min=-5.0).to(torch.bfloat16)
+    b = torch.sigmoid(rn(T, H)).to(torch.bfloat16)
+    s0 = rn(len(lengths), H, D, D) * 0.02
+    sT = torch.empty_like(s0)
+    o = torch.empty((T, H, D), dtype=torch.float32, device="cuda")
+    cu_d = torch.from_numpy(cu).cuda()
+    cu_h = torch.from_numpy(cu)
+    fn = lambda: K.kda_prefill(q, k, v, g, b, o, cu_seqlens=cu_d, cu_seqlens_host=cu_h, num_seqs=len(lengths),
+                               initial_state=s0, final_state=sT)
+    ms, _ = timed(torch, fn, max(3, steps // 4), max(1, warmup // 2))
+    return ms, T, [int(x) for x in lengths]
 
 
 def bench_decode(torch, K, steps, warmup):
@@ -105,6 +163,23 @@ def bench_decode(torch, K, steps, warmup):
     # state (torch's elementwise kernel), the access pattern decode cannot avoid
     ms_ref, _ = timed(torch, lambda: st.mul_(1.0), max(5, steps // 2), 2)
     return ms, ms_conv, ms_ref
+
+
+def bench_decode_multi(torch, K, steps, warmup):
+    """Draft verification: B=256 sequences x 4 tokens x 64 heads, the state
+    after every token kept (4 GiB), the input state only read."""
+    from gated_delta_rule_02_amd import synth
+    d = synth.workload_decode_multi()
+    B, Tq, H = 256, d["Tq"], 64
+    q, k, v, g = (dev(d[x], torch).view(B, Tq, H, 128) for x in ("q", "k", "v", "g"))
+    b = dev(d["beta"], torch).view(B, Tq, H)
+    st = torch.from_numpy(d["state"]).cuda()
+    ts = torch.empty((B, Tq, H, 128, 128), dtype=torch.float32, device="cuda")
+    o = torch.empty((B, Tq, H, 128), dtype=torch.float32, device="cuda")
+    ms, _ = timed(torch, lambda: K.kda_decode_multi(q, k, v, g, b, st, o, token_states=ts), steps, warmup)
+    nbytes = (B * H * 128 * 128 * 4 * (1 + Tq) + 4 * B * Tq * H * 128 * 2 + B * Tq * H * 2
+              + B * Tq * H * 128 * 4)
+    return ms, nbytes
 
 
 def bench_layer(torch, steps, warmup):
@@ -173,8 +248,8 @@ def main():
     out = {}
     if args.only in (None, "prefill"):
         log("prefill T=4096 H=64")
-        ms, wall, d = bench_prefill(torch, K, args.steps, args.warmup)
-        log("prefill %.3f ms/step" % ms)
+        ms, wall, d, ms_cold, ms_snap = bench_prefill(torch, K, args.steps, args.warmup)
+        log("prefill %.3f ms/step (%.3f ms with the caches flushed before each call)" % (ms, ms_cold))
         T = 4096
         achieved = PREFILL_BYTES_PER_TOKEN * T / (ms * 1e-3) / 1e9
         traffic = None
@@ -197,7 +272,20 @@ def main():
                          "algorithmic_bytes_per_launch": PREFILL_BYTES_PER_TOKEN * T,
                          "mfma_tflops": PREFILL_FLOPS_PER_TOKEN * T / (ms * 1e-3) / 1e12,
                          "mfma_frac_of_bf16_peak": PREFILL_FLOPS_PER_TOKEN * T / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+            "prefill_cold_cache": {"ms_per_step": ms_cold, "tokens/s/layer": T / (ms_cold * 1e-3),
+                                   "method": "512 MiB written before each call (untimed); each call timed by its own events"},
+            "prefill_snapshots": {"workload": "the same prefill saving the state every 1024 tokens (4 x 4 MiB)",
+                                  "ms_per_step": ms_snap, "tokens/s/layer": T / (ms_snap * 1e-3)},
         })
+        if args.only is None:
+            log("varlen prefill, 8 packed sequences")
+            ms_v, T_v, lens = bench_varlen(torch, K, args.steps, args.warmup)
+            log("varlen %.3f ms/step for %d tokens" % (ms_v, T_v))
+            out["varlen"] = {"workload": "packed varlen prefill: 8 sequences, lengths %s (%d tokens), H=64 "
+                                         "dk=dv=128, bf16 inputs, fp32 initial and final states, fp32 o" % (lens, T_v),
+                             "ms_per_step": ms_v, "tokens/s/layer": T_v / (ms_v * 1e-3),
+                             "algorithmic_GB/s": (T_v * (4 * 64 * 128 * 2 + 64 * 2 + 64 * 128 * 4)
+                                                  + 2 * 8 * 64 * 128 * 128 * 4) / (ms_v * 1e-3) / 1e9}
         if not args.skip_cpu:
             log("cpu baseline (fp64 oracle)")
             out["cpu_baseline"] = cpu_baseline(d)
@@ -214,6 +302,13 @@ def main():
                          "inplace_stream_reference": "torch mul_ in place on the 1 GiB state buffer (read + write)"}
         out["conv_update"] = {"workload": "x [256,8192] bf16, state [256,3,8192] bf16 in place",
                               "ms_per_step": ms_conv, "GB/s": CONV_BYTES / (ms_conv * 1e-3) / 1e9}
+        log("decode multi-token B=256 x 4 tokens")
+        ms_m, nbytes = bench_decode_multi(torch, K, args.steps, args.warmup)
+        log("decode multi %.3f ms/step" % ms_m)
+        out["decode_multi"] = {"workload": "draft verification B=256 x 4 tokens x H=64, bf16 inputs, fp32 state "
+                                           "read once, the state after every token written (4 GiB), fp32 o",
+                               "ms_per_step": ms_m, "bytes_per_step": nbytes, "GB/s": nbytes / (ms_m * 1e-3) / 1e9,
+                               "frac_of_hbm_peak": nbytes / (ms_m * 1e-3) / 1e9 / HBM_PEAK_GBS}
     if args.only == "layer" or (args.only is None and not args.skip_layer):
         log("layer T=8192 hidden=4096")
         ms, flops = bench_layer(torch, args.steps, args.warmup)

@@ -110,33 +110,74 @@ size_t kda_conv_state_bytes(int streams, int W, int C, kda_dtype dtype)
 }
 
 // ---------------------------------------------------------------- decode
+static int decode_impl(const char* fn, const void* q, const void* k, const void* v, const void* g, const void* beta,
+                       kda_dtype in_dtype, int B, int Tq, int H, int dk, int dv, float scale, float lower_bound,
+                       float* state, float* token_states, void* o, kda_dtype out_dtype, void* hip_stream)
+{
+    REQUIRE(q && k && v && g && beta && state && o, KDA_ERR_INVALID_ARG, "%s: null tensor pointer", fn);
+    REQUIRE(valid_dtype(in_dtype) && valid_dtype(out_dtype), KDA_ERR_INVALID_ARG, "%s: bad dtype", fn);
+    REQUIRE(B >= 1 && H >= 1 && Tq >= 1, KDA_ERR_INVALID_ARG, "%s: B, H and the token count must be >= 1", fn);
+    REQUIRE(dk == 128 && dv == 128, KDA_ERR_UNSUPPORTED, "%s: only dk = dv = 128 is supported (got %d, %d)", fn, dk,
+            dv);
+    REQUIRE((int64_t)B * H <= 0x7fffffff && (int64_t)B * Tq * H <= ((int64_t)1 << 40), KDA_ERR_INVALID_ARG,
+            "%s: B*H too large", fn);
+    for (const void* p : {q, k, v, g, beta, (const void*)state, (const void*)token_states, (const void*)o})
+        REQUIRE(!p || aligned16(p), KDA_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
+    const size_t rows = (size_t)B * H, trows = rows * Tq;
+    const Range rs = rng(state, rows * 128 * 128 * 4), ro = rng(o, trows * 128 * esize(out_dtype));
+    const Range rt = rng(token_states, token_states ? trows * 128 * 128 * 4 : 0);
+    for (Range r : {rng(q, trows * 128 * esize(in_dtype)), rng(k, trows * 128 * esize(in_dtype)),
+                    rng(v, trows * 128 * esize(in_dtype)), rng(g, trows * 128 * esize(in_dtype)),
+                    rng(beta, trows * esize(in_dtype))}) {
+        REQUIRE(!overlap(r, rs), KDA_ERR_INVALID_ARG, "%s: state overlaps an input", fn);
+        REQUIRE(!overlap(r, ro), KDA_ERR_INVALID_ARG, "%s: o overlaps an input", fn);
+        REQUIRE(!overlap(r, rt), KDA_ERR_INVALID_ARG, "%s: token_states overlaps an input", fn);
+    }
+    REQUIRE(!overlap(rs, ro), KDA_ERR_INVALID_ARG, "%s: o overlaps state", fn);
+    REQUIRE(!overlap(rt, rs) && !overlap(rt, ro), KDA_ERR_INVALID_ARG, "%s: token_states overlaps state or o", fn);
+
+    DecodeArgs a{q, k, v, g, beta, state, token_states, o, B, H, Tq, scale, lower_bound, (DType)in_dtype,
+                 (DType)out_dtype};
+    return hip_status(launch_decode(a, static_cast<hipStream_t>(hip_stream)), fn);
+}
+
 int kda_decode_step(const void* q, const void* k, const void* v, const void* g, const void* beta,
                     kda_dtype in_dtype, int B, int H, int dk, int dv, float scale,
                     float lower_bound, float* state, void* o, kda_dtype out_dtype,
                     void* hip_stream)
 {
-    REQUIRE(q && k && v && g && beta && state && o, KDA_ERR_INVALID_ARG,
-            "kda_decode_step: null tensor pointer");
-    REQUIRE(valid_dtype(in_dtype) && valid_dtype(out_dtype), KDA_ERR_INVALID_ARG,
-            "kda_decode_step: bad dtype");
-    REQUIRE(B >= 1 && H >= 1, KDA_ERR_INVALID_ARG, "kda_decode_step: B and H must be >= 1");
-    REQUIRE(dk == 128 && dv == 128, KDA_ERR_UNSUPPORTED,
-            "kda_decode_step: only dk = dv = 128 is supported (got %d, %d)", dk, dv);
-    REQUIRE((int64_t)B * H <= 0x7fffffff, KDA_ERR_INVALID_ARG, "kda_decode_step: B*H too large");
-    for (const void* p : {q, k, v, g, beta, (const void*)state, (const void*)o})
-        REQUIRE(aligned16(p), KDA_ERR_INVALID_ARG, "kda_decode_step: pointers must be 16-byte aligned");
-    const size_t rows = (size_t)B * H;
-    const Range rs = rng(state, rows * 128 * 128 * 4), ro = rng(o, rows * 128 * esize(out_dtype));
-    for (Range r : {rng(q, rows * 128 * esize(in_dtype)), rng(k, rows * 128 * esize(in_dtype)),
-                    rng(v, rows * 128 * esize(in_dtype)), rng(g, rows * 128 * esize(in_dtype)),
-                    rng(beta, rows * esize(in_dtype))}) {
-        REQUIRE(!overlap(r, rs), KDA_ERR_INVALID_ARG, "kda_decode_step: state overlaps an input");
-        REQUIRE(!overlap(r, ro), KDA_ERR_INVALID_ARG, "kda_decode_step: o overlaps an input");
-    }
-    REQUIRE(!overlap(rs, ro), KDA_ERR_INVALID_ARG, "kda_decode_step: o overlaps state");
+    return decode_impl("kda_decode_step", q, k, v, g, beta, in_dtype, B, 1, H, dk, dv, scale, lower_bound, state,
+                       nullptr, o, out_dtype, hip_stream);
+}
 
-    DecodeArgs a{q, k, v, g, beta, state, o, B, H, scale, lower_bound, (DType)in_dtype, (DType)out_dtype};
-    return hip_status(launch_decode(a, static_cast<hipStream_t>(hip_stream)), "kda_decode_step");
+int kda_decode_multi(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                     kda_dtype in_dtype, int B, int num_tokens, int H, int dk, int dv, float scale,
+                     float lower_bound, float* state, float* token_states, void* o, kda_dtype out_dtype,
+                     void* hip_stream)
+{
+    return decode_impl("kda_decode_multi", q, k, v, g, beta, in_dtype, B, num_tokens, H, dk, dv, scale, lower_bound,
+                       state, token_states, o, out_dtype, hip_stream);
+}
+
+int kda_decode_commit(const float* token_states, const int32_t* accepted, int B, int num_tokens, int H, int dk,
+                      int dv, float* state, void* hip_stream)
+{
+    REQUIRE(token_states && accepted && state, KDA_ERR_INVALID_ARG, "kda_decode_commit: null pointer");
+    REQUIRE(B >= 1 && H >= 1 && num_tokens >= 1, KDA_ERR_INVALID_ARG,
+            "kda_decode_commit: B, H and the token count must be >= 1");
+    REQUIRE(dk == 128 && dv == 128, KDA_ERR_UNSUPPORTED,
+            "kda_decode_commit: only dk = dv = 128 is supported (got %d, %d)", dk, dv);
+    REQUIRE((int64_t)B * H <= 0x7fffffff, KDA_ERR_INVALID_ARG, "kda_decode_commit: B*H too large");
+    REQUIRE(aligned16(token_states) && aligned16(state), KDA_ERR_INVALID_ARG,
+            "kda_decode_commit: token_states and state must be 16-byte aligned");
+    const size_t rows = (size_t)B * H;
+    const Range rs = rng(state, rows * 128 * 128 * 4);
+    REQUIRE(!overlap(rs, rng(token_states, rows * num_tokens * 128 * 128 * 4)) &&
+                !overlap(rs, rng(accepted, (size_t)B * 4)),
+            KDA_ERR_INVALID_ARG, "kda_decode_commit: state overlaps token_states or accepted");
+    return hip_status(launch_decode_commit(token_states, accepted, state, B, num_tokens, H,
+                                           static_cast<hipStream_t>(hip_stream)),
+                      "kda_decode_commit");
 }
 
 // ---------------------------------------------------------------- conv
@@ -273,12 +314,12 @@ size_t kda_prefill_workspace_bytes(int64_t num_tokens, int num_seqs, int H, int 
     return bytes;
 }
 
-int kda_prefill(const void* q, const void* k, const void* v, const void* g, const void* beta,
-                kda_dtype in_dtype, int64_t num_tokens, int H, int dk, int dv,
-                const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int num_seqs,
-                float scale, float lower_bound, const float* initial_state, float* final_state,
-                void* o, kda_dtype out_dtype, void* workspace, size_t workspace_bytes,
-                void* hip_stream)
+static int prefill_impl(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                        kda_dtype in_dtype, int64_t num_tokens, int H, int dk, int dv,
+                        const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int num_seqs,
+                        float scale, float lower_bound, const float* initial_state, float* final_state,
+                        void* o, kda_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                        int64_t snap_interval, int64_t snap_slots, float* snapshots, void* hip_stream)
 {
     REQUIRE(valid_dtype(in_dtype) && valid_dtype(out_dtype), KDA_ERR_INVALID_ARG, "kda_prefill: bad dtype");
     REQUIRE(num_tokens >= 0 && H >= 1, KDA_ERR_INVALID_ARG, "kda_prefill: bad num_tokens or H");
@@ -287,7 +328,7 @@ int kda_prefill(const void* q, const void* k, const void* v, const void* g, cons
     REQUIRE(num_tokens == 0 || (q && k && v && g && beta && o), KDA_ERR_INVALID_ARG,
             "kda_prefill: null tensor pointer");
     for (const void* p : {q, k, v, g, beta, (const void*)initial_state, (const void*)final_state, (const void*)o,
-                          (const void*)workspace})
+                          (const void*)workspace, (const void*)snapshots})
         REQUIRE(!p || aligned16(p), KDA_ERR_INVALID_ARG, "kda_prefill: pointers must be 16-byte aligned");
     int64_t seq_len = 0;
     int rc = check_cu(cu_seqlens_dev, cu_seqlens_host, num_seqs, num_tokens, &seq_len);
@@ -302,6 +343,14 @@ int kda_prefill(const void* q, const void* k, const void* v, const void* g, cons
         for (int n = 0; n < num_seqs; ++n)
             max_len = std::max<int64_t>(max_len, (int64_t)cu_seqlens_host[n + 1] - cu_seqlens_host[n]);
     const int64_t max_chunks = (max_len + kChunk - 1) / kChunk;
+    if (snapshots) {
+        REQUIRE(snap_interval >= kChunk && snap_interval % kChunk == 0, KDA_ERR_INVALID_ARG,
+                "kda_prefill_snapshots: snapshot_interval must be a positive multiple of %lld (got %lld)",
+                (long long)kChunk, (long long)snap_interval);
+        REQUIRE(snap_slots >= max_len / snap_interval, KDA_ERR_INVALID_ARG,
+                "kda_prefill_snapshots: %lld snapshot slots per sequence needed (got %lld)",
+                (long long)(max_len / snap_interval), (long long)snap_slots);
+    }
     if (split) {
         const size_t slot = prefill_split_slot_bytes();
         const size_t whole = (size_t)(units * std::max<int64_t>(max_chunks, 1)) * slot;
@@ -316,6 +365,10 @@ int kda_prefill(const void* q, const void* k, const void* v, const void* g, cons
     const Range ro = rng(o, T * H * 128 * esize(out_dtype));
     const Range rs0 = rng(initial_state, initial_state ? sbytes : 0), rsT = rng(final_state, final_state ? sbytes : 0);
     const Range rws = rng(workspace, split ? workspace_bytes : 0);
+    const Range rsn = rng(snapshots, snapshots ? (size_t)num_seqs * snap_slots * H * 128 * 128 * 4 : 0);
+    for (const Range& r : {rng(q, T * H * 128 * ei), rng(k, T * H * 128 * ei), rng(v, T * H * 128 * ei),
+                           rng(g, T * H * 128 * ei), rng(beta, T * H * ei), rs0, ro, rsT, rws})
+        REQUIRE(!overlap(r, rsn), KDA_ERR_INVALID_ARG, "kda_prefill_snapshots: snapshots overlap another tensor");
     const Range ins[] = {rng(q, T * H * 128 * ei), rng(k, T * H * 128 * ei), rng(v, T * H * 128 * ei),
                          rng(g, T * H * 128 * ei), rng(beta, T * H * ei), rs0};
     for (const Range& r : ins) {
@@ -335,10 +388,36 @@ int kda_prefill(const void* q, const void* k, const void* v, const void* g, cons
     a.s0 = initial_state; a.sT = final_state; a.o = o;
     a.num_seqs = num_seqs; a.H = H; a.scale = scale; a.lower_bound = lower_bound;
     a.in_dtype = (DType)in_dtype; a.out_dtype = (DType)out_dtype;
+    a.snap = snapshots; a.snap_interval = snapshots ? snap_interval : 0; a.snap_slots = snapshots ? snap_slots : 0;
     const hipStream_t st = static_cast<hipStream_t>(hip_stream);
     if (split)
         return hip_status(launch_prefill_split(a, workspace, workspace_bytes, max_chunks, st), "kda_prefill");
     return hip_status(launch_prefill(a, st), "kda_prefill");
+}
+
+int kda_prefill(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                kda_dtype in_dtype, int64_t num_tokens, int H, int dk, int dv,
+                const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int num_seqs,
+                float scale, float lower_bound, const float* initial_state, float* final_state,
+                void* o, kda_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                void* hip_stream)
+{
+    return prefill_impl(q, k, v, g, beta, in_dtype, num_tokens, H, dk, dv, cu_seqlens_dev, cu_seqlens_host, num_seqs,
+                        scale, lower_bound, initial_state, final_state, o, out_dtype, workspace, workspace_bytes, 0, 0,
+                        nullptr, hip_stream);
+}
+
+int kda_prefill_snapshots(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                          kda_dtype in_dtype, int64_t num_tokens, int H, int dk, int dv,
+                          const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int num_seqs,
+                          float scale, float lower_bound, const float* initial_state, float* final_state,
+                          void* o, kda_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                          int64_t snapshot_interval, int64_t snapshot_slots, float* snapshots, void* hip_stream)
+{
+    REQUIRE(snapshots, KDA_ERR_INVALID_ARG, "kda_prefill_snapshots: null snapshots");
+    return prefill_impl(q, k, v, g, beta, in_dtype, num_tokens, H, dk, dv, cu_seqlens_dev, cu_seqlens_host, num_seqs,
+                        scale, lower_bound, initial_state, final_state, o, out_dtype, workspace, workspace_bytes,
+                        snapshot_interval, snapshot_slots, snapshots, hip_stream);
 }
 
 // ---------------------------------------------------------------- GEMM

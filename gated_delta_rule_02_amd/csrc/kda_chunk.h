@@ -118,6 +118,17 @@ template <> struct Io<float> {
 // A and B use the same assignment, so the product sums every k exactly once.
 __device__ __forceinline__ f32x4 ld4f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
+// A wavefront's 128 x 16 slice of a float32 128 x 128 state, held as
+// S[t][i] = S[16t + 4q + i][jcol], written to the state at `dst` (row major)
+__device__ __forceinline__ void store_state_slice(float* dst, const f32x4 (&S)[8], int q4, int jcol)
+{
+    float* p = dst + 4 * q4 * D + jcol;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[(16 * t + i) * D] = S[t][i];
+}
+
 __device__ __forceinline__ h4 to_h4(f32x4 x)
 {
     return h4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};

@@ -10,15 +10,20 @@ namespace kda {
 
 enum DType : int { F32 = 0, BF16 = 1 };
 
+// Tq tokens per sequence (1 for a plain decode step); inputs [B, Tq, H, d]
 struct DecodeArgs {
     const void *q, *k, *v, *g, *beta;
-    float* state;  // [B, H, 128, 128] in place
+    float* state;         // [B, H, 128, 128]: written in place unless token_states is set
+    float* token_states;  // [B, Tq, H, 128, 128] (state after each token) or null
     void* o;
-    int B, H;
+    int B, H, Tq;
     float scale, lower_bound;
     DType in_dtype, out_dtype;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+// state[b] <- token_states[b][accepted[b] - 1] for 1 <= accepted[b] <= Tq
+hipError_t launch_decode_commit(const float* token_states, const int32_t* accepted, float* state, int B, int Tq,
+                                int H, hipStream_t s);
 
 struct ConvUpdateArgs {
     const void* x;
@@ -77,6 +82,10 @@ struct PrefillArgs {
     int num_seqs, H;
     float scale, lower_bound;
     DType in_dtype, out_dtype;
+    // state snapshots: after every snap_interval tokens of a sequence (a
+    // multiple of 64), into snap[n][j] of [N, snap_slots, H, 128, 128]; off when null
+    float* snap;
+    int64_t snap_interval, snap_slots;
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 // Two-pass form (bfloat16 inputs): per-chunk products in `ws`, then the state

@@ -84,6 +84,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
         load_v(seq_s, (int)min<int64_t>(C, seq_e - seq_s));
     }
 
+    int64_t snap_next = a.snap_interval;  // tokens of the sequence at the next snapshot
+    int64_t snap_j = 0;                   // its index
     for (int64_t cs = seq_s; cs < seq_e; cs += C) {
         const int ntok = (int)min<int64_t>(C, seq_e - cs);
 
@@ -165,6 +167,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a)
                 acc = O::mma32(O::cat2(O::lds(&sm.KbT[16 * t + m16][16 * Rr + 4 * q4]), O::lds(&sm.KbT[16 * t + m16][16 * Rr + 16 + 4 * q4])),
                                O::cat2(UB[Rr], UB[Rr + 1]), acc);
             S[t] = acc;
+        }
+        // state snapshot when a whole chunk ends on a multiple of the interval
+        if (a.snap && cs + C - seq_s == snap_next && cs + C <= seq_e) {
+            store_state_slice(a.snap + (((size_t)n * a.snap_slots + snap_j) * a.H + h) * D * D, S, q4, jcol);
+            snap_next += a.snap_interval;
+            ++snap_j;
         }
         if (cs + C < seq_e) load_v(cs + C, (int)min<int64_t>(C, seq_e - cs - C));
         __syncthreads();

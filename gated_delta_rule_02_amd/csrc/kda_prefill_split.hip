@@ -342,6 +342,10 @@ void state_kernel(SplitArgs sa)
 
     const int ts = a.H * D;
     TOUT* og = static_cast<TOUT*>(a.o);
+    // snapshots: chunks left to the next multiple of the interval, and its index
+    const int snap_ic = a.snap ? (int)(a.snap_interval / C) : 1;
+    int snap_left = snap_ic - (int)(sa.chunk0 % snap_ic);
+    int snap_j = (int)(sa.chunk0 / snap_ic);
     for (int c = 0; c < nch; ++c) {
         __syncthreads();  // stage c & 1 holds chunk c
         if (loader) {
@@ -418,6 +422,13 @@ void state_kernel(SplitArgs sa)
         // rows past the sequence are dropped by the descriptor range
         const int64_t cs = seq_s + (sa.chunk0 + c) * C;
         const int ntok = (int)min<int64_t>(C, seq_e - cs);
+        // state snapshot when a whole chunk ends on a multiple of the interval
+        if (a.snap && --snap_left == 0) {
+            if (ntok == C)
+                store_state_slice(a.snap + (((size_t)n * a.snap_slots + snap_j) * a.H + h) * D * D, S, q4, jcol);
+            snap_left = snap_ic;
+            ++snap_j;
+        }
         const rsrc_t ro_ = make_rsrc(og + cs * ts, (int64_t)ntok * ts * (int64_t)sizeof(TOUT));
         const int voff = (m16 * ts + h * D + 16 * j + 4 * q4) * (int)sizeof(TOUT);
 #pragma unroll

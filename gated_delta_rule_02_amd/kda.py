@@ -28,7 +28,11 @@ _SZ = ctypes.c_size_t
 _SIGS = {
     "kda_prefill": (_I, [_P] * 5 + [_I, _I64, _I, _I, _I, _P, _P, _I, _F, _F, _P, _P, _P, _I, _P, _SZ, _P]),
     "kda_prefill_workspace_bytes": (_SZ, [_I64, _I, _I, _I, _I, _I]),
+    "kda_prefill_snapshots": (_I, [_P] * 5 + [_I, _I64, _I, _I, _I, _P, _P, _I, _F, _F, _P, _P, _P, _I, _P, _SZ,
+                                              _I64, _I64, _P, _P]),
     "kda_decode_step": (_I, [_P] * 5 + [_I, _I, _I, _I, _I, _F, _F, _P, _P, _I, _P]),
+    "kda_decode_multi": (_I, [_P] * 5 + [_I, _I, _I, _I, _I, _I, _F, _F, _P, _P, _P, _I, _P]),
+    "kda_decode_commit": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "kda_conv_state_update": (_I, [_P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P]),
     "kda_conv_prefill": (_I, [_P, _I64, _I64, _I, _I, _P, _P, _I, _P, _P, _P, _P, _I, _I, _F, _P, _I64, _I, _P]),
     "kda_gate_prologue": (_I, [_P, _I64, _P, _I64, _P, _I64, _I, _I, _F, _I, _P, _P, _I, _P]),
@@ -128,16 +132,20 @@ def _workspace(device, nbytes):
 
 def kda_prefill(q, k, v, g, beta, o, cu_seqlens=None, cu_seqlens_host=None, num_seqs=None,
                 initial_state=None, final_state=None, scale=1.0, lower_bound=-5.0,
-                workspace="auto", stream=None):
+                workspace="auto", stream=None, snapshots=None, snapshot_interval=None):
     """KDA core over packed sequences. q,k,g [T,H,128], v [T,H,128], beta [T,H]
     (one dtype), o [T,H,128] (float32 or bfloat16), states float32 [N,H,128,128].
 
     workspace: "auto" (a cached buffer of kda_prefill_workspace_bytes bytes, so
     bfloat16 inputs take the two-pass form), None (no workspace: single-pass
     form), or a caller-owned uint8 device tensor. Calls sharing the cached
-    buffer must be ordered on one stream."""
+    buffer must be ordered on one stream.
+
+    snapshots: float32 [N, slots, H, 128, 128] with snapshot_interval (a
+    multiple of 64): calls kda_prefill_snapshots, which also stores the state
+    after every snapshot_interval tokens of each sequence."""
     for n_, t_ in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("o", o),
-                   ("initial_state", initial_state), ("final_state", final_state)):
+                   ("initial_state", initial_state), ("final_state", final_state), ("snapshots", snapshots)):
         _dense(t_, n_)
     T, H, dk = q.shape
     dv = v.shape[2]
@@ -150,9 +158,17 @@ def kda_prefill(q, k, v, g, beta, o, cu_seqlens=None, cu_seqlens_host=None, num_
         need = lib().kda_prefill_workspace_bytes(T, num_seqs, H, dk, dv, _dt(q))
         workspace = _workspace(q.device, need) if need else None
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _call("kda_prefill", _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dt(q), T, H, dk, dv,
-          cu_dev, cu_host, num_seqs, scale, lower_bound, _ptr(initial_state), _ptr(final_state),
-          _ptr(o), _dt(o), _ptr(workspace), ws_bytes, _stream(stream))
+    if snapshots is None:
+        _call("kda_prefill", _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dt(q), T, H, dk, dv,
+              cu_dev, cu_host, num_seqs, scale, lower_bound, _ptr(initial_state), _ptr(final_state),
+              _ptr(o), _dt(o), _ptr(workspace), ws_bytes, _stream(stream))
+    else:
+        if snapshot_interval is None or snapshots.dim() != 5:
+            raise ValueError("snapshots [N, slots, H, 128, 128] needs a snapshot_interval")
+        _call("kda_prefill_snapshots", _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dt(q), T, H, dk, dv,
+              cu_dev, cu_host, num_seqs, scale, lower_bound, _ptr(initial_state), _ptr(final_state),
+              _ptr(o), _dt(o), _ptr(workspace), ws_bytes, int(snapshot_interval), snapshots.shape[1],
+              _ptr(snapshots), _stream(stream))
     return o
 
 
@@ -170,6 +186,33 @@ def kda_decode_step(q, k, v, g, beta, state, o, scale=1.0, lower_bound=-5.0, str
     _call("kda_decode_step", _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dt(q), B, H, dk, dv,
           scale, lower_bound, _ptr(state), _ptr(o), _dt(o), _stream(stream))
     return o
+
+
+def kda_decode_multi(q, k, v, g, beta, state, o, token_states=None, scale=1.0, lower_bound=-5.0, stream=None):
+    """Several tokens per sequence. q,k,g,v [B,Tq,H,128], beta [B,Tq,H]; state
+    float32 [B,H,128,128]; o [B,Tq,H,128]. token_states None: state becomes the
+    state after the last token; else token_states [B,Tq,H,128,128] receives the
+    state after every token and state is only read."""
+    for n_, t_ in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("state", state), ("o", o),
+                   ("token_states", token_states)):
+        _dense(t_, n_)
+    B, Tq, H, dk = q.shape
+    dv = v.shape[3]
+    _call("kda_decode_multi", _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dt(q), B, Tq, H, dk, dv,
+          scale, lower_bound, _ptr(state), _ptr(token_states), _ptr(o), _dt(o), _stream(stream))
+    return o
+
+
+def kda_decode_commit(token_states, accepted, state, stream=None):
+    """state[b] <- token_states[b, accepted[b] - 1] where 1 <= accepted[b] <= Tq
+    (accepted: int32 [B] on the device)."""
+    for n_, t_ in (("token_states", token_states), ("accepted", accepted), ("state", state)):
+        _dense(t_, n_)
+    if accepted.dtype != torch.int32:
+        raise TypeError("accepted must be int32")
+    B, Tq, H, dk, dv = token_states.shape
+    _call("kda_decode_commit", _ptr(token_states), _ptr(accepted), B, Tq, H, dk, dv, _ptr(state), _stream(stream))
+    return state
 
 
 def kda_conv_state_update(x, conv_state, weight, y, bias=None, apply_silu=True, l2norm_group=0,

@@ -144,6 +144,16 @@ def workload_decode(B=256, H=64, C=8192, seed=1002):
     return d
 
 
+def workload_decode_multi(B=256, Tq=4, H=64, seed=1005):
+    """Draft verification: B sequences with Tq tokens each (packed [B*Tq, H,
+    d], sequence-major), bf16 inputs, fp32 state [B, H, 128, 128] ~ N(0, 0.02^2)."""
+    rng = np.random.default_rng(seed)
+    d = core_inputs(rng, B * Tq, H, bf16=True)
+    d["state"] = states(rng, B, H)
+    d["Tq"] = Tq
+    return d
+
+
 def workload_varlen(n=8, lo=1024, hi=32768, H=64, seed=1003):
     """Packed variable-length prefill: n lengths ~ U[lo, hi], bf16 inputs,
     fp32 initial states [n, H, 128, 128] ~ N(0, 0.02^2)."""

@@ -112,6 +112,34 @@ size_t kda_prefill_workspace_bytes(int64_t num_tokens, int num_seqs, int H, int 
                                    kda_dtype in_dtype);
 
 /* ------------------------------------------------------------------------
+ * kda_prefill_snapshots -- kda_prefill that also saves the state at fixed
+ * token positions of every sequence.
+ *
+ * A recurrent state summarises everything before it, so a cached prefix can
+ * only be resumed where a state was saved; engines line these checkpoints up
+ * with their cache blocks ("Ling-3.1-flash: What 63 Linear-Attention Layers Do
+ * to the KV Budget", section "Where the hybrid makes serving harder").
+ *
+ * Every argument of kda_prefill keeps its meaning, plus:
+ * snapshot_interval  tokens between snapshots, a positive multiple of 64.
+ * snapshot_slots     snapshots per sequence that `snapshots` has room for:
+ *            at least floor(L / snapshot_interval) for the longest sequence
+ *            length L (else KDA_ERR_INVALID_ARG).
+ * snapshots  float32 [num_seqs, snapshot_slots, H, dk, dv], caller-owned.
+ *            snapshots[n][j] = the state of sequence n after its first
+ *            (j + 1) * snapshot_interval tokens (starting from its initial
+ *            state), for j < floor(L_n / snapshot_interval); other slots are
+ *            not written. Must not overlap any other tensor.
+ * ---------------------------------------------------------------------- */
+int kda_prefill_snapshots(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                          kda_dtype in_dtype, int64_t num_tokens, int H, int dk, int dv,
+                          const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int num_seqs,
+                          float scale, float lower_bound, const float* initial_state, float* final_state,
+                          void* o, kda_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                          int64_t snapshot_interval, int64_t snapshot_slots, float* snapshots,
+                          void* hip_stream);
+
+/* ------------------------------------------------------------------------
  * kda_decode_step -- one new token for each of B sequences, state in place.
  *
  * The same recurrence with T = 1 (retention, corrected write, read after the
@@ -128,6 +156,49 @@ int kda_decode_step(const void* q, const void* k, const void* v, const void* g, 
                     kda_dtype in_dtype, int B, int H, int dk, int dv, float scale,
                     float lower_bound, float* state, void* o, kda_dtype out_dtype,
                     void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * kda_decode_multi -- num_tokens new tokens for each of B sequences in one
+ * pass over the state (the draft tokens of speculative decoding, to verify).
+ *
+ * The recurrence applied token by token, as in kda_decode_step. A multi-token
+ * prediction layer serves as the draft head, and about 2.1 to 2.6 tokens are
+ * accepted per step ("Ling-3.1-flash: What 63 Linear-Attention Layers Do to
+ * the KV Budget", section "Fitting it on a node"); rejected tokens must not
+ * leave their writes in the state, hence the per-token states.
+ *
+ * q, k, g [B, num_tokens, H, dk], v [B, num_tokens, H, dv],
+ * beta [B, num_tokens, H]: in_dtype.
+ * state   float32 [B, H, dk, dv], the state before the first token. With
+ *         token_states NULL it is overwritten with the state after the last
+ *         token; otherwise it is only read.
+ * token_states  float32 [B, num_tokens, H, dk, dv] or NULL: entry [b][t] =
+ *         the state after token t of sequence b. Must not overlap another
+ *         tensor.
+ * o       [B, num_tokens, H, dv] out_dtype.
+ * Supported: dk = dv = 128, B, H, num_tokens >= 1.
+ * ---------------------------------------------------------------------- */
+int kda_decode_multi(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                     kda_dtype in_dtype, int B, int num_tokens, int H, int dk, int dv, float scale,
+                     float lower_bound, float* state, float* token_states, void* o, kda_dtype out_dtype,
+                     void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * kda_decode_commit -- keep the state of the accepted draft prefix.
+ *
+ * After verification, sequence b has accepted[b] of its num_tokens draft
+ * tokens (same page and section as kda_decode_multi): its state becomes the
+ * state after its last accepted token.
+ *
+ * token_states  float32 [B, num_tokens, H, dk, dv], from kda_decode_multi.
+ * accepted      int32 [B], device. 1 <= accepted[b] <= num_tokens:
+ *               state[b] = token_states[b][accepted[b] - 1]; any other value
+ *               leaves state[b] as it is.
+ * state         float32 [B, H, dk, dv], must not overlap token_states.
+ * Supported: dk = dv = 128.
+ * ---------------------------------------------------------------------- */
+int kda_decode_commit(const float* token_states, const int32_t* accepted, int B, int num_tokens, int H, int dk,
+                      int dv, float* state, void* hip_stream);
 
 /* ------------------------------------------------------------------------
  * kda_conv_state_update -- decode-time causal short convolution.

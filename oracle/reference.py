@@ -117,6 +117,54 @@ def kda_serial(q, k, v, g, beta, cu_seqlens=None, initial_state=None, scale=1.0,
 
 
 # --------------------------------------------------------------------------
+# States at fixed positions -- [asivanadi-Memory], sections "Where the hybrid
+# makes serving harder" (a recurrent state can be resumed only where it was
+# saved: snapshots at cache-block boundaries) and "Fitting it on a node"
+# (multi-token-prediction drafts, verified a few tokens at a time: the state
+# after every draft token is kept so rejected ones can be dropped)
+# --------------------------------------------------------------------------
+def kda_serial_snapshots(q, k, v, g, beta, interval, cu_seqlens=None, initial_state=None, scale=1.0,
+                         lower_bound=-5.0, nthreads=None):
+    """The token-serial recurrence, also returning each sequence's state after
+    every `interval` tokens.
+
+    Each sequence is cut at the multiples of `interval` and the pieces are run
+    in order through ``kda_serial``, the FP64 state of one piece being the
+    initial state of the next (exactly the serial run: the state is carried in
+    FP64 between the pieces).
+    Returns (o [T, H, dv], final_state [N, H, dk, dv],
+    snaps [N, max_j, H, dk, dv]) in float64, where snaps[n, j] is the state of
+    sequence n after its first (j + 1) * interval tokens and entries past a
+    sequence's last whole interval are NaN.
+    """
+    q, k, v, g, beta = (_f32(x) for x in (q, k, v, g, beta))
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    cu = np.array([0, T], dtype=np.int64) if cu_seqlens is None else np.asarray(cu_seqlens, dtype=np.int64)
+    N = cu.shape[0] - 1
+    lengths = cu[1:] - cu[:-1]
+    max_j = int(lengths.max() // interval) if N else 0
+    o = np.empty((T, H, dv), dtype=np.float64)
+    sT = np.empty((N, H, dk, dv), dtype=np.float64)
+    snaps = np.full((N, max_j, H, dk, dv), np.nan)
+    for n in range(N):
+        S = np.zeros((1, H, dk, dv)) if initial_state is None else \
+            np.asarray(initial_state[n:n + 1], dtype=np.float64)
+        a, e = int(cu[n]), int(cu[n + 1])
+        cuts = list(range(a, e, interval)) + [e]
+        for j, (s0, s1) in enumerate(zip(cuts[:-1], cuts[1:])):
+            sl = slice(s0, s1)
+            o[sl], S = kda_serial(q[sl], k[sl], v[sl], g[sl], beta[sl], initial_state=S, scale=scale,
+                                  lower_bound=lower_bound, nthreads=nthreads)
+            if s1 - s0 == interval:
+                snaps[n, j] = S[0]
+        if a == e:
+            o[a:e] = 0.0
+        sT[n] = S[0]
+    return o, sT, snaps
+
+
+# --------------------------------------------------------------------------
 # KDA core: chunked reorganisation, FP64 numpy (cross-check of the serial form)
 # --------------------------------------------------------------------------
 def kda_chunked_one(q, k, v, g, beta, S0=None, chunk=64, scale=1.0, lower_bound=-5.0):

@@ -154,3 +154,58 @@ def test_conv_and_misc_validation():
 def test_error_message_cleared_on_success_path_helpers():
     prefill(q=None)
     assert K.kda_last_error() != ""
+
+
+def snapshots_call(interval=128, slots=2, snap=None, **over):
+    a = dict(q=fake(1), k=fake(2), v=fake(3), g=fake(4), beta=fake(5), in_dtype=K.KDA_BF16,
+             T=256, H=4, dk=128, dv=128, cu_dev=None, cu_host=None, N=1, scale=1.0, lb=-5.0,
+             s0=None, sT=None, o=fake(6), out_dtype=K.KDA_F32, ws=None, ws_bytes=0, stream=None)
+    a.update(over)
+    return call("kda_prefill_snapshots", a["q"], a["k"], a["v"], a["g"], a["beta"], a["in_dtype"], a["T"], a["H"],
+                a["dk"], a["dv"], a["cu_dev"], a["cu_host"], a["N"], a["scale"], a["lb"], a["s0"], a["sT"],
+                a["o"], a["out_dtype"], a["ws"], a["ws_bytes"], interval, slots,
+                fake(10) if snap is None else snap, a["stream"])
+
+
+def test_prefill_snapshots_validation():
+    rc, msg = snapshots_call(interval=100)
+    assert rc == K.KDA_ERR_INVALID_ARG and "multiple of 64" in msg
+    assert snapshots_call(interval=0)[0] == K.KDA_ERR_INVALID_ARG
+    rc, msg = snapshots_call(interval=64, slots=3)          # 256 tokens need 4 slots
+    assert rc == K.KDA_ERR_INVALID_ARG and "4 snapshot slots" in msg
+    h = cu_host([0, 64, 256])                               # longest sequence 192 -> 3 slots of 64
+    assert snapshots_call(interval=64, slots=2, cu_dev=fake(7), cu_host=h, N=2)[0] == K.KDA_ERR_INVALID_ARG
+    rc, msg = snapshots_call(snap=fake(6) + 4096)           # snapshots inside o
+    assert rc == K.KDA_ERR_INVALID_ARG and "overlap" in msg
+    assert snapshots_call(snap=fake(10) + 8)[0] == K.KDA_ERR_INVALID_ARG   # misaligned
+    fn = getattr(K.lib(), "kda_prefill_snapshots")
+    rc = fn(fake(1), fake(2), fake(3), fake(4), fake(5), K.KDA_BF16, 256, 4, 128, 128, None, None, 1, 1.0, -5.0,
+            None, None, fake(6), K.KDA_F32, None, 0, 128, 2, None, None)
+    assert rc == K.KDA_ERR_INVALID_ARG and "null snapshots" in K.kda_last_error()
+
+
+def test_decode_multi_and_commit_validation():
+    # q k v g beta dtype B Tq H dk dv scale lb state token_states o out_dtype stream
+    args = [fake(1), fake(2), fake(3), fake(4), fake(5), K.KDA_BF16, 64, 4, 16, 128, 128, 1.0, -5.0,
+            fake(6, 1 << 34), fake(7, 1 << 34), fake(9), K.KDA_F32, None]
+    a = list(args); a[7] = 0
+    assert call("kda_decode_multi", *a)[0] == K.KDA_ERR_INVALID_ARG
+    a = list(args); a[9] = 64
+    assert call("kda_decode_multi", *a)[0] == K.KDA_ERR_UNSUPPORTED
+    a = list(args); a[14] = fake(6, 1 << 34) + 4096         # token_states inside the state
+    rc, msg = call("kda_decode_multi", *a)
+    assert rc == K.KDA_ERR_INVALID_ARG and "token_states overlaps" in msg
+    a = list(args); a[15] = fake(7, 1 << 34) + 1024         # o inside token_states
+    assert call("kda_decode_multi", *a)[0] == K.KDA_ERR_INVALID_ARG
+    a = list(args); a[14] = fake(7, 1 << 34) + 4            # misaligned
+    assert call("kda_decode_multi", *a)[0] == K.KDA_ERR_INVALID_ARG
+    # commit: state overlapping token_states, bad sizes, unsupported dk
+    rc, msg = call("kda_decode_commit", fake(1, 1 << 34), fake(2), 64, 4, 16, 128, 128, fake(1, 1 << 34) + 65536,
+                   None)
+    assert rc == K.KDA_ERR_INVALID_ARG and "overlaps" in msg
+    assert call("kda_decode_commit", fake(1, 1 << 34), fake(2), 64, 0, 16, 128, 128, fake(3, 1 << 34),
+                None)[0] == K.KDA_ERR_INVALID_ARG
+    assert call("kda_decode_commit", fake(1, 1 << 34), fake(2), 64, 4, 16, 128, 64, fake(3, 1 << 34),
+                None)[0] == K.KDA_ERR_UNSUPPORTED
+    assert call("kda_decode_commit", None, fake(2), 64, 4, 16, 128, 128, fake(3, 1 << 34),
+                None)[0] == K.KDA_ERR_INVALID_ARG

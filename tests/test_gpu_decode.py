@@ -120,3 +120,104 @@ def test_conv_state_update_l2_and_fp32():
         ry[b] = R.conv_causal(x[b:b + 1], w, state_in=s0[b:b + 1], bias=bias)[0][0]
     ry = R.l2norm_groups(ry, 128, 1e-6)
     assert relerr(host64(y), ry) < TOL_F32
+
+
+# ---------------------------------------------------------- multi-token decode
+def run_multi(d, state0, B, Tq, keep_states=True, out_dtype=torch.float32):
+    q, k, v, g, b = (dev(d[x]) for x in ("q", "k", "v", "g", "beta"))
+    H = q.shape[1]
+    q, k, v, g = (t.view(B, Tq, H, 128) for t in (q, k, v, g))
+    b = b.view(B, Tq, H)
+    st = dev(state0).contiguous()
+    ts = torch.empty((B, Tq, H, 128, 128), dtype=torch.float32, device="cuda") if keep_states else None
+    o = torch.empty((B, Tq, H, 128), dtype=out_dtype, device="cuda")
+    K.kda_decode_multi(q, k, v, g, b, st, o, token_states=ts)
+    torch.cuda.synchronize()
+    return o, st, ts
+
+
+def oracle_multi(d, state0, B, Tq):
+    cu = np.arange(B + 1) * Tq
+    o, S, st = R.kda_serial_snapshots(d["q"].vals, d["k"].vals, d["v"].vals, d["g"].vals, d["beta"].vals, 1,
+                                      cu_seqlens=cu, initial_state=state0.astype(np.float64))
+    return o, S, st
+
+
+@pytest.mark.parametrize("B,Tq,H,bf16", [(3, 4, 2, False), (5, 3, 3, True), (2, 7, 4, True)])
+def test_decode_multi_token_states(B, Tq, H, bf16):
+    """Per-token states and outputs of Tq draft tokens vs the oracle; the
+    input state is left unchanged."""
+    announce("decode multi B=%d Tq=%d H=%d bf16=%s" % (B, Tq, H, bf16))
+    rng = np.random.default_rng(300 + 10 * B + Tq)
+    d = synth.core_inputs(rng, B * Tq, H, bf16=bf16)
+    s0 = synth.states(rng, B, H, std=0.5)
+    o, st, ts = run_multi(d, s0, B, Tq)
+    ro, rS, rts = oracle_multi(d, s0, B, Tq)
+    tol = TOL_BF16 if bf16 else TOL_F32
+    assert relerr(host64(o).reshape(B * Tq, H, 128), ro) < tol
+    tsh = host64(ts)
+    for n in range(B):
+        for t in range(Tq):
+            assert relerr(tsh[n, t], rts[n, t]) < tol, (n, t)
+    assert np.array_equal(st.cpu().numpy(), s0)
+
+
+def test_decode_multi_in_place_and_single_token_equivalence():
+    """Without token_states the state ends at the last token (equal, bit for
+    bit, to the last per-token state); Tq = 1 equals kda_decode_step bit for
+    bit."""
+    announce("decode multi in place / Tq=1")
+    rng = np.random.default_rng(320)
+    B, Tq, H = 4, 3, 4
+    d = synth.core_inputs(rng, B * Tq, H, bf16=True)
+    s0 = synth.states(rng, B, H, std=0.5)
+    o1, _, ts = run_multi(d, s0, B, Tq, keep_states=True)
+    o2, st2, _ = run_multi(d, s0, B, Tq, keep_states=False)
+    assert torch.equal(o1, o2) and torch.equal(st2, ts[:, Tq - 1])
+    _, rS, _ = oracle_multi(d, s0, B, Tq)
+    for n in range(B):
+        assert relerr(host64(st2[n]), rS[n]) < TOL_BF16
+    d1 = synth.core_inputs(rng, B, H, bf16=True)
+    om, sm, _ = run_multi(d1, s0, B, 1, keep_states=False)
+    od, sd = run_decode(d1, s0)
+    assert torch.equal(om.view(B, H, 128), od) and torch.equal(sm, sd)
+
+
+def test_decode_commit_selects_accepted_state():
+    """state[b] <- token_states[b, accepted[b] - 1]; 0 or out-of-range counts
+    keep the state (bit-exact copies)."""
+    announce("decode commit")
+    rng = np.random.default_rng(330)
+    B, Tq, H = 6, 3, 2
+    d = synth.core_inputs(rng, B * Tq, H, bf16=True)
+    s0 = synth.states(rng, B, H, std=0.5)
+    _, st, ts = run_multi(d, s0, B, Tq)
+    acc = torch.tensor([0, 1, 2, 3, 4, -1], dtype=torch.int32, device="cuda")
+    K.kda_decode_commit(ts, acc, st)
+    torch.cuda.synchronize()
+    for b, a in enumerate([0, 1, 2, 3, 4, -1]):
+        want = ts[b, a - 1] if 1 <= a <= Tq else torch.from_numpy(s0[b]).cuda()
+        assert torch.equal(st[b], want), b
+
+
+def test_decode_multi_workload_full_size_sampled():
+    """Draft verification at full size: B=256 sequences x 4 tokens x 64 heads,
+    per-token states kept (4 GiB). The oracle checks 16 sampled (sequence,
+    head) pairs at every token; every state must be finite."""
+    announce("decode multi full B=256 Tq=4 H=64")
+    d = synth.workload_decode_multi()
+    B, Tq, H = 256, d["Tq"], 64
+    o, st, ts = run_multi(d, d["state"], B, Tq)
+    assert torch.isfinite(ts).all()
+    oh = host64(o)
+    rng = np.random.default_rng(7)
+    for b, h in zip(rng.integers(0, B, 16), rng.integers(0, H, 16)):
+        rows = slice(b * Tq, (b + 1) * Tq)
+        sub = lambda x: x.vals[rows, h:h + 1]
+        ro, _, rts = R.kda_serial_snapshots(sub(d["q"]), sub(d["k"]), sub(d["v"]), sub(d["g"]),
+                                            d["beta"].vals[rows, h:h + 1], 1,
+                                            initial_state=d["state"][b:b + 1, h:h + 1].astype(np.float64))
+        assert relerr(oh[b, :, h], ro[:, 0]) < TOL_BF16
+        tsh = host64(ts[b, :, h])
+        for t in range(Tq):
+            assert relerr(tsh[t], rts[0, t, 0]) < TOL_BF16, (b, h, t)

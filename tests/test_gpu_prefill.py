@@ -19,7 +19,7 @@ PATHS = ["split", "single"]
 
 
 def gpu_prefill(d, cu=None, s0=None, out_dtype=torch.float32, final=True, in_place=False, path="split",
-                workspace=None):
+                workspace=None, snapshots=None, interval=None):
     q, k, v, g, b = (dev(d[x]) for x in ("q", "k", "v", "g", "beta"))
     T, H, _ = q.shape
     o = torch.empty((T, H, 128), dtype=out_dtype, device="cuda")
@@ -32,7 +32,7 @@ def gpu_prefill(d, cu=None, s0=None, out_dtype=torch.float32, final=True, in_pla
         sT = s0_d if in_place else torch.empty((N, H, 128, 128), dtype=torch.float32, device="cuda")
     ws = workspace if workspace is not None else ("auto" if path == "split" else None)
     K.kda_prefill(q, k, v, g, b, o, cu_seqlens=cu_d, cu_seqlens_host=cu_h, num_seqs=N,
-                  initial_state=s0_d, final_state=sT, workspace=ws)
+                  initial_state=s0_d, final_state=sT, workspace=ws, snapshots=snapshots, snapshot_interval=interval)
     torch.cuda.synchronize()
     return o, sT
 
@@ -216,7 +216,7 @@ def test_split_windows_match_one_window(lens):
 def test_varlen_workload_full_size_sampled():
     """Packed varlen workload at full size: 8 sequences (123,444 tokens, up to
     447 chunks each), H = 64, bf16 inputs, random fp32 initial states, final
-    states returned; default two-pass form with 16-chunk windows. The GPU runs
+    states returned; default two-pass form with 24-chunk windows. The GPU runs
     every head; the oracle checks heads 0 and 41 of every sequence (o and
     final state), and every other head's final state must be finite."""
     announce("prefill varlen full size (sampled heads)")
@@ -245,3 +245,90 @@ def test_varlen_workload_full_size_sampled():
             es = relerr(host64(sT[n, h]), rS[n, 0])
             print("  head %d seq %d (T=%d): o err %.3e  state err %.3e" % (h, n, e_ - a_, eo, es), flush=True)
             assert eo < TOL_BF16 and es < TOL_BF16
+
+
+# ------------------------------------------------------------ state snapshots
+def snap_buffer(N, slots, H):
+    return torch.full((N, slots, H, 128, 128), float("nan"), dtype=torch.float32, device="cuda")
+
+
+def check_snapshots(snaps, rsnaps, lens, interval, tol):
+    sh = host64(snaps)
+    worst = 0.0
+    for n, ln in enumerate(lens):
+        for j in range(snaps.shape[1]):
+            if j < ln // interval:
+                e = relerr(sh[n, j], rsnaps[n, j])
+                worst = max(worst, e)
+                assert e < tol, (n, j, e)
+            else:
+                assert np.isnan(sh[n, j]).all(), (n, j)  # slots past the last whole interval stay untouched
+    print("  snapshot err %.3e" % worst, flush=True)
+
+
+@pytest.mark.parametrize("path,interval,bf16", [("split", 64, True), ("split", 128, True), ("single", 64, True),
+                                                ("single", 192, True), ("single", 64, False)])
+def test_snapshots_varlen_small(path, interval, bf16):
+    """States after every `interval` tokens of each sequence (ragged and empty
+    sequences, lengths on and off the interval) vs the oracle; o and final
+    states as without snapshots."""
+    announce("prefill snapshots %s interval=%d bf16=%s" % (path, interval, bf16))
+    lens = [200, 64, 0, 130, 384, 63]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    rng = np.random.default_rng(50 + interval)
+    H, N = 3, len(lens)
+    d = synth.core_inputs(rng, int(cu[-1]), H, bf16=bf16)
+    s0 = synth.states(rng, N, H, std=0.3)
+    slots = max(lens) // interval + 1  # one spare slot that must stay untouched
+    snaps = snap_buffer(N, slots, H)
+    o, sT = gpu_prefill(d, cu=cu, s0=s0, path=path, snapshots=snaps, interval=interval)
+    ro, rS, rsn = R.kda_serial_snapshots(d["q"].vals, d["k"].vals, d["v"].vals, d["g"].vals, d["beta"].vals,
+                                         interval, cu_seqlens=cu, initial_state=s0.astype(np.float64))
+    tol = TOL_BF16 if bf16 else TOL_F32
+    check(o, sT, ro, rS, tol)
+    check_snapshots(snaps, rsn, lens, interval, tol)
+    o2, s2 = gpu_prefill(d, cu=cu, s0=s0, path=path)
+    assert torch.equal(o, o2) and torch.equal(sT, s2)
+
+
+def test_snapshots_across_windows_bit_equal():
+    """One-chunk windows (the smallest workspace) give the same snapshots, bit
+    for bit, as one window holding every chunk."""
+    announce("prefill snapshots across windows")
+    lens = [333, 64, 0, 257]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    rng = np.random.default_rng(61)
+    H, N = 2, len(lens)
+    d = synth.core_inputs(rng, int(cu[-1]), H, bf16=True)
+    s0 = synth.states(rng, N, H, std=0.2)
+    U = N * H
+    small = torch.empty(U * 74240 + U * 128 * 128 * 4, dtype=torch.uint8, device="cuda")
+    big = torch.empty(U * 74240 * ((max(lens) + 63) // 64), dtype=torch.uint8, device="cuda")
+    s1, s2 = snap_buffer(N, 5, H), snap_buffer(N, 5, H)
+    gpu_prefill(d, cu=cu, s0=s0, workspace=small, snapshots=s1, interval=64)
+    gpu_prefill(d, cu=cu, s0=s0, workspace=big, snapshots=s2, interval=64)
+    assert torch.equal(torch.nan_to_num(s1, nan=7.0), torch.nan_to_num(s2, nan=7.0))
+    _, _, rsn = R.kda_serial_snapshots(d["q"].vals, d["k"].vals, d["v"].vals, d["g"].vals, d["beta"].vals, 64,
+                                       cu_seqlens=cu, initial_state=s0.astype(np.float64))
+    check_snapshots(s1, rsn, lens, 64, TOL_BF16)
+
+
+def test_snapshots_prefill_workload_full_size_sampled():
+    """The prefill workload (T = 4096, H = 64) with a snapshot every 1024
+    tokens, as bench.py launches it (two-pass form, 24-chunk windows): the
+    oracle checks heads 0 and 41 at every snapshot."""
+    announce("prefill snapshots full size")
+    d = synth.workload_prefill()
+    snaps = snap_buffer(1, 4, 64)
+    o, sT = gpu_prefill(d, snapshots=snaps, interval=1024)
+    assert torch.isfinite(snaps).all()
+    sh = host64(snaps)
+    for h in (0, 41):
+        sub = lambda x: x.vals[:, h:h + 1]
+        _, rS, rsn = R.kda_serial_snapshots(sub(d["q"]), sub(d["k"]), sub(d["v"]), sub(d["g"]),
+                                            d["beta"].vals[:, h:h + 1], 1024)
+        for j in range(4):
+            e = relerr(sh[0, j, h], rsn[0, j, 0])
+            print("  head %d snapshot %d err %.3e" % (h, j, e), flush=True)
+            assert e < TOL_BF16
+        assert np.array_equal(sh[0, 3, h], host64(sT[0, h]))  # the last snapshot is the final state

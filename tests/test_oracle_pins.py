@@ -420,3 +420,72 @@ def test_conv_bias_shifts_preactivation():
     b = np.array([0.0, 1.0, -2.0])
     y, _ = R.conv_causal(np.ones((2, 3)), np.zeros((3, 4)), bias=b)
     np.testing.assert_allclose(y[0], b / (1 + np.exp(-b)), rtol=1e-15)
+
+
+# ------------------------------------------------- snapshots / per-token states
+def test_snapshots_pure_decay_closed_form():
+    """beta = 0 (no write): the state after t tokens is Diag(exp(sum g)) S_0,
+    so snapshot j of each sequence must equal that at t = (j + 1) L; a wrong
+    cut, index or carried state fails it."""
+    rng = np.random.default_rng(31)
+    H, d, L = 2, 16, 8
+    lengths = [20, 0, 8, 33]
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    q, k, v, g, beta = rand_core(rng, int(cu[-1]), H, d, d)
+    beta[:] = 0
+    s0 = rng.standard_normal((len(lengths), H, d, d))
+    o, S, snaps = R.kda_serial_snapshots(q, k, v, g, beta, L, cu_seqlens=cu, initial_state=s0)
+    assert snaps.shape == (4, 4, H, d, d)
+    for n, ln in enumerate(lengths):
+        cum = np.cumsum(np.maximum(g[cu[n]:cu[n + 1]].astype(np.float64), -5.0), axis=0)  # retention clamp
+        for j in range(4):
+            if (j + 1) * L <= ln:
+                want = np.exp(cum[(j + 1) * L - 1])[..., None] * s0[n]
+                assert relerr(snaps[n, j], want) < 1e-13
+            else:
+                assert np.isnan(snaps[n, j]).all()
+        want_final = s0[n] if ln == 0 else np.exp(cum[-1])[..., None] * s0[n]
+        assert relerr(S[n], want_final) < 1e-13
+
+
+def test_snapshots_equal_prefix_runs():
+    """Snapshot j equals the final state of the sequence's first (j + 1) L
+    tokens run on their own; o and the final state equal the plain run."""
+    rng = np.random.default_rng(32)
+    H, d, L = 2, 16, 6
+    lengths = [19, 12, 5]
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    q, k, v, g, beta = rand_core(rng, int(cu[-1]), H, d, d)
+    s0 = rng.standard_normal((3, H, d, d)) * 0.1
+    o, S, snaps = R.kda_serial_snapshots(q, k, v, g, beta, L, cu_seqlens=cu, initial_state=s0)
+    o_ref, S_ref = R.kda_serial(q, k, v, g, beta, cu_seqlens=cu, initial_state=s0)
+    assert np.array_equal(o, o_ref) and np.array_equal(S, S_ref)
+    for n, ln in enumerate(lengths):
+        for j in range(ln // L):
+            e = int(cu[n]) + (j + 1) * L
+            sl = slice(int(cu[n]), e)
+            _, Sp = R.kda_serial(q[sl], k[sl], v[sl], g[sl], beta[sl], initial_state=s0[n:n + 1])
+            assert np.array_equal(snaps[n, j], Sp[0])
+    # the recurrence changes the state: consecutive snapshots differ
+    assert not np.allclose(snaps[0, 0], snaps[0, 1])
+
+
+def test_per_token_states_orthonormal_write_and_read():
+    """interval 1 (the per-token states of multi-token decode) on the
+    orthonormal-key case with alpha = beta = 1: after token t the state is
+    sum_{s<=t} k_s v_s^T, so S_t^T k_s = v_s for s <= t and 0 after."""
+    H, d, Tq = 1, 8, 5
+    eye = np.eye(d)
+    k = eye[:Tq][:, None, :].astype(np.float32)
+    rng = np.random.default_rng(33)
+    v = rng.standard_normal((Tq, H, d)).astype(np.float32)
+    q = k.copy()
+    g = np.zeros((Tq, H, d), np.float32)
+    beta = np.ones((Tq, H), np.float32)
+    o, S, st = R.kda_serial_snapshots(q, k, v, g, beta, 1)
+    for t in range(Tq):
+        for s in range(Tq):
+            got = st[0, t, 0].T @ k[s, 0].astype(np.float64)
+            want = v[s, 0] if s <= t else np.zeros(d)
+            assert np.allclose(got, want, atol=1e-15)
+        assert np.allclose(o[t, 0], v[t, 0], atol=1e-15)
