@@ -230,7 +230,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--skip-layer", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "layer", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "varlen", "decode", "layer", "copy"], default=None,
                     help="time one path only (for profiler runs); 'copy' times the plain copy that calibrates byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -277,18 +277,18 @@ def main():
             "prefill_snapshots": {"workload": "the same prefill saving the state every 1024 tokens (4 x 4 MiB)",
                                   "ms_per_step": ms_snap, "tokens/s/layer": T / (ms_snap * 1e-3)},
         })
-        if args.only is None:
-            log("varlen prefill, 8 packed sequences")
-            ms_v, T_v, lens = bench_varlen(torch, K, args.steps, args.warmup)
-            log("varlen %.3f ms/step for %d tokens" % (ms_v, T_v))
-            out["varlen"] = {"workload": "packed varlen prefill: 8 sequences, lengths %s (%d tokens), H=64 "
-                                         "dk=dv=128, bf16 inputs, fp32 initial and final states, fp32 o" % (lens, T_v),
-                             "ms_per_step": ms_v, "tokens/s/layer": T_v / (ms_v * 1e-3),
-                             "algorithmic_GB/s": (T_v * (4 * 64 * 128 * 2 + 64 * 2 + 64 * 128 * 4)
-                                                  + 2 * 8 * 64 * 128 * 128 * 4) / (ms_v * 1e-3) / 1e9}
         if not args.skip_cpu:
             log("cpu baseline (fp64 oracle)")
             out["cpu_baseline"] = cpu_baseline(d)
+    if args.only in (None, "varlen"):
+        log("varlen prefill, 8 packed sequences")
+        ms_v, T_v, lens = bench_varlen(torch, K, args.steps, args.warmup)
+        log("varlen %.3f ms/step for %d tokens" % (ms_v, T_v))
+        out["varlen"] = {"workload": "packed varlen prefill: 8 sequences, lengths %s (%d tokens), H=64 "
+                                     "dk=dv=128, bf16 inputs, fp32 initial and final states, fp32 o" % (lens, T_v),
+                         "ms_per_step": ms_v, "tokens/s/layer": T_v / (ms_v * 1e-3),
+                         "algorithmic_GB/s": (T_v * (4 * 64 * 128 * 2 + 64 * 2 + 64 * 128 * 4)
+                                              + 2 * 8 * 64 * 128 * 128 * 4) / (ms_v * 1e-3) / 1e9}
     if args.only in (None, "decode"):
         log("decode B=256 H=64")
         ms, ms_conv, ms_ref = bench_decode(torch, K, args.steps, args.warmup)

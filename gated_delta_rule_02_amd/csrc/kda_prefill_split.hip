@@ -54,12 +54,12 @@ constexpr int kUp = 57344;      // U' in the accumulator layout [8 j][4 t][64][4
                                 // lane (n, q) of column tile j holds U'[16t + 4q + i][16j + n]
 constexpr int kDc = 73728;      // 2^b_C    [128] f32
 constexpr int kSlot = 74240;
-constexpr int kStateWaves = 2;  // compute wavefronts of the state pass, one 16-column tile each
+constexpr int kStateWaves = 2;  // compute wavefronts of the state pass
 constexpr int kStateThreads = 64 * (kStateWaves + 1);  // + a loader wavefront
-constexpr int kColGroups = D / (16 * kStateWaves);  // state-pass workgroups per (sequence, head)
-constexpr int kStage = 62464;   // LDS stage: operand block, U' of the workgroup's tiles, 2^b_C (+ pad)
-constexpr int kStUp = kDma;     // offset of U' (the workgroup's two tiles, 4 KiB) in a stage
-constexpr int kStDc = kDma + 4096;  // offset of 2^b_C in a stage
+constexpr int kStUp = kDma;     // offset of U' (2 KiB per 16-column tile) in an LDS stage
+// LDS stage of a state-pass workgroup with `tiles` 16-column tiles: operand
+// block, U' of its tiles, 2^b_C (copied as 1 KiB: the tail is padding)
+__host__ __device__ constexpr int state_stage_bytes(int tiles) { return kDma + tiles * 2048 + 1024; }
 
 struct SplitArgs {
     PrefillArgs p;
@@ -246,10 +246,14 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
 // product, and the stored A-operand layouts of Q~ and P serve as B operands.
 // The result then holds four consecutive output columns of one token per lane
 // (16-byte stores) instead of four tokens of one column.
-template <typename TOUT>
+template <typename TOUT, int TPW>
 __global__ __launch_bounds__(kStateThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void state_kernel(SplitArgs sa)
 {
+    constexpr int kTiles = kStateWaves * TPW;      // 16-column tiles per workgroup
+    constexpr int kColGroups = D / (16 * kTiles);  // workgroups per (sequence, head)
+    constexpr int kStage = state_stage_bytes(kTiles);
+    constexpr int kStDc = kStUp + kTiles * 2048;   // offset of 2^b_C in a stage
     __shared__ __attribute__((aligned(16))) uint8_t buf[2][kStage];
     const PrefillArgs& a = sa.p;
     constexpr int C = 64;
@@ -276,23 +280,25 @@ void state_kernel(SplitArgs sa)
     const int64_t nchunks = (seq_e - seq_s + C - 1) / C;
     const int64_t c_end = min<int64_t>(nchunks, sa.chunk0 + sa.nwin);
     const int nch = (int)max<int64_t>(0, c_end - sa.chunk0);
-    const int jl = compute ? wave : 0;       // this wavefront's tile within the workgroup
-    const int j = kStateWaves * jq + jl;     // 16-column tile
-    const int jcol = 16 * j + m16;
+    const int jl = compute ? wave * TPW : 0;  // this wavefront's first tile within the workgroup
+    const int j0 = kTiles * jq + jl;         // its first 16-column tile; tile p is j0 + p
     const size_t sbase = (size_t)u * D * D;
 
     if (nch == 0) {
         // an empty sequence still has a final state: the initial one
         if (compute && sa.chunk0 == 0 && a.sT) {
-            int off = 4 * q4 * D + jcol;
-            asm volatile("" : "+v"(off));
 #pragma unroll
-            for (int t = 0; t < 8; ++t)
+            for (int p = 0; p < TPW; ++p) {
+                int off = 4 * q4 * D + 16 * (j0 + p) + m16;
+                asm volatile("" : "+v"(off));
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const size_t e = sbase + off + (size_t)(16 * t + i) * D;
-                    a.sT[e] = a.s0 ? a.s0[e] : 0.0f;
-                }
+                for (int t = 0; t < 8; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const size_t e = sbase + off + (size_t)(16 * t + i) * D;
+                        a.sT[e] = a.s0 ? a.s0[e] : 0.0f;
+                    }
+            }
         }
         return;
     }
@@ -305,7 +311,7 @@ void state_kernel(SplitArgs sa)
     const rsrc_t rs = make_rsrc(slots, (int64_t)nch * kSlot);
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)&buf[0][0];
     // loader: chunk c into stage b, 1 KiB per instruction (lane l moves bytes
-    // 16 l .. 16 l + 15): the operand block, then U' of this workgroup's two
+    // 16 l .. 16 l + 15): the operand block, then U' of this workgroup's
     // tiles, then 2^b_C (the instruction moves 1 KiB; the tail is padding).
     // Measured alternatives moved the same ~61 KiB per chunk and compute unit
     // no faster: two loader wavefronts, or loads through registers + LDS stores.
@@ -316,23 +322,27 @@ void state_kernel(SplitArgs sa)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(uintptr_t)(st + i * 1024), 16, lane * 16,
                                                      c * kSlot + i * 1024, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2 * kTiles; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(uintptr_t)(st + kStUp + i * 1024), 16, lane * 16,
-                                                     c * kSlot + kUp + jq * 4096 + i * 1024, 0, 0);
+                                                     c * kSlot + kUp + jq * kTiles * 2048 + i * 1024, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(uintptr_t)(st + kStDc), 16, lane * 16,
                                                  c * kSlot + kDc, 0, 0);
     };
 
-    f32x4 S[8];  // S[t][i] = S[16t + 4q + i][jcol]
+    f32x4 S[TPW][8];  // S[p][t][i] = S[16t + 4q + i][16 (j0 + p) + m16]
     if (compute) {
-        if (sin) {
 #pragma unroll
-            for (int t = 0; t < 8; ++t)
+        for (int p = 0; p < TPW; ++p) {
+            if (sin) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) S[t][i] = sin[sbase + (size_t)(16 * t + 4 * q4 + i) * D + jcol];
-        } else {
+                for (int t = 0; t < 8; ++t)
 #pragma unroll
-            for (int t = 0; t < 8; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int i = 0; i < 4; ++i)
+                        S[p][t][i] = sin[sbase + (size_t)(16 * t + 4 * q4 + i) * D + 16 * (j0 + p) + m16];
+            } else {
+#pragma unroll
+                for (int t = 0; t < 8; ++t) S[p][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         }
     }
     if (loader) {
@@ -360,17 +370,22 @@ void state_kernel(SplitArgs sa)
         const h8* pm = reinterpret_cast<const h8*>(st + kPm);
 
         // The operand reads run one group ahead of the MFMAs that consume them
-        // (LDS latency is otherwise exposed on every product).
-        h8 sb[4];  // S as the B operand (and S^T as the A operand) of a K step over dk
+        // (LDS latency is otherwise exposed on every product); each operand
+        // read serves the wavefront's TPW tiles.
+        h8 sb[TPW][4];  // S as the B operand (and S^T as the A operand) of a K step over dk
 #pragma unroll
-        for (int s = 0; s < 4; ++s) sb[s] = cat(to_h4(S[2 * s]), to_h4(S[2 * s + 1]));
-        f32x4 U[4], Ot[4];  // U[t]: tokens 16t.. x this tile; Ot[t]: this tile x tokens 16t..
+        for (int p = 0; p < TPW; ++p)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const h4 up = *reinterpret_cast<const h4*>(st + kStUp + ((jl * 4 + t) * 64 + lane) * 8);
-            U[t] = f32x4{(float)up[0], (float)up[1], (float)up[2], (float)up[3]};
-            Ot[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+            for (int s = 0; s < 4; ++s) sb[p][s] = cat(to_h4(S[p][2 * s]), to_h4(S[p][2 * s + 1]));
+        f32x4 U[TPW][4], Ot[TPW][4];  // U[p][t]: tokens 16t.. x tile p; Ot[p][t]: tile p x tokens 16t..
+#pragma unroll
+        for (int p = 0; p < TPW; ++p)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const h4 up = *reinterpret_cast<const h4*>(st + kStUp + (((jl + p) * 4 + t) * 64 + lane) * 8);
+                U[p][t] = f32x4{(float)up[0], (float)up[1], (float)up[2], (float)up[3]};
+                Ot[p][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         h8 an[2][4], aq[2][4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -395,28 +410,39 @@ void state_kernel(SplitArgs sa)
                 }
             }
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                U[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(an[cur][t], sb[s], U[t], 0, 0, 0);
-                Ot[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sb[s], aq[cur][t], Ot[t], 0, 0, 0);
-            }
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int p = 0; p < TPW; ++p) {
+                    U[p][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(an[cur][t], sb[p][s], U[p][t], 0, 0, 0);
+                    Ot[p][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sb[p][s], aq[cur][t], Ot[p][t], 0, 0, 0);
+                }
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) ak[i] = kb[i * 64 + lane];  // [t][s] = index t * 2 + s
-        h8 ub[2];  // U as the B operand (U^T as the A operand) of a K step over tokens
+        h8 ub[TPW][2];  // U as the B operand (U^T as the A operand) of a K step over tokens
 #pragma unroll
-        for (int s = 0; s < 2; ++s) ub[s] = cat(to_h4(U[2 * s]), to_h4(U[2 * s + 1]));
+        for (int p = 0; p < TPW; ++p)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) ub[p][s] = cat(to_h4(U[p][2 * s]), to_h4(U[p][2 * s + 1]));
 #pragma unroll
         for (int i = 0; i < 6; ++i) {
             const int t = i < 2 ? i : 2 + (i - 2) / 2, s2 = i < 2 ? 0 : (i - 2) % 2;
-            Ot[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ub[s2], ap[i], Ot[t], 0, 0, 0);
+#pragma unroll
+            for (int p = 0; p < TPW; ++p)
+                Ot[p][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ub[p][s2], ap[i], Ot[p][t], 0, 0, 0);
         }
         // state: S <- Diag(2^b_C) S + Kbar^T U
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            f32x4 acc = S[t] * *reinterpret_cast<const f32x4*>(st + kStDc + (16 * t + 4 * q4) * 4);
+            const f32x4 dc = *reinterpret_cast<const f32x4*>(st + kStDc + (16 * t + 4 * q4) * 4);
 #pragma unroll
-            for (int s = 0; s < 2; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak[t * 2 + s], ub[s], acc, 0, 0, 0);
-            S[t] = acc;
+            for (int p = 0; p < TPW; ++p) {
+                f32x4 acc = S[p][t] * dc;
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak[t * 2 + s], ub[p][s], acc, 0, 0, 0);
+                S[p][t] = acc;
+            }
         }
         // outputs: lane (token m16 of tile t, q4) holds columns 16j + 4 q4 .. +3;
         // rows past the sequence are dropped by the descriptor range
@@ -424,20 +450,28 @@ void state_kernel(SplitArgs sa)
         const int ntok = (int)min<int64_t>(C, seq_e - cs);
         // state snapshot when a whole chunk ends on a multiple of the interval
         if (a.snap && --snap_left == 0) {
-            if (ntok == C)
-                store_state_slice(a.snap + (((size_t)n * a.snap_slots + snap_j) * a.H + h) * D * D, S, q4, jcol);
+            if (ntok == C) {
+#pragma unroll
+                for (int p = 0; p < TPW; ++p)
+                    store_state_slice(a.snap + (((size_t)n * a.snap_slots + snap_j) * a.H + h) * D * D, S[p], q4,
+                                      16 * (j0 + p) + m16);
+            }
             snap_left = snap_ic;
             ++snap_j;
         }
         const rsrc_t ro_ = make_rsrc(og + cs * ts, (int64_t)ntok * ts * (int64_t)sizeof(TOUT));
-        const int voff = (m16 * ts + h * D + 16 * j + 4 * q4) * (int)sizeof(TOUT);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const f32x4 v = a.scale * Ot[t];
-            if constexpr (sizeof(TOUT) == 4) {
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), ro_, voff, 16 * t * ts * 4, 0);
-            } else {
-                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, to_b4(v)), ro_, voff, 16 * t * ts * 2, 0);
+        for (int p = 0; p < TPW; ++p) {
+            const int voff = (m16 * ts + h * D + 16 * (j0 + p) + 4 * q4) * (int)sizeof(TOUT);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const f32x4 v = a.scale * Ot[p][t];
+                if constexpr (sizeof(TOUT) == 4) {
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), ro_, voff, 16 * t * ts * 4, 0);
+                } else {
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, to_b4(v)), ro_, voff,
+                                                          16 * t * ts * 2, 0);
+                }
             }
         }
     }
@@ -447,14 +481,25 @@ void state_kernel(SplitArgs sa)
         return;
     }
     if (sout) {
-        int off = 4 * q4 * D + jcol;
-        asm volatile("" : "+v"(off));
-        float* so = sout + sbase + off;
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
+        for (int p = 0; p < TPW; ++p) {
+            int off = 4 * q4 * D + 16 * (j0 + p) + m16;
+            asm volatile("" : "+v"(off));
+            float* so = sout + sbase + off;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) so[(16 * t + i) * D] = S[t][i];
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) so[(16 * t + i) * D] = S[p][t][i];
+        }
     }
+}
+
+template <typename TOUT, int TPW>
+void launch_state(const SplitArgs& sa, int64_t U, hipStream_t s)
+{
+    constexpr int kColGroups = D / (16 * kStateWaves * TPW);
+    const dim3 gs((unsigned)(kColGroups * 8 * ((U + 7) / 8))), bs(kStateThreads);
+    hipLaunchKernelGGL((state_kernel<TOUT, TPW>), gs, bs, 0, s, sa);
 }
 
 }  // namespace
@@ -481,14 +526,17 @@ hipError_t launch_prefill_split(const PrefillArgs& a, void* ws, size_t ws_bytes,
     // groups-th chunk of the window with its next chunk prefetched
     sa.groups = (int)std::max<int64_t>(1, std::min<int64_t>(sa.nwin, (256 + U - 1) / U));
     const dim3 gi((unsigned)(U * sa.groups)), bi(kThreads);
-    const dim3 gs((unsigned)(kColGroups * 8 * ((U + 7) / 8))), bs(kStateThreads);
+    // state pass: 4 workgroups of 32 columns per (sequence, head) while they
+    // all fit on the chip at once (one per compute unit), else 2 of 64 columns
+    // (each wavefront then carries two tiles through every operand read)
+    const bool narrow = U * 4 <= 256;
     for (int64_t c0 = 0; c0 < std::max<int64_t>(max_chunks, 1); c0 += sa.nwin) {
         sa.chunk0 = c0;
         if (max_chunks > 0) hipLaunchKernelGGL(intra_kernel<bf16_t>, gi, bi, 0, s, sa);
         if (a.out_dtype == F32)
-            hipLaunchKernelGGL(state_kernel<float>, gs, bs, 0, s, sa);
+            narrow ? launch_state<float, 1>(sa, U, s) : launch_state<float, 2>(sa, U, s);
         else
-            hipLaunchKernelGGL(state_kernel<bf16_t>, gs, bs, 0, s, sa);
+            narrow ? launch_state<bf16_t, 1>(sa, U, s) : launch_state<bf16_t, 2>(sa, U, s);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -332,3 +332,45 @@ def test_snapshots_prefill_workload_full_size_sampled():
             print("  head %d snapshot %d err %.3e" % (h, j, e), flush=True)
             assert e < TOL_BF16
         assert np.array_equal(sh[0, 3, h], host64(sT[0, h]))  # the last snapshot is the final state
+
+
+def test_wide_state_pass_matches_narrow_bit_for_bit():
+    """More than 64 (sequence, head) units switch the state pass to workgroups
+    of 64 columns (two tiles per wavefront). Adding an empty sequence to a
+    33-head problem crosses that line; the real sequence's outputs and final
+    state must not change by a bit, and both match the oracle."""
+    announce("prefill wide vs narrow state pass")
+    rng = np.random.default_rng(71)
+    H, T = 33, 300
+    d = synth.core_inputs(rng, T, H, bf16=True)
+    s0 = synth.states(rng, 2, H, std=0.3)
+    o1, s1 = gpu_prefill(d, cu=np.array([0, T], np.int32), s0=s0[:1])          # 33 units: narrow
+    o2, s2 = gpu_prefill(d, cu=np.array([0, T, T], np.int32), s0=s0)           # 66 units: wide
+    assert torch.equal(o1, o2) and torch.equal(s1[0], s2[0])
+    assert np.array_equal(host64(s2[1]), s0[1].astype(np.float64))             # the empty sequence keeps its state
+    ro, rS = oracle(d, cu=np.array([0, T]), s0=s0[:1])
+    check(o2, s2[:1], ro, rS, TOL_BF16)
+
+
+def test_wide_state_pass_windows_and_snapshots():
+    """80 units (wide state pass), ragged and empty sequences, one-chunk
+    windows vs one window, with snapshots: bit-equal, and equal to the oracle."""
+    announce("prefill wide state pass, windows + snapshots")
+    lens = [200, 64, 130, 0, 257]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    rng = np.random.default_rng(72)
+    H, N = 16, len(lens)
+    d = synth.core_inputs(rng, int(cu[-1]), H, bf16=True)
+    s0 = synth.states(rng, N, H, std=0.2)
+    U = N * H
+    small = torch.empty(U * 74240 + U * 128 * 128 * 4, dtype=torch.uint8, device="cuda")
+    big = torch.empty(U * 74240 * ((max(lens) + 63) // 64), dtype=torch.uint8, device="cuda")
+    n1, n2 = snap_buffer(N, 4, H), snap_buffer(N, 4, H)
+    o1, s1 = gpu_prefill(d, cu=cu, s0=s0, workspace=small, snapshots=n1, interval=64)
+    o2, s2 = gpu_prefill(d, cu=cu, s0=s0, workspace=big, snapshots=n2, interval=64)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    assert torch.equal(torch.nan_to_num(n1, nan=7.0), torch.nan_to_num(n2, nan=7.0))
+    ro, rS, rsn = R.kda_serial_snapshots(d["q"].vals, d["k"].vals, d["v"].vals, d["g"].vals, d["beta"].vals, 64,
+                                         cu_seqlens=cu, initial_state=s0.astype(np.float64))
+    check(o1, s1, ro, rS, TOL_BF16)
+    check_snapshots(n1, rsn, lens, 64, TOL_BF16)
