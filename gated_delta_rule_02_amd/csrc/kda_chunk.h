@@ -294,7 +294,11 @@ struct __attribute__((aligned(16))) Smem {
 // group hh of block R); the next chunk's k, q, g of those tokens and beta
 // stream into registers while the current chunk computes. The caller
 // separates the phases with barriers.
-template <bool F32P, typename TIN, int NQ = 2, bool StageV = false>
+// Lean: the kernel holds no state in registers here (the two-pass intra
+// pass), so P2 can afford more live registers: the diagonal-block inverses by
+// repeated squaring instead of the Horner form (fewer dependent products) and
+// the off-diagonal pairs split evenly over the SIMDs.
+template <bool F32P, typename TIN, int NQ = 2, bool StageV = false, bool Lean = false>
 struct Front {
     using O = Ops<F32P>;
     using OT = typename O::OT;
@@ -477,14 +481,41 @@ struct Front {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        // (I + N)^-1 = sum_{j<16} (-N)^j  (N strictly lower, N^16 = 0), Horner form
-        const F4 nA = O::lds(&sm.Nd[Rd][m16][4 * q4]);
+        if constexpr (!Lean) {
+            // (I + N)^-1 = sum_{j<16} (-N)^j  (N strictly lower, N^16 = 0), Horner form
+            const F4 nA = O::lds(&sm.Nd[Rd][m16][4 * q4]);
+            f32x4 eye;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) eye[i] = (4 * q4 + i == m16) ? 1.0f : 0.0f;
+            f32x4 Y = eye;
+#pragma unroll
+            for (int it = 0; it < 15; ++it) Y = O::mma16(nA, O::cvt(Y), eye);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm.Tb[Rd][4 * q4 + i][m16] = (OT)Y[i];
+            return;
+        }
+        // (I + A_RR)^-1 = sum_{j<16} M^j = (I + M)(I + M^2)(I + M^4)(I + M^8)
+        // with M = -A_RR (strictly lower, M^16 = 0): three squarings and three
+        // products instead of fifteen dependent Horner steps. A square needs
+        // its operand in both layouts; the registers of X in the A layout are
+        // those of X^T in the B layout, so X^2 and (X^2)^T = X^T X^T come from
+        // the same two registers and fill both layouts of the next power.
+        F4 aM = O::lds(&sm.Nd[Rd][m16][4 * q4]);  // M in the A layout
+        F4 bM;                                     // M in the B layout
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bM[i] = sm.Nd[Rd][4 * q4 + i][m16];
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         f32x4 eye;
 #pragma unroll
         for (int i = 0; i < 4; ++i) eye[i] = (4 * q4 + i == m16) ? 1.0f : 0.0f;
-        f32x4 Y = eye;
-#pragma unroll
-        for (int it = 0; it < 15; ++it) Y = O::mma16(nA, O::cvt(Y), eye);
+        const F4 aM1 = aM, bM1 = bM;
+        const F4 bM2 = O::cvt(O::mma16(aM1, bM1, z)), aM2 = O::cvt(O::mma16(bM1, aM1, z));  // M^2
+        const F4 bM4 = O::cvt(O::mma16(aM2, bM2, z)), aM4 = O::cvt(O::mma16(bM2, aM2, z));  // M^4
+        const f32x4 M8 = O::mma16(aM4, bM4, z);                                             // M^8
+        f32x4 Y = M8 + eye;                          // I + M^8
+        Y = O::mma16(aM4, O::cvt(Y), Y);             // (I + M^4)(I + M^8)
+        Y = O::mma16(aM2, O::cvt(Y), Y);             // (I + M^2) ...
+        Y = O::mma16(aM1, O::cvt(Y), Y);             // (I + M) ...
 #pragma unroll
         for (int i = 0; i < 4; ++i) sm.Tb[Rd][4 * q4 + i][m16] = (OT)Y[i];
     }
@@ -516,12 +547,29 @@ struct Front {
     }
 
     // P2 with 8 wavefronts: 0 .. NB-1 the diagonal blocks, the rest the
-    // off-diagonal pairs (A and P together)
+    // off-diagonal pairs. With four blocks the six pairs go to four
+    // wavefronts as one pair (A and P) plus the A or the P half of one of the
+    // last two pairs each; wavefronts w and w + 4 share a SIMD, so every SIMD
+    // gets a diagonal block and one and a half pairs.
     __device__ __forceinline__ void p2()
     {
         constexpr int kW = kWaves;
         if (wave < NB) {
             p2_diag(wave);
+        } else if constexpr (Lean && NB == 4 && kW == 8) {
+            if (wave == 4) {
+                p2_pair<true, true>(1, 0);
+                p2_pair<true, false>(3, 1);
+            } else if (wave == 5) {
+                p2_pair<true, true>(2, 0);
+                p2_pair<true, false>(3, 2);
+            } else if (wave == 6) {
+                p2_pair<true, true>(2, 1);
+                p2_pair<false, true>(3, 1);
+            } else {
+                p2_pair<true, true>(3, 0);
+                p2_pair<false, true>(3, 2);
+            }
         } else {
 #pragma unroll
             for (int Rr = 1; Rr < NB; ++Rr)

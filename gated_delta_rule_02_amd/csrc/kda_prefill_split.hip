@@ -82,6 +82,33 @@ __device__ __forceinline__ void seq_bounds(const PrefillArgs& a, int n, int64_t&
 }
 
 // ------------------------------------------------------------- intra pass
+// Block column I of T = (I + A)^-1 below the diagonal (A strictly lower and
+// beta-scaled, stored negated in An; T_RR in Tb): T_RI = T_RR sum_{I<=J<R}
+// (-A_RJ) T_JI for R = I+1 .. 3, each block rounded to float16 once. The
+// running blocks T_JI stay in registers in the B-operand layout (= the
+// accumulator layout of the product that made them); Tm receives them row
+// major, the A-operand layout of the products with T.
+template <int I, typename SM>
+__device__ __forceinline__ void inverse_column(SM& sm, _Float16 (*Tm)[16][16], int m16, int q4)
+{
+    using O = Ops<false>;
+    using F4 = typename O::F4;
+    constexpr int NB = SM::NB;
+    F4 tc[NB];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tc[I][i] = sm.Tb[I][4 * q4 + i][m16];  // T_II in the B layout
+#pragma unroll
+    for (int R = I + 1; R < NB; ++R) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int J = I; J < R; ++J) acc = O::mma16(O::lds(&sm.An[pair_id(R, J)][m16][4 * q4]), tc[J], acc);
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        tc[R] = O::cvt(O::mma16(O::lds(&sm.Tb[R][m16][4 * q4]), O::cvt(acc), z));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Tm[pair_id(R, I)][4 * q4 + i][m16] = tc[R][i];
+    }
+}
+
 template <typename TIN>
 __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
 {
@@ -97,10 +124,11 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
     static_assert(C == 64 && NB == 4, "slot layout assumes 64-token chunks");
 
     __shared__ SM sm;
+    __shared__ __attribute__((aligned(16))) _Float16 Tm[SM::NPAIR][16][16];  // T = (I + A)^-1 below the diagonal
     const PrefillArgs& a = sa.p;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int m16 = lane & 15;
     const int q4 = lane >> 4;
@@ -121,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
     const TIN* vg = static_cast<const TIN*>(a.v);
     uint8_t* slots = sa.ws + (size_t)u * sa.nwin * kSlot;
 
-    Front<false, TIN> fr(sm, a, h);
+    Front<false, TIN, 2, false, true> fr(sm, a, h);
     uint32_t rv[NB][4];  // v[16R + 4q + i][jcol] (raw bits)
     auto load_v = [&](int64_t c_s, int nt) {
         const rsrc_t rv_ = make_rsrc(vg + c_s * ts, (int64_t)nt * ts * ES);
@@ -151,39 +179,58 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
         fr.p2();
         __syncthreads();
         fr.p2b();
+        // ---- P2c: the blocks of T = (I + A)^-1 below the diagonal, one block
+        // column per wavefront: T_RI = T_RR sum_{I<=J<R} (-A_RJ) T_JI
+        if (wave == 0) inverse_column<0>(sm, Tm, m16, q4);
+        else if (wave == 1) inverse_column<1>(sm, Tm, m16, q4);
+        else if (wave == 2) inverse_column<2>(sm, Tm, m16, q4);
         __syncthreads();
 
-        // ---- -W and U' by block forward substitution, one K~ tile and one V
-        // tile per wavefront: Z_R = T_RR (X_R + sum_{I<R} (-A_RI) Z_I)
+        // ---- -W and U' as products with T, one K~ tile and one V tile per
+        // wavefront: Z_R = sum_{I<=R} T_RI X_I (independent block rows)
         uint8_t* slot = slots + (size_t)(c - sa.chunk0) * kSlot;
-        F4 ZW[NB], ZU[NB];
+        // all LDS reads first, so that they are in flight together
+        f32x4 bt[NB];
+        OT kt[NB][4];
+#pragma unroll
+        for (int Rr = 0; Rr < NB; ++Rr) {
+            bt[Rr] = ld4f(&sm.beta[16 * Rr + 4 * q4]);  // rows past the chunk: k = v = beta = 0
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kt[Rr][i] = sm.key.h.Kt[16 * Rr + 4 * q4 + i][jcol];
+        }
+        F4 XW[NB], XU[NB];
 #pragma unroll
         for (int Rr = 0; Rr < NB; ++Rr) {
             f32x4 yw, yu;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = 16 * Rr + 4 * q4 + i;  // rows past the chunk: k = v = beta = 0
-                const float b = sm.beta[r];
-                yw[i] = -b * (float)sm.key.h.Kt[r][jcol];
-                yu[i] = b * IN::one(rv[Rr][i]);
+                yw[i] = -bt[Rr][i] * (float)kt[Rr][i];
+                yu[i] = bt[Rr][i] * IN::one(rv[Rr][i]);
             }
+            XW[Rr] = O::cvt(yw);
+            XU[Rr] = O::cvt(yu);
+        }
+        // block (R, I) of T in the A-operand layout
+        auto tblk = [&](int Rr, int I) {
+            return I == Rr ? O::lds(&sm.Tb[Rr][m16][4 * q4]) : O::lds(&Tm[pair_id(Rr, I)][m16][4 * q4]);
+        };
+        F4 ZW[NB], ZU[NB];
 #pragma unroll
-            for (int I = 0; I + 1 < Rr; I += 2) {
-                const F8 an = O::cat2(O::lds(&sm.An[pair_id(Rr, I)][m16][4 * q4]),
-                                       O::lds(&sm.An[pair_id(Rr, I + 1)][m16][4 * q4]));
-                yw = O::mma32(an, O::cat2(ZW[I], ZW[I + 1]), yw);
-                yu = O::mma32(an, O::cat2(ZU[I], ZU[I + 1]), yu);
+        for (int Rr = 0; Rr < NB; ++Rr) {
+            f32x4 aw = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int I = 0; I + 1 <= Rr; I += 2) {
+                const F8 t2 = O::cat2(tblk(Rr, I), tblk(Rr, I + 1));
+                aw = O::mma32(t2, O::cat2(XW[I], XW[I + 1]), aw);
+                au = O::mma32(t2, O::cat2(XU[I], XU[I + 1]), au);
             }
-            if (Rr & 1) {
-                const F4 an = O::lds(&sm.An[pair_id(Rr, Rr - 1)][m16][4 * q4]);
-                yw = O::mma16(an, ZW[Rr - 1], yw);
-                yu = O::mma16(an, ZU[Rr - 1], yu);
+            if (!(Rr & 1)) {
+                const F4 tb = tblk(Rr, Rr);
+                aw = O::mma16(tb, XW[Rr], aw);
+                au = O::mma16(tb, XU[Rr], au);
             }
-            const F4 tb = O::lds(&sm.Tb[Rr][m16][4 * q4]);
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            ZW[Rr] = O::cvt(O::mma16(tb, O::cvt(yw), z));
-            ZU[Rr] = O::cvt(O::mma16(tb, O::cvt(yu), z));
-            __builtin_amdgcn_sched_barrier(0);
+            ZW[Rr] = O::cvt(aw);
+            ZU[Rr] = O::cvt(au);
         }
         // U' straight to the slot (its accumulator layout); -W to LDS for the
         // transposed store below
@@ -197,34 +244,47 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
         __syncthreads();
 
         // ---- the operand matrices in the A-operand layout, 16 bytes per lane
+        // (every LDS read is issued before the first store, so that they are
+        // in flight together)
+        h8 cw[2], cq[2], ck[2], cp;
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             const int idx = tid + kThreads * k2;  // [t 4][s 4][lane 64]
             const int t = idx >> 8, s = (idx >> 6) & 3, l = idx & 63;
             const int row = 16 * t + (l & 15), col = 32 * s + 4 * (l >> 4);
-            *reinterpret_cast<h8*>(slot + kNegW + idx * 16) =
-                cat(*reinterpret_cast<const h4*>(&sm.key.h.Wst[row][col]), *reinterpret_cast<const h4*>(&sm.key.h.Wst[row][col + 16]));
-            *reinterpret_cast<h8*>(slot + kQt + idx * 16) =
-                cat(*reinterpret_cast<const h4*>(&sm.key.h.Qt[row][col]), *reinterpret_cast<const h4*>(&sm.key.h.Qt[row][col + 16]));
+            cw[k2] = cat(*reinterpret_cast<const h4*>(&sm.key.h.Wst[row][col]),
+                         *reinterpret_cast<const h4*>(&sm.key.h.Wst[row][col + 16]));
+            cq[k2] = cat(*reinterpret_cast<const h4*>(&sm.key.h.Qt[row][col]),
+                         *reinterpret_cast<const h4*>(&sm.key.h.Qt[row][col + 16]));
         }
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             const int idx = tid + kThreads * k2;  // [t 8][s 2][lane 64]
             const int t = idx >> 7, s = (idx >> 6) & 1, l = idx & 63;
             const int row = 16 * t + (l & 15), col = 32 * s + 4 * (l >> 4);
-            *reinterpret_cast<h8*>(slot + kKbT + idx * 16) =
-                cat(*reinterpret_cast<const h4*>(&sm.KbT[row][col]), *reinterpret_cast<const h4*>(&sm.KbT[row][col + 16]));
+            ck[k2] = cat(*reinterpret_cast<const h4*>(&sm.KbT[row][col]),
+                         *reinterpret_cast<const h4*>(&sm.KbT[row][col + 16]));
         }
         {
             const int idx = tid;  // [t 4][s 2][lane 64]
             const int t = idx >> 7, s = (idx >> 6) & 1, l = idx & 63;
-            const int m = l & 15, cq = 4 * (l >> 4);
+            const int m = l & 15, cq4 = 4 * (l >> 4);
             const h4 zero = {(OT)0.f, (OT)0.f, (OT)0.f, (OT)0.f};
-            const h4 lo = (2 * s <= t) ? *reinterpret_cast<const h4*>(&sm.Pb[tri_id(t, 2 * s)][m][cq]) : zero;
-            const h4 hi = (2 * s + 1 <= t) ? *reinterpret_cast<const h4*>(&sm.Pb[tri_id(t, 2 * s + 1)][m][cq]) : zero;
-            *reinterpret_cast<h8*>(slot + kPm + idx * 16) = cat(lo, hi);
+            const h4 lo = (2 * s <= t) ? *reinterpret_cast<const h4*>(&sm.Pb[tri_id(t, 2 * s)][m][cq4]) : zero;
+            const h4 hi = (2 * s + 1 <= t) ? *reinterpret_cast<const h4*>(&sm.Pb[tri_id(t, 2 * s + 1)][m][cq4]) : zero;
+            cp = cat(lo, hi);
         }
-        if (tid < D / 4) *reinterpret_cast<f32x4*>(slot + kDc + tid * 16) = ld4f(&sm.bC[4 * tid]);
+        f32x4 cdc = {0.f, 0.f, 0.f, 0.f};
+        if (tid < D / 4) cdc = ld4f(&sm.bC[4 * tid]);
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const int idx = tid + kThreads * k2;
+            *reinterpret_cast<h8*>(slot + kNegW + idx * 16) = cw[k2];
+            *reinterpret_cast<h8*>(slot + kQt + idx * 16) = cq[k2];
+            *reinterpret_cast<h8*>(slot + kKbT + idx * 16) = ck[k2];
+        }
+        *reinterpret_cast<h8*>(slot + kPm + tid * 16) = cp;
+        if (tid < D / 4) *reinterpret_cast<f32x4*>(slot + kDc + tid * 16) = cdc;
         // the next P0 writes only Gp and beta, which nothing above reads; its
         // barrier orders these LDS reads before P1 reuses the region
     }
