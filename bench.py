@@ -182,6 +182,21 @@ def bench_decode_multi(torch, K, steps, warmup):
     return ms, nbytes
 
 
+def bench_decode_bf16_state(torch, K, steps, warmup):
+    """The decode step with the state stored in bfloat16 (512 MiB read and
+    written; float32 arithmetic), on the decode workload's inputs."""
+    from gated_delta_rule_02_amd import synth
+    d = synth.workload_decode()
+    B, H = 256, 64
+    q, k, v, g = (dev(d[x], torch).view(B, 1, H, 128) for x in ("q", "k", "v", "g"))
+    b = dev(d["beta"], torch).view(B, 1, H)
+    st = torch.from_numpy(d["state"]).cuda().to(torch.bfloat16)
+    o = torch.empty((B, 1, H, 128), dtype=torch.float32, device="cuda")
+    ms, _ = timed(torch, lambda: K.kda_decode_multi(q, k, v, g, b, st, o), steps, warmup)
+    nbytes = 2 * B * H * 128 * 128 * 2 + 4 * B * H * 128 * 2 + B * H * 2 + B * H * 128 * 4
+    return ms, nbytes
+
+
 def bench_layer(torch, steps, warmup):
     from gated_delta_rule_02_amd import layer, synth
     d = synth.workload_layer()
@@ -302,6 +317,13 @@ def main():
                          "inplace_stream_reference": "torch mul_ in place on the 1 GiB state buffer (read + write)"}
         out["conv_update"] = {"workload": "x [256,8192] bf16, state [256,3,8192] bf16 in place",
                               "ms_per_step": ms_conv, "GB/s": CONV_BYTES / (ms_conv * 1e-3) / 1e9}
+        log("decode B=256 H=64, bf16 state")
+        ms_b, nb = bench_decode_bf16_state(torch, K, args.steps, args.warmup)
+        out["decode_bf16_state"] = {"workload": "decode step B=256 H=64, bf16 inputs, state stored in bf16 "
+                                                "[256,64,128,128] (512 MiB) in place, fp32 arithmetic, fp32 o",
+                                    "ms_per_step": ms_b, "bytes_per_step": nb, "GB/s": nb / (ms_b * 1e-3) / 1e9,
+                                    "frac_of_hbm_peak": nb / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                    "speedup_vs_fp32_state": ms / ms_b}
         log("decode multi-token B=256 x 4 tokens")
         ms_m, nbytes = bench_decode_multi(torch, K, args.steps, args.warmup)
         log("decode multi %.3f ms/step" % ms_m)

@@ -112,10 +112,12 @@ size_t kda_conv_state_bytes(int streams, int W, int C, kda_dtype dtype)
 // ---------------------------------------------------------------- decode
 static int decode_impl(const char* fn, const void* q, const void* k, const void* v, const void* g, const void* beta,
                        kda_dtype in_dtype, int B, int Tq, int H, int dk, int dv, float scale, float lower_bound,
-                       float* state, float* token_states, void* o, kda_dtype out_dtype, void* hip_stream)
+                       void* state, void* token_states, kda_dtype state_dtype, void* o, kda_dtype out_dtype,
+                       void* hip_stream)
 {
     REQUIRE(q && k && v && g && beta && state && o, KDA_ERR_INVALID_ARG, "%s: null tensor pointer", fn);
-    REQUIRE(valid_dtype(in_dtype) && valid_dtype(out_dtype), KDA_ERR_INVALID_ARG, "%s: bad dtype", fn);
+    REQUIRE(valid_dtype(in_dtype) && valid_dtype(out_dtype) && valid_dtype(state_dtype), KDA_ERR_INVALID_ARG,
+            "%s: bad dtype", fn);
     REQUIRE(B >= 1 && H >= 1 && Tq >= 1, KDA_ERR_INVALID_ARG, "%s: B, H and the token count must be >= 1", fn);
     REQUIRE(dk == 128 && dv == 128, KDA_ERR_UNSUPPORTED, "%s: only dk = dv = 128 is supported (got %d, %d)", fn, dk,
             dv);
@@ -123,9 +125,9 @@ static int decode_impl(const char* fn, const void* q, const void* k, const void*
             "%s: B*H too large", fn);
     for (const void* p : {q, k, v, g, beta, (const void*)state, (const void*)token_states, (const void*)o})
         REQUIRE(!p || aligned16(p), KDA_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
-    const size_t rows = (size_t)B * H, trows = rows * Tq;
-    const Range rs = rng(state, rows * 128 * 128 * 4), ro = rng(o, trows * 128 * esize(out_dtype));
-    const Range rt = rng(token_states, token_states ? trows * 128 * 128 * 4 : 0);
+    const size_t rows = (size_t)B * H, trows = rows * Tq, ss = 128 * 128 * esize(state_dtype);
+    const Range rs = rng(state, rows * ss), ro = rng(o, trows * 128 * esize(out_dtype));
+    const Range rt = rng(token_states, token_states ? trows * ss : 0);
     for (Range r : {rng(q, trows * 128 * esize(in_dtype)), rng(k, trows * 128 * esize(in_dtype)),
                     rng(v, trows * 128 * esize(in_dtype)), rng(g, trows * 128 * esize(in_dtype)),
                     rng(beta, trows * esize(in_dtype))}) {
@@ -137,7 +139,7 @@ static int decode_impl(const char* fn, const void* q, const void* k, const void*
     REQUIRE(!overlap(rt, rs) && !overlap(rt, ro), KDA_ERR_INVALID_ARG, "%s: token_states overlaps state or o", fn);
 
     DecodeArgs a{q, k, v, g, beta, state, token_states, o, B, H, Tq, scale, lower_bound, (DType)in_dtype,
-                 (DType)out_dtype};
+                 (DType)out_dtype, (DType)state_dtype};
     return hip_status(launch_decode(a, static_cast<hipStream_t>(hip_stream)), fn);
 }
 
@@ -147,22 +149,23 @@ int kda_decode_step(const void* q, const void* k, const void* v, const void* g, 
                     void* hip_stream)
 {
     return decode_impl("kda_decode_step", q, k, v, g, beta, in_dtype, B, 1, H, dk, dv, scale, lower_bound, state,
-                       nullptr, o, out_dtype, hip_stream);
+                       nullptr, KDA_F32, o, out_dtype, hip_stream);
 }
 
 int kda_decode_multi(const void* q, const void* k, const void* v, const void* g, const void* beta,
                      kda_dtype in_dtype, int B, int num_tokens, int H, int dk, int dv, float scale,
-                     float lower_bound, float* state, float* token_states, void* o, kda_dtype out_dtype,
-                     void* hip_stream)
+                     float lower_bound, void* state, void* token_states, kda_dtype state_dtype, void* o,
+                     kda_dtype out_dtype, void* hip_stream)
 {
     return decode_impl("kda_decode_multi", q, k, v, g, beta, in_dtype, B, num_tokens, H, dk, dv, scale, lower_bound,
-                       state, token_states, o, out_dtype, hip_stream);
+                       state, token_states, state_dtype, o, out_dtype, hip_stream);
 }
 
-int kda_decode_commit(const float* token_states, const int32_t* accepted, int B, int num_tokens, int H, int dk,
-                      int dv, float* state, void* hip_stream)
+int kda_decode_commit(const void* token_states, const int32_t* accepted, int B, int num_tokens, int H, int dk,
+                      int dv, void* state, kda_dtype state_dtype, void* hip_stream)
 {
     REQUIRE(token_states && accepted && state, KDA_ERR_INVALID_ARG, "kda_decode_commit: null pointer");
+    REQUIRE(valid_dtype(state_dtype), KDA_ERR_INVALID_ARG, "kda_decode_commit: bad dtype");
     REQUIRE(B >= 1 && H >= 1 && num_tokens >= 1, KDA_ERR_INVALID_ARG,
             "kda_decode_commit: B, H and the token count must be >= 1");
     REQUIRE(dk == 128 && dv == 128, KDA_ERR_UNSUPPORTED,
@@ -170,14 +173,28 @@ int kda_decode_commit(const float* token_states, const int32_t* accepted, int B,
     REQUIRE((int64_t)B * H <= 0x7fffffff, KDA_ERR_INVALID_ARG, "kda_decode_commit: B*H too large");
     REQUIRE(aligned16(token_states) && aligned16(state), KDA_ERR_INVALID_ARG,
             "kda_decode_commit: token_states and state must be 16-byte aligned");
-    const size_t rows = (size_t)B * H;
-    const Range rs = rng(state, rows * 128 * 128 * 4);
-    REQUIRE(!overlap(rs, rng(token_states, rows * num_tokens * 128 * 128 * 4)) &&
-                !overlap(rs, rng(accepted, (size_t)B * 4)),
+    const size_t rows = (size_t)B * H, ss = 128 * 128 * esize(state_dtype);
+    const Range rs = rng(state, rows * ss);
+    REQUIRE(!overlap(rs, rng(token_states, rows * num_tokens * ss)) && !overlap(rs, rng(accepted, (size_t)B * 4)),
             KDA_ERR_INVALID_ARG, "kda_decode_commit: state overlaps token_states or accepted");
-    return hip_status(launch_decode_commit(token_states, accepted, state, B, num_tokens, H,
+    return hip_status(launch_decode_commit(token_states, accepted, state, B, num_tokens, H, (DType)state_dtype,
                                            static_cast<hipStream_t>(hip_stream)),
                       "kda_decode_commit");
+}
+
+int kda_state_convert(const void* src, kda_dtype src_dtype, void* dst, kda_dtype dst_dtype, int64_t count,
+                      void* hip_stream)
+{
+    REQUIRE(count >= 0, KDA_ERR_INVALID_ARG, "kda_state_convert: negative count");
+    REQUIRE(count == 0 || (src && dst), KDA_ERR_INVALID_ARG, "kda_state_convert: null pointer");
+    REQUIRE(valid_dtype(src_dtype) && valid_dtype(dst_dtype), KDA_ERR_INVALID_ARG, "kda_state_convert: bad dtype");
+    REQUIRE((!src || aligned16(src)) && (!dst || aligned16(dst)), KDA_ERR_INVALID_ARG,
+            "kda_state_convert: pointers must be 16-byte aligned");
+    REQUIRE(!overlap(rng(src, (size_t)count * esize(src_dtype)), rng(dst, (size_t)count * esize(dst_dtype))),
+            KDA_ERR_INVALID_ARG, "kda_state_convert: src and dst overlap");
+    return hip_status(launch_convert(src, (DType)src_dtype, dst, (DType)dst_dtype, count,
+                                     static_cast<hipStream_t>(hip_stream)),
+                      "kda_state_convert");
 }
 
 // ---------------------------------------------------------------- conv

@@ -10,20 +10,23 @@ namespace kda {
 
 enum DType : int { F32 = 0, BF16 = 1 };
 
-// Tq tokens per sequence (1 for a plain decode step); inputs [B, Tq, H, d]
+// Tq tokens per sequence (1 for a plain decode step); inputs [B, Tq, H, d];
+// states in state_dtype (float32 or bfloat16 storage, float32 arithmetic)
 struct DecodeArgs {
     const void *q, *k, *v, *g, *beta;
-    float* state;         // [B, H, 128, 128]: written in place unless token_states is set
-    float* token_states;  // [B, Tq, H, 128, 128] (state after each token) or null
+    void* state;         // [B, H, 128, 128]: written in place unless token_states is set
+    void* token_states;  // [B, Tq, H, 128, 128] (state after each token) or null
     void* o;
     int B, H, Tq;
     float scale, lower_bound;
-    DType in_dtype, out_dtype;
+    DType in_dtype, out_dtype, state_dtype;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 // state[b] <- token_states[b][accepted[b] - 1] for 1 <= accepted[b] <= Tq
-hipError_t launch_decode_commit(const float* token_states, const int32_t* accepted, float* state, int B, int Tq,
-                                int H, hipStream_t s);
+hipError_t launch_decode_commit(const void* token_states, const int32_t* accepted, void* state, int B, int Tq, int H,
+                                DType state_dtype, hipStream_t s);
+// dst[i] = src[i] converted (float32 <-> bfloat16, round to nearest even)
+hipError_t launch_convert(const void* src, DType src_dtype, void* dst, DType dst_dtype, int64_t n, hipStream_t s);
 
 struct ConvUpdateArgs {
     const void* x;

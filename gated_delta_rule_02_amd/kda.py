@@ -31,8 +31,9 @@ _SIGS = {
     "kda_prefill_snapshots": (_I, [_P] * 5 + [_I, _I64, _I, _I, _I, _P, _P, _I, _F, _F, _P, _P, _P, _I, _P, _SZ,
                                               _I64, _I64, _P, _P]),
     "kda_decode_step": (_I, [_P] * 5 + [_I, _I, _I, _I, _I, _F, _F, _P, _P, _I, _P]),
-    "kda_decode_multi": (_I, [_P] * 5 + [_I, _I, _I, _I, _I, _I, _F, _F, _P, _P, _P, _I, _P]),
-    "kda_decode_commit": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P]),
+    "kda_decode_multi": (_I, [_P] * 5 + [_I, _I, _I, _I, _I, _I, _F, _F, _P, _P, _I, _P, _I, _P]),
+    "kda_decode_commit": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _I, _P]),
+    "kda_state_convert": (_I, [_P, _I, _P, _I, _I64, _P]),
     "kda_conv_state_update": (_I, [_P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P]),
     "kda_conv_prefill": (_I, [_P, _I64, _I64, _I, _I, _P, _P, _I, _P, _P, _P, _P, _I, _I, _F, _P, _I64, _I, _P]),
     "kda_gate_prologue": (_I, [_P, _I64, _P, _I64, _P, _I64, _I, _I, _F, _I, _P, _P, _I, _P]),
@@ -190,29 +191,45 @@ def kda_decode_step(q, k, v, g, beta, state, o, scale=1.0, lower_bound=-5.0, str
 
 def kda_decode_multi(q, k, v, g, beta, state, o, token_states=None, scale=1.0, lower_bound=-5.0, stream=None):
     """Several tokens per sequence. q,k,g,v [B,Tq,H,128], beta [B,Tq,H]; state
-    float32 [B,H,128,128]; o [B,Tq,H,128]. token_states None: state becomes the
-    state after the last token; else token_states [B,Tq,H,128,128] receives the
+    [B,H,128,128] in float32 or bfloat16 (its dtype is the state dtype); o
+    [B,Tq,H,128]. token_states None: state becomes the state after the last
+    token; else token_states [B,Tq,H,128,128] (the state's dtype) receives the
     state after every token and state is only read."""
     for n_, t_ in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("state", state), ("o", o),
                    ("token_states", token_states)):
         _dense(t_, n_)
+    if token_states is not None and token_states.dtype != state.dtype:
+        raise TypeError("token_states must have the state's dtype")
     B, Tq, H, dk = q.shape
     dv = v.shape[3]
     _call("kda_decode_multi", _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dt(q), B, Tq, H, dk, dv,
-          scale, lower_bound, _ptr(state), _ptr(token_states), _ptr(o), _dt(o), _stream(stream))
+          scale, lower_bound, _ptr(state), _ptr(token_states), _dt(state), _ptr(o), _dt(o), _stream(stream))
     return o
 
 
 def kda_decode_commit(token_states, accepted, state, stream=None):
     """state[b] <- token_states[b, accepted[b] - 1] where 1 <= accepted[b] <= Tq
-    (accepted: int32 [B] on the device)."""
+    (accepted: int32 [B] on the device; states float32 or bfloat16)."""
     for n_, t_ in (("token_states", token_states), ("accepted", accepted), ("state", state)):
         _dense(t_, n_)
     if accepted.dtype != torch.int32:
         raise TypeError("accepted must be int32")
+    if token_states.dtype != state.dtype:
+        raise TypeError("token_states and state must have one dtype")
     B, Tq, H, dk, dv = token_states.shape
-    _call("kda_decode_commit", _ptr(token_states), _ptr(accepted), B, Tq, H, dk, dv, _ptr(state), _stream(stream))
+    _call("kda_decode_commit", _ptr(token_states), _ptr(accepted), B, Tq, H, dk, dv, _ptr(state), _dt(state),
+          _stream(stream))
     return state
+
+
+def kda_state_convert(src, dst, stream=None):
+    """dst <- src converted between float32 and bfloat16 (same number of elements)."""
+    _dense(src, "src")
+    _dense(dst, "dst")
+    if src.numel() != dst.numel():
+        raise ValueError("src and dst must have the same number of elements")
+    _call("kda_state_convert", _ptr(src), _dt(src), _ptr(dst), _dt(dst), src.numel(), _stream(stream))
+    return dst
 
 
 def kda_conv_state_update(x, conv_state, weight, y, bias=None, apply_silu=True, l2norm_group=0,

@@ -148,7 +148,8 @@ int kda_prefill_snapshots(const void* q, const void* k, const void* v, const voi
  * and writes every sequence's [H, dk, dv] float32 state exactly once.
  *
  * q, k, g [B, H, dk], v [B, H, dv], beta [B, H]: in_dtype.
- * state   float32 [B, H, dk, dv], read and overwritten with the new state.
+ * state   float32 [B, H, dk, dv], read and overwritten with the new state
+ *         (kda_decode_multi with num_tokens = 1 takes a bfloat16 state too).
  * o       [B, H, dv] out_dtype.
  * Supported: dk = dv = 128, B >= 1, H >= 1.
  * ---------------------------------------------------------------------- */
@@ -159,29 +160,34 @@ int kda_decode_step(const void* q, const void* k, const void* v, const void* g, 
 
 /* ------------------------------------------------------------------------
  * kda_decode_multi -- num_tokens new tokens for each of B sequences in one
- * pass over the state (the draft tokens of speculative decoding, to verify).
+ * pass over the state (the draft tokens of speculative decoding, to verify),
+ * with the state stored in float32 or bfloat16.
  *
  * The recurrence applied token by token, as in kda_decode_step. A multi-token
  * prediction layer serves as the draft head, and about 2.1 to 2.6 tokens are
  * accepted per step ("Ling-3.1-flash: What 63 Linear-Attention Layers Do to
  * the KV Budget", section "Fitting it on a node"); rejected tokens must not
- * leave their writes in the state, hence the per-token states.
+ * leave their writes in the state, hence the per-token states. The same page
+ * (section "The memory math") puts the state at 252 MiB per sequence in FP32
+ * and 126 MiB in BF16; with state_dtype BF16 the state is read into float32,
+ * updated in float32 and rounded to bfloat16 (nearest even) when stored, which
+ * halves the bytes of a decode step. num_tokens = 1 is a plain decode step.
  *
  * q, k, g [B, num_tokens, H, dk], v [B, num_tokens, H, dv],
  * beta [B, num_tokens, H]: in_dtype.
- * state   float32 [B, H, dk, dv], the state before the first token. With
- *         token_states NULL it is overwritten with the state after the last
- *         token; otherwise it is only read.
- * token_states  float32 [B, num_tokens, H, dk, dv] or NULL: entry [b][t] =
- *         the state after token t of sequence b. Must not overlap another
- *         tensor.
+ * state   [B, H, dk, dv] in state_dtype, the state before the first token.
+ *         With token_states NULL it is overwritten with the state after the
+ *         last token; otherwise it is only read.
+ * token_states  [B, num_tokens, H, dk, dv] in state_dtype or NULL: entry
+ *         [b][t] = the state after token t of sequence b. Must not overlap
+ *         another tensor.
  * o       [B, num_tokens, H, dv] out_dtype.
  * Supported: dk = dv = 128, B, H, num_tokens >= 1.
  * ---------------------------------------------------------------------- */
 int kda_decode_multi(const void* q, const void* k, const void* v, const void* g, const void* beta,
                      kda_dtype in_dtype, int B, int num_tokens, int H, int dk, int dv, float scale,
-                     float lower_bound, float* state, float* token_states, void* o, kda_dtype out_dtype,
-                     void* hip_stream);
+                     float lower_bound, void* state, void* token_states, kda_dtype state_dtype, void* o,
+                     kda_dtype out_dtype, void* hip_stream);
 
 /* ------------------------------------------------------------------------
  * kda_decode_commit -- keep the state of the accepted draft prefix.
@@ -190,15 +196,28 @@ int kda_decode_multi(const void* q, const void* k, const void* v, const void* g,
  * tokens (same page and section as kda_decode_multi): its state becomes the
  * state after its last accepted token.
  *
- * token_states  float32 [B, num_tokens, H, dk, dv], from kda_decode_multi.
+ * token_states  [B, num_tokens, H, dk, dv] in state_dtype, from
+ *               kda_decode_multi.
  * accepted      int32 [B], device. 1 <= accepted[b] <= num_tokens:
- *               state[b] = token_states[b][accepted[b] - 1]; any other value
- *               leaves state[b] as it is.
- * state         float32 [B, H, dk, dv], must not overlap token_states.
+ *               state[b] = token_states[b][accepted[b] - 1] (a copy); any
+ *               other value leaves state[b] as it is.
+ * state         [B, H, dk, dv] in state_dtype, must not overlap token_states.
  * Supported: dk = dv = 128.
  * ---------------------------------------------------------------------- */
-int kda_decode_commit(const float* token_states, const int32_t* accepted, int B, int num_tokens, int H, int dk,
-                      int dv, float* state, void* hip_stream);
+int kda_decode_commit(const void* token_states, const int32_t* accepted, int B, int num_tokens, int H, int dk,
+                      int dv, void* state, kda_dtype state_dtype, void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * kda_state_convert -- states between float32 and bfloat16 storage.
+ *
+ * The state may be held in BF16 between decode steps ("Ling-3.1-flash: What
+ * 63 Linear-Attention Layers Do to the KV Budget", section "The memory math");
+ * prefill produces float32 states, converted once with this call.
+ * dst[i] = src[i] for i < count, rounded to nearest even when narrowing
+ * (same dtypes: a copy). src and dst must not overlap.
+ * ---------------------------------------------------------------------- */
+int kda_state_convert(const void* src, kda_dtype src_dtype, void* dst, kda_dtype dst_dtype, int64_t count,
+                      void* hip_stream);
 
 /* ------------------------------------------------------------------------
  * kda_conv_state_update -- decode-time causal short convolution.

@@ -185,9 +185,9 @@ def test_prefill_snapshots_validation():
 
 
 def test_decode_multi_and_commit_validation():
-    # q k v g beta dtype B Tq H dk dv scale lb state token_states o out_dtype stream
+    # q k v g beta dtype B Tq H dk dv scale lb state token_states state_dtype o out_dtype stream
     args = [fake(1), fake(2), fake(3), fake(4), fake(5), K.KDA_BF16, 64, 4, 16, 128, 128, 1.0, -5.0,
-            fake(6, 1 << 34), fake(7, 1 << 34), fake(9), K.KDA_F32, None]
+            fake(6, 1 << 34), fake(7, 1 << 34), K.KDA_F32, fake(9), K.KDA_F32, None]
     a = list(args); a[7] = 0
     assert call("kda_decode_multi", *a)[0] == K.KDA_ERR_INVALID_ARG
     a = list(args); a[9] = 64
@@ -195,17 +195,37 @@ def test_decode_multi_and_commit_validation():
     a = list(args); a[14] = fake(6, 1 << 34) + 4096         # token_states inside the state
     rc, msg = call("kda_decode_multi", *a)
     assert rc == K.KDA_ERR_INVALID_ARG and "token_states overlaps" in msg
-    a = list(args); a[15] = fake(7, 1 << 34) + 1024         # o inside token_states
+    a = list(args); a[16] = fake(7, 1 << 34) + 1024         # o inside token_states
     assert call("kda_decode_multi", *a)[0] == K.KDA_ERR_INVALID_ARG
     a = list(args); a[14] = fake(7, 1 << 34) + 4            # misaligned
     assert call("kda_decode_multi", *a)[0] == K.KDA_ERR_INVALID_ARG
-    # commit: state overlapping token_states, bad sizes, unsupported dk
+    a = list(args); a[15] = 5                               # bad state dtype
+    assert call("kda_decode_multi", *a)[0] == K.KDA_ERR_INVALID_ARG
+    # a bf16 state is half the bytes: o right after a bf16 state of 64*16*32 KiB does not overlap it
+    a = list(args); a[15] = K.KDA_BF16; a[16] = fake(6, 1 << 34) + 64 * 16 * 32768
+    a[14] = None
+    fn = getattr(K.lib(), "kda_decode_multi")
+    a2 = list(a); a2[16] = fake(6, 1 << 34) + 64 * 16 * 32768 - 16   # but 16 bytes earlier it does
+    assert call("kda_decode_multi", *a2)[0] == K.KDA_ERR_INVALID_ARG
+    # commit: state overlapping token_states, bad sizes, unsupported dk, bad dtype
     rc, msg = call("kda_decode_commit", fake(1, 1 << 34), fake(2), 64, 4, 16, 128, 128, fake(1, 1 << 34) + 65536,
-                   None)
+                   K.KDA_F32, None)
     assert rc == K.KDA_ERR_INVALID_ARG and "overlaps" in msg
     assert call("kda_decode_commit", fake(1, 1 << 34), fake(2), 64, 0, 16, 128, 128, fake(3, 1 << 34),
-                None)[0] == K.KDA_ERR_INVALID_ARG
+                K.KDA_F32, None)[0] == K.KDA_ERR_INVALID_ARG
     assert call("kda_decode_commit", fake(1, 1 << 34), fake(2), 64, 4, 16, 128, 64, fake(3, 1 << 34),
-                None)[0] == K.KDA_ERR_UNSUPPORTED
+                K.KDA_F32, None)[0] == K.KDA_ERR_UNSUPPORTED
     assert call("kda_decode_commit", None, fake(2), 64, 4, 16, 128, 128, fake(3, 1 << 34),
-                None)[0] == K.KDA_ERR_INVALID_ARG
+                K.KDA_F32, None)[0] == K.KDA_ERR_INVALID_ARG
+    assert call("kda_decode_commit", fake(1, 1 << 34), fake(2), 64, 4, 16, 128, 128, fake(3, 1 << 34),
+                9, None)[0] == K.KDA_ERR_INVALID_ARG
+
+
+def test_state_convert_validation():
+    assert call("kda_state_convert", fake(1), K.KDA_F32, fake(1) + 1024, K.KDA_BF16, 4096, None)[0] == \
+        K.KDA_ERR_INVALID_ARG                                  # overlap
+    assert call("kda_state_convert", fake(1), K.KDA_F32, fake(2) + 8, K.KDA_BF16, 4096, None)[0] == \
+        K.KDA_ERR_INVALID_ARG                                  # misaligned
+    assert call("kda_state_convert", fake(1), 3, fake(2), K.KDA_BF16, 4096, None)[0] == K.KDA_ERR_INVALID_ARG
+    assert call("kda_state_convert", fake(1), K.KDA_F32, fake(2), K.KDA_BF16, -1, None)[0] == K.KDA_ERR_INVALID_ARG
+    assert call("kda_state_convert", None, K.KDA_F32, None, K.KDA_BF16, 0, None)[0] == K.KDA_OK  # nothing to do

@@ -221,3 +221,117 @@ def test_decode_multi_workload_full_size_sampled():
         tsh = host64(ts[b, :, h])
         for t in range(Tq):
             assert relerr(tsh[t], rts[0, t, 0]) < TOL_BF16, (b, h, t)
+
+
+# ------------------------------------------------------------ bf16 state storage
+def bf16_round(x):
+    """float32 -> nearest-even bfloat16 values (as float32), numpy."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)
+
+
+def assert_bf16_of(gpu, ref, slack=1):
+    """gpu (bf16 values) is the bf16 rounding of ref up to `slack` ulps: the
+    float32 arithmetic before the rounding may land on the other side of a tie."""
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+    err = np.abs(gpu - ref)
+    bad = err > (0.5 + slack) * ulp + 1e-6 * np.max(np.abs(ref))
+    assert not bad.any(), (int(bad.sum()), float(err[bad].max()))
+
+
+@pytest.mark.parametrize("Tq", [1, 3])
+def test_decode_bf16_state(Tq):
+    """bfloat16 state storage: the state is read into float32, updated, and
+    each stored state is the bf16 rounding of the FP64 result (within one ulp);
+    o within 2e-3."""
+    announce("decode bf16 state Tq=%d" % Tq)
+    rng = np.random.default_rng(400 + Tq)
+    B, H = 6, 4
+    d = synth.core_inputs(rng, B * Tq, H, bf16=True)
+    s0 = bf16_round(synth.states(rng, B, H, std=0.5))
+    q, k, v, g, b = (dev(d[x]) for x in ("q", "k", "v", "g", "beta"))
+    q, k, v, g = (t.view(B, Tq, H, 128) for t in (q, k, v, g))
+    b = b.view(B, Tq, H)
+    st = torch.from_numpy(s0).cuda().to(torch.bfloat16)
+    ts = torch.empty((B, Tq, H, 128, 128), dtype=torch.bfloat16, device="cuda")
+    o = torch.empty((B, Tq, H, 128), dtype=torch.float32, device="cuda")
+    K.kda_decode_multi(q, k, v, g, b, st, o, token_states=ts)
+    torch.cuda.synchronize()
+    ro, rS, rts = oracle_multi(d, s0, B, Tq)
+    assert relerr(host64(o).reshape(B * Tq, H, 128), ro) < TOL_BF16
+    tsh = host64(ts)
+    for n in range(B):
+        for t in range(Tq):
+            assert_bf16_of(tsh[n, t], rts[n, t])
+    # in place: the last token's state, bit for bit the last per-token state
+    st2 = torch.from_numpy(s0).cuda().to(torch.bfloat16)
+    o2 = torch.empty_like(o)
+    K.kda_decode_multi(q, k, v, g, b, st2, o2)
+    torch.cuda.synchronize()
+    assert torch.equal(st2, ts[:, Tq - 1]) and torch.equal(o, o2)
+    # commit in bf16: exact copies
+    acc = torch.tensor([Tq, 1, 0, Tq, 2 if Tq > 1 else 1, 7], dtype=torch.int32, device="cuda")
+    st3 = torch.from_numpy(s0).cuda().to(torch.bfloat16)
+    K.kda_decode_commit(ts, acc, st3)
+    torch.cuda.synchronize()
+    for bb, a in enumerate(acc.tolist()):
+        want = ts[bb, a - 1] if 1 <= a <= Tq else torch.from_numpy(s0[bb]).cuda().to(torch.bfloat16)
+        assert torch.equal(st3[bb], want), bb
+
+
+def test_state_convert_round_trip():
+    """float32 -> bfloat16 is round-to-nearest-even (numpy reference, bit for
+    bit, ragged length); bfloat16 -> float32 is exact."""
+    announce("state convert")
+    rng = np.random.default_rng(410)
+    x = (rng.standard_normal(1000003) * 3).astype(np.float32)
+    xd = torch.from_numpy(x).cuda()
+    y = torch.empty(x.shape, dtype=torch.bfloat16, device="cuda")
+    K.kda_state_convert(xd, y)
+    z = torch.empty_like(xd)
+    K.kda_state_convert(y, z)
+    torch.cuda.synchronize()
+    assert np.array_equal(z.cpu().numpy(), bf16_round(x))
+
+
+def test_decode_bf16_state_error_study():
+    """64 decode steps, the state stored after every step in bf16 or in fp32,
+    against the FP64 oracle, for the workload's decay (g = -softplus(z)) and a
+    slow decay (g = -0.01: long memory, where rounding errors persist). The
+    numbers are printed; the bounds are the study's findings with a margin."""
+    announce("decode bf16 state error study")
+    rng = np.random.default_rng(420)
+    B, H, N = 8, 4, 64
+    results = {}
+    for regime in ("workload", "slow"):
+        d = synth.core_inputs(rng, B * N, H, bf16=True)
+        if regime == "slow":
+            d["g"] = synth._as(np.full((B * N, H, 128), -0.01, np.float32), True)
+        s0 = bf16_round(synth.states(rng, B, H, std=0.5))
+        cu = np.arange(B + 1) * N
+        # token order: the packed tensors are sequence-major; a decode step takes token t of every sequence
+        ro, rS = R.kda_serial(d["q"].vals, d["k"].vals, d["v"].vals, d["g"].vals, d["beta"].vals, cu_seqlens=cu,
+                              initial_state=s0.astype(np.float64))
+        tens = {x: dev(d[x]) for x in ("q", "k", "v", "g", "beta")}
+        for sd in (torch.float32, torch.bfloat16):
+            st = torch.from_numpy(s0).cuda().to(sd)
+            o = torch.empty((B, 1, H, 128), dtype=torch.float32, device="cuda")
+            errs = []
+            for t in range(N):
+                rows = [bb * N + t for bb in range(B)]
+                step = {x: tens[x][rows].contiguous() for x in tens}
+                K.kda_decode_multi(step["q"].view(B, 1, H, 128), step["k"].view(B, 1, H, 128),
+                                   step["v"].view(B, 1, H, 128), step["g"].view(B, 1, H, 128),
+                                   step["beta"].view(B, 1, H), st, o)
+                torch.cuda.synchronize()
+                errs.append(relerr(host64(o).reshape(B, H, 128), ro[rows]))
+            es = max(relerr(host64(st[n]), rS[n]) for n in range(B))
+            results[(regime, str(sd))] = (errs[0], errs[7], errs[-1], max(errs), es)
+            print("  %-8s state %-14s o err step 1 %.2e, step 8 %.2e, step 64 %.2e (max %.2e); state err after 64 %.2e"
+                  % ((regime, str(sd)) + results[(regime, str(sd))]), flush=True)
+    for regime in ("workload", "slow"):
+        assert results[(regime, "torch.float32")][3] < TOL_BF16
+        assert results[(regime, "torch.bfloat16")][3] < 2e-2
