@@ -65,23 +65,6 @@ typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef __bf16 b4 __attribute__((ext_vector_type(4)));
 typedef __bf16 b8 __attribute__((ext_vector_type(8)));
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-// ---------------------------------------------------------------- buffers
-// Raw buffer over [base, base + bytes): loads beyond return 0, stores beyond
-// are dropped (the descriptor's range check).
-// Every descriptor built here is wave-uniform; readfirstlane states that to
-// the compiler, which otherwise may build it in vector registers and wrap
-// each load in a loop over the distinct values.
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes)
-{
-    const uint32_t nr = bytes <= 0 ? 0u : (bytes >= 0xffffffffll ? 0xffffffffu : (uint32_t)bytes);
-    const uint64_t b = reinterpret_cast<uint64_t>(base);
-    const uint64_t bu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32) |
-                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(bu), (short)0,
-                                             __builtin_amdgcn_readfirstlane((int)nr), 0x00020000);
-}
 template <typename T> struct Io;
 template <> struct Io<bf16_t> {
     using pair_t = uint32_t;

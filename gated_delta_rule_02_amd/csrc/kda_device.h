@@ -81,6 +81,36 @@ template <> __device__ __forceinline__ void st4<bf16_t>(bf16_t* p, f32x4 v)
 }
 
 // ---- math --------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// ---------------------------------------------------------------- buffers
+// Raw buffer over [base, base + bytes): loads beyond return 0, stores beyond
+// are dropped (the descriptor's range check).
+// Every descriptor built here is wave-uniform; readfirstlane states that to
+// the compiler, which otherwise may build it in vector registers and wrap
+// each load in a loop over the distinct values.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes)
+{
+    const uint32_t nr = bytes <= 0 ? 0u : (bytes >= 0xffffffffll ? 0xffffffffu : (uint32_t)bytes);
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint64_t bu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(bu), (short)0,
+                                             __builtin_amdgcn_readfirstlane((int)nr), 0x00020000);
+}
+// Workgroup barrier for LDS hand-offs only: waits for this wavefront's LDS
+// accesses (lgkmcnt(0)), not for its outstanding global loads and stores as
+// __syncthreads() does; the memory clobber keeps the compiler from moving
+// memory accesses across it. Global data a wavefront loaded into LDS must be
+// waited for (vmcnt) by that wavefront before the barrier.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 __device__ __forceinline__ float siluf_(float x) { return x / (1.0f + __expf(-x)); }

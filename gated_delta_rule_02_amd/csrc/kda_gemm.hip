@@ -7,9 +7,22 @@
 // 16x16x32 bf16 MFMA consumes: each lane takes 8 consecutive K values of one
 // row of A and one row of B.
 //
-// Tiling: 256 threads, a 128 x 128 tile of C per workgroup, wavefronts in a
-// 2 x 2 arrangement each owning 64 x 64 (4 x 4 MFMA tiles), K steps of 32
-// staged through double-buffered LDS with 16-byte global loads.
+// Two kernels. The main one (K a multiple of 64): a 256 x 256 tile of C per
+// workgroup of 4 wavefronts, each owning 128 x 128 (8 x 8 MFMA tiles, 256
+// accumulator registers: one wavefront per SIMD), K steps of 32 in four LDS
+// stages filled by buffer-to-LDS copies that the wavefronts issue three steps
+// ahead, and operand fragments read one step ahead. Per K step a wavefront
+// reads 16 KiB of operands from LDS for 64 MFMAs, half the LDS rate the MFMAs
+// could use. The stage
+// layout is row major with the 16-byte K chunks of each row XOR-swizzled by
+// (row / 4) mod 4, so that the 16 rows an MFMA operand read touches fall in
+// distinct banks; the swizzle is applied by choosing each lane's global
+// source address (a buffer-to-LDS copy writes lane l to byte 16 l of its
+// 1 KiB destination). The products are formed transposed
+// (B tile x A tile^T): each lane then holds four consecutive columns of one
+// row of C, stored with one 16-byte (float32) or 8-byte (bfloat16) access.
+// The fallback (any K multiple of 8): 128 x 128 tiles, 2 x 2 wavefronts of
+// 64 x 64, K steps of 32 through double-buffered LDS.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -103,10 +116,163 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a)
         }
 }
 
+// ------------------------------------------------------------ main kernel
+constexpr int TM = 256, TN = 256, TK = 32;   // workgroup tile and K step
+constexpr int kStages = 4;                   // K steps in LDS: the copies run 3 steps ahead
+constexpr int kStageBytes = TM * TK * 2;      // one operand's stage: 256 rows x 64 B
+typedef __attribute__((address_space(3))) void lds_void;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// LDS byte offset of 16-byte chunk c (0..3) of row r of a stage: the chunks
+// are XOR-swizzled by (r / 4) mod 4, so the 16 rows of an operand read cover
+// all 64 banks
+__device__ __forceinline__ int swz(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+
+template <typename TC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm256_kernel(GemmArgs a)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kStages][2][kStageBytes];  // [stage][A, B]
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int m16 = lane & 15, q4 = lane >> 4;
+    const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+
+    // tiles: consecutive workgroup ids run down a column of M tiles, so the
+    // workgroups resident together share B tiles and a few A tiles
+    const int tiles_m = (int)((a.M + TM - 1) / TM);
+    const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
+    const int64_t m0 = (int64_t)tm * TM, n0 = (int64_t)tn * TN;
+
+    // operand rows past M or N read as zero through the descriptor ranges
+    const bf16_t* A = static_cast<const bf16_t*>(a.A) + m0 * a.lda;
+    const bf16_t* B = static_cast<const bf16_t*>(a.B) + n0 * a.ldb;
+    const int64_t rows_a = min<int64_t>(TM, a.M - m0), rows_b = min<int64_t>(TN, a.N - n0);
+    const rsrc_t ra = make_rsrc(A, ((rows_a - 1) * a.lda + a.K) * 2);
+    const rsrc_t rb = make_rsrc(B, ((rows_b - 1) * a.ldb + a.K) * 2);
+
+    // copy of K step kt into stage st: 16 instructions per operand, 4 per
+    // wavefront; instruction i covers rows 16i .. 16i+15, lane l row 16i + l/4
+    // and LDS chunk slot l%4, which holds K chunk slot ^ ((row/4) mod 4)
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)&smem[0][0][0];
+    const int lrow = lane >> 2, lslot = lane & 3;
+    auto copy_part = [&](int kt, int st, int j) {
+        const int i = wave * 4 + j;
+        const int row = 16 * i + lrow;
+        const int chunk = lslot ^ ((row >> 2) & 3);
+        const int koff = (kt * TK + chunk * 8) * 2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(uintptr_t)(lds0 + (st * 2 + 0) * kStageBytes + i * 1024),
+                                                 16, (int)(row * a.lda * 2) + koff, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(uintptr_t)(lds0 + (st * 2 + 1) * kStageBytes + i * 1024),
+                                                 16, (int)(row * a.ldb * 2) + koff, 0, 0, 0);
+    };
+    auto copy = [&](int kt, int st) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) copy_part(kt, st, j);
+    };
+
+    f32x4 acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Pipeline: step kt computes on stage kt % 4 with operand fragments read
+    // during step kt - 1. Between its MFMAs it issues the copy of step kt + 3
+    // (each copy instruction waits for the compute unit's address unit, 1 KiB
+    // at 64 B per clock shared by the four wavefronts, which the matrix unit's
+    // work hides; issued up front they delayed every step's MFMAs) and reloads
+    // each A fragment for step kt + 1 as soon as its last MFMA is issued (the
+    // B fragments, used by every row, after the last row). At its end it waits
+    // for the copy of step kt + 2, so that after the barrier stage kt + 2 is
+    // complete for the next step's early reads. The compiler does not track
+    // the copies: the waits are explicit. A copy is 8 instructions per
+    // wavefront and copies complete in order, so "copy c has landed" is
+    // vmcnt(8 x the copies issued after it).
+    const int nk = (int)(a.K / TK);
+    u32x4_t fa[8], fb[8];
+    auto read_a = [&](int kt, int i) {
+        fa[i] = *reinterpret_cast<const u32x4_t*>(&smem[kt % kStages][0][0] + swz(wm + 16 * i + m16, q4));
+    };
+    auto read_b = [&](int kt, int j) {
+        fb[j] = *reinterpret_cast<const u32x4_t*>(&smem[kt % kStages][1][0] + swz(wn + 16 * j + m16, q4));
+    };
+    for (int p = 0; p < kStages - 1 && p < nk; ++p) copy(p, p);
+    if (nk > 2) __builtin_amdgcn_s_waitcnt(0x0f78);  // vmcnt(8): steps 0 and 1 landed
+    else __builtin_amdgcn_s_waitcnt(0x0f70);         // vmcnt(0)
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        read_a(0, i);
+        read_b(0, i);
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+        const bool cp = kt + kStages - 1 < nk, nx = kt + 1 < nk;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb[j]),
+                                                                    __builtin_bit_cast(bf16x8, fa[i]), acc[i][j], 0, 0, 0);
+            if (i < 4 && cp) copy_part(kt + kStages - 1, (kt + kStages - 1) % kStages, i);
+            if (nx) read_a(kt + 1, i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (nx) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) read_b(kt + 1, j);
+        }
+        // the copy of step kt + 2 has landed (this wavefront's part) ...
+        if (cp) __builtin_amdgcn_s_waitcnt(0x0f78);  // vmcnt(8)
+        else __builtin_amdgcn_s_waitcnt(0x0f70);     // vmcnt(0)
+        lds_barrier();  // ... and everyone's; every read of stage kt % 4 is done
+    }
+
+    // acc[i][j] holds C^T of tile (i, j): lane (m16, q4) element e is
+    // C[row 16i + m16][column 16j + 4q4 + e]
+    TC* Cp = static_cast<TC*>(a.C);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t row = m0 + wm + 16 * i + m16;
+        if (row >= a.M) continue;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t col = n0 + wn + 16 * j + 4 * q4;
+            TC* p = Cp + row * a.ldc + col;
+            if (col + 3 < a.N) {
+                if constexpr (sizeof(TC) == 4) {
+                    *reinterpret_cast<f32x4*>(p) = acc[i][j];
+                } else {
+                    // float -> bfloat16 by the hardware conversion (round to nearest even)
+                    const f32x4 v = acc[i][j];
+                    typedef __bf16 b4_t __attribute__((ext_vector_type(4)));
+                    *reinterpret_cast<b4_t*>(p) = b4_t{(__bf16)v.x, (__bf16)v.y, (__bf16)v.z, (__bf16)v.w};
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (col + e < a.N) st(p + e, acc[i][j][e]);
+            }
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s)
 {
+    // the main kernel's copies address rows through 32-bit offsets
+    const bool main_path = a.K % 64 == 0 && (int64_t)TM * a.lda * 2 < ((int64_t)1 << 31) &&
+                           (int64_t)TN * a.ldb * 2 < ((int64_t)1 << 31);
+    if (main_path) {
+        const int64_t tiles = ((a.M + TM - 1) / TM) * ((a.N + TN - 1) / TN);
+        dim3 grid((unsigned)tiles), block(256);
+        if (a.c_dtype == F32)
+            hipLaunchKernelGGL(gemm256_kernel<float>, grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL(gemm256_kernel<bf16_t>, grid, block, 0, s, a);
+        return hipGetLastError();
+    }
     dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM)), block(kThreads);
     if (a.c_dtype == F32)
         hipLaunchKernelGGL(gemm_kernel<float>, grid, block, 0, s, a);
