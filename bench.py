@@ -207,6 +207,24 @@ def bench_layer(torch, steps, warmup):
     return ms, mixer.flops_per_token() * x.shape[0]
 
 
+def bench_gemm(torch, K, steps, warmup):
+    """The layer's input projection alone (M = 8192 tokens, K = 4096,
+    N = 5 x 8192 + 64, bf16 in and out) with the library's GEMM, and the same
+    product with torch.mm (the vendor BLAS) on a pre-transposed weight as a
+    reference."""
+    M, N, Kd = 8192, 5 * 8192 + 64, 4096
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    A = torch.randn(M, Kd, device="cuda", generator=g).to(torch.bfloat16)
+    B = (torch.randn(N, Kd, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    C = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    ms, _ = timed(torch, lambda: K.kda_gemm(A, B, C), max(3, steps // 2), 2)
+    Bt = B.t().contiguous()
+    C2 = torch.empty_like(C)
+    ms_ref, _ = timed(torch, lambda: torch.mm(A, Bt, out=C2), max(3, steps // 2), 2)
+    return ms, ms_ref, 2.0 * M * N * Kd
+
+
 def cpu_baseline(d, min_seconds=10.0):
     """The FP64 oracle (token-serial, threads over heads) on the prefill
     workload, timed on this host: the whole 4096-token sequence is run again
@@ -338,6 +356,13 @@ def main():
         out["layer"] = {"workload": "full token-mixer layer T=8192 hidden=4096 H=64: projections, conv, gate, "
                                     "KDA core, norm x gate, output projection",
                         "ms_per_step": ms, "tokens/s": 8192 / (ms * 1e-3), "TFLOP/s": flops / (ms * 1e-3) / 1e12}
+        log("input projection GEMM 8192 x 41024 x 4096")
+        ms_g, ms_r, fl = bench_gemm(torch, K, args.steps, args.warmup)
+        out["gemm"] = {"workload": "input projection 8192 x 41024 x 4096, bf16 in and out, fp32 accumulate",
+                       "ms_per_step": ms_g, "TFLOP/s": fl / (ms_g * 1e-3) / 1e12,
+                       "frac_of_bf16_peak": fl / (ms_g * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                       "vendor_blas_reference_TFLOP/s": fl / (ms_r * 1e-3) / 1e12,
+                       "vendor_blas_reference": "torch.mm on the same bf16 operands (weight pre-transposed)"}
     if args.only == "copy":
         log("copy 256 MiB")
         out["copy"] = bench_copy(torch, args.steps, args.warmup)
