@@ -197,6 +197,22 @@ def bench_decode_bf16_state(torch, K, steps, warmup):
     return ms, nbytes
 
 
+def bench_gemv_fp8(torch, K, steps, warmup):
+    """One decode token through the layer's input projection with block-FP8
+    weights (41,024 x 4,096 E4M3 codes + 128 x 128 block scales): HBM-bound
+    on the 168 MB of codes."""
+    N, Kd = 5 * 8192 + 64, 4096
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9)
+    codes = torch.randint(0, 126, (N, Kd), device="cuda", generator=g, dtype=torch.int32).to(torch.uint8)
+    scales = torch.rand(((N + 127) // 128, Kd // 128), device="cuda", generator=g) * 0.01
+    x = torch.randn(1, Kd, device="cuda", generator=g).to(torch.bfloat16)
+    y = torch.empty(1, N, dtype=torch.float32, device="cuda")
+    ms, _ = timed(torch, lambda: K.kda_gemv_fp8(x, codes, scales, y), steps, warmup)
+    nbytes = N * Kd + scales.numel() * 4 + Kd * 2 + N * 4
+    return ms, nbytes
+
+
 def bench_layer(torch, steps, warmup):
     from gated_delta_rule_02_amd import layer, synth
     d = synth.workload_layer()
@@ -342,6 +358,12 @@ def main():
                                     "ms_per_step": ms_b, "bytes_per_step": nb, "GB/s": nb / (ms_b * 1e-3) / 1e9,
                                     "frac_of_hbm_peak": nb / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                     "speedup_vs_fp32_state": ms / ms_b}
+        log("fp8 GEMV 41024 x 4096")
+        ms_f, nbf = bench_gemv_fp8(torch, K, args.steps, args.warmup)
+        out["gemv_fp8"] = {"workload": "one decode token through the input projection, block-FP8 weights "
+                                       "41,024 x 4,096 E4M3 + 128x128 fp32 scales, bf16 x, fp32 y",
+                           "ms_per_step": ms_f, "bytes_per_step": nbf, "GB/s": nbf / (ms_f * 1e-3) / 1e9,
+                           "frac_of_hbm_peak": nbf / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS}
         log("decode multi-token B=256 x 4 tokens")
         ms_m, nbytes = bench_decode_multi(torch, K, args.steps, args.warmup)
         log("decode multi %.3f ms/step" % ms_m)

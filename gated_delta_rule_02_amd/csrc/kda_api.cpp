@@ -312,6 +312,57 @@ int kda_output_norm_gate(const void* o, kda_dtype o_dtype, const void* gate, int
     return hip_status(launch_norm_gate(a, static_cast<hipStream_t>(hip_stream)), "kda_output_norm_gate");
 }
 
+// ---------------------------------------------------------------- block FP8
+int kda_gemv_fp8(const void* x, int64_t ldx, const uint8_t* w, int64_t ldw, const float* w_scale, int64_t ws_ld,
+                 void* y, int64_t ldy, int M, int64_t N, int64_t K, kda_dtype x_dtype, kda_dtype y_dtype,
+                 void* hip_stream)
+{
+    REQUIRE(x && w && w_scale && y, KDA_ERR_INVALID_ARG, "kda_gemv_fp8: null pointer");
+    REQUIRE(valid_dtype(x_dtype) && valid_dtype(y_dtype), KDA_ERR_INVALID_ARG, "kda_gemv_fp8: bad dtype");
+    REQUIRE(x_dtype == KDA_BF16, KDA_ERR_UNSUPPORTED, "kda_gemv_fp8: x must be bfloat16");
+    REQUIRE(M >= 1 && M <= 8, KDA_ERR_UNSUPPORTED, "kda_gemv_fp8: 1 <= M <= 8 rows (got %d)", M);
+    REQUIRE(N >= 1 && K >= 128, KDA_ERR_INVALID_ARG, "kda_gemv_fp8: bad sizes");
+    REQUIRE(K % 128 == 0, KDA_ERR_UNSUPPORTED, "kda_gemv_fp8: K must be a multiple of 128 (the scale block)");
+    REQUIRE(ldx >= K && ldx % 8 == 0 && ldw >= K && ldw % 16 == 0 && ws_ld >= K / 128 && ldy >= N,
+            KDA_ERR_INVALID_ARG,
+            "kda_gemv_fp8: ldx >= K (multiple of 8), ldw >= K (multiple of 16), ws_ld >= K/128, ldy >= N");
+    REQUIRE(aligned16(x) && aligned16(w) && aligned16(y) && ((uintptr_t)w_scale % 4 == 0), KDA_ERR_INVALID_ARG,
+            "kda_gemv_fp8: x, w and y must be 16-byte aligned");
+    const Range ry = rng(y, ((size_t)(M - 1) * ldy + N) * esize(y_dtype));
+    REQUIRE(!overlap(ry, rng(x, ((size_t)(M - 1) * ldx + K) * 2)) && !overlap(ry, rng(w, (size_t)(N - 1) * ldw + K)) &&
+                !overlap(ry, rng(w_scale, ((size_t)((N + 127) / 128 - 1) * ws_ld + K / 128) * 4)),
+            KDA_ERR_INVALID_ARG, "kda_gemv_fp8: y overlaps an input");
+    Fp8GemvArgs a{x, w, w_scale, y, ldx, ldw, ws_ld, ldy, N, K, M, (DType)y_dtype};
+    return hip_status(launch_gemv_fp8(a, static_cast<hipStream_t>(hip_stream)), "kda_gemv_fp8");
+}
+
+int kda_output_norm_gate_fp8(const void* o, kda_dtype o_dtype, const void* gate, int64_t gate_ld,
+                             kda_dtype gate_dtype, const float* norm_weight, int64_t num_tokens, int H, int dv,
+                             float eps, uint8_t* y_codes, float* y_scales, void* hip_stream)
+{
+    REQUIRE(o && gate && norm_weight && y_codes && y_scales, KDA_ERR_INVALID_ARG,
+            "kda_output_norm_gate_fp8: null pointer");
+    REQUIRE(valid_dtype(o_dtype) && valid_dtype(gate_dtype), KDA_ERR_INVALID_ARG,
+            "kda_output_norm_gate_fp8: bad dtype");
+    REQUIRE(num_tokens >= 0 && H >= 1, KDA_ERR_INVALID_ARG, "kda_output_norm_gate_fp8: bad sizes");
+    REQUIRE(dv == 128, KDA_ERR_UNSUPPORTED, "kda_output_norm_gate_fp8: only dv = 128 is supported");
+    REQUIRE(gate_ld >= (int64_t)H * dv && gate_ld % 8 == 0, KDA_ERR_INVALID_ARG,
+            "kda_output_norm_gate_fp8: gate_ld must be >= H*dv and a multiple of 8");
+    for (const void* p : {o, gate, (const void*)norm_weight, (const void*)y_codes, (const void*)y_scales})
+        REQUIRE(aligned16(p), KDA_ERR_INVALID_ARG, "kda_output_norm_gate_fp8: pointers must be 16-byte aligned");
+    const size_t rows = (size_t)num_tokens * H;
+    const Range rc = rng(y_codes, rows * dv), rsc = rng(y_scales, rows * 4);
+    const Range ro = rng(o, rows * dv * esize(o_dtype));
+    const Range rgt = rng(gate, num_tokens ? ((size_t)(num_tokens - 1) * gate_ld + (size_t)H * dv) * esize(gate_dtype) : 0);
+    for (Range r : {ro, rgt, rng(norm_weight, (size_t)dv * 4)})
+        REQUIRE(!overlap(rc, r) && !overlap(rsc, r), KDA_ERR_INVALID_ARG,
+                "kda_output_norm_gate_fp8: an output overlaps an input");
+    REQUIRE(!overlap(rc, rsc), KDA_ERR_INVALID_ARG, "kda_output_norm_gate_fp8: y_codes overlaps y_scales");
+    NormGateFp8Args a{o, gate, gate_ld, num_tokens, norm_weight, y_codes, y_scales, H, eps, (DType)o_dtype,
+                      (DType)gate_dtype};
+    return hip_status(launch_norm_gate_fp8(a, static_cast<hipStream_t>(hip_stream)), "kda_output_norm_gate_fp8");
+}
+
 // ---------------------------------------------------------------- prefill
 namespace {
 constexpr int64_t kChunk = 64;          // chunk of the bfloat16 forms

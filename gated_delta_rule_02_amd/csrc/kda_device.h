@@ -125,4 +125,12 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
+// Maximum over the 64 lanes of a wavefront (every lane gets it).
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+    return v;
+}
+
 }  // namespace kda

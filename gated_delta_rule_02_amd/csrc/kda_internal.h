@@ -98,6 +98,31 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_split(const PrefillArgs& a, void* ws, size_t ws_bytes, int64_t max_chunks, hipStream_t s);
 size_t prefill_split_slot_bytes();
 
+// y[M, N] = x[M, K] W^T, W block-FP8: W[n, k] = e4m3(w[n, k]) * w_scale[n/128, k/128]
+struct Fp8GemvArgs {
+    const void* x;        // bf16 [M, K], row stride ldx
+    const uint8_t* w;     // e4m3 codes [N, K], row stride ldw
+    const float* ws;      // [ceil(N/128), K/128], row stride ws_ld
+    void* y;              // [M, N], row stride ldy
+    int64_t ldx, ldw, ws_ld, ldy, N, K;
+    int M;
+    DType y_dtype;
+};
+hipError_t launch_gemv_fp8(const Fp8GemvArgs& a, hipStream_t s);
+
+// the epilogue with its output quantized to e4m3 per (token, head)
+struct NormGateFp8Args {
+    const void *o, *gate;
+    int64_t gate_ld, num_tokens;
+    const float* w;
+    uint8_t* codes;   // [T, H * 128]
+    float* scales;    // [T, H]
+    int H;
+    float eps;
+    DType o_dtype, gate_dtype;
+};
+hipError_t launch_norm_gate_fp8(const NormGateFp8Args& a, hipStream_t s);
+
 struct GemmArgs {
     const void *A, *B;
     void* C;

@@ -34,6 +34,8 @@ _SIGS = {
     "kda_decode_multi": (_I, [_P] * 5 + [_I, _I, _I, _I, _I, _I, _F, _F, _P, _P, _I, _P, _I, _P]),
     "kda_decode_commit": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _I, _P]),
     "kda_state_convert": (_I, [_P, _I, _P, _I, _I64, _P]),
+    "kda_gemv_fp8": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _I, _I64, _I64, _I, _I, _P]),
+    "kda_output_norm_gate_fp8": (_I, [_P, _I, _P, _I64, _I, _P, _I64, _I, _I, _F, _P, _P, _P]),
     "kda_conv_state_update": (_I, [_P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P]),
     "kda_conv_prefill": (_I, [_P, _I64, _I64, _I, _I, _P, _P, _I, _P, _P, _P, _P, _I, _I, _F, _P, _I64, _I, _P]),
     "kda_gate_prologue": (_I, [_P, _I64, _P, _I64, _P, _I64, _I, _I, _F, _I, _P, _P, _I, _P]),
@@ -299,6 +301,33 @@ def kda_gemm(A, B, C, stream=None):
     _call("kda_gemm", _ptr(A), A.stride(0), _ptr(B), B.stride(0), _ptr(C), C.stride(0), M, N, K,
           _dt(A), _dt(C), _stream(stream))
     return C
+
+
+def kda_gemv_fp8(x, w, w_scale, y, stream=None):
+    """y[M,N] = x[M,K] W^T, W = e4m3(w) (uint8 [N,K]) x w_scale[N/128, K/128]
+    blocks; x bf16, 1 <= M <= 8 (row strides allowed, last dims contiguous)."""
+    for n_, t_ in (("x", x), ("w", w), ("w_scale", w_scale), ("y", y)):
+        if t_.stride(-1) != 1:
+            raise ValueError("%s rows must be contiguous" % n_)
+    if w.dtype != torch.uint8 or w_scale.dtype != torch.float32:
+        raise TypeError("w must be uint8 E4M3 codes and w_scale float32")
+    M, Kd = x.shape
+    N = w.shape[0]
+    _call("kda_gemv_fp8", _ptr(x), x.stride(0), _ptr(w), w.stride(0), _ptr(w_scale), w_scale.stride(0),
+          _ptr(y), y.stride(0), M, N, Kd, _dt(x), _dt(y), _stream(stream))
+    return y
+
+
+def kda_output_norm_gate_fp8(o, gate, norm_weight, y_codes, y_scales, eps=1e-6, stream=None):
+    """o [T,H,128]; gate rows [T, >=H*128]; y_codes uint8 [T, H*128]; y_scales float32 [T, H]."""
+    for n_, t_ in (("o", o), ("norm_weight", norm_weight), ("y_codes", y_codes), ("y_scales", y_scales)):
+        _dense(t_, n_)
+    if gate.stride(1) != 1:
+        raise ValueError("gate rows must be contiguous")
+    T, H, dv = o.shape
+    _call("kda_output_norm_gate_fp8", _ptr(o), _dt(o), _ptr(gate), gate.stride(0), _dt(gate), _ptr(norm_weight),
+          T, H, dv, eps, _ptr(y_codes), _ptr(y_scales), _stream(stream))
+    return y_codes, y_scales
 
 
 def kda_state_bytes(H, dk=128, dv=128, dtype=KDA_F32):

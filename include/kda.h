@@ -220,6 +220,49 @@ int kda_state_convert(const void* src, kda_dtype src_dtype, void* dst, kda_dtype
                       void* hip_stream);
 
 /* ------------------------------------------------------------------------
+ * kda_gemv_fp8 -- y = x W^T for a few rows x, with W in block FP8.
+ *
+ * The release stores its dense weights as FP8 E4M3 in 128 x 128 blocks with
+ * one float32 scale per block ("Ling-3.1-flash: Grouped Routing and Two
+ * Different MLA Caches", section "Production boundaries"; "Ling-3.1-flash: a
+ * 560B hybrid-attention MoE, counted from its safetensors headers", section
+ * "What is in the files"), and a batch-1 decode step is mostly the reading of
+ * those weights (same page, "What the cut does not buy"). E4M3 is the OCP FP8
+ * format (bias 7, no infinities, 0x7F/0xFF NaN, largest 448).
+ *
+ * x        bfloat16 [M, K], row stride ldx (a multiple of 8), 1 <= M <= 8.
+ * w        E4M3 codes [N, K], row stride ldw (bytes, a multiple of 16).
+ * w_scale  float32 [ceil(N/128), K/128], row stride ws_ld:
+ *          W[n, k] = e4m3(w[n, k]) * w_scale[n/128, k/128].
+ * y        [M, N] y_dtype, row stride ldy; y[m, n] = sum_k x[m, k] W[n, k]
+ *          (float32 accumulation). K must be a multiple of 128.
+ * ---------------------------------------------------------------------- */
+int kda_gemv_fp8(const void* x, int64_t ldx, const uint8_t* w, int64_t ldw, const float* w_scale, int64_t ws_ld,
+                 void* y, int64_t ldy, int M, int64_t N, int64_t K, kda_dtype x_dtype, kda_dtype y_dtype,
+                 void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * kda_output_norm_gate_fp8 -- the epilogue with its output quantized to FP8.
+ *
+ * As kda_output_norm_gate (per-head RMSNorm x weight x sigmoid(gate)), with
+ * the output quantized dynamically for an FP8 output projection (the pages
+ * name block FP8 weights with dynamic activation quantization, section
+ * "Production boundaries" above, and a fused KDA output quantization among
+ * the Hopper decode settings: "Ling-3.1-flash: What 63 Linear-Attention Layers
+ * Do to the KV Budget", section "Fitting it on a node"). One group per
+ * (token, head) = 128 channels: scale = amax / 448 (1 for an all-zero group),
+ * code = E4M3 of y / scale, rounded to nearest even.
+ *
+ * o        [num_tokens, H, dv] o_dtype.  gate: [num_tokens, >= H*dv]
+ *          gate_dtype, row stride gate_ld (a multiple of 8).
+ * y_codes  uint8 [num_tokens, H*dv]; y_scales float32 [num_tokens, H].
+ * Supported: dv = 128.
+ * ---------------------------------------------------------------------- */
+int kda_output_norm_gate_fp8(const void* o, kda_dtype o_dtype, const void* gate, int64_t gate_ld,
+                             kda_dtype gate_dtype, const float* norm_weight, int64_t num_tokens, int H, int dv,
+                             float eps, uint8_t* y_codes, float* y_scales, void* hip_stream);
+
+/* ------------------------------------------------------------------------
  * kda_conv_state_update -- decode-time causal short convolution.
  *
  * One causal depthwise convolution of width W (4 in the model) per projection

@@ -362,3 +362,64 @@ def layer_forward(x, Wq, Wk, Wv, Wf, Wg, Wb, Wo, conv_q, conv_k, conv_v, A_log, 
     if return_parts:
         return out, dict(q=q, k=k, v=v, g=g, beta=beta, o=o, S=S, y=y, gate=g_pre)
     return out
+
+
+# --------------------------------------------------------------------------
+# Block FP8 -- [flozi-KDA] section "Production boundaries" (block FP8 E4M3
+# weights with 128 x 128 scaling blocks and dynamic activation quantization)
+# and [satyajit-Eq] section "What is in the files" (E4M3 weights, one fp32
+# scale per 128 x 128 block). E4M3 here is the OCP FP8 E4M3 ("FN") format:
+# 1 sign, 4 exponent (bias 7) and 3 mantissa bits, subnormals when the
+# exponent field is 0, no infinities, 0x7F / 0xFF are NaN, largest finite 448.
+# --------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes):
+    """uint8 codes -> float64 values (the format's definition, written out)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    val = sign * val
+    return np.where((c & 0x7F) == 0x7F, np.nan, val)
+
+
+def e4m3_encode(x):
+    """float64 -> uint8 codes, round to nearest, ties to even, saturating at
+    +-448 (values are scaled into range before encoding). Brute force over the
+    126 positive finite codes: the nearest one, and on a tie the even one."""
+    x = np.asarray(x, dtype=np.float64)
+    grid = e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))   # codes 0 .. 126, increasing
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    d = np.abs(a[..., None] - grid)                          # distance to every code
+    best = d.min(axis=-1, keepdims=True)
+    ties = d == best
+    # among the nearest codes, prefer the even code (mantissa LSB 0)
+    even = (np.arange(0, 0x7F) % 2 == 0)
+    pick = np.where(ties & even, 1, 0) + np.where(ties, 2, 0)
+    code = np.argmax(pick, axis=-1).astype(np.uint8)
+    return np.where((x < 0) & (code != 0), code | 0x80, code).astype(np.uint8)
+
+
+def gemv_fp8_blocks(x, codes, scales, block=128):
+    """y = x W^T with W[n, k] = decode(codes[n, k]) * scales[n // 128, k // 128],
+    in float64. x: [M, K]; codes: [N, K] uint8; scales: [ceil(N/128), K/128]."""
+    W = e4m3_decode(codes)
+    s = np.asarray(scales, dtype=np.float64)
+    W = W * np.repeat(np.repeat(s, block, axis=0), block, axis=1)[:W.shape[0], :W.shape[1]]
+    return np.asarray(x, dtype=np.float64) @ W.T
+
+
+def quantize_fp8_groups(y, group=128):
+    """Dynamic activation quantization of [T, C] values in groups of 128
+    consecutive channels: scale = amax / 448 (1 when the group is all zero),
+    codes = e4m3(y / scale). Returns (codes [T, C] uint8, scales [T, C/128])."""
+    y = np.asarray(y, dtype=np.float64)
+    T, C = y.shape
+    g = y.reshape(T, C // group, group)
+    amax = np.max(np.abs(g), axis=-1)
+    scale = np.where(amax > 0, amax / E4M3_MAX, 1.0)
+    codes = e4m3_encode(g / scale[..., None]).reshape(T, C)
+    return codes, scale

@@ -229,3 +229,29 @@ def test_state_convert_validation():
     assert call("kda_state_convert", fake(1), 3, fake(2), K.KDA_BF16, 4096, None)[0] == K.KDA_ERR_INVALID_ARG
     assert call("kda_state_convert", fake(1), K.KDA_F32, fake(2), K.KDA_BF16, -1, None)[0] == K.KDA_ERR_INVALID_ARG
     assert call("kda_state_convert", None, K.KDA_F32, None, K.KDA_BF16, 0, None)[0] == K.KDA_OK  # nothing to do
+
+
+def test_fp8_validation():
+    # x ldx w ldw ws ws_ld y ldy M N K x_dtype y_dtype stream
+    base = [fake(1), 4096, fake(2), 4096, fake(3), 32, fake(4), 8192, 1, 8192, 4096, K.KDA_BF16, K.KDA_F32, None]
+    a = list(base); a[8] = 9
+    assert call("kda_gemv_fp8", *a)[0] == K.KDA_ERR_UNSUPPORTED          # M > 8
+    a = list(base); a[10] = 4000; a[1] = 4000; a[3] = 4000
+    assert call("kda_gemv_fp8", *a)[0] == K.KDA_ERR_UNSUPPORTED          # K not a multiple of 128
+    a = list(base); a[3] = 4104
+    assert call("kda_gemv_fp8", *a)[0] == K.KDA_ERR_INVALID_ARG          # ldw not a multiple of 16
+    a = list(base); a[11] = K.KDA_F32
+    assert call("kda_gemv_fp8", *a)[0] == K.KDA_ERR_UNSUPPORTED          # x must be bf16
+    a = list(base); a[6] = fake(2) + 1024
+    rc, msg = call("kda_gemv_fp8", *a)
+    assert rc == K.KDA_ERR_INVALID_ARG and "overlaps" in msg
+    a = list(base); a[5] = 16
+    assert call("kda_gemv_fp8", *a)[0] == K.KDA_ERR_INVALID_ARG          # ws_ld < K/128
+    # epilogue: dv != 128, outputs overlapping
+    e = [fake(1), K.KDA_F32, fake(2), 8192, K.KDA_BF16, fake(3), 16, 64, 128, 1e-6, fake(4), fake(5), None]
+    a = list(e); a[8] = 64
+    assert call("kda_output_norm_gate_fp8", *a)[0] == K.KDA_ERR_UNSUPPORTED
+    a = list(e); a[11] = fake(4) + 64
+    assert call("kda_output_norm_gate_fp8", *a)[0] == K.KDA_ERR_INVALID_ARG
+    a = list(e); a[10] = fake(1) + 256
+    assert call("kda_output_norm_gate_fp8", *a)[0] == K.KDA_ERR_INVALID_ARG

@@ -1,0 +1,89 @@
+"""Block FP8 on the GPU against the oracle: the FP8-weight GEMV (decode) and
+the epilogue with its output quantized to E4M3 per (token, head)."""
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_02_amd import kda as K
+from gated_delta_rule_02_amd import synth
+from oracle import reference as R
+from tests.gpu_util import TOL_BF16, announce, dev, host64, relerr
+
+pytestmark = pytest.mark.gpu
+
+
+def fp8_weights(rng, N, Kd):
+    """Random finite E4M3 codes (NaN codes replaced) and per-block scales."""
+    codes = rng.integers(0, 256, (N, Kd), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3C
+    scales = rng.uniform(1e-3, 1e-2, ((N + 127) // 128, Kd // 128)).astype(np.float32)
+    return codes, scales
+
+
+def run_gemv(M, N, Kd, out_dtype=torch.float32, seed=0):
+    rng = np.random.default_rng(seed)
+    codes, scales = fp8_weights(rng, N, Kd)
+    x = synth.normal(rng, (M, Kd))
+    y = torch.full((M, N), float("nan"), dtype=out_dtype, device="cuda")
+    K.kda_gemv_fp8(dev(x), torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(), y)
+    torch.cuda.synchronize()
+    ref = R.gemv_fp8_blocks(x.vals, codes, scales)
+    return y, ref
+
+
+@pytest.mark.parametrize("M,N,Kd", [(1, 300, 128), (3, 257, 1152), (8, 1000, 4096), (2, 16, 2048), (5, 4099, 256)])
+def test_gemv_fp8_small(M, N, Kd):
+    announce("gemv fp8 M=%d N=%d K=%d" % (M, N, Kd))
+    y, ref = run_gemv(M, N, Kd, seed=M * 7 + N)
+    e = relerr(host64(y), ref)
+    print("  err %.2e" % e, flush=True)
+    assert e < 2e-5
+
+
+def test_gemv_fp8_bf16_output():
+    announce("gemv fp8 bf16 out")
+    y, ref = run_gemv(4, 513, 1024, out_dtype=torch.bfloat16, seed=3)
+    assert relerr(host64(y), ref) < 5e-3
+
+
+@pytest.mark.parametrize("N,Kd", [(5 * 8192 + 64, 4096), (4096, 8192)])
+def test_gemv_fp8_layer_shapes_full(N, Kd):
+    """The layer's projections at full size for one decode token: the input
+    projection (41,024 x 4,096) and the output projection (4,096 x 8,192);
+    every output checked."""
+    announce("gemv fp8 full N=%d K=%d" % (N, Kd))
+    y, ref = run_gemv(1, N, Kd, seed=N)
+    e = relerr(host64(y), ref)
+    print("  err %.2e" % e, flush=True)
+    assert e < 2e-5
+
+
+def test_output_norm_gate_fp8():
+    """Codes and scales per (token, head): scales equal the oracle's to 1e-6;
+    every dequantized value within half an E4M3 step (plus float32 slack) of
+    the oracle's exact value; the group maximum sits on +-448; at least 99% of
+    the codes equal the oracle's (the rest are float32 rounding at a tie)."""
+    announce("output norm gate fp8")
+    rng = np.random.default_rng(50)
+    T, H = 37, 5
+    o = (rng.standard_normal((T, H, 128)) * rng.uniform(0.01, 3.0, (T, H, 1))).astype(np.float32)
+    o[3, 2] = 0.0  # an all-zero head: scale 1, codes 0
+    gate = synth.normal(rng, (T, H * 128 + 8))
+    w = rng.uniform(0.5, 1.5, 128).astype(np.float32)
+    codes = torch.empty((T, H * 128), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    K.kda_output_norm_gate_fp8(torch.from_numpy(o).cuda(), dev(gate), torch.from_numpy(w).cuda(), codes, scales)
+    torch.cuda.synchronize()
+    y = R.output_norm_gate(o, gate.vals[:, :H * 128], w).reshape(T, H * 128)
+    rc, rs = R.quantize_fp8_groups(y)
+    gc, gs = codes.cpu().numpy(), scales.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(gs - rs) / rs) < 1e-6
+    assert np.all(gc[3, 256:384] == 0) and gs[3, 2] == 1.0
+    deq = R.e4m3_decode(gc) * np.repeat(gs, 128, axis=1)
+    bound = np.maximum(2.0 ** -4 * np.abs(y), 2.0 ** -10 * np.repeat(rs, 128, axis=1)) * (1 + 2e-3) + 1e-7 * np.abs(y)
+    assert np.all(np.abs(deq - y) <= bound)
+    mx = np.max(gc.reshape(T, H, 128) & 0x7F, axis=-1)
+    assert np.all(mx[rs != 1.0] == 0x7E)
+    same = np.mean(gc == rc)
+    print("  codes equal to the oracle's: %.4f" % same, flush=True)
+    assert same >= 0.99

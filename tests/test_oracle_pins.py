@@ -489,3 +489,73 @@ def test_per_token_states_orthonormal_write_and_read():
             want = v[s, 0] if s <= t else np.zeros(d)
             assert np.allclose(got, want, atol=1e-15)
         assert np.allclose(o[t, 0], v[t, 0], atol=1e-15)
+
+
+# -------------------------------------------------------------- block FP8
+def test_e4m3_decode_closed_values():
+    """OCP E4M3: 0x38 = 1, 0x7E = 448 (largest), 0x01 = 2^-9 (smallest
+    subnormal), 0x08 = 2^-6 (smallest normal), sign bit, NaN codes; the 126
+    positive finite codes increase strictly."""
+    d = R.e4m3_decode(np.arange(256, dtype=np.uint8))
+    assert d[0x38] == 1.0 and d[0x7E] == 448.0 and d[0x01] == 2.0 ** -9 and d[0x08] == 2.0 ** -6
+    assert d[0x07] == 7 * 2.0 ** -9 and d[0x40] == 2.0 and d[0xC0] == -2.0 and d[0x80] == 0.0
+    assert np.isnan(d[0x7F]) and np.isnan(d[0xFF]) and np.isfinite(np.delete(d, [0x7F, 0xFF])).all()
+    assert np.all(np.diff(d[:0x7F]) > 0)
+    assert np.array_equal(d[0x80:0xFF], -d[0x00:0x7F])
+
+
+def test_e4m3_encode_round_to_nearest_even():
+    """Every finite code round-trips; midpoints go to the even code; values
+    beyond 448 saturate; the sign is kept."""
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    vals = R.e4m3_decode(codes)
+    back = R.e4m3_encode(vals)
+    assert np.array_equal(back[vals != 0], codes[vals != 0])
+    assert R.e4m3_encode([1.0625])[0] == 0x38   # between 1 and 1.125: even (1.0)
+    assert R.e4m3_encode([1.1875])[0] == 0x3A   # between 1.125 and 1.25: even (1.25)
+    assert R.e4m3_encode([19.0])[0] == 0x5A     # between 18 and 20: even (20)
+    assert R.e4m3_encode([2.0 ** -10])[0] == 0x00 and R.e4m3_encode([1.5 * 2.0 ** -9])[0] == 0x02
+    assert R.e4m3_encode([1000.0])[0] == 0x7E and R.e4m3_encode([-1000.0])[0] == 0xFE
+    assert R.e4m3_encode([1.07])[0] == 0x39 and R.e4m3_encode([-0.3])[0] == 0x80 | R.e4m3_encode([0.3])[0]
+
+
+def test_gemv_fp8_blocks_closed_form_and_brute_force():
+    """All codes 1.0 with per-block scales: y[m, n] = sum_kb s[n/128, kb] *
+    sum_{k in kb} x[m, k]; and a tiny case against a triple loop."""
+    rng = np.random.default_rng(40)
+    M, N, Kd = 3, 200, 256
+    x = rng.standard_normal((M, Kd))
+    s = rng.uniform(0.5, 2.0, (2, 2))
+    codes = np.full((N, Kd), 0x38, np.uint8)
+    y = R.gemv_fp8_blocks(x, codes, s)
+    for n in (0, 127, 128, 199):
+        want = sum(s[n // 128, kb] * x[:, 128 * kb:128 * (kb + 1)].sum(axis=1) for kb in range(2))
+        assert np.allclose(y[:, n], want, rtol=1e-13, atol=1e-12)
+    codes = rng.integers(0, 256, (5, 128), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x11
+    x = rng.standard_normal((2, 128))
+    s = np.array([[0.37]])
+    y = R.gemv_fp8_blocks(x, codes, s)
+    dec = R.e4m3_decode(codes)
+    for m in range(2):
+        for n in range(5):
+            assert abs(y[m, n] - sum(x[m, k] * dec[n, k] * 0.37 for k in range(128))) < 1e-12
+
+
+def test_quantize_fp8_groups():
+    """The group's largest magnitude maps to +-448 exactly; every value is
+    within half a code step of its quantized value; all-zero groups give
+    scale 1 and code 0."""
+    rng = np.random.default_rng(41)
+    y = rng.standard_normal((4, 256)) * np.array([1e-3, 1.0, 50.0, 0.0])[:, None]
+    codes, scale = R.quantize_fp8_groups(y)
+    assert scale.shape == (4, 2) and np.all(scale[3] == 1.0) and np.all(codes[3] == 0)
+    deq = R.e4m3_decode(codes) * np.repeat(scale, 128, axis=1)
+    for t in range(3):
+        for gidx in range(2):
+            gsl = slice(128 * gidx, 128 * gidx + 128)
+            i = np.argmax(np.abs(y[t, gsl]))
+            assert codes[t, gsl][i] & 0x7F == 0x7E
+            # half a code step: 2^-4 relative for normals, 2^-10 x scale for subnormals
+            err = np.abs(deq[t, gsl] - y[t, gsl])
+            assert np.all(err <= np.maximum(2.0 ** -4 * np.abs(y[t, gsl]), 2.0 ** -10 * scale[t, gidx]) * (1 + 1e-12))
