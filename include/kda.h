@@ -227,8 +227,10 @@ int kda_state_convert(const void* src, kda_dtype src_dtype, void* dst, kda_dtype
  * Different MLA Caches", section "Production boundaries"; "Ling-3.1-flash: a
  * 560B hybrid-attention MoE, counted from its safetensors headers", section
  * "What is in the files"), and a batch-1 decode step is mostly the reading of
- * those weights (same page, "What the cut does not buy"). E4M3 is the OCP FP8
- * format (bias 7, no infinities, 0x7F/0xFF NaN, largest 448).
+ * those weights (same page, "What the cut does not buy"); an FP8 block GEMV is
+ * among the Hopper decode settings ("Ling-3.1-flash: What 63 Linear-Attention
+ * Layers Do to the KV Budget", section "Fitting it on a node"). E4M3 is the
+ * OCP FP8 format (bias 7, no infinities, 0x7F/0xFF NaN, largest 448).
  *
  * x        bfloat16 [M, K], row stride ldx (a multiple of 8), 1 <= M <= 8.
  * w        E4M3 codes [N, K], row stride ldw (bytes, a multiple of 16).
