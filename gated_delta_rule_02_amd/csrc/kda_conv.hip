@@ -8,9 +8,10 @@
 // W-1 steps back. Tokens before a sequence's first come from its conv state
 // (oldest first) or are zero.
 //
-// Both kernels are memory-bound elementwise passes. A wavefront owns one group
-// of 128 channels (two per lane, 4- or 8-byte accesses) so that the per-head L2
-// norm is a single wavefront reduction.
+// Both kernels are memory-bound elementwise passes. The decode update: a
+// wavefront owns one group of 128 channels (two per lane), so that the
+// per-head L2 norm is a single wavefront reduction. The prefill: 16 bytes of
+// channels per lane, the L2 norm a reduction over the lanes of one group.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -20,7 +21,6 @@ namespace {
 constexpr int kMaxW = 8;
 constexpr int kGroup = 128;     // channels per wavefront
 constexpr int kWaves = 4;       // wavefronts per workgroup
-constexpr int kTokTile = 16;    // tokens per workgroup (prefill)
 
 template <typename T>
 __device__ __forceinline__ void st2(T* p, float a, float b);
@@ -103,59 +103,118 @@ __device__ __forceinline__ int find_seq(const int32_t* cu, int num_seqs, int64_t
     return lo;
 }
 
-template <typename T>
-__global__ __launch_bounds__(kWaves * 64) void conv_prefill_kernel(ConvPrefillArgs a)
+// A lane owns 16 bytes of channels (8 bfloat16 or 4 float32) and walks the
+// workgroup's tile of tokens in order, keeping the W-1 inputs before the
+// current token in registers, so every input row is read once (plus W-1 rows
+// of history at the tile start). The rows of the tile are loaded 8 at a time
+// ahead of their use. The current sequence (start s, end e) is tracked per
+// workgroup; at a sequence start the window is refilled from that sequence's
+// conv state, or with zeros.
+constexpr int kConvTok = 32;  // tokens per workgroup
+constexpr int kConvBatch = 8; // rows loaded ahead
+
+template <typename T, int W>
+__global__ __launch_bounds__(256) void conv_prefill_kernel(ConvPrefillArgs a)
 {
-    const int grp = blockIdx.y * kWaves + (threadIdx.x >> 6);
-    if (grp * kGroup >= a.C) return;
-    const int c = grp * kGroup + 2 * (threadIdx.x & 63);
-    const int W = a.W;
+    using V = Vec16<T>;
+    constexpr int N = V::N;          // channels per lane
+    constexpr int GL = kGroup / N;   // lanes per 128-channel group
+    const int c = (blockIdx.y * 256 + threadIdx.x) * N;
+    if (c >= a.C) return;  // C is a multiple of 128: whole groups leave together
     const T* x = static_cast<const T*>(a.x);
     const T* w = static_cast<const T*>(a.weight);
     const T* sin = static_cast<const T*>(a.state_in);
 
-    float wc0[kMaxW], wc1[kMaxW];
+    float wt[W][N];  // wt[j][i] = weight[c + i][j]
 #pragma unroll
-    for (int j = 0; j < kMaxW; ++j)
-        if (j < W) {
-            wc0[j] = ld(w + (size_t)c * W + j);
-            wc1[j] = ld(w + (size_t)(c + 1) * W + j);
-        }
-    f32x2 bias = {0.f, 0.f};
-    if (a.bias) bias = ld2(static_cast<const T*>(a.bias) + c);
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+        for (int j = 0; j < W; ++j) wt[j][i] = ld(w + (size_t)(c + i) * W + j);
+    float bias[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) bias[i] = a.bias ? ld(static_cast<const T*>(a.bias) + c + i) : 0.0f;
 
-    const int64_t t0 = (int64_t)blockIdx.x * kTokTile;
-    for (int i = 0; i < kTokTile; ++i) {
-        const int64_t t = t0 + i;
-        if (t >= a.num_tokens) break;
-        int n;
-        int64_t s;
-        if (a.cu_seqlens) {
-            n = find_seq(a.cu_seqlens, a.num_seqs, t);
-            s = a.cu_seqlens[n];
+    const int64_t t0 = (int64_t)blockIdx.x * kConvTok;
+    const int64_t t1 = min<int64_t>(t0 + kConvTok, a.num_tokens);
+    int n;
+    int64_t s, e;
+    if (a.cu_seqlens) {
+        n = find_seq(a.cu_seqlens, a.num_seqs, t0);
+        s = a.cu_seqlens[n];
+        e = a.cu_seqlens[n + 1];
+    } else {
+        n = (int)(t0 / a.seq_len);
+        s = (int64_t)n * a.seq_len;
+        e = s + a.seq_len;
+    }
+    // input at position p < s of sequence n: its conv state (oldest first) or 0
+    auto history = [&](int64_t p, float* out) {
+        if (sin) {
+            V::unpack(ld16(sin + ((size_t)n * (W - 1) + (size_t)((W - 1) - (s - p))) * a.C + c), out);
         } else {
-            n = (int)(t / a.seq_len);
-            s = (int64_t)n * a.seq_len;
-        }
-        f32x2 acc = bias;
 #pragma unroll
-        for (int j = 0; j < kMaxW; ++j)
-            if (j < W) {
-                const int64_t p = t - (W - 1) + j;  // input position of tap j
-                f32x2 xv;
-                if (p >= s) {
-                    xv = ld2(x + p * a.x_ld + c);
-                } else if (sin) {
-                    // history row (W-1) - (s - p), oldest first
-                    xv = ld2(sin + ((size_t)n * (W - 1) + (size_t)((W - 1) - (s - p))) * a.C + c);
+            for (int i = 0; i < N; ++i) out[i] = 0.0f;
+        }
+    };
+    float win[W - 1][N];  // win[j]: the input W-1-j positions before the current token
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) {
+        const int64_t p = t0 - (W - 1) + j;
+        if (p >= s) V::unpack(ld16(x + p * a.x_ld + c), win[j]);
+        else history(p, win[j]);
+    }
+
+    T* y = static_cast<T*>(a.y);
+    for (int64_t tb = t0; tb < t1; tb += kConvBatch) {
+        u32x4_t raw[kConvBatch];
+#pragma unroll
+        for (int r = 0; r < kConvBatch; ++r)
+            raw[r] = tb + r < t1 ? ld16(x + (tb + r) * a.x_ld + c) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int r = 0; r < kConvBatch; ++r) {
+            const int64_t t = tb + r;
+            if (t >= t1) break;
+            if (t == e) {
+                // the next non-empty sequence starts at t
+                if (a.cu_seqlens) {
+                    do { ++n; } while (a.cu_seqlens[n + 1] <= t);
+                    s = a.cu_seqlens[n];
+                    e = a.cu_seqlens[n + 1];
                 } else {
-                    xv = f32x2{0.f, 0.f};
+                    ++n;
+                    s = e;
+                    e = s + a.seq_len;
                 }
-                acc.x += wc0[j] * xv.x;
-                acc.y += wc1[j] * xv.y;
+#pragma unroll
+                for (int j = 0; j < W - 1; ++j) history(t - (W - 1) + j, win[j]);
             }
-        acc = finish(acc, a.apply_silu, a.l2_group != 0, a.l2_eps);
-        st2(static_cast<T*>(a.y) + t * a.y_ld + c, acc.x, acc.y);
+            float xv[N], acc[N];
+            V::unpack(raw[r], xv);
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                float v = bias[i];
+#pragma unroll
+                for (int j = 0; j < W - 1; ++j) v += wt[j][i] * win[j][i];
+                acc[i] = v + wt[W - 1][i] * xv[i];
+            }
+#pragma unroll
+            for (int j = 0; j < W - 1; ++j)
+#pragma unroll
+                for (int i = 0; i < N; ++i) win[j][i] = j + 1 < W - 1 ? win[j + 1][i] : xv[i];
+            if (a.apply_silu) {
+#pragma unroll
+                for (int i = 0; i < N; ++i) acc[i] = siluf_(acc[i]);
+            }
+            if (a.l2_group) {
+                float ss = 0.0f;
+#pragma unroll
+                for (int i = 0; i < N; ++i) ss += acc[i] * acc[i];
+                const float rn = rsqrtf(group_sum<GL>(ss) + a.l2_eps);
+#pragma unroll
+                for (int i = 0; i < N; ++i) acc[i] *= rn;
+            }
+            st16(y + t * a.y_ld + c, V::pack(acc));
+        }
     }
 }
 
@@ -212,13 +271,19 @@ hipError_t launch_conv_update(const ConvUpdateArgs& a, hipStream_t s)
 hipError_t launch_conv_prefill(const ConvPrefillArgs& a, hipStream_t s)
 {
     if (a.num_tokens > 0) {
-        dim3 grid((unsigned)((a.num_tokens + kTokTile - 1) / kTokTile),
-                  (unsigned)((a.C + kGroup * kWaves - 1) / (kGroup * kWaves))),
-            block(kWaves * 64);
-        if (a.dtype == F32)
-            hipLaunchKernelGGL(conv_prefill_kernel<float>, grid, block, 0, s, a);
-        else
-            hipLaunchKernelGGL(conv_prefill_kernel<bf16_t>, grid, block, 0, s, a);
+        const int ch = a.dtype == F32 ? 256 * 4 : 256 * 8;  // channels per workgroup
+        const dim3 grid((unsigned)((a.num_tokens + kConvTok - 1) / kConvTok), (unsigned)((a.C + ch - 1) / ch)),
+            block(256);
+        switch (a.W) {
+#define KDA_CONV_W(WW)                                                                              \
+    case WW:                                                                                        \
+        if (a.dtype == F32) hipLaunchKernelGGL((conv_prefill_kernel<float, WW>), grid, block, 0, s, a); \
+        else hipLaunchKernelGGL((conv_prefill_kernel<bf16_t, WW>), grid, block, 0, s, a);           \
+        break;
+            KDA_CONV_W(2) KDA_CONV_W(3) KDA_CONV_W(4) KDA_CONV_W(5) KDA_CONV_W(6) KDA_CONV_W(7) KDA_CONV_W(8)
+#undef KDA_CONV_W
+            default: return hipErrorInvalidValue;
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

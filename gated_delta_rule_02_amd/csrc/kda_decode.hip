@@ -60,7 +60,6 @@ template <typename TS> struct Map {
     static constexpr int kQuads = kCols / 4;              // f32x4 per row segment
 };
 
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 // kCols consecutive state elements as floats (kQuads f32x4), streamed once per step
 __device__ __forceinline__ void ld_state(const float* p, f32x4* v) { v[0] = KDA_NT_LOAD(reinterpret_cast<const f32x4*>(p)); }
 __device__ __forceinline__ void ld_state(const bf16_t* p, f32x4* v)

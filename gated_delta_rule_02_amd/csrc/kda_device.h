@@ -112,10 +112,19 @@ __device__ __forceinline__ void lds_barrier()
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
-__device__ __forceinline__ float siluf_(float x) { return x / (1.0f + __expf(-x)); }
-// softplus(x) = log(1 + e^x), computed as max(x, 0) + log1p(e^{-|x|})
-__device__ __forceinline__ float softplusf_(float x) { return fmaxf(x, 0.0f) + log1pf(__expf(-fabsf(x))); }
+// The activations use the hardware exp2, log2 and reciprocal (about one ulp
+// each): the memory-bound kernels that apply them per element would otherwise
+// be bound by full-precision division and log1p sequences.
+__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+__device__ __forceinline__ float siluf_(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^{-|x|}); log1p(e) by its
+// series e - e^2/2 where 1 + e would drop e's low bits (relative error < e^2/3)
+__device__ __forceinline__ float softplusf_(float x)
+{
+    const float e = __expf(-fabsf(x));
+    const float l = e < 0x1p-10f ? e * (1.0f - 0.5f * e) : __logf(1.0f + e);
+    return fmaxf(x, 0.0f) + l;
+}
 
 // Sum over the 64 lanes of a wavefront (every lane gets the total).
 __device__ __forceinline__ float wave_sum(float v)
@@ -124,6 +133,57 @@ __device__ __forceinline__ float wave_sum(float v)
     for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
     return v;
 }
+
+// Sum over aligned groups of G lanes (G a power of two <= 64; every lane of a
+// group gets its group's total).
+template <int G>
+__device__ __forceinline__ float group_sum(float v)
+{
+#pragma unroll
+    for (int m = G / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+// ---- 16-byte vectors of a storage type ------------------------------------
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+template <typename T> struct Vec16;
+template <> struct Vec16<bf16_t> {
+    static constexpr int N = 8;  // elements per 16 bytes
+    __device__ static void unpack(const u32x4_t& u, float* f)
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __uint_as_float(u[i] << 16);
+            f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+        }
+    }
+    // round to nearest even by the hardware conversion (two values per instruction)
+    __device__ static u32x4_t pack(const float* f)
+    {
+        u32x4_t u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+            const b2 h = {(__bf16)f[2 * i], (__bf16)f[2 * i + 1]};
+            u[i] = __builtin_bit_cast(uint32_t, h);
+        }
+        return u;
+    }
+};
+template <> struct Vec16<float> {
+    static constexpr int N = 4;
+    __device__ static void unpack(const u32x4_t& u, float* f)
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(u[i]);
+    }
+    __device__ static u32x4_t pack(const float* f)
+    {
+        return u32x4_t{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
+    }
+};
+__device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+__device__ __forceinline__ void st16(void* p, const u32x4_t& u) { *reinterpret_cast<u32x4_t*>(p) = u; }
 
 // Maximum over the 64 lanes of a wavefront (every lane gets it).
 __device__ __forceinline__ float wave_max(float v)

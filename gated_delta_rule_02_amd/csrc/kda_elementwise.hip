@@ -12,76 +12,102 @@
 // sigmoid gate before the output projection; here a per-head RMSNorm over the
 // 128 value channels, a per-channel weight and sigmoid(gate).
 //
-// Both are one wavefront per (token, head) row of 128 channels, two channels
-// per lane: the RMS is one wavefront reduction, accesses are 4/8-byte per lane.
+// Both are memory-bound passes with 16-byte accesses where the storage type
+// allows (layout and lane mapping at each kernel).
 #include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
 namespace {
 
-constexpr int kRowsPerBlock = 4;
+// Gate: a lane owns 8 consecutive channels (one head: dk = 128) of 8 tokens;
+// the rows are loaded before any is computed, 16-byte accesses for bfloat16.
+constexpr int kGateTok = 8;
+constexpr int kGateCh = 256 * 8;  // channels per workgroup
 
 template <typename T>
-__device__ __forceinline__ void st2(T* p, float a, float b);
-template <>
-__device__ __forceinline__ void st2<float>(float* p, float a, float b)
+__device__ __forceinline__ void ld8(const T* p, float* f)
 {
-    *reinterpret_cast<f32x2*>(p) = f32x2{a, b};
+    if constexpr (sizeof(T) == 2) {
+        Vec16<bf16_t>::unpack(ld16(p), f);
+    } else {
+        Vec16<float>::unpack(ld16(p), f);
+        Vec16<float>::unpack(ld16(p + 4), f + 4);
+    }
 }
-template <>
-__device__ __forceinline__ void st2<bf16_t>(bf16_t* p, float a, float b)
+template <typename T>
+__device__ __forceinline__ void st8(T* p, const float* f)
 {
-    *reinterpret_cast<uint32_t*>(p) = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+    if constexpr (sizeof(T) == 2) {
+        st16(p, Vec16<bf16_t>::pack(f));
+    } else {
+        st16(p, Vec16<float>::pack(f));
+        st16(p + 4, Vec16<float>::pack(f + 4));
+    }
 }
 
 template <typename TI, typename TO>
-__global__ __launch_bounds__(kRowsPerBlock * 64) void gate_kernel(GateArgs a)
+__global__ __launch_bounds__(256) void gate_kernel(GateArgs a)
 {
-    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);  // t * H + h
-    if (row >= a.num_tokens * a.H) return;
-    const int lane = threadIdx.x & 63;
-    const int64_t t = row / a.H;
-    const int h = (int)(row % a.H);
-    const float rate = __expf(a.A_log[h]);
-    const TI* f = static_cast<const TI*>(a.f) + t * a.f_ld + (int64_t)h * a.dk;
-    TO* g = static_cast<TO*>(a.g_out) + row * a.dk;
-    for (int c = 2 * lane; c < a.dk; c += 128) {
-        const f32x2 fv = ld2(f + c);
-        st2(g + c, fmaxf(-rate * softplusf_(fv.x), a.lower_bound),
-            fmaxf(-rate * softplusf_(fv.y), a.lower_bound));
+    const int64_t t0 = (int64_t)blockIdx.x * kGateTok;
+    const int nt = (int)min<int64_t>(kGateTok, a.num_tokens - t0);
+    if (blockIdx.y == 0) {
+        // beta = sigmoid(b) for the workgroup's tokens
+        for (int i = threadIdx.x; i < nt * a.H; i += 256) {
+            const int64_t t = t0 + i / a.H;
+            const int h = i % a.H;
+            st(static_cast<TO*>(a.beta_out) + t * a.H + h, sigmoidf_(ld(static_cast<const TI*>(a.b) + t * a.b_ld + h)));
+        }
     }
-    if (lane == 0) {
-        const float bv = ld(static_cast<const TI*>(a.b) + t * a.b_ld + h);
-        st(static_cast<TO*>(a.beta_out) + row, sigmoidf_(bv));
+    const int cc = blockIdx.y * kGateCh + threadIdx.x * 8;  // channel in [0, H * dk)
+    if (cc >= a.H * a.dk) return;
+    const float rate = __expf(a.A_log[cc / a.dk]);
+    const TI* f = static_cast<const TI*>(a.f) + t0 * a.f_ld + cc;
+    TO* g = static_cast<TO*>(a.g_out) + t0 * (int64_t)a.H * a.dk + cc;
+    float fv[kGateTok][8];
+#pragma unroll
+    for (int r = 0; r < kGateTok; ++r)
+        if (r < nt) ld8(f + r * a.f_ld, fv[r]);
+#pragma unroll
+    for (int r = 0; r < kGateTok; ++r) {
+        if (r >= nt) break;
+        float gv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) gv[i] = fmaxf(-rate * softplusf_(fv[r][i]), a.lower_bound);
+        st8(g + r * (int64_t)a.H * a.dk, gv);
     }
 }
 
+// Epilogue: a lane owns 4 consecutive channels; 32 lanes cover one (token,
+// head) row, so a wavefront handles two rows and the RMS is a 32-lane sum.
+constexpr int kNormRowsPerBlock = 8;
+
 template <typename TO_, typename TY>
-__global__ __launch_bounds__(kRowsPerBlock * 64) void norm_gate_kernel(NormGateArgs a)
+__global__ __launch_bounds__(256) void norm_gate_kernel(NormGateArgs a)
 {
-    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-    if (row >= a.num_tokens * a.H) return;
-    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kNormRowsPerBlock + (threadIdx.x >> 5);  // t * H + h
+    if (row >= a.num_tokens * a.H) return;  // whole 32-lane halves leave together
+    const int c = 4 * (threadIdx.x & 31);   // dv == 128
     const int64_t t = row / a.H;
     const int h = (int)(row % a.H);
-    const int c = 2 * lane;  // dv == 128
-    const f32x2 ov = ld2(static_cast<const TO_*>(a.o) + row * a.dv + c);
-    const float ms = wave_sum(ov.x * ov.x + ov.y * ov.y) * (1.0f / 128.0f);
+    const f32x4 ov = ld4(static_cast<const TO_*>(a.o) + row * a.dv + c);
+    const f32x4 gv = ld4(static_cast<const TY*>(a.gate) + t * a.gate_ld + (int64_t)h * a.dv + c);
+    const f32x4 wv = ld4(a.w + c);
+    const float ms = group_sum<32>(ov.x * ov.x + ov.y * ov.y + ov.z * ov.z + ov.w * ov.w) * (1.0f / 128.0f);
     const float r = rsqrtf(ms + a.eps);
-    const f32x2 gv = ld2(static_cast<const TY*>(a.gate) + t * a.gate_ld + (int64_t)h * a.dv + c);
-    const float w0 = a.w[c], w1 = a.w[c + 1];
-    st2(static_cast<TY*>(a.y) + row * a.dv + c, ov.x * r * w0 * sigmoidf_(gv.x),
-        ov.y * r * w1 * sigmoidf_(gv.y));
+    st4(static_cast<TY*>(a.y) + row * a.dv + c,
+        f32x4{ov.x * r * wv.x * sigmoidf_(gv.x), ov.y * r * wv.y * sigmoidf_(gv.y),
+              ov.z * r * wv.z * sigmoidf_(gv.z), ov.w * r * wv.w * sigmoidf_(gv.w)});
 }
 
 }  // namespace
 
 hipError_t launch_gate(const GateArgs& a, hipStream_t s)
 {
-    const int64_t rows = a.num_tokens * a.H;
-    if (rows == 0) return hipSuccess;
-    dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(kRowsPerBlock * 64);
+    if (a.num_tokens == 0) return hipSuccess;
+    const dim3 grid((unsigned)((a.num_tokens + kGateTok - 1) / kGateTok),
+                    (unsigned)(((int64_t)a.H * a.dk + kGateCh - 1) / kGateCh)),
+        block(256);
     if (a.in_dtype == F32) {
         if (a.out_dtype == F32) hipLaunchKernelGGL((gate_kernel<float, float>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((gate_kernel<float, bf16_t>), grid, block, 0, s, a);
@@ -96,7 +122,7 @@ hipError_t launch_norm_gate(const NormGateArgs& a, hipStream_t s)
 {
     const int64_t rows = a.num_tokens * a.H;
     if (rows == 0) return hipSuccess;
-    dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(kRowsPerBlock * 64);
+    const dim3 grid((unsigned)((rows + kNormRowsPerBlock - 1) / kNormRowsPerBlock)), block(256);
     if (a.o_dtype == F32) {
         if (a.y_dtype == F32) hipLaunchKernelGGL((norm_gate_kernel<float, float>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((norm_gate_kernel<float, bf16_t>), grid, block, 0, s, a);

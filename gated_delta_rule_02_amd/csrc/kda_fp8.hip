@@ -28,7 +28,6 @@ namespace kda {
 namespace {
 
 typedef float f2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kRowsPerWave = 4;
 constexpr int kWaves = 4;

@@ -121,7 +121,6 @@ constexpr int TM = 256, TN = 256, TK = 32;   // workgroup tile and K step
 constexpr int kStages = 4;                   // K steps in LDS: the copies run 3 steps ahead
 constexpr int kStageBytes = TM * TK * 2;      // one operand's stage: 256 rows x 64 B
 typedef __attribute__((address_space(3))) void lds_void;
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // LDS byte offset of 16-byte chunk c (0..3) of row r of a stage: the chunks
 // are XOR-swizzled by (r / 4) mod 4, so the 16 rows of an operand read cover

@@ -38,7 +38,6 @@ namespace kda {
 namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // Byte offsets inside one chunk slot. A-operand layout [t][s][lane][8 halves]:
