@@ -264,9 +264,15 @@ struct __attribute__((aligned(16))) Smem {
         struct {
             OT Kt[C][LDH];     // k o 2^b   (X = diag(beta)(V - Kt S))
             OT Qt[C][LDH];     // q o 2^b   (O = Qt S + P U)
-            OT Wst[C][LDH];    // -W staged for its transposed store (two-pass form)
-            uint16_t Vst[C][LDH];  // v (input storage bits), staged by the producers (two-pass form)
         } h;
+        // two-pass form: the right-hand sides of the products with
+        // T = (I + A)^-1, transposed ([channel][token], so that a lane reads
+        // four consecutive tokens of its channel at once), and Q~
+        struct {
+            OT XWt[D][LDT];    // (-diag(beta) (K o 2^B))^T
+            OT XUt[D][LDT];    // (diag(beta) V)^T
+            OT Qt[C][LDH];     // q o 2^b
+        } x;
     } key;
 };
 
@@ -277,11 +283,13 @@ struct __attribute__((aligned(16))) Smem {
 // group hh of block R); the next chunk's k, q, g of those tokens and beta
 // stream into registers while the current chunk computes. The caller
 // separates the phases with barriers.
-// Lean: the kernel holds no state in registers here (the two-pass intra
-// pass), so P2 can afford more live registers: the diagonal-block inverses by
+// Lean: the two-pass intra pass. The kernel holds no state in registers
+// here, so P2 can afford more live registers: the diagonal-block inverses by
 // repeated squaring instead of the Horner form (fewer dependent products) and
-// the off-diagonal pairs split evenly over the SIMDs.
-template <bool F32P, typename TIN, int NQ = 2, bool StageV = false, bool Lean = false>
+// the off-diagonal pairs split evenly over the SIMDs. The producers also load
+// v and, in P2b, stage the right-hand sides -diag(beta)(K o 2^B) and
+// diag(beta) V of the products with T, transposed and rounded once.
+template <bool F32P, typename TIN, int NQ = 2, bool Lean = false>
 struct Front {
     using O = Ops<F32P>;
     using OT = typename O::OT;
@@ -304,10 +312,12 @@ struct Front {
     const TIN *qg, *kg, *gg, *bg;
 
     PT rk[RP], rq[RP], rg[RP];  // k, q, g of this producer's tokens
-    PT rvv[StageV ? RP : 1];    // v of this producer's tokens (StageV)
+    PT rvv[Lean ? RP : 1];      // v of this producer's tokens (Lean)
     uint32_t rb = 0;            // beta[tid] (threads < C)
     f32x2 g2[RP];               // clamped base-2 log-retention
-    typename O::P2 kt2[RP], qt2[RP];  // k o 2^b, q o 2^b of this producer's tokens
+    // k o 2^b (or, Lean, -beta k o 2^b) and q o 2^b of this producer's tokens
+    typename O::P2 kt2[RP], qt2[RP];
+    typename O::P2 xu2[Lean ? RP : 1];  // Lean: beta v of this producer's tokens
 
     // the wavefront index is read through readfirstlane so that the compiler
     // knows every quantity derived from it is wave-uniform (scalar offsets)
@@ -321,29 +331,39 @@ struct Front {
     }
 
     // k, q, g, beta of the nt tokens starting at c_s (rows past nt read as 0)
-    // (and v with StageV)
+    // (and v when Lean). Parts (bit mask): 1 = g, k and beta, 2 = q, 4 = v,
+    // so that a caller can spread the issue of the next chunk's loads over
+    // several phases.
+    template <int Parts = 7>
     __device__ __forceinline__ void load(int64_t c_s, int nt, const TIN* vg = nullptr)
     {
         const int64_t bytes = (int64_t)nt * ts * ES;
-        const rsrc_t rk_ = make_rsrc(kg + c_s * ts, bytes), rq_ = make_rsrc(qg + c_s * ts, bytes),
-                     rg_ = make_rsrc(gg + c_s * ts, bytes);
         if (prod) {
             const int voff = (c0 + h * D) * ES;  // per lane
+            if constexpr (Parts & 1) {
+                const rsrc_t rk_ = make_rsrc(kg + c_s * ts, bytes), rg_ = make_rsrc(gg + c_s * ts, bytes);
 #pragma unroll
-            for (int t = 0; t < RP; ++t) {
-                const int soff = (rbase + t) * ts * ES;  // wave-uniform row term
-                rk[t] = IN::ld_pair(rk_, voff, soff);
-                rq[t] = IN::ld_pair(rq_, voff, soff);
-                rg[t] = IN::ld_pair(rg_, voff, soff);
+                for (int t = 0; t < RP; ++t) {
+                    const int soff = (rbase + t) * ts * ES;  // wave-uniform row term
+                    rg[t] = IN::ld_pair(rg_, voff, soff);
+                    rk[t] = IN::ld_pair(rk_, voff, soff);
+                }
             }
-            if constexpr (StageV) {
+            if constexpr (Parts & 2) {
+                const rsrc_t rq_ = make_rsrc(qg + c_s * ts, bytes);
+#pragma unroll
+                for (int t = 0; t < RP; ++t) rq[t] = IN::ld_pair(rq_, voff, (rbase + t) * ts * ES);
+            }
+            if constexpr (Lean && (Parts & 4)) {
                 const rsrc_t rv_ = make_rsrc(vg + c_s * ts, bytes);
 #pragma unroll
                 for (int t = 0; t < RP; ++t) rvv[t] = IN::ld_pair(rv_, voff, (rbase + t) * ts * ES);
             }
         }
-        const rsrc_t rb_ = make_rsrc(bg + c_s * H, (int64_t)nt * H * ES);  // uniform: built outside the branch
-        if (tid < C) rb = IN::ld_one(rb_, (tid * H + h) * ES, 0);
+        if constexpr (Parts & 1) {
+            const rsrc_t rb_ = make_rsrc(bg + c_s * H, (int64_t)nt * H * ES);  // uniform: built outside the branch
+            if (tid < C) rb = IN::ld_one(rb_, (tid * H + h) * ES, 0);
+        }
     }
 
     // P0: row-group sums of the log-retention (base 2), beta to LDS
@@ -411,6 +431,15 @@ struct Front {
 #pragma unroll
         for (int t = 0; t < RP; ++t) al[t] = f32x2{exp2_fast(g2[t].x), exp2_fast(g2[t].y)};
         f32x2 el = {exp2_fast(pre.x), exp2_fast(pre.y)};
+        float nb[RP];  // Lean: -beta of this producer's tokens (rows past the chunk: 0)
+        if constexpr (Lean) {
+#pragma unroll
+            for (int t = 0; t < RP; t += 4) {
+                const f32x4 b4v = ld4f(&sm.beta[rbase + t]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) nb[t + i] = -b4v[i];
+            }
+        }
 #pragma unroll
         for (int t = 0; t < RP; ++t) {
             el *= al[t];
@@ -418,7 +447,12 @@ struct Front {
             const f32x2 klv = kv * el, qlv = qv * el;
             *reinterpret_cast<f32x2*>(&sm.key.f.KL[rbase + t][c0]) = klv;
             *reinterpret_cast<f32x2*>(&sm.key.f.QL[rbase + t][c0]) = qlv;
-            kt2[t] = O::pack2(klv.x * DR.x, klv.y * DR.y);
+            if constexpr (Lean) {
+                kt2[t] = O::pack2(klv.x * (DR.x * nb[t]), klv.y * (DR.y * nb[t]));
+                const f32x2 vv = IN::unpack(rvv[t]);  // the next chunk's loads reuse rvv after P1
+                xu2[t] = O::pack2(-nb[t] * vv.x, -nb[t] * vv.y);
+            } else
+                kt2[t] = O::pack2(klv.x * DR.x, klv.y * DR.y);
             qt2[t] = O::pack2(qlv.x * DR.x, qlv.y * DR.y);
         }
         // reverse: e_s = prod_{j>r} alpha_j over the block (starts before the later row groups)
@@ -562,15 +596,33 @@ struct Front {
         }
     }
 
-    // P2b: k o 2^b, q o 2^b over the dead float32 region
+    // P2b: k o 2^b, q o 2^b over the dead float32 region. Lean: q o 2^b, and
+    // the transposed right-hand sides -beta k o 2^b and beta v (each rounded
+    // once to the operand type; the 8 tokens of a channel in one 16-byte store)
     __device__ __forceinline__ void p2b()
     {
         if (!prod) return;
+        if constexpr (Lean) {
+            static_assert(RP == 8 && !F32P, "transposed staging: 8 tokens per producer thread, float16 operands");
+            h8 w0, w1, u0, u1;
+#pragma unroll
+            for (int t = 0; t < RP; ++t) {
+                *reinterpret_cast<typename O::P2*>(&sm.key.x.Qt[rbase + t][c0]) = qt2[t];
+                w0[t] = kt2[t].x;
+                w1[t] = kt2[t].y;
+                u0[t] = xu2[t].x;
+                u1[t] = xu2[t].y;
+            }
+            *reinterpret_cast<h8*>(&sm.key.x.XWt[c0][rbase]) = w0;
+            *reinterpret_cast<h8*>(&sm.key.x.XWt[c0 + 1][rbase]) = w1;
+            *reinterpret_cast<h8*>(&sm.key.x.XUt[c0][rbase]) = u0;
+            *reinterpret_cast<h8*>(&sm.key.x.XUt[c0 + 1][rbase]) = u1;
+            return;
+        }
 #pragma unroll
         for (int t = 0; t < RP; ++t) {
             *reinterpret_cast<typename O::P2*>(&sm.key.h.Kt[rbase + t][c0]) = kt2[t];
             *reinterpret_cast<typename O::P2*>(&sm.key.h.Qt[rbase + t][c0]) = qt2[t];
-            if constexpr (StageV) *reinterpret_cast<uint32_t*>(&sm.key.h.Vst[rbase + t][c0]) = rvv[t];
         }
     }
 };

@@ -116,10 +116,8 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
     using F4 = typename O::F4;
     using F8 = typename O::F8;
     using SM = Smem<false>;
-    using IN = Io<TIN>;
     constexpr int C = SM::C;
     constexpr int NB = SM::NB;
-    constexpr int ES = sizeof(TIN);
     static_assert(C == 64 && NB == 4, "slot layout assumes 64-token chunks");
 
     __shared__ SM sm;
@@ -144,24 +142,13 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
     const int64_t c_first = sa.chunk0 + grp;
     if (c_first >= c_end) return;
 
-    const int ts = a.H * D;
     const TIN* vg = static_cast<const TIN*>(a.v);
     uint8_t* slots = sa.ws + (size_t)u * sa.nwin * kSlot;
 
-    Front<false, TIN, 2, false, true> fr(sm, a, h);
-    uint32_t rv[NB][4];  // v[16R + 4q + i][jcol] (raw bits)
-    auto load_v = [&](int64_t c_s, int nt) {
-        const rsrc_t rv_ = make_rsrc(vg + c_s * ts, (int64_t)nt * ts * ES);
-        const int voff = (4 * q4 * ts + h * D + jcol) * ES;
-#pragma unroll
-        for (int Rr = 0; Rr < NB; ++Rr)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) rv[Rr][i] = IN::ld_one(rv_, voff, (16 * Rr + i) * ts * ES);
-    };
+    Front<false, TIN, 2, true> fr(sm, a, h);
     {
         const int64_t cs = seq_s + c_first * C;
-        fr.load(cs, (int)min<int64_t>(C, seq_e - cs));
-        load_v(cs, (int)min<int64_t>(C, seq_e - cs));
+        fr.load(cs, (int)min<int64_t>(C, seq_e - cs), vg);
     }
 
     for (int64_t c = c_first; c < c_end; c += sa.groups) {
@@ -173,9 +160,14 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
         fr.p0();
         __syncthreads();
         fr.p1();
-        if (more) fr.load(csn, (int)min<int64_t>(C, seq_e - csn));
+        // the next chunk's inputs, issued in three parts (g, k, beta; q; v) so
+        // that they stream in behind P2, P2c and the products rather than
+        // stalling one phase
+        const int ntn = (int)min<int64_t>(C, seq_e - csn);
+        if (more) fr.template load<1>(csn, ntn, vg);
         __syncthreads();
         fr.p2();
+        if (more) fr.template load<2>(csn, ntn, vg);
         __syncthreads();
         fr.p2b();
         // ---- P2c: the blocks of T = (I + A)^-1 below the diagonal, one block
@@ -183,78 +175,63 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
         if (wave == 0) inverse_column<0>(sm, Tm, m16, q4);
         else if (wave == 1) inverse_column<1>(sm, Tm, m16, q4);
         else if (wave == 2) inverse_column<2>(sm, Tm, m16, q4);
+        if (more) fr.template load<4>(csn, ntn, vg);
         __syncthreads();
 
         // ---- -W and U' as products with T, one K~ tile and one V tile per
-        // wavefront: Z_R = sum_{I<=R} T_RI X_I (independent block rows)
+        // wavefront: Z_R = sum_{I<=R} T_RI X_I (independent block rows). The
+        // right-hand sides come transposed from P2b, so that a lane reads the
+        // four tokens of its channel that it holds as an operand at once. U'
+        // is formed as T X (its accumulator layout is the slot's), -W as
+        // (T X)^T = X^T T^T: the same registers with the operands swapped,
+        // which leaves four consecutive channels of one token per lane, half
+        // of a slot fragment, stored straight to the slot.
         uint8_t* slot = slots + (size_t)(c - sa.chunk0) * kSlot;
-        // all LDS reads first, so that they are in flight together
-        f32x4 bt[NB];
-        OT kt[NB][4];
-#pragma unroll
-        for (int Rr = 0; Rr < NB; ++Rr) {
-            bt[Rr] = ld4f(&sm.beta[16 * Rr + 4 * q4]);  // rows past the chunk: k = v = beta = 0
-#pragma unroll
-            for (int i = 0; i < 4; ++i) kt[Rr][i] = sm.key.h.Kt[16 * Rr + 4 * q4 + i][jcol];
-        }
         F4 XW[NB], XU[NB];
 #pragma unroll
-        for (int Rr = 0; Rr < NB; ++Rr) {
-            f32x4 yw, yu;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                yw[i] = -bt[Rr][i] * (float)kt[Rr][i];
-                yu[i] = bt[Rr][i] * IN::one(rv[Rr][i]);
-            }
-            XW[Rr] = O::cvt(yw);
-            XU[Rr] = O::cvt(yu);
+        for (int I = 0; I < NB; ++I) {
+            XW[I] = O::lds(&sm.key.x.XWt[jcol][16 * I + 4 * q4]);
+            XU[I] = O::lds(&sm.key.x.XUt[jcol][16 * I + 4 * q4]);
         }
         // block (R, I) of T in the A-operand layout
         auto tblk = [&](int Rr, int I) {
             return I == Rr ? O::lds(&sm.Tb[Rr][m16][4 * q4]) : O::lds(&Tm[pair_id(Rr, I)][m16][4 * q4]);
         };
-        F4 ZW[NB], ZU[NB];
 #pragma unroll
         for (int Rr = 0; Rr < NB; ++Rr) {
             f32x4 aw = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int I = 0; I + 1 <= Rr; I += 2) {
                 const F8 t2 = O::cat2(tblk(Rr, I), tblk(Rr, I + 1));
-                aw = O::mma32(t2, O::cat2(XW[I], XW[I + 1]), aw);
+                aw = O::mma32(O::cat2(XW[I], XW[I + 1]), t2, aw);
                 au = O::mma32(t2, O::cat2(XU[I], XU[I + 1]), au);
             }
             if (!(Rr & 1)) {
                 const F4 tb = tblk(Rr, Rr);
-                aw = O::mma16(tb, XW[Rr], aw);
+                aw = O::mma16(XW[Rr], tb, aw);
                 au = O::mma16(tb, XU[Rr], au);
             }
-            ZW[Rr] = O::cvt(aw);
-            ZU[Rr] = O::cvt(au);
+            // U' in its accumulator layout; -W: lane (token m16, q4) holds
+            // channels 16 wave + 4 q4 .. +3, elements 4 (wave & 1) .. +3 of the
+            // fragment (tile Rr, K step wave / 2) of lane m16 + 16 q4
+            *reinterpret_cast<F4*>(slot + kUp + ((wave * 4 + Rr) * 64 + lane) * 8) = O::cvt(au);
+            *reinterpret_cast<F4*>(slot + kNegW + ((Rr * 4 + (wave >> 1)) * 64 + lane) * 16 + (wave & 1) * 8) =
+                O::cvt(aw);
         }
-        // U' straight to the slot (its accumulator layout); -W to LDS for the
-        // transposed store below
-#pragma unroll
-        for (int Rr = 0; Rr < NB; ++Rr) {
-            *reinterpret_cast<F4*>(slot + kUp + ((wave * 4 + Rr) * 64 + lane) * 8) = ZU[Rr];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sm.key.h.Wst[16 * Rr + 4 * q4 + i][jcol] = ZW[Rr][i];
-        }
-        if (more) load_v(csn, (int)min<int64_t>(C, seq_e - csn));
-        __syncthreads();
+        // (no barrier: the products wrote nothing to LDS, and what the copy
+        // reads was complete before the last one)
 
         // ---- the operand matrices in the A-operand layout, 16 bytes per lane
         // (every LDS read is issued before the first store, so that they are
         // in flight together)
-        h8 cw[2], cq[2], ck[2], cp;
+        h8 cq[2], ck[2], cp;
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             const int idx = tid + kThreads * k2;  // [t 4][s 4][lane 64]
             const int t = idx >> 8, s = (idx >> 6) & 3, l = idx & 63;
             const int row = 16 * t + (l & 15), col = 32 * s + 4 * (l >> 4);
-            cw[k2] = cat(*reinterpret_cast<const h4*>(&sm.key.h.Wst[row][col]),
-                         *reinterpret_cast<const h4*>(&sm.key.h.Wst[row][col + 16]));
-            cq[k2] = cat(*reinterpret_cast<const h4*>(&sm.key.h.Qt[row][col]),
-                         *reinterpret_cast<const h4*>(&sm.key.h.Qt[row][col + 16]));
+            cq[k2] = cat(*reinterpret_cast<const h4*>(&sm.key.x.Qt[row][col]),
+                         *reinterpret_cast<const h4*>(&sm.key.x.Qt[row][col + 16]));
         }
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
@@ -278,7 +255,6 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             const int idx = tid + kThreads * k2;
-            *reinterpret_cast<h8*>(slot + kNegW + idx * 16) = cw[k2];
             *reinterpret_cast<h8*>(slot + kQt + idx * 16) = cq[k2];
             *reinterpret_cast<h8*>(slot + kKbT + idx * 16) = ck[k2];
         }
