@@ -26,7 +26,7 @@
 //
 // The products are stored as float16 (their magnitudes are bounded by the
 // key, value and state magnitudes; entries that underflow are below 2^-24 of
-// the terms they multiply), which keeps the workspace at 72.5 KiB per chunk
+// the terms they multiply), which keeps the workspace at 70.5 KiB per chunk
 // and head. Chunks are processed in windows of up to `nwin` chunks per
 // sequence so that the workspace is bounded; between windows the state pass
 // carries the state through a float32 buffer in the workspace.
@@ -47,12 +47,13 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 constexpr int kNegW = 0;        // -W       [4][4][64][8] f16
 constexpr int kQt = 16384;      // Q~       [4][4][64][8] f16
 constexpr int kKbT = 32768;     // Kbar^T   [8][2][64][8] f16
-constexpr int kPm = 49152;      // P        [4][2][64][8] f16
-constexpr int kDma = 57344;     // the four matrices above: copied to LDS as one block
-constexpr int kUp = 57344;      // U' in the accumulator layout [8 j][4 t][64][4] f16:
+constexpr int kPm = 49152;      // P        [6][64][8] f16: the fragments (t, s) with 2s <= t, in the order
+                                // (0,0) (1,0) (2,0) (2,1) (3,0) (3,1); the two above the diagonal are zero
+constexpr int kDma = 55296;     // the four matrices above: copied to LDS as one block
+constexpr int kUp = 55296;      // U' in the accumulator layout [8 j][4 t][64][4] f16:
                                 // lane (n, q) of column tile j holds U'[16t + 4q + i][16j + n]
-constexpr int kDc = 73728;      // 2^b_C    [128] f32
-constexpr int kSlot = 74240;
+constexpr int kDc = 71680;      // 2^b_C    [128] f32
+constexpr int kSlot = 72192;
 constexpr int kStateWaves = 2;  // compute wavefronts of the state pass
 constexpr int kStateThreads = 64 * (kStateWaves + 1);  // + a loader wavefront
 constexpr int kStUp = kDma;     // offset of U' (2 KiB per 16-column tile) in an LDS stage
@@ -224,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
         // ---- the operand matrices in the A-operand layout, 16 bytes per lane
         // (every LDS read is issued before the first store, so that they are
         // in flight together)
-        h8 cq[2], ck[2], cp;
+        h8 cq[2], ck[2], cp = {};
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             const int idx = tid + kThreads * k2;  // [t 4][s 4][lane 64]
@@ -241,12 +242,12 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
             ck[k2] = cat(*reinterpret_cast<const h4*>(&sm.KbT[row][col]),
                          *reinterpret_cast<const h4*>(&sm.KbT[row][col + 16]));
         }
-        {
-            const int idx = tid;  // [t 4][s 2][lane 64]
-            const int t = idx >> 7, s = (idx >> 6) & 1, l = idx & 63;
+        if (tid < 6 * 64) {
+            const int i = tid >> 6, l = tid & 63;  // fragment i = (t, s) with 2s <= t
+            const int t = i < 2 ? i : 2 + (i - 2) / 2, s = i < 2 ? 0 : (i - 2) % 2;
             const int m = l & 15, cq4 = 4 * (l >> 4);
             const h4 zero = {(OT)0.f, (OT)0.f, (OT)0.f, (OT)0.f};
-            const h4 lo = (2 * s <= t) ? *reinterpret_cast<const h4*>(&sm.Pb[tri_id(t, 2 * s)][m][cq4]) : zero;
+            const h4 lo = *reinterpret_cast<const h4*>(&sm.Pb[tri_id(t, 2 * s)][m][cq4]);
             const h4 hi = (2 * s + 1 <= t) ? *reinterpret_cast<const h4*>(&sm.Pb[tri_id(t, 2 * s + 1)][m][cq4]) : zero;
             cp = cat(lo, hi);
         }
@@ -258,7 +259,7 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
             *reinterpret_cast<h8*>(slot + kQt + idx * 16) = cq[k2];
             *reinterpret_cast<h8*>(slot + kKbT + idx * 16) = ck[k2];
         }
-        *reinterpret_cast<h8*>(slot + kPm + tid * 16) = cp;
+        if (tid < 6 * 64) *reinterpret_cast<h8*>(slot + kPm + tid * 16) = cp;
         if (tid < D / 4) *reinterpret_cast<f32x4*>(slot + kDc + tid * 16) = cdc;
         // the next P0 writes only Gp and beta, which nothing above reads; its
         // barrier orders these LDS reads before P1 reuses the region
@@ -439,10 +440,7 @@ void state_kernel(SplitArgs sa)
                 }
             } else {
 #pragma unroll
-                for (int i = 0; i < 6; ++i) {
-                    const int t = i < 2 ? i : 2 + (i - 2) / 2, s2 = i < 2 ? 0 : (i - 2) % 2;  // (t, s) with 2s <= t
-                    ap[i] = pm[(t * 2 + s2) * 64 + lane];
-                }
+                for (int i = 0; i < 6; ++i) ap[i] = pm[i * 64 + lane];  // (t, s) with 2s <= t
             }
 #pragma unroll
             for (int t = 0; t < 4; ++t)

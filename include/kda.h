@@ -87,7 +87,7 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  *            per (sequence, head) carries the state through all chunks; no
  *            scratch). With BF16 inputs and a workspace, the two-pass form runs:
  *            the chunk-local products of every chunk are computed in parallel
- *            and stored in the workspace (72.5 KiB per chunk and head, float16),
+ *            and stored in the workspace (70.5 KiB per chunk and head, float16),
  *            then a sequential pass over the chunks carries the state. The
  *            chunks of each sequence are taken in windows of as many as the
  *            workspace holds; with more than one window a float32 state carry

@@ -12,6 +12,10 @@ from gated_delta_rule_02_amd import synth
 from oracle import reference as R
 from tests.gpu_util import TOL_BF16, TOL_F32, announce, dev, host64, relerr
 
+# workspace bytes of one chunk slot (one 64-token chunk of one (sequence, head));
+# a workspace of one slot per unit plus the float32 state carry forces one-chunk windows
+SLOT = K.kda_prefill_workspace_bytes(64, 1, 1)
+
 pytestmark = pytest.mark.gpu
 
 
@@ -204,8 +208,8 @@ def test_split_windows_match_one_window(lens):
     d = synth.core_inputs(rng, int(cu[-1]), H, bf16=True)
     s0 = synth.states(rng, N, H, std=0.2)
     U = N * H
-    small = torch.empty(U * 74240 + U * 128 * 128 * 4, dtype=torch.uint8, device="cuda")
-    big = torch.empty(U * 74240 * ((max(lens) + 63) // 64), dtype=torch.uint8, device="cuda")
+    small = torch.empty(U * SLOT + U * 128 * 128 * 4, dtype=torch.uint8, device="cuda")
+    big = torch.empty(U * SLOT * ((max(lens) + 63) // 64), dtype=torch.uint8, device="cuda")
     o1, s1 = gpu_prefill(d, cu=cu, s0=s0, workspace=small)
     o2, s2 = gpu_prefill(d, cu=cu, s0=s0, workspace=big)
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
@@ -302,8 +306,8 @@ def test_snapshots_across_windows_bit_equal():
     d = synth.core_inputs(rng, int(cu[-1]), H, bf16=True)
     s0 = synth.states(rng, N, H, std=0.2)
     U = N * H
-    small = torch.empty(U * 74240 + U * 128 * 128 * 4, dtype=torch.uint8, device="cuda")
-    big = torch.empty(U * 74240 * ((max(lens) + 63) // 64), dtype=torch.uint8, device="cuda")
+    small = torch.empty(U * SLOT + U * 128 * 128 * 4, dtype=torch.uint8, device="cuda")
+    big = torch.empty(U * SLOT * ((max(lens) + 63) // 64), dtype=torch.uint8, device="cuda")
     s1, s2 = snap_buffer(N, 5, H), snap_buffer(N, 5, H)
     gpu_prefill(d, cu=cu, s0=s0, workspace=small, snapshots=s1, interval=64)
     gpu_prefill(d, cu=cu, s0=s0, workspace=big, snapshots=s2, interval=64)
@@ -363,8 +367,8 @@ def test_wide_state_pass_windows_and_snapshots():
     d = synth.core_inputs(rng, int(cu[-1]), H, bf16=True)
     s0 = synth.states(rng, N, H, std=0.2)
     U = N * H
-    small = torch.empty(U * 74240 + U * 128 * 128 * 4, dtype=torch.uint8, device="cuda")
-    big = torch.empty(U * 74240 * ((max(lens) + 63) // 64), dtype=torch.uint8, device="cuda")
+    small = torch.empty(U * SLOT + U * 128 * 128 * 4, dtype=torch.uint8, device="cuda")
+    big = torch.empty(U * SLOT * ((max(lens) + 63) // 64), dtype=torch.uint8, device="cuda")
     n1, n2 = snap_buffer(N, 4, H), snap_buffer(N, 4, H)
     o1, s1 = gpu_prefill(d, cu=cu, s0=s0, workspace=small, snapshots=n1, interval=64)
     o2, s2 = gpu_prefill(d, cu=cu, s0=s0, workspace=big, snapshots=n2, interval=64)
