@@ -61,9 +61,24 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
+def settle(torch, fn, seconds=0.25):
+    """Untimed calls for about `seconds` of wall time. The GPU raises its
+    clocks only after some milliseconds of sustained load (the first calls
+    of a fresh process ran about 13% slower than later ones), so every
+    measurement starts from the steady state rather than from the ramp."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+
+
 def timed(torch, fn, steps, warmup):
-    """Average ms per call over `steps` calls after `warmup` untimed ones."""
+    """Average ms per call over `steps` calls after a settling period and
+    `warmup` untimed calls."""
     stream = torch.cuda.current_stream()
+    settle(torch, fn)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -317,7 +332,7 @@ def main():
                        "global_batch": 1, "seq_len": T, "heads": 64, "head_dim": 128, "chunk": 64},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                         "kernel": "kda_prefill call (two-pass form: intra_kernel + state_kernel per window of 24 chunks, 3 windows)",
+                         "kernel": "kda_prefill call (two-pass form: intra_kernel + state_kernel per window, 2 windows of 32 chunks)",
                          "algorithmic_bytes_per_launch": PREFILL_BYTES_PER_TOKEN * T,
                          "mfma_tflops": PREFILL_FLOPS_PER_TOKEN * T / (ms * 1e-3) / 1e12,
                          "mfma_frac_of_bf16_peak": PREFILL_FLOPS_PER_TOKEN * T / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},

@@ -366,7 +366,7 @@ int kda_output_norm_gate_fp8(const void* o, kda_dtype o_dtype, const void* gate,
 // ---------------------------------------------------------------- prefill
 namespace {
 constexpr int64_t kChunk = 64;          // chunk of the bfloat16 forms
-constexpr int64_t kWindowChunks = 24;   // recommended window of the two-pass form (measured best of 8..64)
+constexpr int64_t kWindowChunks = 32;   // recommended window of the two-pass form (measured best of 16..48)
 size_t state_carry_bytes(int64_t units) { return (size_t)units * 128 * 128 * sizeof(float); }
 }  // namespace
 

@@ -549,8 +549,11 @@ struct Front {
             const float* kl = &sm.key.f.KL[16 * Rr + m16][c];
             const float* ql = &sm.key.f.QL[16 * Rr + m16][c];
             const float* ks = &sm.key.f.KS[16 * I + m16][c];
-            const F8 b = O::cat2(O::cvt(ld4f(ks) * ld4f(&sm.Fo[pid][c])),
-                                 O::cvt(ld4f(ks + 16) * ld4f(&sm.Fo[pid][c + 16])));
+            // adjacent blocks (I = Rr - 1) have no block between them: their
+            // factor 2^(rho_Rr - rho_{I+1}) is exactly 1
+            const F8 b = I + 1 == Rr ? O::cat2(O::cvt(ld4f(ks)), O::cvt(ld4f(ks + 16)))
+                                     : O::cat2(O::cvt(ld4f(ks) * ld4f(&sm.Fo[pid][c])),
+                                               O::cvt(ld4f(ks + 16) * ld4f(&sm.Fo[pid][c + 16])));
             if (DoA) accA = O::mma32(O::cat2(O::cvt(ld4f(kl)), O::cvt(ld4f(kl + 16))), b, accA);
             if (DoP) accP = O::mma32(O::cat2(O::cvt(ld4f(ql)), O::cvt(ld4f(ql + 16))), b, accP);
             __builtin_amdgcn_sched_barrier(0);

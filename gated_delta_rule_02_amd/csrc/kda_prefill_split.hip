@@ -552,8 +552,16 @@ hipError_t launch_prefill_split(const PrefillArgs& a, void* ws, size_t ws_bytes,
         sa.nwin = (int)max_chunks;
     } else {
         const size_t carry = (size_t)U * D * D * sizeof(float);
-        sa.nwin = (int)std::min<int64_t>(max_chunks, (int64_t)((ws_bytes - carry) / ((size_t)U * kSlot)));
-        sa.carry = reinterpret_cast<float*>(sa.ws + (size_t)U * sa.nwin * kSlot);
+        const int64_t most = std::min<int64_t>(max_chunks, (int64_t)((ws_bytes - carry) / ((size_t)U * kSlot)));
+        // as few windows as the workspace allows, about equal in size (a short
+        // last window leaves much of the GPU idle), rounded up to a multiple
+        // of the intra-pass workgroups per unit (below) so that they all take
+        // the same number of chunks
+        const int64_t windows = (max_chunks + most - 1) / most;
+        const int64_t grp = std::max<int64_t>(1, std::min<int64_t>(most, (256 + U - 1) / U));
+        const int64_t even = (max_chunks + windows - 1) / windows;
+        sa.nwin = (int)std::min<int64_t>(most, (even + grp - 1) / grp * grp);
+        sa.carry = reinterpret_cast<float*>(sa.ws + (size_t)U * most * kSlot);
     }
     // about one intra-pass workgroup per compute unit, each taking every
     // groups-th chunk of the window with its next chunk prefetched

@@ -95,7 +95,7 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  *            minimum is one chunk slot per (sequence, head) plus that carry
  *            (or a slot for every chunk, if smaller); less returns
  *            KDA_ERR_WORKSPACE. kda_prefill_workspace_bytes() gives the
- *            recommended size (windows of 24 chunks; 0 for F32 inputs, which
+ *            recommended size (windows of up to 32 chunks; 0 for F32 inputs, which
  *            always run the single-pass form and ignore the workspace). The
  *            contents need no initialisation and are garbage afterwards; calls
  *            that share a workspace must be ordered on one stream.

@@ -220,7 +220,7 @@ def test_split_windows_match_one_window(lens):
 def test_varlen_workload_full_size_sampled():
     """Packed varlen workload at full size: 8 sequences (123,444 tokens, up to
     447 chunks each), H = 64, bf16 inputs, random fp32 initial states, final
-    states returned; default two-pass form with 24-chunk windows. The GPU runs
+    states returned; default two-pass form with windows of up to 32 chunks. The GPU runs
     every head; the oracle checks heads 0 and 41 of every sequence (o and
     final state), and every other head's final state must be finite."""
     announce("prefill varlen full size (sampled heads)")
@@ -319,7 +319,7 @@ def test_snapshots_across_windows_bit_equal():
 
 def test_snapshots_prefill_workload_full_size_sampled():
     """The prefill workload (T = 4096, H = 64) with a snapshot every 1024
-    tokens, as bench.py launches it (two-pass form, 24-chunk windows): the
+    tokens, as bench.py launches it (two-pass form, two 32-chunk windows): the
     oracle checks heads 0 and 41 at every snapshot."""
     announce("prefill snapshots full size")
     d = synth.workload_prefill()
