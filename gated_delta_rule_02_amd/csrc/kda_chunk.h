@@ -66,11 +66,21 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef __bf16 b4 __attribute__((ext_vector_type(4)));
 typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 template <typename T> struct Io;
+// Loads take a cache policy: kStream (the non-temporal hint) for data that is
+// read or written exactly once, so that it does not displace data still to be
+// reused from the caches. In the two-pass prefill the inputs are streamed in
+// and the outputs streamed out, which keeps the last-level cache for the
+// workspace that the state pass reads back: with the caches flushed before
+// each call (512 MiB written) the call ran 0.278 ms with ordinary accesses
+// and 0.212 ms with these hints (0.204 and 0.206 ms without the flush).
+constexpr int kStream = 2;
 template <> struct Io<bf16_t> {
     using pair_t = uint32_t;
-    __device__ static pair_t ld_pair(rsrc_t r, int off, int soff) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0); }
+    template <int Pol = 0>
+    __device__ static pair_t ld_pair(rsrc_t r, int off, int soff) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, Pol); }
     __device__ static f32x2 unpack(pair_t u) { return f32x2{__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u)}; }
-    __device__ static uint32_t ld_one(rsrc_t r, int off, int soff) { return __builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0); }
+    template <int Pol = 0>
+    __device__ static uint32_t ld_one(rsrc_t r, int off, int soff) { return __builtin_amdgcn_raw_buffer_load_b16(r, off, soff, Pol); }
     __device__ static float one(uint32_t u) { return __uint_as_float(u << 16); }
     __device__ static void st(rsrc_t r, int off, int soff, float v)
     {
@@ -79,13 +89,15 @@ template <> struct Io<bf16_t> {
 };
 template <> struct Io<float> {
     using pair_t = uint2;
+    template <int Pol = 0>
     __device__ static pair_t ld_pair(rsrc_t r, int off, int soff)
     {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, Pol);
         return make_uint2(v[0], v[1]);
     }
     __device__ static f32x2 unpack(pair_t u) { return f32x2{__uint_as_float(u.x), __uint_as_float(u.y)}; }
-    __device__ static uint32_t ld_one(rsrc_t r, int off, int soff) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0); }
+    template <int Pol = 0>
+    __device__ static uint32_t ld_one(rsrc_t r, int off, int soff) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, Pol); }
     __device__ static float one(uint32_t u) { return __uint_as_float(u); }
     __device__ static void st(rsrc_t r, int off, int soff, float v)
     {
@@ -224,6 +236,12 @@ template <> struct Ops<true> {
     }
 };
 
+// Row stride of the 16 x 16 blocks: four elements of padding, so that the
+// A-layout reads (lane m reads four or eight bytes of row m) of a wavefront's
+// 16 rows fall in distinct LDS banks (with a stride of 16 every fourth row
+// shares a bank, a four-way conflict).
+constexpr int BLD = 20;
+
 // index of the off-diagonal block pair (R, I), I < R
 __host__ __device__ constexpr int pair_id(int R, int I) { return R * (R - 1) / 2 + I; }
 // index of the lower-triangle block (R, I), I <= R
@@ -239,10 +257,10 @@ struct __attribute__((aligned(16))) Smem {
     static constexpr int LDK = D + 4;               // row stride of the float32 [C][128] arrays
     static constexpr int LDH = D + Ops<F32P>::PAD;  // row stride of the operand-type [C][128] arrays
     static constexpr int LDT = C + Ops<F32P>::PAD;  // row stride of [128][C]
-    OT Nd[NB][16][16];                      // -A diagonal blocks (strictly lower, beta-scaled)
-    OT Tb[NB][16][16];                      // (I + A_RR)^-1
-    OT An[NPAIR > 0 ? NPAIR : 1][16][16];   // -A off-diagonal blocks (beta-scaled)
-    OT Pb[NB * (NB + 1) / 2][16][16];       // P lower-triangle blocks
+    OT Nd[NB][16][BLD];                     // -A diagonal blocks (strictly lower, beta-scaled)
+    OT Tb[NB][16][BLD];                     // (I + A_RR)^-1
+    OT An[NPAIR > 0 ? NPAIR : 1][16][BLD];  // -A off-diagonal blocks (beta-scaled)
+    OT Pb[NB * (NB + 1) / 2][16][BLD];      // P lower-triangle blocks
     float Fd[NB][D];                        // 2^-G_R
     float Fo[NPAIR > 0 ? NPAIR : 1][D];     // 2^(rho_R - rho_{I+1})
     float Gp[NB][NQ][D];                    // row-group sums of the log-retention (base 2)
@@ -338,6 +356,7 @@ struct Front {
     __device__ __forceinline__ void load(int64_t c_s, int nt, const TIN* vg = nullptr)
     {
         const int64_t bytes = (int64_t)nt * ts * ES;
+        constexpr int Pol = Lean ? kStream : 0;  // the two-pass intra pass reads its inputs once
         if (prod) {
             const int voff = (c0 + h * D) * ES;  // per lane
             if constexpr (Parts & 1) {
@@ -345,24 +364,24 @@ struct Front {
 #pragma unroll
                 for (int t = 0; t < RP; ++t) {
                     const int soff = (rbase + t) * ts * ES;  // wave-uniform row term
-                    rg[t] = IN::ld_pair(rg_, voff, soff);
-                    rk[t] = IN::ld_pair(rk_, voff, soff);
+                    rg[t] = IN::template ld_pair<Pol>(rg_, voff, soff);
+                    rk[t] = IN::template ld_pair<Pol>(rk_, voff, soff);
                 }
             }
             if constexpr (Parts & 2) {
                 const rsrc_t rq_ = make_rsrc(qg + c_s * ts, bytes);
 #pragma unroll
-                for (int t = 0; t < RP; ++t) rq[t] = IN::ld_pair(rq_, voff, (rbase + t) * ts * ES);
+                for (int t = 0; t < RP; ++t) rq[t] = IN::template ld_pair<Pol>(rq_, voff, (rbase + t) * ts * ES);
             }
             if constexpr (Lean && (Parts & 4)) {
                 const rsrc_t rv_ = make_rsrc(vg + c_s * ts, bytes);
 #pragma unroll
-                for (int t = 0; t < RP; ++t) rvv[t] = IN::ld_pair(rv_, voff, (rbase + t) * ts * ES);
+                for (int t = 0; t < RP; ++t) rvv[t] = IN::template ld_pair<Pol>(rv_, voff, (rbase + t) * ts * ES);
             }
         }
         if constexpr (Parts & 1) {
             const rsrc_t rb_ = make_rsrc(bg + c_s * H, (int64_t)nt * H * ES);  // uniform: built outside the branch
-            if (tid < C) rb = IN::ld_one(rb_, (tid * H + h) * ES, 0);
+            if (tid < C) rb = IN::template ld_one<Pol>(rb_, (tid * H + h) * ES, 0);
         }
     }
 

@@ -89,7 +89,7 @@ __device__ __forceinline__ void seq_bounds(const PrefillArgs& a, int n, int64_t&
 // accumulator layout of the product that made them); Tm receives them row
 // major, the A-operand layout of the products with T.
 template <int I, typename SM>
-__device__ __forceinline__ void inverse_column(SM& sm, _Float16 (*Tm)[16][16], int m16, int q4)
+__device__ __forceinline__ void inverse_column(SM& sm, _Float16 (*Tm)[16][BLD], int m16, int q4)
 {
     using O = Ops<false>;
     using F4 = typename O::F4;
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
     static_assert(C == 64 && NB == 4, "slot layout assumes 64-token chunks");
 
     __shared__ SM sm;
-    __shared__ __attribute__((aligned(16))) _Float16 Tm[SM::NPAIR][16][16];  // T = (I + A)^-1 below the diagonal
+    __shared__ __attribute__((aligned(16))) _Float16 Tm[SM::NPAIR][16][BLD];  // T = (I + A)^-1 below the diagonal
     const PrefillArgs& a = sa.p;
 
     const int tid = threadIdx.x;
@@ -130,7 +130,6 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
     const int lane = tid & 63;
     const int m16 = lane & 15;
     const int q4 = lane >> 4;
-    const int jcol = 16 * wave + m16;  // this lane's column of the K~ and V tiles
 
     const int grp = blockIdx.x % sa.groups;
     const int u = blockIdx.x / sa.groups;  // n * H + h
@@ -179,20 +178,26 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
         if (more) fr.template load<4>(csn, ntn, vg);
         __syncthreads();
 
-        // ---- -W and U' as products with T, one K~ tile and one V tile per
-        // wavefront: Z_R = sum_{I<=R} T_RI X_I (independent block rows). The
-        // right-hand sides come transposed from P2b, so that a lane reads the
-        // four tokens of its channel that it holds as an operand at once. U'
-        // is formed as T X (its accumulator layout is the slot's), -W as
-        // (T X)^T = X^T T^T: the same registers with the operands swapped,
-        // which leaves four consecutive channels of one token per lane, half
-        // of a slot fragment, stored straight to the slot.
+        // ---- -W and U' as products with T: Z_R = sum_{I<=R} T_RI X_I
+        // (independent block rows). The right-hand sides come transposed from
+        // P2b, so that a lane reads the four tokens of its channel that it
+        // holds as an operand at once. U' is formed as T X (its accumulator
+        // layout is the slot's), -W as (T X)^T = X^T T^T: the same registers
+        // with the operands swapped, which leaves four consecutive channels of
+        // one token per lane, stored straight to the slot.
         uint8_t* slot = slots + (size_t)(c - sa.chunk0) * kSlot;
-        F4 XW[NB], XU[NB];
+        // wavefront 2p forms -W for the tiles 2p, 2p + 1 (so that each lane
+        // holds the whole 16-byte slot fragment: channels 32p + 4q4 .. +3 and
+        // 32p + 16 + 4q4 .. +3 of one token), wavefront 2p + 1 forms U' for
+        // the same two tiles
+        const bool isW = !(wave & 1);
+        const int col0 = 32 * (wave >> 1) + m16;  // this lane's column of the first tile
+        const OT(*X)[SM::LDT] = isW ? sm.key.x.XWt : sm.key.x.XUt;
+        F4 X0[NB], X1[NB];
 #pragma unroll
         for (int I = 0; I < NB; ++I) {
-            XW[I] = O::lds(&sm.key.x.XWt[jcol][16 * I + 4 * q4]);
-            XU[I] = O::lds(&sm.key.x.XUt[jcol][16 * I + 4 * q4]);
+            X0[I] = O::lds(&X[col0][16 * I + 4 * q4]);
+            X1[I] = O::lds(&X[col0 + 16][16 * I + 4 * q4]);
         }
         // block (R, I) of T in the A-operand layout
         auto tblk = [&](int Rr, int I) {
@@ -200,24 +205,38 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
         };
 #pragma unroll
         for (int Rr = 0; Rr < NB; ++Rr) {
-            f32x4 aw = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
+            f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+            if (isW) {
 #pragma unroll
-            for (int I = 0; I + 1 <= Rr; I += 2) {
-                const F8 t2 = O::cat2(tblk(Rr, I), tblk(Rr, I + 1));
-                aw = O::mma32(O::cat2(XW[I], XW[I + 1]), t2, aw);
-                au = O::mma32(t2, O::cat2(XU[I], XU[I + 1]), au);
+                for (int I = 0; I + 1 <= Rr; I += 2) {
+                    const F8 t2 = O::cat2(tblk(Rr, I), tblk(Rr, I + 1));
+                    a0 = O::mma32(O::cat2(X0[I], X0[I + 1]), t2, a0);
+                    a1 = O::mma32(O::cat2(X1[I], X1[I + 1]), t2, a1);
+                }
+                if (!(Rr & 1)) {
+                    const F4 tb = tblk(Rr, Rr);
+                    a0 = O::mma16(X0[Rr], tb, a0);
+                    a1 = O::mma16(X1[Rr], tb, a1);
+                }
+                // lane (token m16, q4) holds the fragment (tile Rr, K step p) of lane m16 + 16 q4
+                *reinterpret_cast<F8*>(slot + kNegW + ((Rr * 4 + (wave >> 1)) * 64 + lane) * 16) =
+                    O::cat2(O::cvt(a0), O::cvt(a1));
+            } else {
+#pragma unroll
+                for (int I = 0; I + 1 <= Rr; I += 2) {
+                    const F8 t2 = O::cat2(tblk(Rr, I), tblk(Rr, I + 1));
+                    a0 = O::mma32(t2, O::cat2(X0[I], X0[I + 1]), a0);
+                    a1 = O::mma32(t2, O::cat2(X1[I], X1[I + 1]), a1);
+                }
+                if (!(Rr & 1)) {
+                    const F4 tb = tblk(Rr, Rr);
+                    a0 = O::mma16(tb, X0[Rr], a0);
+                    a1 = O::mma16(tb, X1[Rr], a1);
+                }
+                // U' in its accumulator layout, tiles 2p and 2p + 1
+                *reinterpret_cast<F4*>(slot + kUp + (((wave - 1) * 4 + Rr) * 64 + lane) * 8) = O::cvt(a0);
+                *reinterpret_cast<F4*>(slot + kUp + ((wave * 4 + Rr) * 64 + lane) * 8) = O::cvt(a1);
             }
-            if (!(Rr & 1)) {
-                const F4 tb = tblk(Rr, Rr);
-                aw = O::mma16(XW[Rr], tb, aw);
-                au = O::mma16(tb, XU[Rr], au);
-            }
-            // U' in its accumulator layout; -W: lane (token m16, q4) holds
-            // channels 16 wave + 4 q4 .. +3, elements 4 (wave & 1) .. +3 of the
-            // fragment (tile Rr, K step wave / 2) of lane m16 + 16 q4
-            *reinterpret_cast<F4*>(slot + kUp + ((wave * 4 + Rr) * 64 + lane) * 8) = O::cvt(au);
-            *reinterpret_cast<F4*>(slot + kNegW + ((Rr * 4 + (wave >> 1)) * 64 + lane) * 16 + (wave & 1) * 8) =
-                O::cvt(aw);
         }
         // (no barrier: the products wrote nothing to LDS, and what the copy
         // reads was complete before the last one)
@@ -500,10 +519,11 @@ void state_kernel(SplitArgs sa)
             for (int t = 0; t < 4; ++t) {
                 const f32x4 v = a.scale * Ot[p][t];
                 if constexpr (sizeof(TOUT) == 4) {
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), ro_, voff, 16 * t * ts * 4, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), ro_, voff, 16 * t * ts * 4,
+                                                           kStream);
                 } else {
                     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, to_b4(v)), ro_, voff,
-                                                          16 * t * ts * 2, 0);
+                                                          16 * t * ts * 2, kStream);
                 }
             }
         }
