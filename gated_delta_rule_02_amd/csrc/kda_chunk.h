@@ -68,11 +68,13 @@ typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 template <typename T> struct Io;
 // Loads take a cache policy: kStream (the non-temporal hint) for data that is
 // read or written exactly once, so that it does not displace data still to be
-// reused from the caches. In the two-pass prefill the inputs are streamed in
-// and the outputs streamed out, which keeps the last-level cache for the
-// workspace that the state pass reads back: with the caches flushed before
-// each call (512 MiB written) the call ran 0.278 ms with ordinary accesses
-// and 0.212 ms with these hints (0.204 and 0.206 ms without the flush).
+// reused from the caches. The two-pass prefill streams its inputs in and its
+// outputs out when a window's workspace fits the last-level cache, which then
+// keeps that workspace for the state pass: with the caches flushed before each
+// call (512 MiB written) the 4096-token call ran 0.278 ms with ordinary
+// accesses and 0.212 ms with these hints (0.204 and 0.206 ms without the
+// flush). When the workspace is far larger than the cache the hints only cost
+// (the packed varlen workload: 7.12 ms against 7.35 ms).
 constexpr int kStream = 2;
 template <> struct Io<bf16_t> {
     using pair_t = uint32_t;
@@ -307,7 +309,7 @@ struct __attribute__((aligned(16))) Smem {
 // the off-diagonal pairs split evenly over the SIMDs. The producers also load
 // v and, in P2b, stage the right-hand sides -diag(beta)(K o 2^B) and
 // diag(beta) V of the products with T, transposed and rounded once.
-template <bool F32P, typename TIN, int NQ = 2, bool Lean = false>
+template <bool F32P, typename TIN, int NQ = 2, bool Lean = false, int LoadPol = 0>
 struct Front {
     using O = Ops<F32P>;
     using OT = typename O::OT;
@@ -356,7 +358,7 @@ struct Front {
     __device__ __forceinline__ void load(int64_t c_s, int nt, const TIN* vg = nullptr)
     {
         const int64_t bytes = (int64_t)nt * ts * ES;
-        constexpr int Pol = Lean ? kStream : 0;  // the two-pass intra pass reads its inputs once
+        constexpr int Pol = LoadPol;  // cache policy of the input loads
         if (prod) {
             const int voff = (c0 + h * D) * ES;  // per lane
             if constexpr (Parts & 1) {

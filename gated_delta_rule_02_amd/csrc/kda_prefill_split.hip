@@ -109,7 +109,8 @@ __device__ __forceinline__ void inverse_column(SM& sm, _Float16 (*Tm)[16][BLD], 
     }
 }
 
-template <typename TIN>
+// POL: cache policy of the input loads (0 or kStream)
+template <typename TIN, int POL>
 __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
 {
     using O = Ops<false>;
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
     const TIN* vg = static_cast<const TIN*>(a.v);
     uint8_t* slots = sa.ws + (size_t)u * sa.nwin * kSlot;
 
-    Front<false, TIN, 2, true> fr(sm, a, h);
+    Front<false, TIN, 2, true, POL> fr(sm, a, h);
     {
         const int64_t cs = seq_s + c_first * C;
         fr.load(cs, (int)min<int64_t>(C, seq_e - cs), vg);
@@ -301,7 +302,8 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
 // product, and the stored A-operand layouts of Q~ and P serve as B operands.
 // The result then holds four consecutive output columns of one token per lane
 // (16-byte stores) instead of four tokens of one column.
-template <typename TOUT, int TPW>
+// POL: cache policy of the output stores (0 or kStream)
+template <typename TOUT, int TPW, int POL>
 __global__ __launch_bounds__(kStateThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void state_kernel(SplitArgs sa)
 {
@@ -520,10 +522,10 @@ void state_kernel(SplitArgs sa)
                 const f32x4 v = a.scale * Ot[p][t];
                 if constexpr (sizeof(TOUT) == 4) {
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), ro_, voff, 16 * t * ts * 4,
-                                                           kStream);
+                                                           POL);
                 } else {
                     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, to_b4(v)), ro_, voff,
-                                                          16 * t * ts * 2, kStream);
+                                                          16 * t * ts * 2, POL);
                 }
             }
         }
@@ -548,12 +550,19 @@ void state_kernel(SplitArgs sa)
 }
 
 template <typename TOUT, int TPW>
-void launch_state(const SplitArgs& sa, int64_t U, hipStream_t s)
+void launch_state(const SplitArgs& sa, int64_t U, bool stream, hipStream_t s)
 {
     constexpr int kColGroups = D / (16 * kStateWaves * TPW);
     const dim3 gs((unsigned)(kColGroups * 8 * ((U + 7) / 8))), bs(kStateThreads);
-    hipLaunchKernelGGL((state_kernel<TOUT, TPW>), gs, bs, 0, s, sa);
+    if (stream)
+        hipLaunchKernelGGL((state_kernel<TOUT, TPW, kStream>), gs, bs, 0, s, sa);
+    else
+        hipLaunchKernelGGL((state_kernel<TOUT, TPW, 0>), gs, bs, 0, s, sa);
 }
+
+// A window's workspace up to this size is left to the last-level cache (256
+// MiB): the inputs and outputs then go around it (non-temporal hints).
+constexpr size_t kStreamWorkspace = (size_t)192 << 20;
 
 }  // namespace
 
@@ -591,13 +600,19 @@ hipError_t launch_prefill_split(const PrefillArgs& a, void* ws, size_t ws_bytes,
     // all fit on the chip at once (one per compute unit), else 2 of 64 columns
     // (each wavefront then carries two tiles through every operand read)
     const bool narrow = U * 4 <= 256;
+    const bool stream = (size_t)U * sa.nwin * kSlot <= kStreamWorkspace;
     for (int64_t c0 = 0; c0 < std::max<int64_t>(max_chunks, 1); c0 += sa.nwin) {
         sa.chunk0 = c0;
-        if (max_chunks > 0) hipLaunchKernelGGL(intra_kernel<bf16_t>, gi, bi, 0, s, sa);
+        if (max_chunks > 0) {
+            if (stream)
+                hipLaunchKernelGGL((intra_kernel<bf16_t, kStream>), gi, bi, 0, s, sa);
+            else
+                hipLaunchKernelGGL((intra_kernel<bf16_t, 0>), gi, bi, 0, s, sa);
+        }
         if (a.out_dtype == F32)
-            narrow ? launch_state<float, 1>(sa, U, s) : launch_state<float, 2>(sa, U, s);
+            narrow ? launch_state<float, 1>(sa, U, stream, s) : launch_state<float, 2>(sa, U, stream, s);
         else
-            narrow ? launch_state<bf16_t, 1>(sa, U, s) : launch_state<bf16_t, 2>(sa, U, s);
+            narrow ? launch_state<bf16_t, 1>(sa, U, stream, s) : launch_state<bf16_t, 2>(sa, U, stream, s);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
