@@ -506,7 +506,7 @@ struct Front {
             const f32x4 x1 = ld4f(ks + 16) * ld4f(&sm.Fd[Rd][c + 16]);
             accA = O::diagA(ld4f(kl), ld4f(kl + 16), x0, x1, accA);
             accP = O::diagP(ld4f(ql), ld4f(ql + 16), x0, x1, accP);
-            __builtin_amdgcn_sched_barrier(0);  // one K step at a time (register pressure)
+            if constexpr (!Lean) __builtin_amdgcn_sched_barrier(0);  // one K step at a time (register pressure)
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -577,7 +577,7 @@ struct Front {
                                                O::cvt(ld4f(ks + 16) * ld4f(&sm.Fo[pid][c + 16])));
             if (DoA) accA = O::mma32(O::cat2(O::cvt(ld4f(kl)), O::cvt(ld4f(kl + 16))), b, accA);
             if (DoP) accP = O::mma32(O::cat2(O::cvt(ld4f(ql)), O::cvt(ld4f(ql + 16))), b, accP);
-            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (!Lean) __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {

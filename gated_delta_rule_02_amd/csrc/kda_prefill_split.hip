@@ -283,6 +283,7 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
         if (tid < D / 4) *reinterpret_cast<f32x4*>(slot + kDc + tid * 16) = cdc;
         // the next P0 writes only Gp and beta, which nothing above reads; its
         // barrier orders these LDS reads before P1 reuses the region
+
     }
 }
 
