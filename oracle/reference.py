@@ -229,6 +229,44 @@ def kda_chunked_segment_map(k, g, beta, lower_bound=-5.0):
 
 
 # --------------------------------------------------------------------------
+# Affine segment maps -- the state after a stretch of tokens is an affine
+# function of the state before it ([flozi-KDA]: the per-token update is
+# linear in the state, S_t = A_t S_{t-1} + beta_t k_t v_t^T with
+# A_t = (I - beta_t k_t k_t^T) Diag(alpha_t)), which is what lets a long
+# sequence be cut into segments processed apart and stitched together
+# --------------------------------------------------------------------------
+def kda_segment_maps(k, v, g, beta, cu_seqlens=None, lower_bound=-5.0, nthreads=None):
+    """Affine map of each segment (a sequence of ``cu_seqlens``) on the state:
+    S_out = M S_in + N, with M = A_T ... A_1 (dk x dk) and N the state after the
+    segment from a zero state (dk x dv).
+
+    Written out from the definition with the serial recurrence: N is its final
+    state from S_in = 0; with v = 0 the update is S_t = A_t S_{t-1}, so its final
+    state from S_in = I (dk x dk) is the product M. Needs dk == dv for the
+    identity start. Returns (M [N, H, dk, dk], N [N, H, dk, dv]) in float64.
+    """
+    q = np.zeros_like(np.asarray(k, dtype=np.float64))
+    T, H, dk = q.shape
+    dv = np.asarray(v).shape[2]
+    assert dk == dv, "identity start state needs dk == dv"
+    cu = np.array([0, T], dtype=np.int64) if cu_seqlens is None else np.asarray(cu_seqlens, dtype=np.int64)
+    nseq = cu.shape[0] - 1
+    _, Nmap = kda_serial(q, k, v, g, beta, cu_seqlens=cu, lower_bound=lower_bound, nthreads=nthreads)
+    eye = np.broadcast_to(np.eye(dk), (nseq, H, dk, dk)).copy()
+    _, Mmap = kda_serial(q, k, np.zeros_like(np.asarray(v, dtype=np.float64)), g, beta, cu_seqlens=cu,
+                         initial_state=eye, lower_bound=lower_bound, nthreads=nthreads)
+    return Mmap, Nmap
+
+
+def affine_apply(M, X, N=None):
+    """Y = M X (+ N) over leading batch dimensions: the map (M, N) applied to a
+    state X, or, with X the M of an earlier map, the first half of composing
+    two maps: (M2, N2) after (M1, N1) is (M2 M1, M2 N1 + N2)."""
+    Y = np.matmul(np.asarray(M, dtype=np.float64), np.asarray(X, dtype=np.float64))
+    return Y if N is None else Y + np.asarray(N, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
 # Prologue / epilogue pieces (numpy float64)
 # --------------------------------------------------------------------------
 def round_bf16(x):

@@ -559,3 +559,86 @@ def test_quantize_fp8_groups():
             # half a code step: 2^-4 relative for normals, 2^-10 x scale for subnormals
             err = np.abs(deq[t, gsl] - y[t, gsl])
             assert np.all(err <= np.maximum(2.0 ** -4 * np.abs(y[t, gsl]), 2.0 ** -10 * scale[t, gidx]) * (1 + 1e-12))
+
+
+# ------------------------------------------------- affine segment maps (sequence-parallel prefill)
+def _explicit_map(k, v, g, beta, lb=-5.0):
+    """M = A_T ... A_1 and N by an explicit matrix loop over one (segment, head):
+    A_t = (I - beta_t k_t k_t^T) Diag(exp(max(g_t, lb))), N_t = A_t N_{t-1} + beta_t k_t v_t^T."""
+    k, v, g, beta = (np.asarray(x, dtype=np.float64) for x in (k, v, g, beta))
+    T, dk = k.shape
+    M = np.eye(dk)
+    N = np.zeros((dk, v.shape[1]))
+    for t in range(T):
+        A = (np.eye(dk) - beta[t] * np.outer(k[t], k[t])) @ np.diag(np.exp(np.maximum(g[t], lb)))
+        M = A @ M
+        N = A @ N + beta[t] * np.outer(k[t], v[t])
+    return M, N
+
+
+def test_segment_map_is_the_product_of_token_maps():
+    """The oracle's segment maps (serial runs from I with v = 0, and from 0)
+    equal the explicit ordered product of the per-token affine maps, for
+    segments of a packed batch (one empty) and two heads."""
+    rng = np.random.default_rng(301)
+    cu = np.array([0, 5, 5, 12, 13])
+    q, k, v, g, beta = rand_core(rng, int(cu[-1]), 2, 6, 6)
+    g[3, 1, 2] = -9.0  # below the clamp
+    M, N = R.kda_segment_maps(k, v, g, beta, cu_seqlens=cu)
+    for n in range(len(cu) - 1):
+        sl = slice(cu[n], cu[n + 1])
+        for h in range(2):
+            Me, Ne = _explicit_map(k[sl, h], v[sl, h], g[sl, h], beta[sl, h])
+            assert np.max(np.abs(M[n, h] - Me)) < 1e-12
+            assert np.max(np.abs(N[n, h] - Ne)) < 1e-12
+    assert np.array_equal(M[1], np.broadcast_to(np.eye(6), (2, 6, 6)))  # empty segment: identity map
+    assert np.all(N[1] == 0)
+
+
+def test_segment_map_is_affine_in_the_state():
+    """For any start state the serial run ends in M S0 + N (P7)."""
+    rng = np.random.default_rng(302)
+    q, k, v, g, beta = rand_core(rng, 40, 2, 8, 8)
+    M, N = R.kda_segment_maps(k, v, g, beta)
+    S0 = rng.standard_normal((1, 2, 8, 8))
+    _, S = R.kda_serial(q, k, v, g, beta, initial_state=S0)
+    assert relerr(R.affine_apply(M, S0, N), S) < 1e-12
+
+
+def test_segment_maps_compose_to_the_whole():
+    """Cutting a sequence at a: the map of the whole is (M2 M1, M2 N1 + N2), and
+    running the second part from M1 S0 + N1 gives the tail of the whole run's
+    outputs and its final state."""
+    rng = np.random.default_rng(303)
+    T, a = 50, 21
+    q, k, v, g, beta = rand_core(rng, T, 3, 8, 8)
+    M, N = R.kda_segment_maps(k, v, g, beta, cu_seqlens=[0, a, T])
+    Mw, Nw = R.kda_segment_maps(k, v, g, beta)
+    assert relerr(R.affine_apply(M[1], M[0]), Mw[0]) < 1e-12
+    assert relerr(R.affine_apply(M[1], N[0], N[1]), Nw[0]) < 1e-12
+    S0 = rng.standard_normal((1, 3, 8, 8))
+    o, S = R.kda_serial(q, k, v, g, beta, initial_state=S0)
+    Sa = R.affine_apply(M[0], S0[0], N[0])[None]
+    o2, S2 = R.kda_serial(q[a:], k[a:], v[a:], g[a:], beta[a:], initial_state=Sa)
+    assert relerr(o2, o[a:]) < 1e-12 and relerr(S2, S) < 1e-12
+
+
+def test_segment_map_closed_forms():
+    """beta = 0: M = Diag(exp(sum max(g, -5))), N = 0. alpha = beta = 1 with
+    orthonormal keys k_1..k_m: M = I - sum k_j k_j^T (the projector off their
+    span) and N = sum k_j v_j^T."""
+    rng = np.random.default_rng(304)
+    q, k, v, g, beta = rand_core(rng, 9, 1, 8, 8)
+    M, N = R.kda_segment_maps(k, v, g, np.zeros_like(beta))
+    G = np.maximum(g[:, 0].astype(np.float64), -5.0).sum(0)
+    assert np.max(np.abs(M[0, 0] - np.diag(np.exp(G)))) < 1e-14
+    assert np.all(N == 0)
+    # rows of a 4 x 4 Hadamard matrix / 2: orthonormal exactly in binary floating point
+    Hd = 0.5 * np.array([[1, 1, 1, 1], [1, -1, 1, -1], [1, 1, -1, -1], [1, -1, -1, 1]], dtype=np.float64)
+    m = 3
+    kk = Hd[:m].reshape(m, 1, 4)
+    vv = rng.standard_normal((m, 1, 4)).astype(np.float32).astype(np.float64)
+    M, N = R.kda_segment_maps(kk, vv, np.zeros((m, 1, 4)), np.ones((m, 1)))
+    P = np.eye(4) - Hd[:m].T @ Hd[:m]
+    assert np.max(np.abs(M[0, 0] - P)) < 1e-15
+    assert np.max(np.abs(N[0, 0] - Hd[:m].T @ vv[:, 0])) < 1e-14
