@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkda.so")
 SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_conv.hip", "kda_elementwise.hip",
-           "kda_prefill.hip", "kda_prefill_split.hip", "kda_gemm.hip", "kda_fp8.hip"]
+           "kda_prefill.hip", "kda_prefill_split.hip", "kda_gemm.hip", "kda_fp8.hip", "kda_affine.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,

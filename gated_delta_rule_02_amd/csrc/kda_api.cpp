@@ -488,6 +488,82 @@ int kda_prefill_snapshots(const void* q, const void* k, const void* v, const voi
                         snapshot_interval, snapshot_slots, snapshots, hip_stream);
 }
 
+// ---------------------------------------------------------------- segment maps
+int kda_prefill_segment_maps(const void* k, const void* v, const void* g, const void* beta, kda_dtype in_dtype,
+                             int64_t num_tokens, int H, int dk, int dv,
+                             const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int num_seqs,
+                             float lower_bound, float* M_out, float* N_out, void* workspace, size_t workspace_bytes,
+                             void* hip_stream)
+{
+    REQUIRE(valid_dtype(in_dtype), KDA_ERR_INVALID_ARG, "kda_prefill_segment_maps: bad dtype");
+    REQUIRE(in_dtype == KDA_BF16, KDA_ERR_UNSUPPORTED,
+            "kda_prefill_segment_maps: only bfloat16 inputs are supported (the two-pass form)");
+    REQUIRE(num_tokens >= 0 && H >= 1, KDA_ERR_INVALID_ARG, "kda_prefill_segment_maps: bad num_tokens or H");
+    REQUIRE(dk == 128 && dv == 128, KDA_ERR_UNSUPPORTED,
+            "kda_prefill_segment_maps: only dk = dv = 128 is supported (got %d, %d)", dk, dv);
+    REQUIRE(M_out && N_out, KDA_ERR_INVALID_ARG, "kda_prefill_segment_maps: null M_out or N_out");
+    REQUIRE(num_tokens == 0 || (k && v && g && beta), KDA_ERR_INVALID_ARG,
+            "kda_prefill_segment_maps: null tensor pointer");
+    REQUIRE(workspace, KDA_ERR_WORKSPACE, "kda_prefill_segment_maps: a workspace is required");
+    for (const void* p : {k, v, g, beta, (const void*)M_out, (const void*)N_out, (const void*)workspace})
+        REQUIRE(!p || aligned16(p), KDA_ERR_INVALID_ARG, "kda_prefill_segment_maps: pointers must be 16-byte aligned");
+    int64_t seq_len = 0;
+    int rc = check_cu(cu_seqlens_dev, cu_seqlens_host, num_seqs, num_tokens, &seq_len);
+    if (rc != KDA_OK) return rc;
+    REQUIRE((int64_t)num_seqs * H * 4 <= 0x7fffffff, KDA_ERR_INVALID_ARG, "kda_prefill_segment_maps: num_seqs*H too large");
+    const int64_t units = (int64_t)num_seqs * H;
+    int64_t max_len = seq_len;
+    if (cu_seqlens_host)
+        for (int n = 0; n < num_seqs; ++n)
+            max_len = std::max<int64_t>(max_len, (int64_t)cu_seqlens_host[n + 1] - cu_seqlens_host[n]);
+    const int64_t max_chunks = (max_len + kChunk - 1) / kChunk;
+    const size_t slot = prefill_split_slot_bytes();
+    const size_t whole = (size_t)(units * std::max<int64_t>(max_chunks, 1)) * slot;
+    const size_t least = (size_t)units * slot + state_carry_bytes(units);
+    REQUIRE(workspace_bytes >= std::min(whole, least), KDA_ERR_WORKSPACE,
+            "kda_prefill_segment_maps: workspace of at least %zu bytes required (got %zu)", std::min(whole, least),
+            workspace_bytes);
+    const size_t T = (size_t)num_tokens, mbytes = (size_t)units * 128 * 128 * 4;
+    const Range rM = rng(M_out, mbytes), rN = rng(N_out, mbytes), rws = rng(workspace, workspace_bytes);
+    REQUIRE(!overlap(rM, rN), KDA_ERR_INVALID_ARG, "kda_prefill_segment_maps: M_out overlaps N_out");
+    for (const Range& r : {rng(k, T * H * 256), rng(v, T * H * 256), rng(g, T * H * 256), rng(beta, T * H * 2), rws})
+        REQUIRE(!overlap(r, rM) && !overlap(r, rN), KDA_ERR_INVALID_ARG,
+                "kda_prefill_segment_maps: M_out or N_out overlaps an input or the workspace");
+    for (const Range& r : {rng(k, T * H * 256), rng(v, T * H * 256), rng(g, T * H * 256), rng(beta, T * H * 2)})
+        REQUIRE(!overlap(r, rws), KDA_ERR_INVALID_ARG, "kda_prefill_segment_maps: workspace overlaps an input");
+
+    PrefillArgs a{};
+    a.q = k;  // the intra pass also forms the read-side products from a query array; they go unused here
+    a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.cu_seqlens = cu_seqlens_dev; a.seq_len = seq_len;
+    a.sT = N_out; a.map_M = M_out;
+    a.num_seqs = num_seqs; a.H = H; a.scale = 1.0f; a.lower_bound = lower_bound;
+    a.in_dtype = BF16; a.out_dtype = F32;
+    return hip_status(launch_prefill_split(a, workspace, workspace_bytes, max_chunks,
+                                           static_cast<hipStream_t>(hip_stream)),
+                      "kda_prefill_segment_maps");
+}
+
+int kda_affine_apply(const float* M, const float* X, const float* N, float* Y, int64_t count, int dk, int dv,
+                     void* hip_stream)
+{
+    REQUIRE(dk == 128 && dv == 128, KDA_ERR_UNSUPPORTED,
+            "kda_affine_apply: only dk = dv = 128 is supported (got %d, %d)", dk, dv);
+    REQUIRE(count >= 0, KDA_ERR_INVALID_ARG, "kda_affine_apply: negative count");
+    if (count == 0) return KDA_OK;
+    REQUIRE(M && X && Y, KDA_ERR_INVALID_ARG, "kda_affine_apply: null M, X or Y");
+    for (const void* p : {(const void*)M, (const void*)X, (const void*)N, (const void*)Y})
+        REQUIRE(!p || aligned16(p), KDA_ERR_INVALID_ARG, "kda_affine_apply: pointers must be 16-byte aligned");
+    const size_t bytes = (size_t)count * 128 * 128 * 4;
+    const Range rY = rng(Y, bytes), rN = rng(N, N ? bytes : 0);
+    REQUIRE(!overlap(rY, rng(M, bytes)) && !overlap(rY, rng(X, bytes)), KDA_ERR_INVALID_ARG,
+            "kda_affine_apply: Y overlaps M or X");
+    REQUIRE(!overlap(rY, rN) || N == Y, KDA_ERR_INVALID_ARG,
+            "kda_affine_apply: Y and N overlap without being the same buffer");
+    return hip_status(launch_affine_apply(M, X, N, Y, count, static_cast<hipStream_t>(hip_stream)),
+                      "kda_affine_apply");
+}
+
 // ---------------------------------------------------------------- GEMM
 int kda_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
              int64_t M, int64_t N, int64_t K, kda_dtype ab_dtype, kda_dtype c_dtype,

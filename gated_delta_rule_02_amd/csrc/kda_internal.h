@@ -89,6 +89,10 @@ struct PrefillArgs {
     // multiple of 64), into snap[n][j] of [N, snap_slots, H, 128, 128]; off when null
     float* snap;
     int64_t snap_interval, snap_slots;
+    // segment maps (two-pass form only): when set, the call computes for every
+    // sequence the affine map S_out = M S_in + N of its tokens, M into map_M
+    // [N, H, 128, 128] and N into sT, and writes no output (s0, o and snap unused)
+    float* map_M;
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 // Two-pass form (bfloat16 inputs): per-chunk products in `ws`, then the state
@@ -97,6 +101,9 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 // plus the float32 state carry when the slots cannot hold every chunk.
 hipError_t launch_prefill_split(const PrefillArgs& a, void* ws, size_t ws_bytes, int64_t max_chunks, hipStream_t s);
 size_t prefill_split_slot_bytes();
+// Y[b] = M[b] X[b] (+ N[b]) for b < count: float32 [count, 128, 128] matrices
+hipError_t launch_affine_apply(const float* M, const float* X, const float* N, float* Y, int64_t count,
+                               hipStream_t s);
 
 // y[M, N] = x[M, K] W^T, W block-FP8: W[n, k] = e4m3(w[n, k]) * w_scale[n/128, k/128]
 struct Fp8GemvArgs {

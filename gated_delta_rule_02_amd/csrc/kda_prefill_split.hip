@@ -68,6 +68,7 @@ struct SplitArgs {
     int64_t chunk0;   // first chunk (of each sequence) in this window
     int nwin;         // chunk slots per (sequence, head)
     int groups;       // intra-pass workgroups per (sequence, head)
+    int map_half;     // segment maps: state-pass workgroups of each half of the grid
 };
 
 __device__ __forceinline__ void seq_bounds(const PrefillArgs& a, int n, int64_t& s, int64_t& e)
@@ -327,7 +328,12 @@ void state_kernel(SplitArgs sa)
     // Workgroup ids are dealt to the 8 XCDs round robin; the kColGroups
     // workgroups of one (sequence, head) get ids congruent mod 8, so they read
     // the chunk products through the same L2.
-    const int bid = blockIdx.x;
+    // Segment maps: the grid is doubled; its first half carries M (from the
+    // identity, with U' = 0: the map's linear part), the second half N (from
+    // zero); no output is formed.
+    const bool map = a.map_M != nullptr;
+    const int half = map ? (int)(blockIdx.x / sa.map_half) : 1;  // 0: M, 1: N (or the ordinary state)
+    const int bid = map ? (int)(blockIdx.x % sa.map_half) : (int)blockIdx.x;
     const int jq = (bid >> 3) % kColGroups;
     const int u = (bid & 7) + 8 * ((bid >> 3) / kColGroups);  // n * H + h
     if (u >= a.num_seqs * a.H) return;
@@ -342,9 +348,15 @@ void state_kernel(SplitArgs sa)
     const int j0 = kTiles * jq + jl;         // its first 16-column tile; tile p is j0 + p
     const size_t sbase = (size_t)u * D * D;
 
+    // M's half starts from the identity and N's from zero; across windows each
+    // is carried in its own output (every workgroup reads and writes only its
+    // own columns)
+    float* const mapout = half ? a.sT : a.map_M;
     if (nch == 0) {
-        // an empty sequence still has a final state: the initial one
-        if (compute && sa.chunk0 == 0 && a.sT) {
+        // an empty sequence still has a final state: the initial one (for a
+        // segment map: M = I, N = 0)
+        if (compute && sa.chunk0 == 0 && (map || a.sT)) {
+            float* const dst = map ? mapout : a.sT;
 #pragma unroll
             for (int p = 0; p < TPW; ++p) {
                 int off = 4 * q4 * D + 16 * (j0 + p) + m16;
@@ -354,14 +366,17 @@ void state_kernel(SplitArgs sa)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const size_t e = sbase + off + (size_t)(16 * t + i) * D;
-                        a.sT[e] = a.s0 ? a.s0[e] : 0.0f;
+                        dst[e] = map ? ((half == 0 && 16 * t + 4 * q4 + i == 16 * (j0 + p) + m16) ? 1.0f : 0.0f)
+                                     : (a.s0 ? a.s0[e] : 0.0f);
                     }
             }
         }
         return;
     }
-    const float* sin = sa.chunk0 == 0 ? a.s0 : sa.carry;
-    float* sout = c_end >= nchunks ? a.sT : sa.carry;
+    const float* sin = map ? (sa.chunk0 == 0 ? nullptr : mapout) : (sa.chunk0 == 0 ? a.s0 : sa.carry);
+    float* sout = map ? mapout : (c_end >= nchunks ? a.sT : sa.carry);
+    const bool ident = map && half == 0 && sa.chunk0 == 0;  // M's first window starts from I
+    const bool zeroU = map && half == 0;                      // M's half: U' = 0
 
     // this (sequence, head)'s slots through one descriptor; the wave-uniform
     // parts of every address are scalar
@@ -397,6 +412,11 @@ void state_kernel(SplitArgs sa)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         S[p][t][i] = sin[sbase + (size_t)(16 * t + 4 * q4 + i) * D + 16 * (j0 + p) + m16];
+            } else if (ident) {
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) S[p][t][i] = (16 * t + 4 * q4 + i == 16 * (j0 + p) + m16) ? 1.0f : 0.0f;
             } else {
 #pragma unroll
                 for (int t = 0; t < 8; ++t) S[p][t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -441,7 +461,7 @@ void state_kernel(SplitArgs sa)
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const h4 up = *reinterpret_cast<const h4*>(st + kStUp + (((jl + p) * 4 + t) * 64 + lane) * 8);
-                U[p][t] = f32x4{(float)up[0], (float)up[1], (float)up[2], (float)up[3]};
+                U[p][t] = zeroU ? f32x4{0.f, 0.f, 0.f, 0.f} : f32x4{(float)up[0], (float)up[1], (float)up[2], (float)up[3]};
                 Ot[p][t] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         h8 an[2][4], aq[2][4];
@@ -503,6 +523,7 @@ void state_kernel(SplitArgs sa)
         // rows past the sequence are dropped by the descriptor range
         const int64_t cs = seq_s + (sa.chunk0 + c) * C;
         const int ntok = (int)min<int64_t>(C, seq_e - cs);
+        if (map) continue;  // segment maps: no output, no snapshots
         // state snapshot when a whole chunk ends on a multiple of the interval
         if (a.snap && --snap_left == 0) {
             if (ntok == C) {
@@ -551,10 +572,11 @@ void state_kernel(SplitArgs sa)
 }
 
 template <typename TOUT, int TPW>
-void launch_state(const SplitArgs& sa, int64_t U, bool stream, hipStream_t s)
+void launch_state(SplitArgs sa, int64_t U, bool stream, hipStream_t s)
 {
     constexpr int kColGroups = D / (16 * kStateWaves * TPW);
-    const dim3 gs((unsigned)(kColGroups * 8 * ((U + 7) / 8))), bs(kStateThreads);
+    sa.map_half = (int)(kColGroups * 8 * ((U + 7) / 8));
+    const dim3 gs((unsigned)(sa.map_half * (sa.p.map_M ? 2 : 1))), bs(kStateThreads);
     if (stream)
         hipLaunchKernelGGL((state_kernel<TOUT, TPW, kStream>), gs, bs, 0, s, sa);
     else

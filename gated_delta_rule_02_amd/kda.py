@@ -30,6 +30,8 @@ _SIGS = {
     "kda_prefill_workspace_bytes": (_SZ, [_I64, _I, _I, _I, _I, _I]),
     "kda_prefill_snapshots": (_I, [_P] * 5 + [_I, _I64, _I, _I, _I, _P, _P, _I, _F, _F, _P, _P, _P, _I, _P, _SZ,
                                               _I64, _I64, _P, _P]),
+    "kda_prefill_segment_maps": (_I, [_P] * 4 + [_I, _I64, _I, _I, _I, _P, _P, _I, _F, _P, _P, _P, _SZ, _P]),
+    "kda_affine_apply": (_I, [_P, _P, _P, _P, _I64, _I, _I, _P]),
     "kda_decode_step": (_I, [_P] * 5 + [_I, _I, _I, _I, _I, _F, _F, _P, _P, _I, _P]),
     "kda_decode_multi": (_I, [_P] * 5 + [_I, _I, _I, _I, _I, _I, _F, _F, _P, _P, _I, _P, _I, _P]),
     "kda_decode_commit": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _I, _P]),
@@ -177,6 +179,41 @@ def kda_prefill(q, k, v, g, beta, o, cu_seqlens=None, cu_seqlens_host=None, num_
 
 def kda_prefill_workspace_bytes(num_tokens, num_seqs, H, dk=128, dv=128, in_dtype=KDA_BF16):
     return lib().kda_prefill_workspace_bytes(num_tokens, num_seqs, H, dk, dv, in_dtype)
+
+
+def kda_prefill_segment_maps(k, v, g, beta, M_out, N_out, cu_seqlens=None, cu_seqlens_host=None, num_seqs=None,
+                             lower_bound=-5.0, workspace="auto", stream=None):
+    """Affine map S_out = M S_in + N of every segment (sequence of cu_seqlens).
+    k, g [T,H,128], v [T,H,128], beta [T,H] bfloat16; M_out, N_out float32
+    [N,H,128,128]. workspace as for kda_prefill (required: "auto" or a tensor)."""
+    for n_, t_ in (("k", k), ("v", v), ("g", g), ("beta", beta), ("M_out", M_out), ("N_out", N_out)):
+        _dense(t_, n_)
+    T, H, dk = k.shape
+    dv = v.shape[2]
+    cu_dev, cu_host, keep = _cu(cu_seqlens, cu_seqlens_host)
+    if num_seqs is None:
+        num_seqs = (keep.numel() - 1) if keep is not None else 1
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto' or a tensor")
+        workspace = _workspace(k.device, max(lib().kda_prefill_workspace_bytes(max(T, 1), num_seqs, H, dk, dv, _dt(k)), 16))
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _call("kda_prefill_segment_maps", _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dt(k), T, H, dk, dv,
+          cu_dev, cu_host, num_seqs, lower_bound, _ptr(M_out), _ptr(N_out), _ptr(workspace), ws_bytes,
+          _stream(stream))
+    return M_out, N_out
+
+
+def kda_affine_apply(M, X, Y, N=None, stream=None):
+    """Y = M X (+ N) for float32 [..., 128, 128] batches (segment maps applied
+    to states, or composed)."""
+    for n_, t_ in (("M", M), ("X", X), ("Y", Y), ("N", N)):
+        _dense(t_, n_)
+    count = M.numel() // (128 * 128)
+    if X.numel() != M.numel() or Y.numel() != M.numel() or (N is not None and N.numel() != M.numel()):
+        raise ValueError("M, X, N and Y must hold the same number of 128 x 128 matrices")
+    _call("kda_affine_apply", _ptr(M), _ptr(X), _ptr(N), _ptr(Y), count, 128, 128, _stream(stream))
+    return Y
 
 
 def kda_decode_step(q, k, v, g, beta, state, o, scale=1.0, lower_bound=-5.0, stream=None):

@@ -74,13 +74,14 @@ def _softplus32(z):
     return np.logaddexp(np.float32(0), z).astype(np.float32)
 
 
-def core_inputs(rng, T, H, dk=CORE_D, dv=CORE_D, bf16=True, lower_bound=-5.0):
-    """q, k, v, g, beta for T packed tokens and H heads (draw order q, k, v, g, beta)."""
+def core_inputs(rng, T, H, dk=CORE_D, dv=CORE_D, bf16=True, lower_bound=-5.0, g_scale=1.0):
+    """q, k, v, g, beta for T packed tokens and H heads (draw order q, k, v, g, beta).
+    g_scale < 1 gives slower retention (longer memory): g = max(-g_scale softplus(z), lower_bound)."""
     q = _unit_rows(rng.standard_normal((T, H, dk), dtype=np.float32))
     k = _unit_rows(rng.standard_normal((T, H, dk), dtype=np.float32))
     v = rng.standard_normal((T, H, dv), dtype=np.float32)
     zg = rng.standard_normal((T, H, dk), dtype=np.float32)
-    g = np.maximum(-_softplus32(zg), np.float32(lower_bound)).astype(np.float32)
+    g = np.maximum(-np.float32(g_scale) * _softplus32(zg), np.float32(lower_bound)).astype(np.float32)
     zb = rng.standard_normal((T, H), dtype=np.float32)
     beta = (1.0 / (1.0 + np.exp(-zb))).astype(np.float32)
     return dict(q=_as(q, bf16), k=_as(k, bf16), v=_as(v, bf16), g=_as(g, bf16),

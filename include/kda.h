@@ -140,6 +140,50 @@ int kda_prefill_snapshots(const void* q, const void* k, const void* v, const voi
                           void* hip_stream);
 
 /* ------------------------------------------------------------------------
+ * kda_prefill_segment_maps -- the affine map of every segment on the state.
+ *
+ * A prefill can be cut along the sequence only if the recurrent state can be
+ * handed across the cuts; the engine the pages describe leaves prefill context
+ * parallelism off for this mixer because it lacks that state handling
+ * ("Ling-3.1-flash: What 63 Linear-Attention Layers Do to the KV Budget",
+ * section "Where the hybrid makes serving harder"). The update of "Ling-3.1-
+ * flash: Grouped Routing and Two Different MLA Caches", section "KDA replaces a
+ * token list with a recurrent matrix", is linear in the state, so a segment of
+ * tokens maps a start state S_in to S_out = M S_in + N with
+ *   M = A_T ... A_1,  A_t = (I - beta_t k_t k_t^T) Diag(alpha_t)  (dk x dk),
+ *   N = the state after the segment from a zero state             (dk x dv).
+ * Every segment's (M, N) is computed at once without knowing the states
+ * before it; kda_affine_apply then chains them and kda_prefill (with those
+ * initial states) forms each segment's outputs.
+ *
+ * Arguments as kda_prefill (each sequence of cu_seqlens is a segment), less q,
+ * o and the states, plus:
+ * M_out  float32 [num_seqs, H, dk, dk], caller-owned; an empty segment gives I.
+ * N_out  float32 [num_seqs, H, dk, dv], caller-owned; an empty segment gives 0.
+ *        Neither may overlap the other, an input or the workspace.
+ * Supported: in_dtype BF16 only (the two-pass form; a workspace is required,
+ * sized as for kda_prefill), dk = dv = 128.
+ * ---------------------------------------------------------------------- */
+int kda_prefill_segment_maps(const void* k, const void* v, const void* g, const void* beta, kda_dtype in_dtype,
+                             int64_t num_tokens, int H, int dk, int dv,
+                             const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int num_seqs,
+                             float lower_bound, float* M_out, float* N_out, void* workspace,
+                             size_t workspace_bytes, void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * kda_affine_apply -- Y[b] = M[b] X[b] (+ N[b]) for b < count.
+ *
+ * Applies segment maps (kda_prefill_segment_maps) to states, and composes
+ * maps: (M2, N2) after (M1, N1) is (M2 M1, M2 N1 + N2), two calls.
+ * M float32 [count, dk, dk]; X, N, Y float32 [count, dk, dv]; N may be NULL
+ * (no addition). Y must not overlap M or X; it may be N itself (exactly).
+ * float32 arithmetic, accumulation in a fixed order (deterministic).
+ * Supported: dk = dv = 128; count = 0 does nothing.
+ * ---------------------------------------------------------------------- */
+int kda_affine_apply(const float* M, const float* X, const float* N, float* Y, int64_t count, int dk, int dv,
+                     void* hip_stream);
+
+/* ------------------------------------------------------------------------
  * kda_decode_step -- one new token for each of B sequences, state in place.
  *
  * The same recurrence with T = 1 (retention, corrected write, read after the

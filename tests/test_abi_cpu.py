@@ -255,3 +255,49 @@ def test_fp8_validation():
     assert call("kda_output_norm_gate_fp8", *a)[0] == K.KDA_ERR_INVALID_ARG
     a = list(e); a[10] = fake(1) + 256
     assert call("kda_output_norm_gate_fp8", *a)[0] == K.KDA_ERR_INVALID_ARG
+
+
+def segmaps(**over):
+    a = dict(k=fake(2), v=fake(3), g=fake(4), beta=fake(5), in_dtype=K.KDA_BF16, T=256, H=4, dk=128, dv=128,
+             cu_dev=None, cu_host=None, N=1, lb=-5.0, M=fake(7), Nout=fake(8), ws=fake(9), ws_bytes=1 << 28,
+             stream=None)
+    a.update(over)
+    return call("kda_prefill_segment_maps", a["k"], a["v"], a["g"], a["beta"], a["in_dtype"], a["T"], a["H"],
+                a["dk"], a["dv"], a["cu_dev"], a["cu_host"], a["N"], a["lb"], a["M"], a["Nout"], a["ws"],
+                a["ws_bytes"], a["stream"])
+
+
+def test_segment_maps_validation():
+    """Rejected before any launch: float32 inputs (no two-pass form), other
+    head sizes, missing outputs or workspace, a workspace below one slot per
+    unit plus the carry, overlapping outputs, misalignment, bad boundaries."""
+    assert segmaps(in_dtype=K.KDA_F32)[0] == K.KDA_ERR_UNSUPPORTED
+    assert segmaps(dk=64)[0] == K.KDA_ERR_UNSUPPORTED
+    assert segmaps(M=None)[0] == K.KDA_ERR_INVALID_ARG
+    assert segmaps(Nout=None)[0] == K.KDA_ERR_INVALID_ARG
+    rc, msg = segmaps(ws=None)
+    assert rc == K.KDA_ERR_WORKSPACE and "workspace" in msg
+    assert segmaps(ws_bytes=1000)[0] == K.KDA_ERR_WORKSPACE
+    rc, msg = segmaps(Nout=fake(7) + 2 * 128 * 128 * 4)  # inside M_out (4 units x 64 KiB)
+    assert rc == K.KDA_ERR_INVALID_ARG and "overlaps" in msg
+    assert segmaps(M=fake(7) + 8)[0] == K.KDA_ERR_INVALID_ARG
+    assert segmaps(k=None)[0] == K.KDA_ERR_INVALID_ARG
+    cu = cu_host([0, 200, 100, 256])
+    assert segmaps(cu_dev=fake(10), cu_host=cu, N=3)[0] == K.KDA_ERR_INVALID_ARG
+    assert segmaps(ws=fake(2) + 4096)[0] == K.KDA_ERR_INVALID_ARG  # workspace inside k
+
+
+def test_affine_apply_validation():
+    """Rejected before any launch: other sizes, negative counts, missing
+    operands, Y overlapping M or X, Y partly overlapping N, misalignment;
+    count = 0 does nothing and succeeds."""
+    f = lambda M=fake(1), X=fake(2), N=fake(3), Y=fake(4), count=4, dk=128, dv=128: \
+        call("kda_affine_apply", M, X, N, Y, count, dk, dv, None)
+    assert f(dk=64)[0] == K.KDA_ERR_UNSUPPORTED
+    assert f(count=-1)[0] == K.KDA_ERR_INVALID_ARG
+    assert f(count=0)[0] == K.KDA_OK
+    assert f(M=None)[0] == K.KDA_ERR_INVALID_ARG
+    assert f(Y=fake(2) + 65536)[0] == K.KDA_ERR_INVALID_ARG       # inside X
+    assert f(Y=fake(1))[0] == K.KDA_ERR_INVALID_ARG               # is M
+    assert f(Y=fake(3) + 65536)[0] == K.KDA_ERR_INVALID_ARG       # partly N
+    assert f(X=fake(2) + 4)[0] == K.KDA_ERR_INVALID_ARG
