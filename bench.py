@@ -164,6 +164,54 @@ def bench_varlen(torch, K, steps, warmup):
     return ms, T, [int(x) for x in lengths]
 
 
+def bench_seqpar(torch, K, steps, warmup, P=4):
+    """The prefill workload cut into P equal segments and stitched with the
+    segment maps (what P ranks of a sequence-parallel prefill would each do
+    on their share, here all on one GPU): every segment's map at once, P - 1
+    chained map applications, then every segment's outputs at once from its
+    incoming state. Also the per-rank share alone: one segment's map and its
+    prefill (T / P tokens, 64 heads)."""
+    import numpy as np
+    from gated_delta_rule_02_amd import synth
+    d = synth.workload_prefill()
+    q, k, v, g, b = (dev(d[x], torch) for x in ("q", "k", "v", "g", "beta"))
+    T, H, D = q.shape
+    cuts = np.linspace(0, T, P + 1).astype(np.int32)
+    cu_d, cu_h = torch.from_numpy(cuts).cuda(), torch.from_numpy(cuts)
+    M = torch.empty((P, H, D, D), dtype=torch.float32, device="cuda")
+    Nm = torch.empty_like(M)
+    S = torch.zeros_like(M)
+    sT = torch.empty_like(M)
+    o = torch.empty((T, H, D), dtype=torch.float32, device="cuda")
+    maps = lambda: K.kda_prefill_segment_maps(k, v, g, b, M, Nm, cu_seqlens=cu_d, cu_seqlens_host=cu_h, num_seqs=P)
+
+    def chain():
+        for i in range(1, P):
+            K.kda_affine_apply(M[i - 1], S[i - 1], S[i], N=Nm[i - 1])
+
+    seg = lambda: K.kda_prefill(q, k, v, g, b, o, cu_seqlens=cu_d, cu_seqlens_host=cu_h, num_seqs=P,
+                                initial_state=S, final_state=sT)
+
+    def whole():
+        maps()
+        chain()
+        seg()
+
+    L = T // P
+    q1, k1, v1, g1, b1 = (x[:L] for x in (q, k, v, g, b))
+    M1, N1, S1, sT1 = M[:1], Nm[:1], S[:1], sT[:1]
+    o1 = o[:L]
+    rank_maps = lambda: K.kda_prefill_segment_maps(k1, v1, g1, b1, M1, N1)
+    rank_seg = lambda: K.kda_prefill(q1, k1, v1, g1, b1, o1, initial_state=S1, final_state=sT1)
+    n = max(5, steps // 2)
+    return {"workload": "the prefill workload (T=4096, H=64) cut into %d segments of %d tokens" % (P, L),
+            "ms_total": timed(torch, whole, n, 2)[0], "ms_segment_maps": timed(torch, maps, n, 2)[0],
+            "ms_chain": timed(torch, chain, n, 2)[0], "ms_segment_prefill": timed(torch, seg, n, 2)[0],
+            "per_rank_share": {"workload": "one segment: %d tokens x 64 heads" % L,
+                               "ms_segment_map": timed(torch, rank_maps, n, 2)[0],
+                               "ms_prefill_from_incoming_state": timed(torch, rank_seg, n, 2)[0]}}
+
+
 def bench_decode(torch, K, steps, warmup):
     from gated_delta_rule_02_amd import synth
     d = synth.workload_decode()
@@ -341,6 +389,9 @@ def main():
             "prefill_snapshots": {"workload": "the same prefill saving the state every 1024 tokens (4 x 4 MiB)",
                                   "ms_per_step": ms_snap, "tokens/s/layer": T / (ms_snap * 1e-3)},
         })
+        log("sequence-parallel prefill pieces, 4 segments")
+        out["sequence_parallel"] = bench_seqpar(torch, K, args.steps, args.warmup)
+        log("sequence-parallel total %.3f ms" % out["sequence_parallel"]["ms_total"])
         if not args.skip_cpu:
             log("cpu baseline (fp64 oracle)")
             out["cpu_baseline"] = cpu_baseline(d)
