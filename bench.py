@@ -342,7 +342,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--skip-layer", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "varlen", "decode", "layer", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "seqpar", "varlen", "decode", "layer", "copy"], default=None,
                     help="time one path only (for profiler runs); 'copy' times the plain copy that calibrates byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -389,12 +389,13 @@ def main():
             "prefill_snapshots": {"workload": "the same prefill saving the state every 1024 tokens (4 x 4 MiB)",
                                   "ms_per_step": ms_snap, "tokens/s/layer": T / (ms_snap * 1e-3)},
         })
-        log("sequence-parallel prefill pieces, 4 segments")
-        out["sequence_parallel"] = bench_seqpar(torch, K, args.steps, args.warmup)
-        log("sequence-parallel total %.3f ms" % out["sequence_parallel"]["ms_total"])
         if not args.skip_cpu:
             log("cpu baseline (fp64 oracle)")
             out["cpu_baseline"] = cpu_baseline(d)
+    if args.only in (None, "seqpar"):
+        log("sequence-parallel prefill pieces, 4 segments")
+        out["sequence_parallel"] = bench_seqpar(torch, K, args.steps, args.warmup)
+        log("sequence-parallel total %.3f ms" % out["sequence_parallel"]["ms_total"])
     if args.only in (None, "varlen"):
         log("varlen prefill, 8 packed sequences")
         ms_v, T_v, lens = bench_varlen(torch, K, args.steps, args.warmup)

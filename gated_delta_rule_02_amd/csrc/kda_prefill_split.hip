@@ -304,8 +304,8 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
 // product, and the stored A-operand layouts of Q~ and P serve as B operands.
 // The result then holds four consecutive output columns of one token per lane
 // (16-byte stores) instead of four tokens of one column.
-// POL: cache policy of the output stores (0 or kStream)
-template <typename TOUT, int TPW, int POL>
+// POL: cache policy of the output stores (0 or kStream); MAP: segment maps
+template <typename TOUT, int TPW, int POL, bool MAP>
 __global__ __launch_bounds__(kStateThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void state_kernel(SplitArgs sa)
 {
@@ -331,7 +331,7 @@ void state_kernel(SplitArgs sa)
     // Segment maps: the grid is doubled; its first half carries M (from the
     // identity, with U' = 0: the map's linear part), the second half N (from
     // zero); no output is formed.
-    const bool map = a.map_M != nullptr;
+    constexpr bool map = MAP;
     const int half = map ? (int)(blockIdx.x / sa.map_half) : 1;  // 0: M, 1: N (or the ordinary state)
     const int bid = map ? (int)(blockIdx.x % sa.map_half) : (int)blockIdx.x;
     const int jq = (bid >> 3) % kColGroups;
@@ -468,7 +468,7 @@ void state_kernel(SplitArgs sa)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             an[0][t] = nw[(t * 4 + 0) * 64 + lane];
-            aq[0][t] = qt[(t * 4 + 0) * 64 + lane];
+            if constexpr (!MAP) aq[0][t] = qt[(t * 4 + 0) * 64 + lane];
         }
         h8 ap[6], ak[16];  // P and Kbar^T operands, read during the first products
 #pragma unroll
@@ -478,9 +478,9 @@ void state_kernel(SplitArgs sa)
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     an[nxt][t] = nw[(t * 4 + s + 1) * 64 + lane];
-                    aq[nxt][t] = qt[(t * 4 + s + 1) * 64 + lane];
+                    if constexpr (!MAP) aq[nxt][t] = qt[(t * 4 + s + 1) * 64 + lane];
                 }
-            } else {
+            } else if constexpr (!MAP) {
 #pragma unroll
                 for (int i = 0; i < 6; ++i) ap[i] = pm[i * 64 + lane];  // (t, s) with 2s <= t
             }
@@ -489,7 +489,8 @@ void state_kernel(SplitArgs sa)
 #pragma unroll
                 for (int p = 0; p < TPW; ++p) {
                     U[p][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(an[cur][t], sb[p][s], U[p][t], 0, 0, 0);
-                    Ot[p][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sb[p][s], aq[cur][t], Ot[p][t], 0, 0, 0);
+                    if constexpr (!MAP)
+                        Ot[p][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sb[p][s], aq[cur][t], Ot[p][t], 0, 0, 0);
                 }
         }
 #pragma unroll
@@ -501,6 +502,7 @@ void state_kernel(SplitArgs sa)
             for (int s = 0; s < 2; ++s) ub[p][s] = cat(to_h4(U[p][2 * s]), to_h4(U[p][2 * s + 1]));
 #pragma unroll
         for (int i = 0; i < 6; ++i) {
+            if constexpr (MAP) break;  // segment maps form no output
             const int t = i < 2 ? i : 2 + (i - 2) / 2, s2 = i < 2 ? 0 : (i - 2) % 2;
 #pragma unroll
             for (int p = 0; p < TPW; ++p)
@@ -523,7 +525,7 @@ void state_kernel(SplitArgs sa)
         // rows past the sequence are dropped by the descriptor range
         const int64_t cs = seq_s + (sa.chunk0 + c) * C;
         const int ntok = (int)min<int64_t>(C, seq_e - cs);
-        if (map) continue;  // segment maps: no output, no snapshots
+        if constexpr (MAP) continue;  // segment maps: no output, no snapshots
         // state snapshot when a whole chunk ends on a multiple of the interval
         if (a.snap && --snap_left == 0) {
             if (ntok == C) {
@@ -577,10 +579,12 @@ void launch_state(SplitArgs sa, int64_t U, bool stream, hipStream_t s)
     constexpr int kColGroups = D / (16 * kStateWaves * TPW);
     sa.map_half = (int)(kColGroups * 8 * ((U + 7) / 8));
     const dim3 gs((unsigned)(sa.map_half * (sa.p.map_M ? 2 : 1))), bs(kStateThreads);
-    if (stream)
-        hipLaunchKernelGGL((state_kernel<TOUT, TPW, kStream>), gs, bs, 0, s, sa);
+    if (sa.p.map_M)
+        hipLaunchKernelGGL((state_kernel<TOUT, TPW, 0, true>), gs, bs, 0, s, sa);
+    else if (stream)
+        hipLaunchKernelGGL((state_kernel<TOUT, TPW, kStream, false>), gs, bs, 0, s, sa);
     else
-        hipLaunchKernelGGL((state_kernel<TOUT, TPW, 0>), gs, bs, 0, s, sa);
+        hipLaunchKernelGGL((state_kernel<TOUT, TPW, 0, false>), gs, bs, 0, s, sa);
 }
 
 // A window's workspace up to this size is left to the last-level cache (256
