@@ -31,13 +31,31 @@ def run_gemv(M, N, Kd, out_dtype=torch.float32, seed=0):
     return y, ref
 
 
-@pytest.mark.parametrize("M,N,Kd", [(1, 300, 128), (3, 257, 1152), (8, 1000, 4096), (2, 16, 2048), (5, 4099, 256)])
+@pytest.mark.parametrize("M,N,Kd", [(1, 300, 128), (3, 257, 1152), (8, 1000, 4096), (2, 16, 2048), (5, 4099, 256),
+                                    (6, 130, 384), (7, 64, 8192), (1, 1, 3072)])
 def test_gemv_fp8_small(M, N, Kd):
     announce("gemv fp8 M=%d N=%d K=%d" % (M, N, Kd))
     y, ref = run_gemv(M, N, Kd, seed=M * 7 + N)
     e = relerr(host64(y), ref)
     print("  err %.2e" % e, flush=True)
     assert e < 2e-5
+
+
+def test_gemv_fp8_strided_rows():
+    """x and y as row-strided views of wider buffers (ldx > K, ldy > N), for
+    one token and for four."""
+    for M, N, Kd in ((1, 777, 2048), (4, 300, 1024)):
+        announce("gemv fp8 strided M=%d N=%d K=%d" % (M, N, Kd))
+        rng = np.random.default_rng(40 + M)
+        codes, scales = fp8_weights(rng, N, Kd)
+        x = synth.normal(rng, (M, Kd))
+        xb = torch.zeros((M, Kd + 64), dtype=torch.bfloat16, device="cuda")
+        xb[:, :Kd] = dev(x)
+        yb = torch.full((M, N + 5), float("nan"), dtype=torch.float32, device="cuda")
+        K.kda_gemv_fp8(xb[:, :Kd], torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(), yb[:, :N])
+        torch.cuda.synchronize()
+        assert relerr(host64(yb[:, :N]), R.gemv_fp8_blocks(x.vals, codes, scales)) < 2e-5
+        assert torch.isnan(yb[:, N:]).all()
 
 
 def test_gemv_fp8_bf16_output():
