@@ -459,7 +459,7 @@ static int prefill_impl(const void* q, const void* k, const void* v, const void*
     a.snap = snapshots; a.snap_interval = snapshots ? snap_interval : 0; a.snap_slots = snapshots ? snap_slots : 0;
     const hipStream_t st = static_cast<hipStream_t>(hip_stream);
     if (split)
-        return hip_status(launch_prefill_split(a, workspace, workspace_bytes, max_chunks, st), "kda_prefill");
+        return hip_status(launch_prefill_split(a, workspace, workspace_bytes, max_chunks, cu_seqlens_host, st), "kda_prefill");
     return hip_status(launch_prefill(a, st), "kda_prefill");
 }
 
@@ -539,7 +539,7 @@ int kda_prefill_segment_maps(const void* k, const void* v, const void* g, const 
     a.sT = N_out; a.map_M = M_out;
     a.num_seqs = num_seqs; a.H = H; a.scale = 1.0f; a.lower_bound = lower_bound;
     a.in_dtype = BF16; a.out_dtype = F32;
-    return hip_status(launch_prefill_split(a, workspace, workspace_bytes, max_chunks,
+    return hip_status(launch_prefill_split(a, workspace, workspace_bytes, max_chunks, cu_seqlens_host,
                                            static_cast<hipStream_t>(hip_stream)),
                       "kda_prefill_segment_maps");
 }

@@ -99,7 +99,10 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 // recurrence. max_chunks = the largest number of 64-token chunks of one
 // sequence. ws_bytes must hold at least one chunk slot per (sequence, head),
 // plus the float32 state carry when the slots cannot hold every chunk.
-hipError_t launch_prefill_split(const PrefillArgs& a, void* ws, size_t ws_bytes, int64_t max_chunks, hipStream_t s);
+// cu_host: the host copy of cu_seqlens (null for equal lengths), from which
+// each window's count of sequences still running sizes its launches.
+hipError_t launch_prefill_split(const PrefillArgs& a, void* ws, size_t ws_bytes, int64_t max_chunks,
+                                const int32_t* cu_host, hipStream_t s);
 size_t prefill_split_slot_bytes();
 // Y[b] = M[b] X[b] (+ N[b]) for b < count: float32 [count, 128, 128] matrices
 hipError_t launch_affine_apply(const float* M, const float* X, const float* N, float* Y, int64_t count,

@@ -595,7 +595,26 @@ constexpr size_t kStreamWorkspace = (size_t)192 << 20;
 
 size_t prefill_split_slot_bytes() { return kSlot; }
 
-hipError_t launch_prefill_split(const PrefillArgs& a, void* ws, size_t ws_bytes, int64_t max_chunks, hipStream_t s)
+// Intra-pass workgroups per (sequence, head) for a window of nwin chunks with
+// `active` (sequence, head) units still running: the grouping that needs the
+// fewest rounds of chunks per compute unit (about one workgroup fits a unit),
+// the smallest such (every group pays its own first load).
+static int intra_groups(int64_t active, int nwin)
+{
+    int best = 1;
+    int64_t best_cost = INT64_MAX;
+    for (int g = 1; g <= std::max(nwin, 1); g *= 2) {
+        const int64_t cost = (active * g + 255) / 256 * ((nwin + g - 1) / g);
+        if (cost < best_cost) {
+            best_cost = cost;
+            best = g;
+        }
+    }
+    return best;
+}
+
+hipError_t launch_prefill_split(const PrefillArgs& a, void* ws, size_t ws_bytes, int64_t max_chunks,
+                                const int32_t* cu_host, hipStream_t s)
 {
     const int64_t U = (int64_t)a.num_seqs * a.H;
     SplitArgs sa{};
@@ -619,17 +638,28 @@ hipError_t launch_prefill_split(const PrefillArgs& a, void* ws, size_t ws_bytes,
         sa.nwin = (int)std::min<int64_t>(most, (even + grp - 1) / grp * grp);
         sa.carry = reinterpret_cast<float*>(sa.ws + (size_t)U * most * kSlot);
     }
-    // about one intra-pass workgroup per compute unit, each taking every
-    // groups-th chunk of the window with its next chunk prefetched
-    sa.groups = (int)std::max<int64_t>(1, std::min<int64_t>(sa.nwin, (256 + U - 1) / U));
-    const dim3 gi((unsigned)(U * sa.groups)), bi(kThreads);
-    // state pass: 4 workgroups of 32 columns per (sequence, head) while they
-    // all fit on the chip at once (one per compute unit), else 2 of 64 columns
-    // (each wavefront then carries two tiles through every operand read)
-    const bool narrow = U * 4 <= 256;
     const bool stream = (size_t)U * sa.nwin * kSlot <= kStreamWorkspace;
     for (int64_t c0 = 0; c0 < std::max<int64_t>(max_chunks, 1); c0 += sa.nwin) {
         sa.chunk0 = c0;
+        // the (sequence, head) units with chunks in this window: packed
+        // sequences of different lengths leave fewer in the later windows
+        int64_t active = U;
+        if (cu_host) {
+            int64_t running = 0;
+            for (int n = 0; n < a.num_seqs; ++n)
+                running += ((int64_t)cu_host[n + 1] - cu_host[n] + 63) / 64 > c0;
+            active = running * a.H;
+        }
+        // intra pass: each workgroup takes every groups-th chunk of its unit's
+        // window, its next chunk prefetched; the workgroups of finished units
+        // return at once
+        sa.groups = intra_groups(active, sa.nwin);
+        const dim3 gi((unsigned)(U * sa.groups)), bi(kThreads);
+        // state pass: 4 workgroups of 32 columns per unit while they all fit
+        // on the chip at once (one per compute unit), else 2 of 64 columns
+        // (each wavefront then carries two tiles through every operand read);
+        // the two give identical results
+        const bool narrow = active * 4 <= 256;
         if (max_chunks > 0) {
             if (stream)
                 hipLaunchKernelGGL((intra_kernel<bf16_t, kStream>), gi, bi, 0, s, sa);

@@ -217,6 +217,37 @@ def test_split_windows_match_one_window(lens):
     check(o1, s1, ro, rS, TOL_BF16)
 
 
+def test_packed_sequences_equal_separate_calls():
+    """Packed sequences that end in different windows (32-chunk windows: the
+    later ones have fewer (sequence, head) units running, so the intra pass
+    spreads each unit's chunks over more workgroups and the state pass moves
+    from 64- to 32-column workgroups) give, bit for bit, the outputs and final
+    states of one call per sequence; an empty sequence keeps its state."""
+    lens = [5000, 2500, 200, 64, 0, 1000]
+    announce("prefill packed vs separate lens=%s" % lens)
+    H = 16
+    N = len(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    rng = np.random.default_rng(31)
+    d = synth.core_inputs(rng, int(cu[-1]), H, bf16=True)
+    s0 = synth.states(rng, N, H, std=0.05)
+    o, sT = gpu_prefill(d, cu=cu, s0=s0)
+    q, k, v, g, b = (dev(d[x]) for x in ("q", "k", "v", "g", "beta"))
+    s0_d = dev(s0)
+    for n, L in enumerate(lens):
+        if L == 0:
+            continue
+        a, e = int(cu[n]), int(cu[n + 1])
+        on = torch.empty((L, H, 128), dtype=torch.float32, device="cuda")
+        sn = torch.empty((1, H, 128, 128), dtype=torch.float32, device="cuda")
+        K.kda_prefill(q[a:e], k[a:e], v[a:e], g[a:e], b[a:e], on, initial_state=s0_d[n:n + 1].contiguous(),
+                      final_state=sn, workspace="auto")
+        torch.cuda.synchronize()
+        assert torch.equal(on, o[a:e]), "sequence %d: o differs" % n
+        assert torch.equal(sn[0], sT[n]), "sequence %d: final state differs" % n
+    assert torch.equal(sT[4], s0_d[4])
+
+
 def test_varlen_workload_full_size_sampled():
     """Packed varlen workload at full size: 8 sequences (123,444 tokens, up to
     447 chunks each), H = 64, bf16 inputs, random fp32 initial states, final
