@@ -46,6 +46,21 @@ __device__ __forceinline__ void st8(T* p, const float* f)
     }
 }
 
+// softplus(x) = max(x, 0) + ln(1 + e^-|x|) on the hardware base-2 exponential
+// and logarithm: e^-|x| lies in (0, 1], so the logarithm sees [1, 2] and
+// needs no denormal handling, and an exponential below the float32 normal
+// range flushes to 0, which the formula absorbs; ln(1 + e) by e - e^2/2 where
+// 1 + e would drop e's low bits (relative error < e^2/3). About half the
+// instructions of the library forms, which handle denormal arguments: this
+// kernel was bound by them.
+constexpr float kLn2 = 0.69314718055994531f;
+__device__ __forceinline__ float softplus_hw(float x)
+{
+    const float e = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
+    const float l = e < 0x1p-10f ? e * (1.0f - 0.5f * e) : kLn2 * __builtin_amdgcn_logf(1.0f + e);
+    return fmaxf(x, 0.0f) + l;
+}
+
 template <typename TI, typename TO>
 __global__ __launch_bounds__(256) void gate_kernel(GateArgs a)
 {
@@ -73,7 +88,7 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a)
         if (r >= nt) break;
         float gv[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) gv[i] = fmaxf(-rate * softplusf_(fv[r][i]), a.lower_bound);
+        for (int i = 0; i < 8; ++i) gv[i] = fmaxf(-rate * softplus_hw(fv[r][i]), a.lower_bound);
         st8(g + r * (int64_t)a.H * a.dk, gv);
     }
 }
