@@ -127,32 +127,41 @@ typedef __attribute__((address_space(3))) void lds_void;
 // all 64 banks
 __device__ __forceinline__ int swz(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
 
-template <typename TC>
+// NJ: 16-column MFMA tiles per wavefront in N (8: the 256 x 256 tile; 2 or 4:
+// a 256 x 64 or 256 x 128 tile for the last N mod 256 columns, so that they
+// cost a fraction of a full tile instead of a whole one)
+template <typename TC, int NJ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm256_kernel(GemmArgs a)
 {
+    constexpr int TNW = 32 * NJ;         // columns of C per workgroup
+    constexpr int kBCopy = TNW / 64;     // B copy instructions per wavefront and K step
+    constexpr int kCopyInstr = 4 + kBCopy;
+    constexpr int kWaitOneCopy = 0x0f70 | kCopyInstr;  // s_waitcnt vmcnt(kCopyInstr)
+    static_assert(NJ == 2 || NJ == 4 || NJ == 8, "64, 128 or 256 columns");
     __shared__ __attribute__((aligned(16))) uint8_t smem[kStages][2][kStageBytes];  // [stage][A, B]
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m16 = lane & 15, q4 = lane >> 4;
-    const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+    const int wm = (wave >> 1) * 128, wn = (wave & 1) * 16 * NJ;
 
     // tiles: consecutive workgroup ids run down a column of M tiles, so the
     // workgroups resident together share B tiles and a few A tiles
     const int tiles_m = (int)((a.M + TM - 1) / TM);
     const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
-    const int64_t m0 = (int64_t)tm * TM, n0 = (int64_t)tn * TN;
+    const int64_t m0 = (int64_t)tm * TM, n0 = (int64_t)tn * TNW;
 
     // operand rows past M or N read as zero through the descriptor ranges
     const bf16_t* A = static_cast<const bf16_t*>(a.A) + m0 * a.lda;
     const bf16_t* B = static_cast<const bf16_t*>(a.B) + n0 * a.ldb;
-    const int64_t rows_a = min<int64_t>(TM, a.M - m0), rows_b = min<int64_t>(TN, a.N - n0);
+    const int64_t rows_a = min<int64_t>(TM, a.M - m0), rows_b = min<int64_t>(TNW, a.N - n0);
     const rsrc_t ra = make_rsrc(A, ((rows_a - 1) * a.lda + a.K) * 2);
     const rsrc_t rb = make_rsrc(B, ((rows_b - 1) * a.ldb + a.K) * 2);
 
-    // copy of K step kt into stage st: 16 instructions per operand, 4 per
-    // wavefront; instruction i covers rows 16i .. 16i+15, lane l row 16i + l/4
-    // and LDS chunk slot l%4, which holds K chunk slot ^ ((row/4) mod 4)
+    // copy of K step kt into stage st: 16 instructions for A (4 per
+    // wavefront) and TNW / 16 for B (kBCopy per wavefront); instruction i
+    // covers rows 16i .. 16i+15, lane l row 16i + l/4 and LDS chunk slot l%4,
+    // which holds K chunk slot ^ ((row/4) mod 4)
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)&smem[0][0][0];
     const int lrow = lane >> 2, lslot = lane & 3;
     auto copy_part = [&](int kt, int st, int j) {
@@ -162,19 +171,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int koff = (kt * TK + chunk * 8) * 2;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(uintptr_t)(lds0 + (st * 2 + 0) * kStageBytes + i * 1024),
                                                  16, (int)(row * a.lda * 2) + koff, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(uintptr_t)(lds0 + (st * 2 + 1) * kStageBytes + i * 1024),
-                                                 16, (int)(row * a.ldb * 2) + koff, 0, 0, 0);
+        if (j < kBCopy) {
+            // B has TNW rows: instruction ib = wave * kBCopy + j covers rows 16 ib .. 16 ib + 15
+            const int ib = wave * kBCopy + j;
+            const int rowb = 16 * ib + lrow;
+            const int chunkb = lslot ^ ((rowb >> 2) & 3);
+            const int koffb = (kt * TK + chunkb * 8) * 2;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(uintptr_t)(lds0 + (st * 2 + 1) * kStageBytes + ib * 1024),
+                                                     16, (int)(rowb * a.ldb * 2) + koffb, 0, 0, 0);
+        }
     };
     auto copy = [&](int kt, int st) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) copy_part(kt, st, j);
     };
 
-    f32x4 acc[8][8];
+    f32x4 acc[8][NJ];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // Pipeline: step kt computes on stage kt % 4 with operand fragments read
     // during step kt - 1. Between its MFMAs it issues the copy of step kt + 3
@@ -185,11 +201,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // B fragments, used by every row, after the last row). At its end it waits
     // for the copy of step kt + 2, so that after the barrier stage kt + 2 is
     // complete for the next step's early reads. The compiler does not track
-    // the copies: the waits are explicit. A copy is 8 instructions per
-    // wavefront and copies complete in order, so "copy c has landed" is
-    // vmcnt(8 x the copies issued after it).
+    // the copies: the waits are explicit. A copy is kCopyInstr instructions
+    // per wavefront (4 of A, kBCopy of B) and copies complete in order, so
+    // "copy c has landed" is vmcnt(kCopyInstr x the copies issued after it).
     const int nk = (int)(a.K / TK);
-    u32x4_t fa[8], fb[8];
+    u32x4_t fa[8], fb[NJ];
     auto read_a = [&](int kt, int i) {
         fa[i] = *reinterpret_cast<const u32x4_t*>(&smem[kt % kStages][0][0] + swz(wm + 16 * i + m16, q4));
     };
@@ -197,20 +213,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         fb[j] = *reinterpret_cast<const u32x4_t*>(&smem[kt % kStages][1][0] + swz(wn + 16 * j + m16, q4));
     };
     for (int p = 0; p < kStages - 1 && p < nk; ++p) copy(p, p);
-    if (nk > 2) __builtin_amdgcn_s_waitcnt(0x0f78);  // vmcnt(8): steps 0 and 1 landed
-    else __builtin_amdgcn_s_waitcnt(0x0f70);         // vmcnt(0)
+    if (nk > 2) __builtin_amdgcn_s_waitcnt(kWaitOneCopy);  // steps 0 and 1 landed (step 2 in flight)
+    else __builtin_amdgcn_s_waitcnt(0x0f70);               // vmcnt(0)
     lds_barrier();
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        read_a(0, i);
-        read_b(0, i);
-    }
+    for (int i = 0; i < 8; ++i) read_a(0, i);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) read_b(0, j);
     for (int kt = 0; kt < nk; ++kt) {
         const bool cp = kt + kStages - 1 < nk, nx = kt + 1 < nk;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < NJ; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb[j]),
                                                                     __builtin_bit_cast(bf16x8, fa[i]), acc[i][j], 0, 0, 0);
             if (i < 4 && cp) copy_part(kt + kStages - 1, (kt + kStages - 1) % kStages, i);
@@ -219,11 +234,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
         if (nx) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) read_b(kt + 1, j);
+            for (int j = 0; j < NJ; ++j) read_b(kt + 1, j);
         }
         // the copy of step kt + 2 has landed (this wavefront's part) ...
-        if (cp) __builtin_amdgcn_s_waitcnt(0x0f78);  // vmcnt(8)
-        else __builtin_amdgcn_s_waitcnt(0x0f70);     // vmcnt(0)
+        if (cp) __builtin_amdgcn_s_waitcnt(kWaitOneCopy);  // vmcnt(kCopyInstr)
+        else __builtin_amdgcn_s_waitcnt(0x0f70);           // vmcnt(0)
         lds_barrier();  // ... and everyone's; every read of stage kt % 4 is done
     }
 
@@ -235,7 +250,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int64_t row = m0 + wm + 16 * i + m16;
         if (row >= a.M) continue;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             const int64_t col = n0 + wn + 16 * j + 4 * q4;
             TC* p = Cp + row * a.ldc + col;
             if (col + 3 < a.N) {
@@ -264,12 +279,32 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s)
     const bool main_path = a.K % 64 == 0 && (int64_t)TM * a.lda * 2 < ((int64_t)1 << 31) &&
                            (int64_t)TN * a.ldb * 2 < ((int64_t)1 << 31);
     if (main_path) {
-        const int64_t tiles = ((a.M + TM - 1) / TM) * ((a.N + TN - 1) / TN);
-        dim3 grid((unsigned)tiles), block(256);
-        if (a.c_dtype == F32)
-            hipLaunchKernelGGL(gemm256_kernel<float>, grid, block, 0, s, a);
-        else
-            hipLaunchKernelGGL(gemm256_kernel<bf16_t>, grid, block, 0, s, a);
+        // whole 256-column tiles, then the last N mod 256 columns in 64- or
+        // 128-column tiles (the 64 columns of the beta projection in the
+        // 41,024-wide input projection: one more round of 32 workgroups)
+        const int64_t tiles_m = (a.M + TM - 1) / TM;
+        GemmArgs m = a;
+        m.N = a.N / TN * TN;
+        if (m.N > 0) {
+            dim3 grid((unsigned)(tiles_m * (m.N / TN))), block(256);
+            if (a.c_dtype == F32) hipLaunchKernelGGL((gemm256_kernel<float, 8>), grid, block, 0, s, m);
+            else hipLaunchKernelGGL((gemm256_kernel<bf16_t, 8>), grid, block, 0, s, m);
+        }
+        GemmArgs r = a;
+        r.N = a.N - m.N;
+        if (r.N > 0) {
+            r.B = static_cast<const bf16_t*>(a.B) + m.N * a.ldb;
+            r.C = static_cast<uint8_t*>(a.C) + m.N * (a.c_dtype == F32 ? 4 : 2);
+            const int nj = r.N <= 64 ? 2 : (r.N <= 128 ? 4 : 8);
+            dim3 grid((unsigned)(tiles_m * ((r.N + 32 * nj - 1) / (32 * nj)))), block(256);
+#define KDA_GEMM_REM(NJ)                                                                            \
+    if (a.c_dtype == F32) hipLaunchKernelGGL((gemm256_kernel<float, NJ>), grid, block, 0, s, r);     \
+    else hipLaunchKernelGGL((gemm256_kernel<bf16_t, NJ>), grid, block, 0, s, r);
+            if (nj == 2) { KDA_GEMM_REM(2) }
+            else if (nj == 4) { KDA_GEMM_REM(4) }
+            else { KDA_GEMM_REM(8) }
+#undef KDA_GEMM_REM
+        }
         return hipGetLastError();
     }
     dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM)), block(kThreads);
