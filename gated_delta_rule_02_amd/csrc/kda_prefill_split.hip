@@ -655,11 +655,15 @@ hipError_t launch_prefill_split(const PrefillArgs& a, void* ws, size_t ws_bytes,
         // return at once
         sa.groups = intra_groups(active, sa.nwin);
         const dim3 gi((unsigned)(U * sa.groups)), bi(kThreads);
-        // state pass: 4 workgroups of 32 columns per unit while they all fit
-        // on the chip at once (one per compute unit), else 2 of 64 columns
-        // (each wavefront then carries two tiles through every operand read);
-        // the two give identical results
-        const bool narrow = active * 4 <= 256;
+        // state pass: 4 workgroups of 32 columns per state chain while they
+        // all fit on the chip at once (one per compute unit), else 2 of 64
+        // columns (each wavefront then carries two tiles through every
+        // operand read); segment maps run two chains per unit. Measured: a
+        // second round of 32-column workgroups costs more than the wider
+        // ones (packed varlen 6.66 against 6.47 ms; one segment's maps, 64
+        // heads, 0.070 against 0.064 ms). The two give identical results.
+        const int64_t chains = active * (a.map_M ? 2 : 1);
+        const bool narrow = chains * 4 <= 256;
         if (max_chunks > 0) {
             if (stream)
                 hipLaunchKernelGGL((intra_kernel<bf16_t, kStream>), gi, bi, 0, s, sa);
