@@ -17,8 +17,12 @@
 //   instruction covers 1 KiB of a row, and several such steps of every row
 //   are loaded before any is used; the partial dot products are summed
 //   across the wavefront at the end. Reading whole rows in 1-KiB pieces
-//   matters: forms that fed the matrix cores directly (16 rows x 64 bytes per
-//   load instruction) streamed W at only 3.5-4.2 TB/s.
+//   matters: the matrix-core form below (16 rows x 64 bytes per load
+//   instruction) streams W at only about 3.7 TB/s, so it serves only 5 to 8
+//   tokens, where the arithmetic of this form grows past it.
+// * gemv_fp8_mfma_kernel: 16 rows of W per workgroup through 16x16x32 bf16
+//   products (the E4M3 codes converted exactly to bf16, x's rows as the other
+//   operand), float32 block partials scaled once per 128-k block.
 // * norm_gate_fp8_kernel: the epilogue (per-head RMSNorm x weight x
 //   sigmoid(gate)) with its output quantized per (token, head) -- one group
 //   of 128 channels: scale = amax / 448, codes = round-to-nearest-even E4M3
@@ -124,6 +128,110 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_fp8_kernel(Fp8GemvArgs a)
     }
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kMfmaSteps = 4;            // 128-k blocks of W (and x) in flight per wavefront
+constexpr int64_t kWaveTarget = 2560;  // about ten wavefronts per compute unit, all resident at once
+
+// 8 E4M3 codes (two dwords, lowest byte first) -> 8 bfloat16 by the hardware
+// conversion with unit scale; exact, since every E4M3 value is a bfloat16
+__device__ __forceinline__ bf16x8_t codes_to_bf16(uint32_t d0, uint32_t d1)
+{
+    const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)d0, 1.0f, false);
+    const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)d0, 1.0f, true);
+    const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)d1, 1.0f, false);
+    const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)d1, 1.0f, true);
+    return bf16x8_t{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+// Several tokens (5 to 8): the arithmetic of the form above grows with the
+// token count and bounds it, so the 16-row tiles go through the matrix cores.
+// One workgroup per 16 rows of W, KS wavefronts splitting its 128-k blocks
+// round robin (block kb to wavefront kb % KS). Per block a lane loads 2 x 16
+// codes of its row (lane % 16) at k = 16 (lane / 16) and 64 + 16 (lane / 16)
+// and the same k of x's row lane % 16, so that four 16x16x32 products give the
+// block's 16 x 16 partial y in float32; the block scale (staged in LDS)
+// multiplies it once. The loads of the next kMfmaSteps - 1 blocks are in flight
+// while a block is computed; the loop body has no branches (loads past a
+// wavefront's last block re-read that block and are not accumulated), so the
+// waits stay exact. The KS partial results are summed in a fixed order through
+// LDS.
+template <typename TOUT, int KS>
+__global__ __launch_bounds__(KS * 64) void gemv_fp8_mfma_kernel(Fp8GemvArgs a)
+{
+    extern __shared__ float scl[];  // the K / 128 block scales of these rows
+    __shared__ f32x4 red[KS > 1 ? KS - 1 : 1][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r16 = lane & 15, q4 = lane >> 4;
+    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int nkb = (int)(a.K >> 7);
+    const int cnt = (nkb - wave + KS - 1) / KS;  // this wavefront's blocks: wave, wave + KS, ... (at least one)
+    // A lane past the last row of W or the last token reads row 0 instead: an
+    // output row or column depends only on its own row of W or x, and those
+    // past the ends are never stored.
+    const bool xok = r16 < a.M;
+    const uint8_t* wp = a.w + (n0 + r16 < a.N ? n0 + r16 : 0) * a.ldw + 16 * q4;
+    const bf16_t* xp = static_cast<const bf16_t*>(a.x) + (xok ? r16 : 0) * a.ldx + 16 * q4;
+
+    u32x4_t wb[kMfmaSteps][2], xb[kMfmaSteps][4];
+#define KDA_GEMV_LOAD(T, S)                                                                         \
+    {                                                                                               \
+        const int64_t k_ = (int64_t)(wave + KS * min((T), cnt - 1)) * 128;                          \
+        wb[S][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wp + k_));            \
+        wb[S][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wp + k_ + 64));       \
+        xb[S][0] = ld16(xp + k_);                                                                   \
+        xb[S][1] = ld16(xp + k_ + 8);                                                               \
+        xb[S][2] = ld16(xp + k_ + 64);                                                              \
+        xb[S][3] = ld16(xp + k_ + 72);                                                              \
+    }
+#pragma unroll
+    for (int s = 0; s < kMfmaSteps; ++s) KDA_GEMV_LOAD(s, s)
+    {
+        const float* sp = a.ws + (n0 >> 7) * a.ws_ld;  // 16 | 128: the rows share one block row of scales
+        for (int i = threadIdx.x; i < nkb; i += KS * 64) scl[i] = sp[i];
+        __syncthreads();
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int t0 = 0; t0 < cnt; t0 += kMfmaSteps) {
+#pragma unroll
+        for (int s = 0; s < kMfmaSteps; ++s) {
+            const int t = t0 + s;
+            f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(wb[s][h][0], wb[s][h][1]),
+                                                            __builtin_bit_cast(bf16x8_t, xb[s][2 * h]), c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(wb[s][h][2], wb[s][h][3]),
+                                                            __builtin_bit_cast(bf16x8_t, xb[s][2 * h + 1]), c, 0, 0, 0);
+            }
+            const float sc = scl[wave + KS * min(t, cnt - 1)];
+            const bool live = t < cnt;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = live ? fmaf(sc, c[e], acc[e]) : acc[e];
+            KDA_GEMV_LOAD(t + kMfmaSteps, s)
+        }
+    }
+#undef KDA_GEMV_LOAD
+    // lane (j, q) holds y[token j][rows n0 + 4q .. n0 + 4q + 3]
+    if constexpr (KS > 1) {
+        if (wave > 0) red[wave - 1][lane] = acc;
+        __syncthreads();
+        if (wave > 0) return;
+#pragma unroll
+        for (int w = 0; w < KS - 1; ++w) acc += red[w][lane];
+    }
+    if (xok) {
+        TOUT* y = static_cast<TOUT*>(a.y) + r16 * a.ldy;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t n = n0 + 4 * q4 + e;
+            if (n < a.N) st(y + n, acc[e]);
+        }
+    }
+}
+
 constexpr int kNormRows = 4;  // (token, head) rows per workgroup, one wavefront each
 
 template <typename TO, typename TG>
@@ -158,20 +266,41 @@ void launch_gemv_rs(const Fp8GemvArgs& a, hipStream_t s)
     else hipLaunchKernelGGL((gemv_fp8_kernel<bf16_t, M, R, S>), grid, block, 0, s, a);
 }
 
+static void launch_gemv_mfma(const Fp8GemvArgs& a, hipStream_t s)
+{
+    // split K over up to 8 wavefronts per 16 rows while the whole grid stays
+    // within about ten wavefronts per compute unit (one round, no tail)
+    const int64_t tiles = (a.N + 15) / 16;
+    const int64_t nkb = a.K / 128;
+    int ks = 1;
+    while (ks < 8 && 2 * ks <= nkb && tiles * 2 * ks <= kWaveTarget) ks *= 2;
+    const dim3 grid((unsigned)tiles), block(64 * ks);
+    const size_t lds = (size_t)nkb * sizeof(float);
+#define KDA_GEMV_CASE(KS)                                                                                  \
+    case KS:                                                                                               \
+        if (a.y_dtype == F32) hipLaunchKernelGGL((gemv_fp8_mfma_kernel<float, KS>), grid, block, lds, s, a); \
+        else hipLaunchKernelGGL((gemv_fp8_mfma_kernel<bf16_t, KS>), grid, block, lds, s, a);                \
+        break;
+    switch (ks) {
+        KDA_GEMV_CASE(1) KDA_GEMV_CASE(2) KDA_GEMV_CASE(4) KDA_GEMV_CASE(8)
+    }
+#undef KDA_GEMV_CASE
+}
+
 hipError_t launch_gemv_fp8(const Fp8GemvArgs& a, hipStream_t s)
 {
-    // one token: 2 rows per wavefront, 4 KiB of each in flight (measured
-    // 29.2 us on the 41,024 x 4,096 projection against 30.7 us for 4 rows x
-    // 1 KiB); more tokens: 4 rows x 1 KiB, x's values then serve 4 rows
+    // measured on the 41,024 x 4,096 projection: one token, 2 rows per
+    // wavefront with 4 KiB of each in flight (29.2 us; 4 rows x 1 KiB 30.7);
+    // two tokens, 2 rows x 2 KiB (32.0 us; 4 x 1 KiB 34.2); three or four,
+    // 4 rows x 1 KiB, so that x's values serve 4 rows (4 tokens 42.9 us); 5 to
+    // 8 tokens, the matrix-core form, whose cost hardly grows with the token
+    // count (8 tokens: the 4 x 1 KiB form took 79.7 us)
     switch (a.M) {
         case 1: launch_gemv_rs<1, 2, 4>(a, s); break;
-        case 2: launch_gemv_rs<2, 4, 1>(a, s); break;
+        case 2: launch_gemv_rs<2, 2, 2>(a, s); break;
         case 3: launch_gemv_rs<3, 4, 1>(a, s); break;
         case 4: launch_gemv_rs<4, 4, 1>(a, s); break;
-        case 5: launch_gemv_rs<5, 4, 1>(a, s); break;
-        case 6: launch_gemv_rs<6, 4, 1>(a, s); break;
-        case 7: launch_gemv_rs<7, 4, 1>(a, s); break;
-        case 8: launch_gemv_rs<8, 4, 1>(a, s); break;
+        case 5: case 6: case 7: case 8: launch_gemv_mfma(a, s); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
