@@ -64,13 +64,14 @@ def test_gemv_fp8_bf16_output():
     assert relerr(host64(y), ref) < 5e-3
 
 
-@pytest.mark.parametrize("N,Kd", [(5 * 8192 + 64, 4096), (4096, 8192)])
-def test_gemv_fp8_layer_shapes_full(N, Kd):
-    """The layer's projections at full size for one decode token: the input
-    projection (41,024 x 4,096) and the output projection (4,096 x 8,192);
-    every output checked."""
-    announce("gemv fp8 full N=%d K=%d" % (N, Kd))
-    y, ref = run_gemv(1, N, Kd, seed=N)
+@pytest.mark.parametrize("M,N,Kd", [(1, 5 * 8192 + 64, 4096), (1, 4096, 8192), (8, 5 * 8192 + 64, 4096),
+                                    (6, 4096, 8192)])
+def test_gemv_fp8_layer_shapes_full(M, N, Kd):
+    """The layer's projections at full size: the input projection (41,024 x
+    4,096) and the output projection (4,096 x 8,192), for one decode token and
+    for several (the matrix-core form); every output checked."""
+    announce("gemv fp8 full M=%d N=%d K=%d" % (M, N, Kd))
+    y, ref = run_gemv(M, N, Kd, seed=N + M)
     e = relerr(host64(y), ref)
     print("  err %.2e" % e, flush=True)
     assert e < 2e-5
