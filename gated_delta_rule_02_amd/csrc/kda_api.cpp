@@ -64,6 +64,25 @@ bool overlap(Range a, Range b)
         if (!(cond)) return fail(code, __VA_ARGS__); \
     } while (0)
 
+// Log-retention floor of the chunked forms. Every factor 2^x those forms
+// build spans the clamped log-retentions of at most one 16-token block, so
+// |x| <= 16 |lower_bound| log2(e); at -5.4 that is 124.7, which keeps every
+// factor a normal float32 (|x| < 126). NaN and positive floors (retention
+// above one) are invalid; floors below -5.4 are not supported by the chunk
+// form (the token-serial decode takes any floor <= 0).
+constexpr float kChunkLowerBoundMin = -5.4f;
+
+int check_lower_bound(const char* fn, float lb, bool chunked)
+{
+    REQUIRE(lb == lb && lb <= 0.0f, KDA_ERR_INVALID_ARG, "%s: lower_bound must be <= 0 and not NaN (got %g)", fn,
+            (double)lb);
+    if (chunked)
+        REQUIRE(lb >= kChunkLowerBoundMin, KDA_ERR_UNSUPPORTED,
+                "%s: lower_bound below %g is not supported by the chunk form (got %g)", fn,
+                (double)kChunkLowerBoundMin, (double)lb);
+    return KDA_OK;
+}
+
 // cu_seqlens on the host: cu[0] = 0, non-decreasing, cu[N] = T.
 int check_cu(const int32_t* cu_dev, const int32_t* cu_host, int num_seqs, int64_t T, int64_t* seq_len)
 {
@@ -123,6 +142,7 @@ static int decode_impl(const char* fn, const void* q, const void* k, const void*
             dv);
     REQUIRE((int64_t)B * H <= 0x7fffffff && (int64_t)B * Tq * H <= ((int64_t)1 << 40), KDA_ERR_INVALID_ARG,
             "%s: B*H too large", fn);
+    if (int rc = check_lower_bound(fn, lower_bound, false); rc != KDA_OK) return rc;
     for (const void* p : {q, k, v, g, beta, (const void*)state, (const void*)token_states, (const void*)o})
         REQUIRE(!p || aligned16(p), KDA_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
     const size_t rows = (size_t)B * H, trows = rows * Tq, ss = 128 * 128 * esize(state_dtype);
@@ -277,6 +297,7 @@ int kda_gate_prologue(const void* f, int64_t f_ld, const void* b, int64_t b_ld,
     REQUIRE(valid_dtype(in_dtype) && valid_dtype(out_dtype), KDA_ERR_INVALID_ARG, "kda_gate_prologue: bad dtype");
     REQUIRE(num_tokens >= 0 && H >= 1, KDA_ERR_INVALID_ARG, "kda_gate_prologue: bad sizes");
     REQUIRE(dk == 128, KDA_ERR_UNSUPPORTED, "kda_gate_prologue: only dk = 128 is supported");
+    if (int rc = check_lower_bound("kda_gate_prologue", lower_bound, false); rc != KDA_OK) return rc;
     REQUIRE(f_ld >= (int64_t)H * dk && f_ld % 8 == 0 && b_ld >= H, KDA_ERR_INVALID_ARG,
             "kda_gate_prologue: f_ld must be >= H*dk and a multiple of 8; b_ld >= H");
     for (const void* p : {f, b, (const void*)A_log, (const void*)g_out, (const void*)beta_out})
@@ -393,6 +414,7 @@ static int prefill_impl(const void* q, const void* k, const void* v, const void*
     REQUIRE(num_tokens >= 0 && H >= 1, KDA_ERR_INVALID_ARG, "kda_prefill: bad num_tokens or H");
     REQUIRE(dk == 128 && dv == 128, KDA_ERR_UNSUPPORTED,
             "kda_prefill: only dk = dv = 128 is supported (got %d, %d)", dk, dv);
+    if (int rc = check_lower_bound("kda_prefill", lower_bound, true); rc != KDA_OK) return rc;
     REQUIRE(num_tokens == 0 || (q && k && v && g && beta && o), KDA_ERR_INVALID_ARG,
             "kda_prefill: null tensor pointer");
     for (const void* p : {q, k, v, g, beta, (const void*)initial_state, (const void*)final_state, (const void*)o,
@@ -501,6 +523,7 @@ int kda_prefill_segment_maps(const void* k, const void* v, const void* g, const 
     REQUIRE(num_tokens >= 0 && H >= 1, KDA_ERR_INVALID_ARG, "kda_prefill_segment_maps: bad num_tokens or H");
     REQUIRE(dk == 128 && dv == 128, KDA_ERR_UNSUPPORTED,
             "kda_prefill_segment_maps: only dk = dv = 128 is supported (got %d, %d)", dk, dv);
+    if (int rc = check_lower_bound("kda_prefill_segment_maps", lower_bound, true); rc != KDA_OK) return rc;
     REQUIRE(M_out && N_out, KDA_ERR_INVALID_ARG, "kda_prefill_segment_maps: null M_out or N_out");
     REQUIRE(num_tokens == 0 || (k && v && g && beta), KDA_ERR_INVALID_ARG,
             "kda_prefill_segment_maps: null tensor pointer");

@@ -23,9 +23,11 @@
 // i's block, and G_R the block total:
 //   b_r - b_i = l_r + (rho_R - rho_{I+1}) + s_i   (i in block I < R: all <= 0)
 //   b_r - b_i = l_r + s_i - G_R                   (i, r in the same block R)
-// Every factor 2^x of a block product then lies in [2^-116, 2^116] because the
-// log-retention is clamped at -5 ("safe forget gate ... lower bound -5" in the
-// flozi.net section above): 15 tokens x 5 x log2(e) < 116 < 127.
+// Every factor 2^x of a block product then spans the clamped log-retentions of
+// at most one block (16 tokens), so |x| <= 16 |lower_bound| log2(e): 115.4 at
+// the -5 floor of the safe forget gate (flozi.net section above), and 124.7 at
+// -5.4, the lowest floor the library accepts, which keeps every factor a
+// normal float32 (neither infinite nor subnormal).
 //
 // Work split. A workgroup of 8 wavefronts handles one chunk at a time:
 //   P0  each producer thread (2 key channels, a row group of a 16-token

@@ -81,7 +81,12 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  *            overlap is rejected.
  * o          [num_tokens, H, dv]   out_dtype (float32 keeps full precision).
  * scale      read-out multiplier (1.0 for the plain S^T q read).
- * lower_bound  log-retention floor, -5 for the safe forget gate.
+ * lower_bound  log-retention floor: -5 for the safe forget gate of the same
+ *            section. Must lie in [-5.4, 0]: the chunk form multiplies decay
+ *            factors 2^x with |x| up to 16 |lower_bound| log2(e) (one 16-token
+ *            block of clamped log-retentions), which must stay within the
+ *            normal float32 range. NaN or a positive floor returns
+ *            KDA_ERR_INVALID_ARG, a floor below -5.4 KDA_ERR_UNSUPPORTED.
  * workspace / workspace_bytes  device scratch, caller-owned, not touching
  *            any tensor above. NULL: the single-pass form runs (one workgroup
  *            per (sequence, head) carries the state through all chunks; no
@@ -100,6 +105,13 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  *            contents need no initialisation and are garbage afterwards; calls
  *            that share a workspace must be ordered on one stream.
  * Supported: dk = dv = 128, H >= 1, in_dtype F32 or BF16.
+ * Value range (BF16 inputs): the value side of the chunk form (v, the states,
+ *            the corrected writes u_r = beta_r (v_r - S'^T k_r) and the
+ *            products formed from them) runs on float16 matrix operands, so
+ *            every such entry must stay below 65,504 in magnitude (values of
+ *            order one in the model; a larger one overflows to inf in o and
+ *            the state). F32 inputs and the decode entry points have no such
+ *            limit (float32 arithmetic throughout).
  * ---------------------------------------------------------------------- */
 int kda_prefill(const void* q, const void* k, const void* v, const void* g, const void* beta,
                 kda_dtype in_dtype, int64_t num_tokens, int H, int dk, int dv,
@@ -195,6 +207,9 @@ int kda_affine_apply(const float* M, const float* X, const float* N, float* Y, i
  * state   float32 [B, H, dk, dv], read and overwritten with the new state
  *         (kda_decode_multi with num_tokens = 1 takes a bfloat16 state too).
  * o       [B, H, dv] out_dtype.
+ * lower_bound  log-retention floor (-5 in the model): any value <= 0, -inf
+ *         included (no clamp); NaN or a positive floor returns
+ *         KDA_ERR_INVALID_ARG.
  * Supported: dk = dv = 128, B >= 1, H >= 1.
  * ---------------------------------------------------------------------- */
 int kda_decode_step(const void* q, const void* k, const void* v, const void* g, const void* beta,
@@ -370,6 +385,7 @@ int kda_conv_prefill(const void* x, int64_t x_ld, int64_t num_tokens, int C, int
  *   beta = sigmoid(b)                                            [T, H]
  * f rows of H*dk at f + t * f_ld; b rows of H at b + t * b_ld (in_dtype);
  * A_log float32 [H]; g_out [T, H, dk] and beta_out [T, H] in out_dtype.
+ * lower_bound <= 0 and not NaN (else KDA_ERR_INVALID_ARG).
  * ---------------------------------------------------------------------- */
 int kda_gate_prologue(const void* f, int64_t f_ld, const void* b, int64_t b_ld,
                       const float* A_log, int64_t num_tokens, int H, int dk, float lower_bound,
@@ -379,9 +395,9 @@ int kda_gate_prologue(const void* f, int64_t f_ld, const void* b, int64_t b_ld,
 /* ------------------------------------------------------------------------
  * kda_output_norm_gate -- epilogue: per-head RMSNorm times sigmoid gate.
  *
- * "An output normalization and sigmoid gate precede the projection back to
- * width 4,096" (flozi.net page, section "KDA replaces a token list with a
- * recurrent matrix"). Per token and head:
+ * The mixer normalises its output and multiplies it by a sigmoid gate before
+ * the projection back to the hidden width of 4,096 (flozi.net page, section
+ * "KDA replaces a token list with a recurrent matrix"). Per token and head:
  *   y = o / sqrt(mean(o^2) + eps) * norm_weight * sigmoid(gate)
  * o [T, H, dv] (o_dtype); gate rows of H*dv at gate + t * gate_ld (stored in
  * y_dtype); norm_weight float32 [dv]; y [T, H*dv] (y_dtype), must not overlap o.

@@ -279,6 +279,15 @@ def round_bf16(x):
     """
     x = np.asarray(x, dtype=np.float64)
     out = np.empty_like(x)
+    flat_in, flat_out = x.reshape(-1), out.reshape(-1)
+    step = 1 << 20  # element-wise, so taken in pieces (small temporaries)
+    for i in range(0, flat_in.size, step):
+        flat_out[i:i + step] = _round_bf16_piece(flat_in[i:i + step])
+    return out
+
+
+def _round_bf16_piece(x):
+    out = np.empty_like(x)
     m, e = np.frexp(x)
     normal = np.abs(x) >= 2.0 ** -126
     out[normal] = np.ldexp(np.rint(m[normal] * 256.0) / 256.0, e[normal])
@@ -371,13 +380,15 @@ def output_norm_gate(o, gate, w, eps=1e-6):
 
 def layer_forward(x, Wq, Wk, Wv, Wf, Wg, Wb, Wo, conv_q, conv_k, conv_v, A_log, norm_w,
                   H, d=128, scale=1.0, lower_bound=-5.0, l2_eps=1e-6, rms_eps=1e-6,
-                  nthreads=None, return_parts=False):
+                  nthreads=None, return_parts=False, initial_state=None):
     """Whole KDA token mixer on one sequence, FP64, rounding to bfloat16 exactly
     where the library stores bfloat16 (projection outputs, conv outputs, gate
     outputs, epilogue output).
 
-    x: [T, hidden]; W*: [out, in] (y = x W^T); conv_*: [H*d, 4].
-    Returns out [T, hidden] float64 (and a dict of intermediates if asked).
+    x: [T, hidden]; W*: [out, in] (y = x W^T); conv_*: [H*d, 4];
+    initial_state: the KDA state [1, H, d, d] before the first token, or None
+    (zeros). Returns out [T, hidden] float64 (and a dict of intermediates,
+    the final state among them as "S", if asked).
     """
     x = np.asarray(x, dtype=np.float64)
     T = x.shape[0]
@@ -394,7 +405,7 @@ def layer_forward(x, Wq, Wk, Wv, Wf, Wg, Wb, Wo, conv_q, conv_k, conv_v, A_log, 
     g, beta = gate_prologue(f_pre.reshape(T, H, d), b_pre, A_log, lower_bound)
     g, beta = round_bf16(g), round_bf16(beta)
     o, S = kda_serial(q.reshape(T, H, d), k.reshape(T, H, d), v.reshape(T, H, d), g, beta,
-                      scale=scale, lower_bound=lower_bound, nthreads=nthreads)
+                      initial_state=initial_state, scale=scale, lower_bound=lower_bound, nthreads=nthreads)
     y = round_bf16(output_norm_gate(o, g_pre, norm_w, rms_eps)).reshape(T, H * d)
     out = mm(y, Wo)
     if return_parts:

@@ -301,3 +301,40 @@ def test_affine_apply_validation():
     assert f(Y=fake(1))[0] == K.KDA_ERR_INVALID_ARG               # is M
     assert f(Y=fake(3) + 65536)[0] == K.KDA_ERR_INVALID_ARG       # partly N
     assert f(X=fake(2) + 4)[0] == K.KDA_ERR_INVALID_ARG
+
+
+def test_lower_bound_validation():
+    """The log-retention floor is checked before any launch. The chunked forms
+    (prefill, snapshots, segment maps) take floors in [-5.4, 0]: below that a
+    block of 16 clamped log-retentions would push a decay factor 2^x out of the
+    normal float32 range. NaN and positive floors are invalid everywhere; the
+    token-serial decode and the gate take any floor <= 0 (-inf: no clamp)."""
+    nan, inf = float("nan"), float("inf")
+    for lb in (nan, 0.5, inf):
+        rc, msg = prefill(lb=lb)
+        assert rc == K.KDA_ERR_INVALID_ARG and "lower_bound" in msg, (lb, rc, msg)
+        rc, msg = segmaps(lb=lb)
+        assert rc == K.KDA_ERR_INVALID_ARG and "lower_bound" in msg, (lb, rc, msg)
+    for lb in (-5.41, -6.0, -20.0, -inf):
+        rc, msg = prefill(lb=lb)
+        assert rc == K.KDA_ERR_UNSUPPORTED and "lower_bound" in msg, (lb, rc, msg)
+        rc, msg = segmaps(lb=lb)
+        assert rc == K.KDA_ERR_UNSUPPORTED and "lower_bound" in msg, (lb, rc, msg)
+    # in range: validation moves on to the next check (a misaligned q here)
+    for lb in (-5.4, -5.0, -1.0, 0.0):
+        rc, msg = prefill(lb=lb, q=fake(1) + 8)
+        assert rc == K.KDA_ERR_INVALID_ARG and "aligned" in msg, (lb, rc, msg)
+    dec = [fake(1), fake(2), fake(3), fake(4), fake(5), K.KDA_BF16, 256, 64, 128, 128, 1.0, -5.0,
+           fake(6, 1 << 34), fake(9), K.KDA_F32, None]
+    for lb in (nan, 0.5):
+        a = list(dec); a[11] = lb
+        rc, msg = call("kda_decode_step", *a)
+        assert rc == K.KDA_ERR_INVALID_ARG and "lower_bound" in msg
+    for lb in (-6.0, -inf):
+        a = list(dec); a[11] = lb; a[0] = fake(1) + 8
+        rc, msg = call("kda_decode_step", *a)
+        assert rc == K.KDA_ERR_INVALID_ARG and "aligned" in msg
+    gate = [fake(1), 8192, fake(2), 64, fake(3), 16, 64, 128, -5.0, K.KDA_BF16, fake(4), fake(5), K.KDA_BF16, None]
+    a = list(gate); a[8] = nan
+    rc, msg = call("kda_gate_prologue", *a)
+    assert rc == K.KDA_ERR_INVALID_ARG and "lower_bound" in msg

@@ -200,27 +200,26 @@ def test_decode_commit_selects_accepted_state():
         assert torch.equal(st[b], want), b
 
 
-def test_decode_multi_workload_full_size_sampled():
+def test_decode_multi_workload_full_size():
     """Draft verification at full size: B=256 sequences x 4 tokens x 64 heads,
-    per-token states kept (4 GiB). The oracle checks 16 sampled (sequence,
-    head) pairs at every token; every state must be finite."""
+    per-token states kept (4 GiB). Every output and every per-token state of
+    every (sequence, head) against the oracle's states after each token (per
+    tensor: o whole, each sequence's state after each token over its heads)."""
     announce("decode multi full B=256 Tq=4 H=64")
     d = synth.workload_decode_multi()
     B, Tq, H = 256, d["Tq"], 64
     o, st, ts = run_multi(d, d["state"], B, Tq)
-    assert torch.isfinite(ts).all()
-    oh = host64(o)
-    rng = np.random.default_rng(7)
-    for b, h in zip(rng.integers(0, B, 16), rng.integers(0, H, 16)):
-        rows = slice(b * Tq, (b + 1) * Tq)
-        sub = lambda x: x.vals[rows, h:h + 1]
-        ro, _, rts = R.kda_serial_snapshots(sub(d["q"]), sub(d["k"]), sub(d["v"]), sub(d["g"]),
-                                            d["beta"].vals[rows, h:h + 1], 1,
-                                            initial_state=d["state"][b:b + 1, h:h + 1].astype(np.float64))
-        assert relerr(oh[b, :, h], ro[:, 0]) < TOL_BF16
-        tsh = host64(ts[b, :, h])
+    cu = np.arange(0, B * Tq + 1, Tq)
+    ro, _, rts = R.kda_serial_snapshots(d["q"].vals, d["k"].vals, d["v"].vals, d["g"].vals, d["beta"].vals, 1,
+                                        cu_seqlens=cu, initial_state=d["state"].astype(np.float64))
+    eo = relerr(host64(o).reshape(B * Tq, H, 128), ro)
+    es = 0.0
+    for b in range(B):
+        tsh = host64(ts[b])
         for t in range(Tq):
-            assert relerr(tsh[t], rts[0, t, 0]) < TOL_BF16, (b, h, t)
+            es = max(es, relerr(tsh[t], rts[b, t]))
+    print("  o err %.3e  token-state err %.3e" % (eo, es), flush=True)
+    assert eo < TOL_BF16 and es < TOL_BF16
 
 
 # ------------------------------------------------------------ bf16 state storage

@@ -275,13 +275,15 @@ def test_random_varlen_two_chunk_windows(seed):
     check(o1, s1, ro, rS, TOL_BF16)
 
 
-def test_varlen_workload_full_size_sampled():
+def test_varlen_workload_full_size():
     """Packed varlen workload at full size: 8 sequences (123,444 tokens, up to
     447 chunks each), H = 64, bf16 inputs, random fp32 initial states, final
-    states returned; default two-pass form with windows of up to 32 chunks. The GPU runs
-    every head; the oracle checks heads 0 and 41 of every sequence (o and
-    final state), and every other head's final state must be finite."""
-    announce("prefill varlen full size (sampled heads)")
+    states returned; default two-pass form with windows of up to 32 chunks.
+    Every head of every sequence is compared with the oracle (o and final
+    state). The oracle runs in slices of 8 heads to bound host memory; the
+    error of each sequence's o and final state is max|gpu - ref| / max|ref|
+    over all of its heads, accumulated across the slices."""
+    announce("prefill varlen full size (all heads)")
     d = synth.workload_varlen()
     cu = d["cu_seqlens"]
     q, k, v, g, b = (dev(d[x]) for x in ("q", "k", "v", "g", "beta"))
@@ -294,19 +296,29 @@ def test_varlen_workload_full_size_sampled():
     K.kda_prefill(q, k, v, g, b, o, cu_seqlens=cu_d, cu_seqlens_host=torch.from_numpy(cu), num_seqs=N,
                   initial_state=s0, final_state=sT)
     torch.cuda.synchronize()
-    assert torch.isfinite(sT).all()
     del q, k, v, g, b
-    for h in (0, 41):
-        ro, rS = R.kda_serial(d["q"].vals[:, h:h + 1], d["k"].vals[:, h:h + 1], d["v"].vals[:, h:h + 1],
-                              d["g"].vals[:, h:h + 1], d["beta"].vals[:, h:h + 1], cu_seqlens=cu,
-                              initial_state=d["initial_state"][:, h:h + 1].astype(np.float64))
-        oh = o[:, h:h + 1].cpu().numpy().astype(np.float64)
+    sTh = host64(sT)
+    o_diff, o_ref = np.zeros(N), np.zeros(N)
+    s_diff, s_ref = np.zeros(N), np.zeros(N)
+    HS = 8
+    for h0 in range(0, H, HS):
+        sl = slice(h0, h0 + HS)
+        ro, rS = R.kda_serial(d["q"].vals[:, sl], d["k"].vals[:, sl], d["v"].vals[:, sl], d["g"].vals[:, sl],
+                              d["beta"].vals[:, sl], cu_seqlens=cu,
+                              initial_state=d["initial_state"][:, sl].astype(np.float64))
+        oh = o[:, sl].cpu().numpy().astype(np.float64)
         for n in range(N):
             a_, e_ = int(cu[n]), int(cu[n + 1])
-            eo = relerr(oh[a_:e_], ro[a_:e_])
-            es = relerr(host64(sT[n, h]), rS[n, 0])
-            print("  head %d seq %d (T=%d): o err %.3e  state err %.3e" % (h, n, e_ - a_, eo, es), flush=True)
-            assert eo < TOL_BF16 and es < TOL_BF16
+            o_diff[n] = max(o_diff[n], float(np.max(np.abs(oh[a_:e_] - ro[a_:e_]))))
+            o_ref[n] = max(o_ref[n], float(np.max(np.abs(ro[a_:e_]))))
+            s_diff[n] = max(s_diff[n], float(np.max(np.abs(sTh[n, sl] - rS[n]))))
+            s_ref[n] = max(s_ref[n], float(np.max(np.abs(rS[n]))))
+        print("  heads %d-%d done" % (h0, h0 + HS - 1), flush=True)
+        del ro, rS, oh
+    for n in range(N):
+        eo, es = o_diff[n] / o_ref[n], s_diff[n] / s_ref[n]
+        print("  seq %d (T=%d): o err %.3e  state err %.3e" % (n, int(cu[n + 1] - cu[n]), eo, es), flush=True)
+        assert eo < TOL_BF16 and es < TOL_BF16
 
 
 # ------------------------------------------------------------ state snapshots
@@ -375,25 +387,22 @@ def test_snapshots_across_windows_bit_equal():
     check_snapshots(s1, rsn, lens, 64, TOL_BF16)
 
 
-def test_snapshots_prefill_workload_full_size_sampled():
+def test_snapshots_prefill_workload_full_size():
     """The prefill workload (T = 4096, H = 64) with a snapshot every 1024
-    tokens, as bench.py launches it (two-pass form, two 32-chunk windows): the
-    oracle checks heads 0 and 41 at every snapshot."""
+    tokens, as bench.py launches it (two-pass form, two 32-chunk windows):
+    every head of every snapshot against the oracle."""
     announce("prefill snapshots full size")
     d = synth.workload_prefill()
     snaps = snap_buffer(1, 4, 64)
     o, sT = gpu_prefill(d, snapshots=snaps, interval=1024)
-    assert torch.isfinite(snaps).all()
     sh = host64(snaps)
-    for h in (0, 41):
-        sub = lambda x: x.vals[:, h:h + 1]
-        _, rS, rsn = R.kda_serial_snapshots(sub(d["q"]), sub(d["k"]), sub(d["v"]), sub(d["g"]),
-                                            d["beta"].vals[:, h:h + 1], 1024)
-        for j in range(4):
-            e = relerr(sh[0, j, h], rsn[0, j, 0])
-            print("  head %d snapshot %d err %.3e" % (h, j, e), flush=True)
-            assert e < TOL_BF16
-        assert np.array_equal(sh[0, 3, h], host64(sT[0, h]))  # the last snapshot is the final state
+    ro, rS, rsn = R.kda_serial_snapshots(d["q"].vals, d["k"].vals, d["v"].vals, d["g"].vals, d["beta"].vals, 1024)
+    for j in range(4):
+        e = relerr(sh[0, j], rsn[0, j])
+        print("  snapshot %d err %.3e" % (j, e), flush=True)
+        assert e < TOL_BF16
+    assert np.array_equal(sh[0, 3], host64(sT[0]))  # the last snapshot is the final state
+    check(o, sT, ro, rS, TOL_BF16)
 
 
 def test_wide_state_pass_matches_narrow_bit_for_bit():

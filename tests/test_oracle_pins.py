@@ -414,6 +414,113 @@ def test_layer_composition_identity():
     np.testing.assert_allclose(out, y @ Wo.T, rtol=1e-13)
 
 
+def _layer_case(seed, T=9, hidden=32, H=2, d=128):
+    rng = np.random.default_rng(seed)
+    W = H * d
+    r = lambda shape, sd: R.round_bf16(rng.standard_normal(shape) * sd)
+    return dict(x=r((T, hidden), 1.0), Wq=r((W, hidden), 0.2), Wk=r((W, hidden), 0.2), Wv=r((W, hidden), 0.2),
+                Wf=r((W, hidden), 0.2), Wg=r((W, hidden), 0.2), Wb=r((H, hidden), 0.5), Wo=r((hidden, W), 0.1),
+                cq=r((W, 4), 0.5), ck=r((W, 4), 0.5), cv=r((W, 4), 0.5), A_log=np.zeros(H), norm_w=np.ones(d),
+                H=H, d=d, S0=None)
+
+
+def _layer_run(c, **over):
+    a = dict(c)
+    a.update(over)
+    return R.layer_forward(a["x"], a["Wq"], a["Wk"], a["Wv"], a["Wf"], a["Wg"], a["Wb"], a["Wo"], a["cq"], a["ck"],
+                           a["cv"], a["A_log"], a["norm_w"], a["H"], a["d"], return_parts=True,
+                           initial_state=a["S0"])
+
+
+def test_layer_wiring_gate_decay_and_beta():
+    """Which projection feeds which step of the layer. W_f = 0 gives
+    softplus(0) = ln 2, so g = -exp(A_log[h]) ln 2 for every token and channel
+    (A_log = [0, ln 2]: -ln 2 and -2 ln 2), and the output gate is untouched;
+    W_g = 0 gives the gate sigmoid(0) = 1/2 (y = RMSNorm(o) / 2) and leaves the
+    decay and the core untouched; a zero b_proj row gives beta = 1/2 for that
+    head only. A swap of W_f and W_g, of the heads' rows, or a misuse of A_log
+    fails one of these."""
+    c = _layer_case(41)
+    c["A_log"] = np.array([0.0, math.log(2.0)])
+    T, H, d = c["x"].shape[0], c["H"], c["d"]
+    _, base = _layer_run(c)
+    assert np.ptp(base["g"]) > 0.1                      # the decay varies with W_f
+    _, pf = _layer_run(c, Wf=np.zeros_like(c["Wf"]))
+    np.testing.assert_array_equal(pf["g"][:, 0], np.full((T, d), R.round_bf16(-math.log(2.0))))
+    np.testing.assert_array_equal(pf["g"][:, 1], np.full((T, d), R.round_bf16(-2 * math.log(2.0))))
+    np.testing.assert_array_equal(pf["gate"], base["gate"])
+    _, pg = _layer_run(c, Wg=np.zeros_like(c["Wg"]))
+    np.testing.assert_array_equal(pg["g"], base["g"])
+    np.testing.assert_array_equal(pg["o"], base["o"])
+    o = pg["o"]
+    half = 0.5 * o / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + 1e-6)
+    np.testing.assert_array_equal(pg["y"], R.round_bf16(half).reshape(T, H * d))
+    Wb = c["Wb"].copy()
+    Wb[0] = 0.0
+    _, pb = _layer_run(c, Wb=Wb)
+    assert np.all(pb["beta"][:, 0] == 0.5) and np.ptp(pb["beta"][:, 1]) > 0.05
+    np.testing.assert_array_equal(pb["beta"][:, 1], base["beta"][:, 1])
+
+
+def test_layer_wiring_query_key_value():
+    """q is what the core reads with, k what it writes and decays along, v what
+    it writes. With a random initial state: zero q taps give o = 0 exactly; zero
+    k taps leave only the retention, o_t = (Diag(exp(sum_{s<=t} g_s)) S0)^T q_t
+    and final S = Diag(exp(sum g)) S0 (closed form); zero v taps with a zero
+    state give o = 0. A swap of q and k, or of v with either, fails one of
+    them. Only q and k are L2-normalised per head."""
+    c = _layer_case(42)
+    T, H, d = c["x"].shape[0], c["H"], c["d"]
+    rng = np.random.default_rng(43)
+    S0 = rng.standard_normal((1, H, d, d)) * 0.3
+    _, p0 = _layer_run(c, S0=S0)
+    assert np.max(np.abs(p0["o"])) > 1e-2
+    _, pq = _layer_run(c, S0=S0, cq=np.zeros_like(c["cq"]))
+    assert np.all(pq["q"] == 0.0) and np.all(pq["o"] == 0.0)
+    _, pk = _layer_run(c, S0=S0, ck=np.zeros_like(c["ck"]))
+    assert np.all(pk["k"] == 0.0)
+    q = pk["q"].reshape(T, H, d)
+    decay = np.exp(np.cumsum(np.maximum(pk["g"], -5.0), axis=0))       # [T, H, d]
+    closed = np.einsum("thc,hcj,thc->thj", decay, S0[0], q)
+    np.testing.assert_allclose(pk["o"], closed, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(pk["S"][0], decay[-1][:, :, None] * S0[0], rtol=1e-12, atol=1e-300)
+    _, pv = _layer_run(c, cv=np.zeros_like(c["cv"]))
+    assert np.all(pv["v"] == 0.0) and np.all(pv["o"] == 0.0) and np.all(pv["S"] == 0.0)
+    nq = np.linalg.norm(p0["q"].reshape(T, H, d), axis=-1)
+    nk = np.linalg.norm(p0["k"].reshape(T, H, d), axis=-1)
+    nv = np.linalg.norm(p0["v"].reshape(T, H, d), axis=-1)
+    assert np.max(np.abs(nq - 1)) < 1e-2 and np.max(np.abs(nk - 1)) < 1e-2
+    assert np.max(np.abs(nv - 1)) > 0.2
+
+
+def test_layer_wiring_conv_taps_and_output_projection():
+    """With W_k = W_q, q taps whose oldest entry is 0 and k taps = the q taps
+    moved one step older ([a, b, c, d] with a = 0 -> [b, c, d, 0]), the key at t
+    is exactly the query at t - 1 and the first key is 0: the taps run oldest to
+    newest and each stream has its own conv. A selection matrix as W_o copies
+    columns of y: out[:, j] = y[:, idx[j]] exactly. A head's zero query rows
+    silence that head's output only."""
+    c = _layer_case(44)
+    T, H, d = c["x"].shape[0], c["H"], c["d"]
+    hidden = c["x"].shape[1]
+    cq = c["cq"].copy()
+    cq[:, 0] = 0.0
+    ck = np.zeros_like(cq)
+    ck[:, :3] = cq[:, 1:]
+    _, p = _layer_run(c, Wk=c["Wq"], cq=cq, ck=ck)
+    np.testing.assert_array_equal(p["k"][1:], p["q"][:-1])
+    assert np.all(p["k"][0] == 0.0) and np.any(p["q"][0] != 0.0)
+    idx = np.random.default_rng(45).integers(0, H * d, hidden)
+    Wo = np.zeros((hidden, H * d))
+    Wo[np.arange(hidden), idx] = 1.0
+    out, p = _layer_run(c, Wo=Wo)
+    np.testing.assert_array_equal(out, p["y"][:, idx])
+    Wq = c["Wq"].copy()
+    Wq[d:] = 0.0                                       # head 1 reads with q = 0
+    _, p = _layer_run(c, Wq=Wq)
+    assert np.all(p["o"][:, 1] == 0.0) and np.max(np.abs(p["o"][:, 0])) > 1e-2
+
+
 def test_conv_bias_shifts_preactivation():
     """A per-channel bias adds to the pre-activation: with zero taps the output
     is SiLU(bias)."""
