@@ -408,7 +408,8 @@ static int prefill_impl(const void* q, const void* k, const void* v, const void*
                         const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int num_seqs,
                         float scale, float lower_bound, const float* initial_state, float* final_state,
                         void* o, kda_dtype out_dtype, void* workspace, size_t workspace_bytes,
-                        int64_t snap_interval, int64_t snap_slots, float* snapshots, void* hip_stream)
+                        int64_t snap_interval, int64_t snap_slots, float* snapshots, void* hip_stream,
+                        bool static_ws = false)
 {
     REQUIRE(valid_dtype(in_dtype) && valid_dtype(out_dtype), KDA_ERR_INVALID_ARG, "kda_prefill: bad dtype");
     REQUIRE(num_tokens >= 0 && H >= 1, KDA_ERR_INVALID_ARG, "kda_prefill: bad num_tokens or H");
@@ -426,7 +427,8 @@ static int prefill_impl(const void* q, const void* k, const void* v, const void*
     REQUIRE((int64_t)num_seqs * H * 2 <= 0x7fffffff, KDA_ERR_INVALID_ARG, "kda_prefill: num_seqs*H too large");
 
     // the two-pass form runs for bfloat16 inputs when a workspace is given
-    const bool split = in_dtype == KDA_BF16 && workspace != nullptr;
+    // (kda_prefill_noalloc: always, in the static scratch)
+    const bool split = in_dtype == KDA_BF16 && (workspace != nullptr || static_ws);
     const int64_t units = (int64_t)num_seqs * H;
     int64_t max_len = seq_len;
     if (cu_seqlens_host)
@@ -445,11 +447,27 @@ static int prefill_impl(const void* q, const void* k, const void* v, const void*
         const size_t slot = prefill_split_slot_bytes();
         const size_t whole = (size_t)(units * std::max<int64_t>(max_chunks, 1)) * slot;
         const size_t least = (size_t)units * slot + state_carry_bytes(units);
-        REQUIRE(workspace_bytes >= std::min(whole, least), KDA_ERR_WORKSPACE,
-                "kda_prefill: workspace of at least %zu bytes required (got %zu)", std::min(whole, least),
-                workspace_bytes);
+        if (static_ws) {
+            REQUIRE(std::min(whole, least) <= kStaticScratchBytes, KDA_ERR_WORKSPACE,
+                    "kda_prefill_noalloc: %lld (sequence, head) units need at least %zu bytes of workspace, more "
+                    "than the %zu-byte static scratch (at most %zu units)",
+                    (long long)units, std::min(whole, least), kStaticScratchBytes,
+                    kStaticScratchBytes / (slot + (size_t)128 * 128 * sizeof(float)));
+        } else {
+            REQUIRE(workspace_bytes >= std::min(whole, least), KDA_ERR_WORKSPACE,
+                    "kda_prefill: workspace of at least %zu bytes required (got %zu)", std::min(whole, least),
+                    workspace_bytes);
+        }
     }
 
+    if (static_ws && split) {
+        // every argument is valid: look up this device's scratch array
+        void* p = nullptr;
+        const hipError_t e = prefill_static_scratch(&p);
+        if (e != hipSuccess) return hip_status(e, "kda_prefill_noalloc: static scratch");
+        workspace = p;
+        workspace_bytes = kStaticScratchBytes;
+    }
     const size_t ei = esize(in_dtype), T = (size_t)num_tokens;
     const size_t sbytes = (size_t)num_seqs * H * 128 * 128 * 4;
     const Range ro = rng(o, T * H * 128 * esize(out_dtype));
@@ -509,6 +527,19 @@ int kda_prefill_snapshots(const void* q, const void* k, const void* v, const voi
                         scale, lower_bound, initial_state, final_state, o, out_dtype, workspace, workspace_bytes,
                         snapshot_interval, snapshot_slots, snapshots, hip_stream);
 }
+
+int kda_prefill_noalloc(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                        kda_dtype in_dtype, int64_t num_tokens, int H, int dk, int dv,
+                        const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int num_seqs,
+                        float scale, float lower_bound, const float* initial_state, float* final_state,
+                        void* o, kda_dtype out_dtype, void* hip_stream)
+{
+    return prefill_impl(q, k, v, g, beta, in_dtype, num_tokens, H, dk, dv, cu_seqlens_dev, cu_seqlens_host, num_seqs,
+                        scale, lower_bound, initial_state, final_state, o, out_dtype, nullptr, 0, 0, 0, nullptr,
+                        hip_stream, true);
+}
+
+size_t kda_prefill_noalloc_scratch_bytes(void) { return kStaticScratchBytes; }
 
 // ---------------------------------------------------------------- segment maps
 int kda_prefill_segment_maps(const void* k, const void* v, const void* g, const void* beta, kda_dtype in_dtype,

@@ -104,6 +104,11 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_split(const PrefillArgs& a, void* ws, size_t ws_bytes, int64_t max_chunks,
                                 const int32_t* cu_host, hipStream_t s);
 size_t prefill_split_slot_bytes();
+// kda_prefill_noalloc: the two-pass workspace lives in a device array of this
+// size (one per GPU, held until the process ends); prefill_static_scratch
+// returns its address on the current device (looked up once per device).
+constexpr size_t kStaticScratchBytes = (size_t)160 << 20;
+hipError_t prefill_static_scratch(void** ptr);
 // Y[b] = M[b] X[b] (+ N[b]) for b < count: float32 [count, 128, 128] matrices
 hipError_t launch_affine_apply(const float* M, const float* X, const float* N, float* Y, int64_t count,
                                hipStream_t s);

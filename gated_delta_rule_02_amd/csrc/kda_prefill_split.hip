@@ -31,6 +31,7 @@
 // sequence so that the workspace is bounded; between windows the state pass
 // carries the state through a float32 buffer in the workspace.
 #include <algorithm>
+#include <mutex>
 
 #include "kda_chunk.h"
 
@@ -594,6 +595,35 @@ constexpr size_t kStreamWorkspace = (size_t)192 << 20;
 }  // namespace
 
 size_t prefill_split_slot_bytes() { return kSlot; }
+
+// ------------------------------------------------------------ static scratch
+// The workspace of kda_prefill_noalloc, for callers that cannot allocate
+// device memory. Each GPU holds its own copy. In host code `scratch` names a
+// host-side stand-in, not the device array: the device address comes from
+// hipGetSymbolAddress, once per device with that device current, and only
+// that address is ever passed to a kernel.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+hipError_t prefill_static_scratch(void** ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 // Intra-pass workgroups per (sequence, head) for a window of nwin chunks with
 // `active` (sequence, head) units still running: the grouping that needs the

@@ -28,6 +28,8 @@ _SZ = ctypes.c_size_t
 _SIGS = {
     "kda_prefill": (_I, [_P] * 5 + [_I, _I64, _I, _I, _I, _P, _P, _I, _F, _F, _P, _P, _P, _I, _P, _SZ, _P]),
     "kda_prefill_workspace_bytes": (_SZ, [_I64, _I, _I, _I, _I, _I]),
+    "kda_prefill_noalloc": (_I, [_P] * 5 + [_I, _I64, _I, _I, _I, _P, _P, _I, _F, _F, _P, _P, _P, _I, _P]),
+    "kda_prefill_noalloc_scratch_bytes": (_SZ, []),
     "kda_prefill_snapshots": (_I, [_P] * 5 + [_I, _I64, _I, _I, _I, _P, _P, _I, _F, _F, _P, _P, _P, _I, _P, _SZ,
                                               _I64, _I64, _P, _P]),
     "kda_prefill_segment_maps": (_I, [_P] * 4 + [_I, _I64, _I, _I, _I, _P, _P, _I, _F, _P, _P, _P, _SZ, _P]),
@@ -175,6 +177,28 @@ def kda_prefill(q, k, v, g, beta, o, cu_seqlens=None, cu_seqlens_host=None, num_
               _ptr(o), _dt(o), _ptr(workspace), ws_bytes, int(snapshot_interval), snapshots.shape[1],
               _ptr(snapshots), _stream(stream))
     return o
+
+
+def kda_prefill_noalloc(q, k, v, g, beta, o, cu_seqlens=None, cu_seqlens_host=None, num_seqs=None,
+                        initial_state=None, final_state=None, scale=1.0, lower_bound=-5.0, stream=None):
+    """kda_prefill with the library's device-resident scratch in place of a
+    workspace (allocates nothing). Arguments as kda_prefill."""
+    for n_, t_ in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("o", o),
+                   ("initial_state", initial_state), ("final_state", final_state)):
+        _dense(t_, n_)
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    cu_dev, cu_host, keep = _cu(cu_seqlens, cu_seqlens_host)
+    if num_seqs is None:
+        num_seqs = (keep.numel() - 1) if keep is not None else 1
+    _call("kda_prefill_noalloc", _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _dt(q), T, H, dk, dv,
+          cu_dev, cu_host, num_seqs, scale, lower_bound, _ptr(initial_state), _ptr(final_state),
+          _ptr(o), _dt(o), _stream(stream))
+    return o
+
+
+def kda_prefill_noalloc_scratch_bytes():
+    return lib().kda_prefill_noalloc_scratch_bytes()
 
 
 def kda_prefill_workspace_bytes(num_tokens, num_seqs, H, dk=128, dv=128, in_dtype=KDA_BF16):

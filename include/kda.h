@@ -124,6 +124,35 @@ size_t kda_prefill_workspace_bytes(int64_t num_tokens, int num_seqs, int H, int 
                                    kda_dtype in_dtype);
 
 /* ------------------------------------------------------------------------
+ * kda_prefill_noalloc -- kda_prefill without a caller workspace, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.
+ *
+ * Every argument keeps its meaning in kda_prefill; there is no workspace
+ * argument. BF16 inputs run the two-pass form in a device-resident scratch
+ * array of kda_prefill_noalloc_scratch_bytes() bytes (160 MiB), defined in the
+ * library and held by each GPU the library runs on until the process ends;
+ * its address is looked up once per device, on the first call with that
+ * device current. F32 inputs run the single-pass form, which needs no scratch.
+ * The call allocates nothing. A problem whose minimum workspace (one chunk slot
+ * of 72,192 bytes plus a 64 KiB state carry per (sequence, head) unit, or a
+ * slot for every chunk if that is less) exceeds the scratch is rejected with
+ * KDA_ERR_WORKSPACE before anything is launched (at most 1,218 units, e.g. 19
+ * sequences of 64 heads); below that, the chunks run in windows of as many
+ * as the scratch holds (32-chunk windows at 64 heads). The scratch needs no
+ * initialisation and keeps the last call's garbage. All calls on one GPU share it: calls that
+ * overlap in time on one GPU (another stream, another host thread) race and
+ * must be ordered by the caller.
+ * ---------------------------------------------------------------------- */
+int kda_prefill_noalloc(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                        kda_dtype in_dtype, int64_t num_tokens, int H, int dk, int dv,
+                        const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int num_seqs,
+                        float scale, float lower_bound, const float* initial_state, float* final_state,
+                        void* o, kda_dtype out_dtype, void* hip_stream);
+
+size_t kda_prefill_noalloc_scratch_bytes(void);
+
+/* ------------------------------------------------------------------------
  * kda_prefill_snapshots -- kda_prefill that also saves the state at fixed
  * token positions of every sequence.
  *

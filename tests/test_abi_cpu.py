@@ -338,3 +338,19 @@ def test_lower_bound_validation():
     a = list(gate); a[8] = nan
     rc, msg = call("kda_gate_prologue", *a)
     assert rc == K.KDA_ERR_INVALID_ARG and "lower_bound" in msg
+
+
+def test_prefill_noalloc_validation():
+    """kda_prefill_noalloc validates like kda_prefill and rejects a problem
+    whose minimum workspace exceeds the static scratch before touching the
+    device (1,300 units x (72,192-byte slot + 64 KiB carry) > 160 MiB)."""
+    assert K.kda_prefill_noalloc_scratch_bytes() == 160 << 20
+    f = lambda T=256, H=4, N=1, lb=-5.0, q=fake(1), in_dtype=K.KDA_BF16: call(
+        "kda_prefill_noalloc", q, fake(2), fake(3), fake(4), fake(5), in_dtype, T, H, 128, 128, None, None, N,
+        1.0, lb, None, None, fake(6), K.KDA_F32, None)
+    rc, msg = f(T=2 * 1300 * 64, H=1300, N=1)
+    assert rc == K.KDA_ERR_WORKSPACE and "static scratch" in msg, msg
+    rc, msg = f(lb=-6.0)
+    assert rc == K.KDA_ERR_UNSUPPORTED and "lower_bound" in msg
+    assert f(q=None)[0] == K.KDA_ERR_INVALID_ARG
+    assert f(q=fake(1) + 8)[0] == K.KDA_ERR_INVALID_ARG
