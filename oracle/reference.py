@@ -472,3 +472,18 @@ def quantize_fp8_groups(y, group=128):
     scale = np.where(amax > 0, amax / E4M3_MAX, 1.0)
     codes = e4m3_encode(g / scale[..., None]).reshape(T, C)
     return codes, scale
+
+
+def gemm_fp8_w8a8(x_codes, x_scales, w_codes, w_scales, block=128):
+    """y = X W^T with both operands block FP8, in float64 (W8A8):
+    X[m, k] = decode(x_codes[m, k]) * x_scales[m, k // 128] (activations,
+    quantized per token and group of 128 channels) and
+    W[n, k] = decode(w_codes[n, k]) * w_scales[n // 128, k // 128] (weights,
+    128 x 128 blocks). x_codes: [M, K]; x_scales: [M, K/128]; w_codes: [N, K];
+    w_scales: [ceil(N/128), K/128]. Returns [M, N] float64."""
+    xc = np.asarray(x_codes)
+    X = e4m3_decode(xc) * np.repeat(np.asarray(x_scales, dtype=np.float64), block, axis=1)[:, :xc.shape[1]]
+    W = e4m3_decode(w_codes)
+    s = np.asarray(w_scales, dtype=np.float64)
+    W = W * np.repeat(np.repeat(s, block, axis=0), block, axis=1)[:W.shape[0], :W.shape[1]]
+    return X @ W.T

@@ -749,3 +749,53 @@ def test_segment_map_closed_forms():
     P = np.eye(4) - Hd[:m].T @ Hd[:m]
     assert np.max(np.abs(M[0, 0] - P)) < 1e-15
     assert np.max(np.abs(N[0, 0] - Hd[:m].T @ vv[:, 0])) < 1e-14
+
+
+
+# ------------------------------------------------------------ block FP8 W8A8
+def test_gemm_fp8_w8a8_brute_force():
+    """W8A8 against a triple loop over (m, n, k) that decodes each code and
+    applies its own two scales: the row scale of the activation group and the
+    128 x 128 block scale of the weight (ragged N past a block boundary)."""
+    rng = np.random.default_rng(61)
+    M, N, K = 3, 133, 256
+    finite = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    xc = rng.choice(finite, (M, K))
+    wc = rng.choice(finite, (N, K))
+    xs = rng.uniform(0.5, 2.0, (M, K // 128))
+    ws = rng.uniform(1e-3, 1e-2, ((N + 127) // 128, K // 128))
+    y = R.gemm_fp8_w8a8(xc, xs, wc, ws)
+    ref = np.zeros((M, N))
+    dec = R.e4m3_decode(np.arange(256, dtype=np.uint8))
+    for m in range(M):
+        for n in range(N):
+            acc = 0.0
+            for k in range(K):
+                acc += dec[xc[m, k]] * xs[m, k // 128] * dec[wc[n, k]] * ws[n // 128, k // 128]
+            ref[m, n] = acc
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_fp8_activation_quantization_exact_case():
+    """Activations that already lie on the E4M3 grid times a per-group scale,
+    with each group's largest magnitude exactly 448 x scale, quantize without
+    loss: the codes and scales come back exactly, and the W8A8 product then
+    equals the float64 product of the unquantized values with the dequantized
+    weights."""
+    rng = np.random.default_rng(62)
+    M, K, N = 4, 384, 64
+    pos = np.array([c for c in range(1, 0x7F)], dtype=np.uint8)
+    codes = rng.choice(pos, (M, K)) | (rng.integers(0, 2, (M, K)).astype(np.uint8) << 7)
+    for m in range(M):
+        for g in range(K // 128):
+            codes[m, 128 * g + rng.integers(0, 128)] = 0x7E      # 448: the group's maximum
+    scale = np.exp2(rng.integers(-8, 4, (M, K // 128))).astype(np.float64) * rng.uniform(1, 2, (M, K // 128))
+    x = R.e4m3_decode(codes) * np.repeat(scale, 128, axis=1)
+    qc, qs = R.quantize_fp8_groups(x)
+    np.testing.assert_array_equal(qc, codes)
+    np.testing.assert_allclose(qs, scale, rtol=1e-15)
+    wc = rng.integers(0, 0x7F, (N, K)).astype(np.uint8)
+    ws = rng.uniform(1e-3, 1e-2, (1, K // 128))
+    W = R.e4m3_decode(wc) * np.repeat(ws, 128, axis=1)
+    np.testing.assert_allclose(R.gemm_fp8_w8a8(qc, qs, wc, ws), x @ W.T, rtol=1e-12,
+                               atol=1e-12 * np.abs(x @ W.T).max())
