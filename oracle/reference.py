@@ -474,6 +474,24 @@ def quantize_fp8_groups(y, group=128):
     return codes, scale
 
 
+def quantize_fp8_groups_f32(x, group=128):
+    """The dynamic activation quantization of ``quantize_fp8_groups`` with
+    every rounding decision taken in float32, as a float32 implementation
+    takes it: the values are float32, amax is exact, scale = fl32(amax / 448)
+    (1 for an all-zero group), r = fl32(x / scale) by IEEE division, and the
+    code is the E4M3 value nearest to r (ties to even, saturating at 448),
+    decided exactly from the float32 r. Returns (codes [T, C] uint8,
+    scales [T, C/128] float32)."""
+    x = np.asarray(x, dtype=np.float32)
+    T, C = x.shape
+    g = x.reshape(T, C // group, group)
+    amax = np.max(np.abs(g), axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    r = (g / scale[..., None]).astype(np.float32)
+    codes = e4m3_encode(r.astype(np.float64)).reshape(T, C)
+    return codes, scale
+
+
 def gemm_fp8_w8a8(x_codes, x_scales, w_codes, w_scales, block=128):
     """y = X W^T with both operands block FP8, in float64 (W8A8):
     X[m, k] = decode(x_codes[m, k]) * x_scales[m, k // 128] (activations,

@@ -799,3 +799,50 @@ def test_fp8_activation_quantization_exact_case():
     W = R.e4m3_decode(wc) * np.repeat(ws, 128, axis=1)
     np.testing.assert_allclose(R.gemm_fp8_w8a8(qc, qs, wc, ws), x @ W.T, rtol=1e-12,
                                atol=1e-12 * np.abs(x @ W.T).max())
+
+
+def test_fp8_quantization_float32_decisions():
+    """The float32-decision quantizer: (1) on-grid activations with power-of-two
+    group scales (every float32 step exact) come back losslessly; (2) each
+    scale is fl32(amax / 448) computed by hand; (3) on random data it agrees
+    with the float64 quantizer except at a rare near-tie, and then by one code
+    step; (4) every value is within half a code step of its dequantized value;
+    (5) a value whose float32 quotient lies on a tie of the grid rounds to the
+    even code."""
+    rng = np.random.default_rng(63)
+    M, K = 3, 256
+    pos = np.arange(1, 0x7F, dtype=np.uint8)
+    codes = rng.choice(pos, (M, K)) | (rng.integers(0, 2, (M, K)).astype(np.uint8) << 7)
+    for m in range(M):
+        for gi in range(K // 128):
+            codes[m, 128 * gi + rng.integers(0, 128)] = 0x7E
+    scale = np.exp2(rng.integers(-10, 6, (M, K // 128))).astype(np.float32)
+    x = (R.e4m3_decode(codes) * np.repeat(scale, 128, axis=1)).astype(np.float32)
+    qc, qs = R.quantize_fp8_groups_f32(x)
+    np.testing.assert_array_equal(qc, codes)
+    np.testing.assert_array_equal(qs, scale)
+    # (2), (3), (4) on random float32 data of several magnitudes
+    y = (rng.standard_normal((64, 512)) * np.exp2(rng.integers(-12, 12, (64, 1)))).astype(np.float32)
+    y[5, 128:256] = 0.0
+    c32, s32 = R.quantize_fp8_groups_f32(y)
+    assert s32.dtype == np.float32 and s32[5, 1] == 1.0 and np.all(c32[5, 128:256] == 0)
+    for (t, gi) in ((0, 0), (17, 3), (63, 2)):
+        am = np.float32(np.max(np.abs(y[t, 128 * gi:128 * gi + 128])))
+        assert s32[t, gi] == np.float32(am / np.float32(448.0))
+    c64, _ = R.quantize_fp8_groups(y.astype(np.float64))
+    diff = c32 != c64
+    assert diff.mean() < 1e-3
+    if diff.any():
+        step = np.abs(R.e4m3_decode(c32[diff]) - R.e4m3_decode(c64[diff]))
+        mag = np.abs(R.e4m3_decode(c64[diff]))
+        assert np.all(step <= np.maximum(mag * 2.0 ** -3, 2.0 ** -9) * (1 + 1e-12))
+    deq = R.e4m3_decode(c32) * np.repeat(s32.astype(np.float64), 128, axis=1)
+    bound = np.maximum(2.0 ** -4 * np.abs(y), 2.0 ** -10 * np.repeat(s32, 128, axis=1)) * (1 + 1e-6)
+    assert np.all(np.abs(deq - y) <= bound)
+    # (5) 448 as the group maximum gives scale 1; 1.0625 sits halfway between
+    # 1.0 (code 0x38, even) and 1.125 (0x39): ties to even gives 0x38; 1.1875
+    # halfway between 1.125 (0x39) and 1.25 (0x3A) gives 0x3A
+    z = np.zeros((1, 128), np.float32)
+    z[0, :4] = [448.0, 1.0625, 1.1875, -1.0625]
+    ct, st = R.quantize_fp8_groups_f32(z)
+    assert st[0, 0] == 1.0 and list(ct[0, :4]) == [0x7E, 0x38, 0x3A, 0xB8]
