@@ -435,10 +435,11 @@ def e4m3_decode(codes):
     return np.where((c & 0x7F) == 0x7F, np.nan, val)
 
 
-def e4m3_encode(x):
+def e4m3_encode_brute(x):
     """float64 -> uint8 codes, round to nearest, ties to even, saturating at
     +-448 (values are scaled into range before encoding). Brute force over the
-    126 positive finite codes: the nearest one, and on a tie the even one."""
+    127 non-negative finite codes: the nearest one, and on a tie the even one.
+    (Memory grows as 127 x the input: small inputs only.)"""
     x = np.asarray(x, dtype=np.float64)
     grid = e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))   # codes 0 .. 126, increasing
     a = np.minimum(np.abs(x), E4M3_MAX)
@@ -449,6 +450,21 @@ def e4m3_encode(x):
     even = (np.arange(0, 0x7F) % 2 == 0)
     pick = np.where(ties & even, 1, 0) + np.where(ties, 2, 0)
     code = np.argmax(pick, axis=-1).astype(np.uint8)
+    return np.where((x < 0) & (code != 0), code | 0x80, code).astype(np.uint8)
+
+
+def e4m3_encode(x):
+    """The same rounding as e4m3_encode_brute for inputs of any size: the
+    non-negative codes 0 .. 126 increase with their values, so the nearest
+    code is one of the two grid neighbours that a binary search finds; the
+    nearer one is taken, and on a tie the even one."""
+    x = np.asarray(x, dtype=np.float64)
+    grid = e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.minimum(np.searchsorted(grid, a, side="left"), 0x7E)  # first code with value >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - grid[lo], grid[hi] - a
+    code = np.where(d_hi < d_lo, hi, np.where(d_lo < d_hi, lo, np.where(lo % 2 == 0, lo, hi))).astype(np.uint8)
     return np.where((x < 0) & (code != 0), code | 0x80, code).astype(np.uint8)
 
 

@@ -846,3 +846,17 @@ def test_fp8_quantization_float32_decisions():
     z[0, :4] = [448.0, 1.0625, 1.1875, -1.0625]
     ct, st = R.quantize_fp8_groups_f32(z)
     assert st[0, 0] == 1.0 and list(ct[0, :4]) == [0x7E, 0x38, 0x3A, 0xB8]
+
+
+def test_e4m3_encode_search_equals_brute_force():
+    """The binary-search encoder takes the same decision as the brute-force
+    nearest-code search on every grid point, every midpoint between
+    neighbours (the ties), points just off them, zero, tiny values, values
+    past 448, and random magnitudes of both signs."""
+    grid = R.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+    mids = (grid[1:] + grid[:-1]) / 2
+    rng = np.random.default_rng(64)
+    x = np.concatenate([grid, mids, mids * (1 + 1e-12), mids * (1 - 1e-12), [0.0, 1e-30, 2.0 ** -10, 449.0, 1e6],
+                        rng.standard_normal(4000) * np.exp2(rng.integers(-12, 10, 4000))])
+    x = np.concatenate([x, -x])
+    np.testing.assert_array_equal(R.e4m3_encode(x), R.e4m3_encode_brute(x))
