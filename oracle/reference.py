@@ -437,7 +437,9 @@ def e4m3_decode(codes):
 
 def e4m3_encode_brute(x):
     """float64 -> uint8 codes, round to nearest, ties to even, saturating at
-    +-448 (values are scaled into range before encoding). Brute force over the
+    +-448 (values are scaled into range before encoding); the format is
+    sign-magnitude, so a negative value (or -0) that rounds to zero keeps its
+    sign bit (code 0x80, -0), as IEEE rounding does. Brute force over the
     127 non-negative finite codes: the nearest one, and on a tie the even one.
     (Memory grows as 127 x the input: small inputs only.)"""
     x = np.asarray(x, dtype=np.float64)
@@ -450,7 +452,7 @@ def e4m3_encode_brute(x):
     even = (np.arange(0, 0x7F) % 2 == 0)
     pick = np.where(ties & even, 1, 0) + np.where(ties, 2, 0)
     code = np.argmax(pick, axis=-1).astype(np.uint8)
-    return np.where((x < 0) & (code != 0), code | 0x80, code).astype(np.uint8)
+    return np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
 
 
 def e4m3_encode(x):
@@ -465,7 +467,7 @@ def e4m3_encode(x):
     lo = np.maximum(hi - 1, 0)
     d_lo, d_hi = a - grid[lo], grid[hi] - a
     code = np.where(d_hi < d_lo, hi, np.where(d_lo < d_hi, lo, np.where(lo % 2 == 0, lo, hi))).astype(np.uint8)
-    return np.where((x < 0) & (code != 0), code | 0x80, code).astype(np.uint8)
+    return np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
 
 
 def gemv_fp8_blocks(x, codes, scales, block=128):

@@ -656,7 +656,7 @@ def test_quantize_fp8_groups():
     rng = np.random.default_rng(41)
     y = rng.standard_normal((4, 256)) * np.array([1e-3, 1.0, 50.0, 0.0])[:, None]
     codes, scale = R.quantize_fp8_groups(y)
-    assert scale.shape == (4, 2) and np.all(scale[3] == 1.0) and np.all(codes[3] == 0)
+    assert scale.shape == (4, 2) and np.all(scale[3] == 1.0) and np.all(codes[3] & 0x7F == 0)  # +-0
     deq = R.e4m3_decode(codes) * np.repeat(scale, 128, axis=1)
     for t in range(3):
         for gidx in range(2):
@@ -860,3 +860,11 @@ def test_e4m3_encode_search_equals_brute_force():
                         rng.standard_normal(4000) * np.exp2(rng.integers(-12, 10, 4000))])
     x = np.concatenate([x, -x])
     np.testing.assert_array_equal(R.e4m3_encode(x), R.e4m3_encode_brute(x))
+
+
+def test_e4m3_sign_of_zero():
+    """Sign-magnitude: a negative value too small for the smallest subnormal
+    (2^-9) rounds to -0 (code 0x80), a positive one to +0; -0.0 itself is 0x80."""
+    x = np.array([-1e-4, 1e-4, -0.0, 0.0, -2.0 ** -10, -2.0 ** -9])
+    assert list(R.e4m3_encode(x)) == [0x80, 0x00, 0x80, 0x00, 0x80, 0x81]
+    assert list(R.e4m3_encode_brute(x)) == [0x80, 0x00, 0x80, 0x00, 0x80, 0x81]
