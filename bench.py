@@ -12,8 +12,11 @@ sequences, ~135K tokens), the prefill with caches flushed before each call, and
 
 Timing: W untimed warm-up steps, then exactly K steps bracketed by
 torch.cuda.synchronize() on both sides, with HIP events recorded on the stream
-the kernels are launched on. Inputs are resident in device memory before the
-timed region starts. Prints one JSON line.
+the kernels are launched on. The headline prefill figure is the median of K
+calls with the caches flushed (512 MiB written, untimed) before each call, each
+call bracketed by its own events; the other paths are timed back to back.
+Inputs are resident in device memory before the timed region starts. Prints
+one JSON line.
 """
 import argparse
 import hashlib
@@ -27,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16/fp16 MFMA, TFLOP/s
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # dense fp8 MFMA, TFLOP/s
 
 # algorithmic bytes per token-layer of the prefill: q,k,v,g bf16 (4 x 64 x 128 x 2)
 # + beta (64 x 2) + o float32 (64 x 128 x 4) + state in and out amortised over
@@ -95,24 +99,29 @@ def timed(torch, fn, steps, warmup):
 
 
 def timed_cold(torch, fn, steps, warmup, flush_bytes=512 << 20):
-    """Average ms per call when, before every call, a 512 MiB buffer is
-    written so that the 256 MB last-level cache (MALL) and L2 hold none of the
-    call's inputs. Each call is bracketed by its own events; the flush is not
-    timed."""
+    """Per-call ms when, before every call, a 512 MiB buffer is written so that
+    the 256 MB last-level cache (MALL) and L2 hold none of the call's inputs.
+    Each call is bracketed by its own events on the launch stream; the flush
+    is not timed. Returns (median, mean, wall seconds of the timed loop)."""
     stream = torch.cuda.current_stream()
     buf = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+    settle(torch, fn)
     for i in range(warmup):
         buf.fill_(float(i))
         fn()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
     for i in range(steps):
         buf.fill_(float(i))
         ev[i][0].record(stream)
         fn()
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in ev) / steps
+    wall = time.perf_counter() - t0
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    med = t[len(t) // 2] if len(t) % 2 else 0.5 * (t[len(t) // 2 - 1] + t[len(t) // 2])
+    return med, sum(t) / len(t), wall
 
 
 def bench_prefill(torch, K, steps, warmup):
@@ -124,13 +133,13 @@ def bench_prefill(torch, K, steps, warmup):
     sT = torch.empty_like(s0)
     o = torch.empty((T, H, D), dtype=torch.float32, device="cuda")
     fn = lambda: K.kda_prefill(q, k, v, g, b, o, initial_state=s0, final_state=sT)
-    ms, wall = timed(torch, fn, steps, warmup)
-    ms_cold = timed_cold(torch, fn, max(5, steps // 2), 2)
+    ms_cold, ms_cold_mean, wall = timed_cold(torch, fn, steps, warmup)
+    ms, _ = timed(torch, fn, steps, warmup)
     snaps = torch.empty((1, 4, H, D, D), dtype=torch.float32, device="cuda")
     fs = lambda: K.kda_prefill(q, k, v, g, b, o, initial_state=s0, final_state=sT, snapshots=snaps,
                                snapshot_interval=1024)
     ms_snap, _ = timed(torch, fs, max(5, steps // 2), 2)
-    return ms, wall, d, ms_cold, ms_snap
+    return ms, wall, d, (ms_cold, ms_cold_mean), ms_snap
 
 
 def bench_varlen(torch, K, steps, warmup):
@@ -276,6 +285,29 @@ def bench_gemv_fp8(torch, K, steps, warmup):
     return ms, nbytes
 
 
+def bench_w8a8(torch, K, steps, warmup):
+    """Block-FP8 W8A8 on the layer's input projection (41,024 x 4,096 E4M3
+    weights, 128 x 128 scales): the activations quantized per token and
+    128-column group, then the FP8 product; for one decode token (weight
+    streaming) and for the 8,192-token prefill (matrix cores)."""
+    N, Kd, M = 5 * 8192 + 64, 4096, 8192
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    wc = torch.randint(0, 126, (N, Kd), device="cuda", generator=g, dtype=torch.int32).to(torch.uint8)
+    ws = torch.rand(((N + 127) // 128, Kd // 128), device="cuda", generator=g) * 0.01
+    x = torch.randn(M, Kd, device="cuda", generator=g).to(torch.bfloat16)
+    xc = torch.empty(M, Kd, dtype=torch.uint8, device="cuda")
+    xs = torch.empty(M, Kd // 128, dtype=torch.float32, device="cuda")
+    y1 = torch.empty(1, N, dtype=torch.float32, device="cuda")
+    ms_q1, _ = timed(torch, lambda: K.kda_quantize_fp8(x[:1], xc[:1], xs[:1]), steps, warmup)
+    ms_d, _ = timed(torch, lambda: K.kda_gemm_fp8(xc[:1], xs[:1], wc, ws, y1), steps, warmup)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    ms_q, _ = timed(torch, lambda: K.kda_quantize_fp8(x, xc, xs), steps, warmup)
+    ms_g, _ = timed(torch, lambda: K.kda_gemm_fp8(xc, xs, wc, ws, y), max(3, steps // 2), 2)
+    return {"decode": (ms_q1, ms_d, N * Kd + ws.numel() * 4 + Kd + Kd // 128 * 4 + N * 4),
+            "prefill": (ms_q, ms_g, 2.0 * M * N * Kd, M * Kd * 2 + M * Kd + M * Kd // 128 * 4)}
+
+
 def bench_layer(torch, steps, warmup):
     from gated_delta_rule_02_amd import layer, synth
     d = synth.workload_layer()
@@ -342,7 +374,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--skip-layer", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "seqpar", "varlen", "decode", "layer", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "seqpar", "varlen", "decode", "layer", "fp8", "copy"], default=None,
                     help="time one path only (for profiler runs); 'copy' times the plain copy that calibrates byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -360,8 +392,9 @@ def main():
     out = {}
     if args.only in (None, "prefill"):
         log("prefill T=4096 H=64")
-        ms, wall, d, ms_cold, ms_snap = bench_prefill(torch, K, args.steps, args.warmup)
-        log("prefill %.3f ms/step (%.3f ms with the caches flushed before each call)" % (ms, ms_cold))
+        ms_warm, wall, d, (ms, ms_cold_mean), ms_snap = bench_prefill(torch, K, args.steps, args.warmup)
+        log("prefill %.3f ms/step median with the caches flushed before each call (%.3f ms warm, back to back)"
+            % (ms, ms_warm))
         T = 4096
         achieved = PREFILL_BYTES_PER_TOKEN * T / (ms * 1e-3) / 1e9
         traffic = None
@@ -384,8 +417,11 @@ def main():
                          "algorithmic_bytes_per_launch": PREFILL_BYTES_PER_TOKEN * T,
                          "mfma_tflops": PREFILL_FLOPS_PER_TOKEN * T / (ms * 1e-3) / 1e12,
                          "mfma_frac_of_bf16_peak": PREFILL_FLOPS_PER_TOKEN * T / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
-            "prefill_cold_cache": {"ms_per_step": ms_cold, "tokens/s/layer": T / (ms_cold * 1e-3),
-                                   "method": "512 MiB written before each call (untimed); each call timed by its own events"},
+            "timing": "median of the timed calls, each bracketed by its own HIP events on the launch stream, "
+                      "with 512 MiB written before every call (untimed) so that no input is cached",
+            "prefill_cold_cache_mean_ms": ms_cold_mean,
+            "prefill_warm": {"ms_per_step": ms_warm, "tokens/s/layer": T / (ms_warm * 1e-3),
+                             "method": "the same call back to back, caches warm: mean over the timed calls"},
             "prefill_snapshots": {"workload": "the same prefill saving the state every 1024 tokens (4 x 4 MiB)",
                                   "ms_per_step": ms_snap, "tokens/s/layer": T / (ms_snap * 1e-3)},
         })
@@ -452,6 +488,20 @@ def main():
                        "frac_of_bf16_peak": fl / (ms_g * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                        "vendor_blas_reference_TFLOP/s": fl / (ms_r * 1e-3) / 1e12,
                        "vendor_blas_reference": "torch.mm on the same bf16 operands (weight pre-transposed)"}
+    if args.only in (None, "fp8"):
+        log("block-FP8 W8A8 input projection (decode token and 8192-token prefill)")
+        r = bench_w8a8(torch, K, args.steps, args.warmup)
+        q1, d1, nb1 = r["decode"]
+        qp, gp, fl, nbq = r["prefill"]
+        log("w8a8 decode %.4f ms (+ quantize %.4f), prefill gemm %.3f ms (+ quantize %.3f)" % (d1, q1, gp, qp))
+        out["w8a8"] = {
+            "workload": "input projection 41,024 x 4,096 with E4M3 weights in 128x128 blocks and activations "
+                        "quantized per (token, 128 channels); bf16 x quantized by kda_quantize_fp8",
+            "decode_token": {"ms_gemm": d1, "ms_quantize": q1, "bytes_per_step": nb1,
+                             "GB/s": nb1 / (d1 * 1e-3) / 1e9, "frac_of_hbm_peak": nb1 / (d1 * 1e-3) / 1e9 / HBM_PEAK_GBS},
+            "prefill_8192": {"ms_gemm": gp, "ms_quantize": qp, "TFLOP/s": fl / (gp * 1e-3) / 1e12,
+                             "frac_of_fp8_peak": fl / (gp * 1e-3) / 1e12 / MFMA_FP8_PEAK_TFLOPS,
+                             "quantize_GB/s": nbq / (qp * 1e-3) / 1e9}}
     if args.only == "copy":
         log("copy 256 MiB")
         out["copy"] = bench_copy(torch, args.steps, args.warmup)

@@ -357,6 +357,57 @@ int kda_gemv_fp8(const void* x, int64_t ldx, const uint8_t* w, int64_t ldw, cons
     return hip_status(launch_gemv_fp8(a, static_cast<hipStream_t>(hip_stream)), "kda_gemv_fp8");
 }
 
+int kda_quantize_fp8(const void* x, int64_t ldx, kda_dtype x_dtype, int64_t M, int64_t K, uint8_t* codes,
+                     int64_t ldc, float* scales, int64_t ld_scale, void* hip_stream)
+{
+    REQUIRE(x && codes && scales, KDA_ERR_INVALID_ARG, "kda_quantize_fp8: null pointer");
+    REQUIRE(valid_dtype(x_dtype), KDA_ERR_INVALID_ARG, "kda_quantize_fp8: bad dtype");
+    REQUIRE(M >= 0 && K >= 128, KDA_ERR_INVALID_ARG, "kda_quantize_fp8: bad sizes");
+    REQUIRE(K % 128 == 0, KDA_ERR_UNSUPPORTED, "kda_quantize_fp8: K must be a multiple of 128 (the group)");
+    REQUIRE(ldx >= K && ldx % 8 == 0 && ldc >= K && ldc % 8 == 0 && ld_scale >= K / 128, KDA_ERR_INVALID_ARG,
+            "kda_quantize_fp8: ldx >= K and ldc >= K (multiples of 8), ld_scale >= K/128");
+    REQUIRE(aligned16(x) && ((uintptr_t)codes % 8 == 0) && ((uintptr_t)scales % 4 == 0), KDA_ERR_INVALID_ARG,
+            "kda_quantize_fp8: x must be 16-byte aligned, codes 8-byte aligned");
+    if (M == 0) return KDA_OK;
+    const Range rx = rng(x, ((size_t)(M - 1) * ldx + K) * esize(x_dtype));
+    const Range rc = rng(codes, (size_t)(M - 1) * ldc + K), rs = rng(scales, ((size_t)(M - 1) * ld_scale + K / 128) * 4);
+    REQUIRE(!overlap(rc, rx) && !overlap(rs, rx) && !overlap(rc, rs), KDA_ERR_INVALID_ARG,
+            "kda_quantize_fp8: outputs overlap each other or the input");
+    QuantFp8Args a{x, codes, scales, ldx, ldc, ld_scale, M, K, (DType)x_dtype};
+    return hip_status(launch_quantize_fp8(a, static_cast<hipStream_t>(hip_stream)), "kda_quantize_fp8");
+}
+
+int kda_gemm_fp8(const uint8_t* x, int64_t ldx, const float* x_scale, int64_t xs_ld, const uint8_t* w, int64_t ldw,
+                 const float* w_scale, int64_t ws_ld, void* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                 kda_dtype y_dtype, void* hip_stream)
+{
+    REQUIRE(x && x_scale && w && w_scale && y, KDA_ERR_INVALID_ARG, "kda_gemm_fp8: null pointer");
+    REQUIRE(valid_dtype(y_dtype), KDA_ERR_INVALID_ARG, "kda_gemm_fp8: bad dtype");
+    REQUIRE(M >= 0 && N >= 1 && K >= 128, KDA_ERR_INVALID_ARG, "kda_gemm_fp8: bad sizes");
+    REQUIRE(K % 128 == 0, KDA_ERR_UNSUPPORTED, "kda_gemm_fp8: K must be a multiple of 128 (the scale block)");
+    REQUIRE(ldx >= K && ldx % 16 == 0 && ldw >= K && ldw % 16 == 0 && xs_ld >= K / 128 && ws_ld >= K / 128 &&
+                ldy >= N,
+            KDA_ERR_INVALID_ARG,
+            "kda_gemm_fp8: ldx, ldw >= K (multiples of 16), xs_ld, ws_ld >= K/128, ldy >= N");
+    REQUIRE(aligned16(x) && aligned16(w) && ((uintptr_t)x_scale % 4 == 0) && ((uintptr_t)w_scale % 4 == 0) &&
+                ((uintptr_t)y % esize(y_dtype) == 0),
+            KDA_ERR_INVALID_ARG, "kda_gemm_fp8: x and w must be 16-byte aligned");
+    // the matrix-core kernel addresses a tile's rows through 32-bit offsets
+    REQUIRE(256 * std::max(ldx, ldw) + K < ((int64_t)1 << 31), KDA_ERR_UNSUPPORTED,
+            "kda_gemm_fp8: row strides too large");
+    if (M == 0) return KDA_OK;
+    const Range ry = rng(y, ((size_t)(M - 1) * ldy + N) * esize(y_dtype));
+    for (Range r : {rng(x, (size_t)(M - 1) * ldx + K), rng(w, (size_t)(N - 1) * ldw + K),
+                    rng(x_scale, ((size_t)(M - 1) * xs_ld + K / 128) * 4),
+                    rng(w_scale, ((size_t)((N + 127) / 128 - 1) * ws_ld + K / 128) * 4)})
+        REQUIRE(!overlap(ry, r), KDA_ERR_INVALID_ARG, "kda_gemm_fp8: y overlaps an input");
+    Fp8GemvArgs a{x, w, w_scale, y, ldx, ldw, ws_ld, ldy, N, K, M, (DType)y_dtype, x_scale, xs_ld};
+    const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    // a few rows (decode): the weight-streaming forms of kda_gemv_fp8;
+    // more: the matrix-core GEMM
+    return hip_status(M <= 8 ? launch_gemv_fp8(a, st) : launch_gemm_fp8(a, st), "kda_gemm_fp8");
+}
+
 int kda_output_norm_gate_fp8(const void* o, kda_dtype o_dtype, const void* gate, int64_t gate_ld,
                              kda_dtype gate_dtype, const float* norm_weight, int64_t num_tokens, int H, int dv,
                              float eps, uint8_t* y_codes, float* y_scales, void* hip_stream)

@@ -185,6 +185,16 @@ template <> struct Vec16<float> {
 __device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 __device__ __forceinline__ void st16(void* p, const u32x4_t& u) { *reinterpret_cast<u32x4_t*>(p) = u; }
 
+// Maximum over aligned groups of G lanes (G a power of two <= 64; every lane
+// of a group gets its group's maximum).
+template <int G>
+__device__ __forceinline__ float group_max(float v)
+{
+#pragma unroll
+    for (int m = G / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+    return v;
+}
+
 // Maximum over the 64 lanes of a wavefront (every lane gets it).
 __device__ __forceinline__ float wave_max(float v)
 {

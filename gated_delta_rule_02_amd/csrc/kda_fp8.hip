@@ -54,7 +54,9 @@ __device__ __forceinline__ void decode16(const u32x4_t& u, float* f)
 // R rows of W per wavefront; the codes of S 1-KiB steps of every row are
 // loaded at once (a lane's 16 values of each), then used. The R rows lie in
 // one 128-row block (R divides 128), so a step's block scale is one load.
-template <typename TOUT, int M, int R, int S>
+// XQ: x holds E4M3 codes with per-(row, 128-column group) scales (W8A8); a
+// lane's 16 values lie in one group, so each row adds one scale per step.
+template <typename TOUT, int M, int R, int S, bool XQ>
 __global__ __launch_bounds__(kWaves * 64) void gemv_fp8_kernel(Fp8GemvArgs a)
 {
     const int lane = threadIdx.x & 63;
@@ -87,15 +89,21 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_fp8_kernel(Fp8GemvArgs a)
             const int64_t k = kc + s * 1024 + 16 * lane;
             if (k < a.K) {
                 const float sc = srow[k >> 7];
-                float xv[M][16];
+                float xv[M][16], xsc[M];
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
-                    const bf16_t* xp = x + m * a.ldx + k;
-                    const f32x4 x0 = ld4(xp), x1 = ld4(xp + 4), x2 = ld4(xp + 8), x3 = ld4(xp + 12);
-                    const float t[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
-                                         x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+                    if constexpr (XQ) {
+                        decode16(ld16(static_cast<const uint8_t*>(a.x) + m * a.ldx + k), xv[m]);
+                        xsc[m] = sc * a.xs[m * a.xs_ld + (k >> 7)];
+                    } else {
+                        const bf16_t* xp = x + m * a.ldx + k;
+                        const f32x4 x0 = ld4(xp), x1 = ld4(xp + 4), x2 = ld4(xp + 8), x3 = ld4(xp + 12);
+                        const float t[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
+                                             x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) xv[m][e] = t[e];
+                        for (int e = 0; e < 16; ++e) xv[m][e] = t[e];
+                        xsc[m] = sc;
+                    }
                 }
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
@@ -106,7 +114,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_fp8_kernel(Fp8GemvArgs a)
                         float d = 0.f;
 #pragma unroll
                         for (int e = 0; e < 16; ++e) d += w[e] * xv[m][e];
-                        acc[r][m] += sc * d;
+                        acc[r][m] += xsc[m] * d;
                     }
                 }
             }
@@ -157,7 +165,9 @@ __device__ __forceinline__ bf16x8_t codes_to_bf16(uint32_t d0, uint32_t d1)
 // wavefront's last block re-read that block and are not accumulated), so the
 // waits stay exact. The KS partial results are summed in a fixed order through
 // LDS.
-template <typename TOUT, int KS>
+// XQ: x holds E4M3 codes (converted exactly to bfloat16 like W's) and its
+// per-(token, block) scale joins the block scale of W.
+template <typename TOUT, int KS, bool XQ>
 __global__ __launch_bounds__(KS * 64) void gemv_fp8_mfma_kernel(Fp8GemvArgs a)
 {
     extern __shared__ float scl[];  // the K / 128 block scales of these rows
@@ -174,17 +184,25 @@ __global__ __launch_bounds__(KS * 64) void gemv_fp8_mfma_kernel(Fp8GemvArgs a)
     const bool xok = r16 < a.M;
     const uint8_t* wp = a.w + (n0 + r16 < a.N ? n0 + r16 : 0) * a.ldw + 16 * q4;
     const bf16_t* xp = static_cast<const bf16_t*>(a.x) + (xok ? r16 : 0) * a.ldx + 16 * q4;
+    const uint8_t* xq = static_cast<const uint8_t*>(a.x) + (xok ? r16 : 0) * a.ldx + 16 * q4;
+    const float* xsr = XQ ? a.xs + (xok ? r16 : 0) * a.xs_ld : nullptr;
 
+    // x: bfloat16 (four 16-byte pieces per block) or codes (two, as W's)
     u32x4_t wb[kMfmaSteps][2], xb[kMfmaSteps][4];
 #define KDA_GEMV_LOAD(T, S)                                                                         \
     {                                                                                               \
         const int64_t k_ = (int64_t)(wave + KS * min((T), cnt - 1)) * 128;                          \
         wb[S][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wp + k_));            \
         wb[S][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wp + k_ + 64));       \
-        xb[S][0] = ld16(xp + k_);                                                                   \
-        xb[S][1] = ld16(xp + k_ + 8);                                                               \
-        xb[S][2] = ld16(xp + k_ + 64);                                                              \
-        xb[S][3] = ld16(xp + k_ + 72);                                                              \
+        if constexpr (XQ) {                                                                         \
+            xb[S][0] = ld16(xq + k_);                                                               \
+            xb[S][1] = ld16(xq + k_ + 64);                                                          \
+        } else {                                                                                    \
+            xb[S][0] = ld16(xp + k_);                                                               \
+            xb[S][1] = ld16(xp + k_ + 8);                                                           \
+            xb[S][2] = ld16(xp + k_ + 64);                                                          \
+            xb[S][3] = ld16(xp + k_ + 72);                                                          \
+        }                                                                                           \
     }
 #pragma unroll
     for (int s = 0; s < kMfmaSteps; ++s) KDA_GEMV_LOAD(s, s)
@@ -201,12 +219,13 @@ __global__ __launch_bounds__(KS * 64) void gemv_fp8_mfma_kernel(Fp8GemvArgs a)
             f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(wb[s][h][0], wb[s][h][1]),
-                                                            __builtin_bit_cast(bf16x8_t, xb[s][2 * h]), c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(wb[s][h][2], wb[s][h][3]),
-                                                            __builtin_bit_cast(bf16x8_t, xb[s][2 * h + 1]), c, 0, 0, 0);
+                const bf16x8_t x0 = XQ ? codes_to_bf16(xb[s][h][0], xb[s][h][1]) : __builtin_bit_cast(bf16x8_t, xb[s][2 * h]);
+                const bf16x8_t x1 = XQ ? codes_to_bf16(xb[s][h][2], xb[s][h][3]) : __builtin_bit_cast(bf16x8_t, xb[s][2 * h + 1]);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(wb[s][h][0], wb[s][h][1]), x0, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16(wb[s][h][2], wb[s][h][3]), x1, c, 0, 0, 0);
             }
-            const float sc = scl[wave + KS * min(t, cnt - 1)];
+            const int kb_ = wave + KS * min(t, cnt - 1);
+            const float sc = XQ ? scl[kb_] * xsr[kb_] : scl[kb_];
             const bool live = t < cnt;
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[e] = live ? fmaf(sc, c[e], acc[e]) : acc[e];
@@ -256,14 +275,211 @@ __global__ __launch_bounds__(kNormRows * 64) void norm_gate_fp8_kernel(NormGateF
     if (lane == 0) a.scales[row] = scale;
 }
 
+
+// ------------------------------------------------ activation quantization
+// One wavefront per 512 columns of a row: a lane takes 8 consecutive values,
+// so each 16-lane row of the wavefront holds one 128-column group, whose
+// maximum magnitude is a 16-lane reduction. Every rounding step is float32:
+// scale = amax / 448 and x / scale by correctly rounded division, the
+// quotient clamped to +-448 (a quotient a hair above 448 stays on the largest
+// code) and converted to E4M3 with ties to even by the hardware conversion.
+template <typename TX>
+__global__ __launch_bounds__(256) void quantize_fp8_kernel(QuantFp8Args a)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t strips = (a.K + 511) / 512;
+    const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (wid >= a.M * strips) return;
+    const int64_t m = wid / strips;
+    const int64_t k = (wid % strips) * 512 + 8 * lane;
+    const bool in = k < a.K;  // K is a multiple of 128: whole groups are in or out
+    float v[8];
+    if (in) {
+        const TX* xp = static_cast<const TX*>(a.x) + m * a.ldx + k;
+        if constexpr (sizeof(TX) == 2) {
+            Vec16<bf16_t>::unpack(ld16(xp), v);
+        } else {
+            Vec16<float>::unpack(ld16(xp), v);
+            Vec16<float>::unpack(ld16(xp + 4), v + 4);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    }
+    float am = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(v[e]));
+    am = group_max<16>(am);
+    const float scale = am > 0.f ? __fdiv_rn(am, 448.0f) : 1.0f;
+    if (!in) return;
+    uint32_t w[2];
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+        float r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = fminf(fmaxf(__fdiv_rn(v[4 * d + e], scale), -448.0f), 448.0f);
+        int p = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+        p = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], p, true);
+        w[d] = (uint32_t)p;
+    }
+    *reinterpret_cast<uint2*>(a.codes + m * a.ldc + k) = make_uint2(w[0], w[1]);
+    if ((lane & 15) == 0) a.scales[m * a.lds + (k >> 7)] = scale;
+}
+
+// ---------------------------------------------------------- W8A8 GEMM
+// Y[M, N] = X W^T, both operands block FP8 (X per row and 128-column group,
+// W per 128 x 128 block). A workgroup of eight wavefronts computes a 256 x 256
+// tile of Y, a wavefront 64 rows of X by 128 rows of W (one block row of W's
+// scales). K runs in steps of one 128-wide scale block, double-buffered in
+// LDS by buffer-to-LDS copies: per step and 16 x 16 tile one 16x16x128 FP8
+// matrix product from zero (the E4M3 products are exact and summed in
+// float32), then acc += (sx[row, kb] * sw[n / 128, kb]) * P on the vector
+// unit, which runs beside the matrix unit. Rows are 128 bytes in LDS with
+// their 16-byte chunks XOR-swizzled by row mod 8 (the swizzle is applied
+// through each lane's source address), so that the rows of an operand read
+// spread over the banks. As in the bf16 GEMM, the product is formed
+// transposed, so that a lane holds four consecutive columns of one row of Y.
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+constexpr int kF8Tile = 256;                  // rows of X and of W per workgroup
+constexpr int kF8Stage = 2 * kF8Tile * 128;   // one K step: X rows, then W rows
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ int swz8(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+
+template <typename TC, bool VEC>
+__global__ __launch_bounds__(512) void gemm_fp8_kernel(Fp8GemvArgs a)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2][kF8Stage];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int m16 = lane & 15, q4 = lane >> 4;
+    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 128;
+    const int64_t tiles_m = (a.M + kF8Tile - 1) / kF8Tile;
+    const int64_t tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
+    const int64_t m0 = tm * kF8Tile, n0 = tn * kF8Tile;
+
+    // rows past M or N read as zero through the descriptor ranges
+    const uint8_t* X = static_cast<const uint8_t*>(a.x) + m0 * a.ldx;
+    const uint8_t* Wr = a.w + n0 * a.ldw;
+    const int64_t rows_x = min<int64_t>(kF8Tile, a.M - m0), rows_w = min<int64_t>(kF8Tile, a.N - n0);
+    const rsrc_t rx = make_rsrc(X, (rows_x - 1) * a.ldx + a.K);
+    const rsrc_t rw = make_rsrc(Wr, (rows_w - 1) * a.ldw + a.K);
+
+    // copy of K step kb into stage st: 64 instructions of 1 KiB, 8 per
+    // wavefront; instruction i covers 8 rows (X rows for i < 32, W rows
+    // after), lane l row 8 i' + l / 8 and LDS chunk slot l % 8, which holds
+    // K chunk slot ^ (row mod 8)
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t*)&smem[0][0];
+    const int crow = lane >> 3, cchunk = (lane & 7) ^ (lane >> 3);
+    auto copy = [&](int kb, int st) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i = wave * 8 + j;  // wave-uniform: X for waves 0-3, W for 4-7
+            const int r = 8 * (i & 31) + crow;
+            const int koff = kb * 128 + 16 * cchunk;
+            const uint32_t dst = lds0 + st * kF8Stage + i * 1024;
+            if (i < 32)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(uintptr_t)dst, 16, (int)(r * a.ldx) + koff, 0, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t*)(uintptr_t)dst, 16, (int)(r * a.ldw) + koff, 0, 0, 0);
+        }
+    };
+
+    // scales: this lane's four rows of X, and the block row of W of this wavefront
+    const float* sxp[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t r = m0 + wm + 16 * i + m16;
+        sxp[i] = a.xs + (r < a.M ? r : a.M - 1) * a.xs_ld;
+    }
+    const int64_t wb_row = (n0 + wn) >> 7, wb_last = (a.N - 1) >> 7;
+    const float* swp = a.ws + (wb_row < wb_last ? wb_row : wb_last) * a.ws_ld;
+
+    f32x4 acc[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = (int)(a.K >> 7);
+    copy(0, 0);
+    __syncthreads();
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < nk; ++kb) {
+        const int st = kb & 1;
+        if (kb + 1 < nk) copy(kb + 1, st ^ 1);
+        const float sw = swp[kb];
+        float s[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[i] = sxp[i][kb] * sw;
+        const uint8_t* sa = &smem[st][0];
+        const uint8_t* sb = &smem[st][kF8Tile * 128];
+        i32x8_t fa[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = wm + 16 * i + m16;
+            const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(sa + swz8(r, 2 * q4));
+            const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(sa + swz8(r, 2 * q4 + 1));
+            fa[i] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            i32x8_t fb[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = wn + 16 * (4 * h + j) + m16;
+                const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(sb + swz8(r, 2 * q4));
+                const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(sb + swz8(r, 2 * q4 + 1));
+                fb[j] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    // formats 0 / 0: E4M3 operands; block scales 127 (E8M0 1.0)
+                    const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[j], fa[i], zero, 0, 0, 0, 127, 0, 127);
+                    f32x4& c = acc[i][4 * h + j];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) c[e] = fmaf(p[e], s[i], c[e]);
+                }
+        }
+        __syncthreads();  // the copy of step kb + 1 has landed and every read of stage st is done
+    }
+
+    // acc[i][j]: lane (m16, q4) element e is Y[row 16i + m16][column 16j + 4q4 + e]
+    TC* Y = static_cast<TC*>(a.y);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t row = m0 + wm + 16 * i + m16;
+        if (row >= a.M) continue;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t col = n0 + wn + 16 * j + 4 * q4;
+            TC* p = Y + row * a.ldy + col;
+            if (VEC && col + 3 < a.N) {
+                st4(p, acc[i][j]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (col + e < a.N) st(p + e, acc[i][j][e]);
+            }
+        }
+    }
+}
 }  // namespace
 
 template <int M, int R, int S>
 void launch_gemv_rs(const Fp8GemvArgs& a, hipStream_t s)
 {
     const dim3 grid((unsigned)((a.N + kWaves * R - 1) / (kWaves * R))), block(kWaves * 64);
-    if (a.y_dtype == F32) hipLaunchKernelGGL((gemv_fp8_kernel<float, M, R, S>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((gemv_fp8_kernel<bf16_t, M, R, S>), grid, block, 0, s, a);
+    if (a.xs) {
+        if (a.y_dtype == F32) hipLaunchKernelGGL((gemv_fp8_kernel<float, M, R, S, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((gemv_fp8_kernel<bf16_t, M, R, S, true>), grid, block, 0, s, a);
+    } else {
+        if (a.y_dtype == F32) hipLaunchKernelGGL((gemv_fp8_kernel<float, M, R, S, false>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((gemv_fp8_kernel<bf16_t, M, R, S, false>), grid, block, 0, s, a);
+    }
 }
 
 static void launch_gemv_mfma(const Fp8GemvArgs& a, hipStream_t s)
@@ -276,10 +492,15 @@ static void launch_gemv_mfma(const Fp8GemvArgs& a, hipStream_t s)
     while (ks < 8 && 2 * ks <= nkb && tiles * 2 * ks <= kWaveTarget) ks *= 2;
     const dim3 grid((unsigned)tiles), block(64 * ks);
     const size_t lds = (size_t)nkb * sizeof(float);
-#define KDA_GEMV_CASE(KS)                                                                                  \
-    case KS:                                                                                               \
-        if (a.y_dtype == F32) hipLaunchKernelGGL((gemv_fp8_mfma_kernel<float, KS>), grid, block, lds, s, a); \
-        else hipLaunchKernelGGL((gemv_fp8_mfma_kernel<bf16_t, KS>), grid, block, lds, s, a);                \
+#define KDA_GEMV_CASE(KS)                                                                                         \
+    case KS:                                                                                                      \
+        if (a.xs) {                                                                                               \
+            if (a.y_dtype == F32) hipLaunchKernelGGL((gemv_fp8_mfma_kernel<float, KS, true>), grid, block, lds, s, a); \
+            else hipLaunchKernelGGL((gemv_fp8_mfma_kernel<bf16_t, KS, true>), grid, block, lds, s, a);              \
+        } else {                                                                                                  \
+            if (a.y_dtype == F32) hipLaunchKernelGGL((gemv_fp8_mfma_kernel<float, KS, false>), grid, block, lds, s, a); \
+            else hipLaunchKernelGGL((gemv_fp8_mfma_kernel<bf16_t, KS, false>), grid, block, lds, s, a);             \
+        }                                                                                                         \
         break;
     switch (ks) {
         KDA_GEMV_CASE(1) KDA_GEMV_CASE(2) KDA_GEMV_CASE(4) KDA_GEMV_CASE(8)
@@ -317,6 +538,32 @@ hipError_t launch_norm_gate_fp8(const NormGateFp8Args& a, hipStream_t s)
     } else {
         if (a.gate_dtype == F32) hipLaunchKernelGGL((norm_gate_fp8_kernel<bf16_t, float>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((norm_gate_fp8_kernel<bf16_t, bf16_t>), grid, block, 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp8(const QuantFp8Args& a, hipStream_t s)
+{
+    const int64_t waves = a.M * ((a.K + 511) / 512);
+    if (waves == 0) return hipSuccess;
+    const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+    if (a.x_dtype == F32) hipLaunchKernelGGL(quantize_fp8_kernel<float>, grid, block, 0, s, a);
+    else hipLaunchKernelGGL(quantize_fp8_kernel<bf16_t>, grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp8(const Fp8GemvArgs& a, hipStream_t s)
+{
+    const int64_t tiles = ((a.M + kF8Tile - 1) / kF8Tile) * ((a.N + kF8Tile - 1) / kF8Tile);
+    const dim3 grid((unsigned)tiles), block(512);
+    const size_t ysz = a.y_dtype == F32 ? 4 : 2;
+    const bool vec = a.ldy % 4 == 0 && (uintptr_t)a.y % (4 * ysz) == 0;
+    if (a.y_dtype == F32) {
+        if (vec) hipLaunchKernelGGL((gemm_fp8_kernel<float, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((gemm_fp8_kernel<float, false>), grid, block, 0, s, a);
+    } else {
+        if (vec) hipLaunchKernelGGL((gemm_fp8_kernel<bf16_t, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((gemm_fp8_kernel<bf16_t, false>), grid, block, 0, s, a);
     }
     return hipGetLastError();
 }

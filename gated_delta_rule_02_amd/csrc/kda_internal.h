@@ -114,16 +114,35 @@ hipError_t launch_affine_apply(const float* M, const float* X, const float* N, f
                                hipStream_t s);
 
 // y[M, N] = x[M, K] W^T, W block-FP8: W[n, k] = e4m3(w[n, k]) * w_scale[n/128, k/128]
+// With xs set, x holds E4M3 codes and X[m, k] = e4m3(x[m, k]) * xs[m, k/128]
+// (activations quantized per row and 128-column group: W8A8).
 struct Fp8GemvArgs {
-    const void* x;        // bf16 [M, K], row stride ldx
+    const void* x;        // bf16 [M, K] (xs null) or e4m3 codes [M, K], row stride ldx
     const uint8_t* w;     // e4m3 codes [N, K], row stride ldw
     const float* ws;      // [ceil(N/128), K/128], row stride ws_ld
     void* y;              // [M, N], row stride ldy
     int64_t ldx, ldw, ws_ld, ldy, N, K;
-    int M;
+    int64_t M;
     DType y_dtype;
+    const float* xs = nullptr;  // [M, K/128], row stride xs_ld
+    int64_t xs_ld = 0;
 };
 hipError_t launch_gemv_fp8(const Fp8GemvArgs& a, hipStream_t s);
+
+// W8A8 for many rows: y[M, N] = X W^T with X and W as above (xs required),
+// on the FP8 matrix cores
+hipError_t launch_gemm_fp8(const Fp8GemvArgs& a, hipStream_t s);
+
+// dynamic activation quantization: per row and group of 128 columns,
+// scale = amax / 448 (1 for an all-zero group), code = E4M3(x / scale)
+struct QuantFp8Args {
+    const void* x;
+    uint8_t* codes;
+    float* scales;
+    int64_t ldx, ldc, lds, M, K;
+    DType x_dtype;
+};
+hipError_t launch_quantize_fp8(const QuantFp8Args& a, hipStream_t s);
 
 // the epilogue with its output quantized to e4m3 per (token, head)
 struct NormGateFp8Args {

@@ -40,6 +40,8 @@ _SIGS = {
     "kda_state_convert": (_I, [_P, _I, _P, _I, _I64, _P]),
     "kda_gemv_fp8": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _I, _I64, _I64, _I, _I, _P]),
     "kda_output_norm_gate_fp8": (_I, [_P, _I, _P, _I64, _I, _P, _I64, _I, _I, _F, _P, _P, _P]),
+    "kda_quantize_fp8": (_I, [_P, _I64, _I, _I64, _I64, _P, _I64, _P, _I64, _P]),
+    "kda_gemm_fp8": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _I, _P]),
     "kda_conv_state_update": (_I, [_P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P]),
     "kda_conv_prefill": (_I, [_P, _I64, _I64, _I, _I, _P, _P, _I, _P, _P, _P, _P, _I, _I, _F, _P, _I64, _I, _P]),
     "kda_gate_prologue": (_I, [_P, _I64, _P, _I64, _P, _I64, _I, _I, _F, _I, _P, _P, _I, _P]),
@@ -376,6 +378,37 @@ def kda_gemv_fp8(x, w, w_scale, y, stream=None):
     N = w.shape[0]
     _call("kda_gemv_fp8", _ptr(x), x.stride(0), _ptr(w), w.stride(0), _ptr(w_scale), w_scale.stride(0),
           _ptr(y), y.stride(0), M, N, Kd, _dt(x), _dt(y), _stream(stream))
+    return y
+
+
+def kda_quantize_fp8(x, codes, scales, stream=None):
+    """x [M,K] float32/bfloat16 -> codes uint8 [M,K] (E4M3), scales float32 [M,K/128]
+    (row strides allowed, last dims contiguous)."""
+    for n_, t_ in (("x", x), ("codes", codes), ("scales", scales)):
+        if t_.stride(-1) != 1:
+            raise ValueError("%s rows must be contiguous" % n_)
+    if codes.dtype != torch.uint8 or scales.dtype != torch.float32:
+        raise TypeError("codes must be uint8 and scales float32")
+    M, Kd = x.shape
+    _call("kda_quantize_fp8", _ptr(x), x.stride(0), _dt(x), M, Kd, _ptr(codes), codes.stride(0), _ptr(scales),
+          scales.stride(0), _stream(stream))
+    return codes, scales
+
+
+def kda_gemm_fp8(x, x_scale, w, w_scale, y, stream=None):
+    """y[M,N] = X W^T with X = e4m3(x) x x_scale[M, K/128] and W = e4m3(w) x
+    w_scale[N/128, K/128] (x, w uint8 codes; row strides allowed)."""
+    for n_, t_ in (("x", x), ("x_scale", x_scale), ("w", w), ("w_scale", w_scale), ("y", y)):
+        if t_.stride(-1) != 1:
+            raise ValueError("%s rows must be contiguous" % n_)
+    if x.dtype != torch.uint8 or w.dtype != torch.uint8:
+        raise TypeError("x and w must be uint8 E4M3 codes")
+    if x_scale.dtype != torch.float32 or w_scale.dtype != torch.float32:
+        raise TypeError("scales must be float32")
+    M, Kd = x.shape
+    N = w.shape[0]
+    _call("kda_gemm_fp8", _ptr(x), x.stride(0), _ptr(x_scale), x_scale.stride(0), _ptr(w), w.stride(0),
+          _ptr(w_scale), w_scale.stride(0), _ptr(y), y.stride(0), M, N, Kd, _dt(y), _stream(stream))
     return y
 
 

@@ -353,6 +353,57 @@ int kda_output_norm_gate_fp8(const void* o, kda_dtype o_dtype, const void* gate,
                              float eps, uint8_t* y_codes, float* y_scales, void* hip_stream);
 
 /* ------------------------------------------------------------------------
+ * kda_quantize_fp8 -- dynamic activation quantization to block FP8.
+ *
+ * The pages pair block-FP8 E4M3 weights (128 x 128 scale blocks) with a
+ * dynamic quantization of the activations ("Ling-3.1-flash: Grouped Routing
+ * and Two Different MLA Caches", section "Production boundaries"). Here each
+ * row is quantized in groups of 128 consecutive columns, each group with its
+ * own float32 scale, so that X W^T can run on FP8 operands (kda_gemm_fp8).
+ * Every rounding decision is taken in float32: scale = amax / 448 (1 for an
+ * all-zero group), q = x / scale (correctly rounded division), clamped to
+ * +-448, code = E4M3 nearest to q, ties to even.
+ *
+ * x       [M, K] x_dtype (float32 or bfloat16), row stride ldx (a multiple
+ *         of 8), 16-byte aligned; finite values.
+ * codes   uint8 [M, K] E4M3, row stride ldc (a multiple of 8), 8-byte aligned.
+ * scales  float32 [M, K/128], row stride ld_scale.
+ * K must be a multiple of 128. Outputs may not overlap each other or x.
+ * ---------------------------------------------------------------------- */
+int kda_quantize_fp8(const void* x, int64_t ldx, kda_dtype x_dtype, int64_t M, int64_t K, uint8_t* codes,
+                     int64_t ldc, float* scales, int64_t ld_scale, void* hip_stream);
+
+/* ------------------------------------------------------------------------
+ * kda_gemm_fp8 -- Y = X W^T with both operands block FP8 (W8A8).
+ *
+ * The projection form of the pages' block-FP8 scheme (section "Production
+ * boundaries" above; the Hopper decode settings list an FP8 block GEMV,
+ * "Ling-3.1-flash: What 63 Linear-Attention Layers Do to the KV Budget",
+ * section "Fitting it on a node"):
+ *   X[m, k] = e4m3(x[m, k]) * x_scale[m, k/128]      (as kda_quantize_fp8 or
+ *                                                     kda_output_norm_gate_fp8 write them)
+ *   W[n, k] = e4m3(w[n, k]) * w_scale[n/128, k/128]  (128 x 128 blocks)
+ *   Y[m, n] = sum_k X[m, k] W[n, k]: each 128-column block's sum of E4M3
+ *             products is scaled once and the blocks are added in float32.
+ *             M <= 8 forms the block sums in float32 as well; the matrix-core
+ *             form's FP8 instruction forms them with about 14 bits of
+ *             relative precision (the product of a block then differs from
+ *             the exact one by ~1e-4 of the output's magnitude).
+ *
+ * x        uint8 [M, K], row stride ldx (a multiple of 16), 16-byte aligned.
+ * x_scale  float32 [M, K/128], row stride xs_ld.
+ * w        uint8 [N, K], row stride ldw (a multiple of 16), 16-byte aligned.
+ * w_scale  float32 [ceil(N/128), K/128], row stride ws_ld.
+ * y        [M, N] y_dtype (float32 or bfloat16, rounded to nearest even), row
+ *          stride ldy; may not overlap an input.
+ * K must be a multiple of 128. M <= 8 runs the weight-streaming GEMV forms of
+ * kda_gemv_fp8 (decode); larger M the matrix-core GEMM (prefill).
+ * ---------------------------------------------------------------------- */
+int kda_gemm_fp8(const uint8_t* x, int64_t ldx, const float* x_scale, int64_t xs_ld, const uint8_t* w, int64_t ldw,
+                 const float* w_scale, int64_t ws_ld, void* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                 kda_dtype y_dtype, void* hip_stream);
+
+/* ------------------------------------------------------------------------
  * kda_conv_state_update -- decode-time causal short convolution.
  *
  * One causal depthwise convolution of width W (4 in the model) per projection

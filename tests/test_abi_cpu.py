@@ -257,6 +257,41 @@ def test_fp8_validation():
     assert call("kda_output_norm_gate_fp8", *a)[0] == K.KDA_ERR_INVALID_ARG
 
 
+def test_w8a8_validation():
+    """kda_quantize_fp8 and kda_gemm_fp8 refuse bad groups, strides and overlaps
+    before any launch."""
+    # quantize: x ldx x_dtype M K codes ldc scales ld_scale stream
+    q = [fake(1), 4096, K.KDA_BF16, 64, 4096, fake(2), 4096, fake(3), 32, None]
+    a = list(q); a[4] = 4000; a[1] = 4000; a[6] = 4000
+    assert call("kda_quantize_fp8", *a)[0] == K.KDA_ERR_UNSUPPORTED       # K not a multiple of 128
+    a = list(q); a[8] = 31
+    assert call("kda_quantize_fp8", *a)[0] == K.KDA_ERR_INVALID_ARG       # ld_scale < K/128
+    a = list(q); a[5] = fake(1) + 4096
+    rc, msg = call("kda_quantize_fp8", *a)
+    assert rc == K.KDA_ERR_INVALID_ARG and "overlap" in msg               # codes over x
+    a = list(q); a[7] = fake(2) + 1024
+    assert call("kda_quantize_fp8", *a)[0] == K.KDA_ERR_INVALID_ARG       # scales over codes
+    a = list(q); a[0] = None
+    assert call("kda_quantize_fp8", *a)[0] == K.KDA_ERR_INVALID_ARG
+    a = list(q); a[3] = 0
+    assert call("kda_quantize_fp8", *a)[0] == K.KDA_OK                    # no rows: nothing to do
+    # gemm: x ldx xs xs_ld w ldw ws ws_ld y ldy M N K y_dtype stream
+    g = [fake(1), 4096, fake(2), 32, fake(3), 4096, fake(4), 32, fake(5), 8192, 512, 8192, 4096, K.KDA_BF16, None]
+    a = list(g); a[12] = 4000; a[1] = 4000; a[5] = 4000
+    assert call("kda_gemm_fp8", *a)[0] == K.KDA_ERR_UNSUPPORTED           # K not a multiple of 128
+    a = list(g); a[1] = 4104
+    assert call("kda_gemm_fp8", *a)[0] == K.KDA_ERR_INVALID_ARG           # ldx not a multiple of 16
+    a = list(g); a[3] = 16
+    assert call("kda_gemm_fp8", *a)[0] == K.KDA_ERR_INVALID_ARG           # xs_ld < K/128
+    a = list(g); a[8] = fake(3) + 4096
+    rc, msg = call("kda_gemm_fp8", *a)
+    assert rc == K.KDA_ERR_INVALID_ARG and "overlaps" in msg
+    a = list(g); a[2] = None
+    assert call("kda_gemm_fp8", *a)[0] == K.KDA_ERR_INVALID_ARG
+    a = list(g); a[10] = 0
+    assert call("kda_gemm_fp8", *a)[0] == K.KDA_OK
+
+
 def segmaps(**over):
     a = dict(k=fake(2), v=fake(3), g=fake(4), beta=fake(5), in_dtype=K.KDA_BF16, T=256, H=4, dk=128, dv=128,
              cu_dev=None, cu_host=None, N=1, lb=-5.0, M=fake(7), Nout=fake(8), ws=fake(9), ws_bytes=1 << 28,

@@ -106,3 +106,140 @@ def test_output_norm_gate_fp8():
     same = np.mean(gc == rc)
     print("  codes equal to the oracle's: %.4f" % same, flush=True)
     assert same >= 0.99
+
+
+# ------------------------------------------------------------ block FP8 W8A8
+def fp8_codes(rng, shape):
+    """Random finite E4M3 codes (NaN codes replaced)."""
+    c = rng.integers(0, 256, shape, dtype=np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x3C
+    return c
+
+
+@pytest.mark.parametrize("M,Kd,xdt,ld_pad", [(1, 128, "bf16", 0), (7, 384, "bf16", 16), (64, 4096, "bf16", 0),
+                                            (33, 640, "f32", 8), (8192, 4096, "bf16", 0)])
+def test_quantize_fp8_bit_exact(M, Kd, xdt, ld_pad):
+    """Dynamic activation quantization: codes and scales equal the oracle's
+    float32-decision quantizer bit for bit (magnitudes over 2^-20 .. 2^20 per
+    row, all-zero groups, groups with one large outlier; ragged 512-column
+    strips; row-strided input and output); the prefill shape 8192 x 4096 in full."""
+    announce("quantize fp8 M=%d Kd=%d %s" % (M, Kd, xdt))
+    rng = np.random.default_rng(70 + M + Kd)
+    xv = (rng.standard_normal((M, Kd)) * np.exp2(rng.integers(-20, 20, (M, 1)))).astype(np.float32)
+    xv[0, :128] = 0.0
+    if M > 2:
+        xv[2, 5] = 3e4 * np.abs(xv[2]).max()
+    if xdt == "bf16":
+        xt = torch.from_numpy(xv).to(torch.bfloat16)
+        xv = xt.float().numpy()            # the values the kernel sees
+        buf = torch.zeros((M, Kd + ld_pad), dtype=torch.bfloat16)
+        buf[:, :Kd] = xt
+    else:
+        buf = torch.zeros((M, Kd + ld_pad), dtype=torch.float32)
+        buf[:, :Kd] = torch.from_numpy(xv)
+    x = buf.cuda()[:, :Kd]
+    codes_b = torch.full((M, Kd + ld_pad), 0xEE, dtype=torch.uint8, device="cuda")
+    scales_b = torch.full((M, Kd // 128 + 1), -1.0, dtype=torch.float32, device="cuda")
+    K.kda_quantize_fp8(x, codes_b[:, :Kd], scales_b[:, :Kd // 128])
+    torch.cuda.synchronize()
+    rc, rs = R.quantize_fp8_groups_f32(xv)
+    gc, gs = codes_b[:, :Kd].cpu().numpy(), scales_b[:, :Kd // 128].cpu().numpy()
+    nbad = int(np.sum(gc != rc))
+    print("  codes differing: %d of %d; scales equal: %s" % (nbad, gc.size, np.array_equal(gs, rs)), flush=True)
+    assert nbad == 0
+    np.testing.assert_array_equal(gs, rs)
+    assert np.all(codes_b[:, Kd:].cpu().numpy() == 0xEE) and np.all(scales_b[:, Kd // 128:].cpu().numpy() == -1.0)
+
+
+def run_w8a8(M, N, Kd, out_dtype=torch.float32, seed=0, pad=0):
+    rng = np.random.default_rng(seed)
+    xc = fp8_codes(rng, (M, Kd))
+    xs = rng.uniform(1e-2, 1.0, (M, Kd // 128)).astype(np.float32)
+    wc = fp8_codes(rng, (N, Kd))
+    ws = rng.uniform(1e-3, 1e-2, ((N + 127) // 128, Kd // 128)).astype(np.float32)
+    xb = torch.zeros((M, Kd + pad), dtype=torch.uint8)
+    xb[:, :Kd] = torch.from_numpy(xc)
+    y = torch.full((M, N + pad), float("nan"), dtype=out_dtype, device="cuda")
+    K.kda_gemm_fp8(xb.cuda()[:, :Kd], torch.from_numpy(xs).cuda(), torch.from_numpy(wc).cuda(),
+                   torch.from_numpy(ws).cuda(), y[:, :N])
+    torch.cuda.synchronize()
+    if pad:
+        assert torch.isnan(y[:, N:]).all()
+    return y[:, :N], R.gemm_fp8_w8a8(xc, xs, wc, ws)
+
+
+# Bounds of the W8A8 paths against the exact product. The GEMV forms (M <= 8)
+# convert the codes exactly to bfloat16 or float32 and accumulate in float32:
+# 2e-5. The FP8 matrix instruction sums the 128 E4M3 products of a block with
+# about 14 bits of relative precision (measured 6-7e-5 of the largest output
+# for normal and subnormal codes alike; sums of subnormal products alone come
+# out to 1e-7), and the blocks are then summed in float32 after scaling:
+# 2.5e-4 leaves a 3.5x margin. Either is far below the quantization error of
+# W8A8 itself (about 2^-4 per value).
+TOL_W8A8_GEMV, TOL_W8A8_MFMA = 2e-5, 2.5e-4
+
+
+@pytest.mark.parametrize("M,N,Kd", [(1, 300, 128), (4, 257, 1152), (6, 130, 384), (8, 1000, 4096),
+                                    (9, 300, 256), (100, 513, 512), (300, 356, 1024), (257, 1000, 2048),
+                                    (1000, 64, 128), (512, 512, 8192)])
+def test_gemm_fp8_w8a8(M, N, Kd):
+    """W8A8 against the oracle's float64 product of the decoded, scaled codes:
+    the GEMV forms (M <= 8) and the matrix-core GEMM (ragged M and N, one to
+    64 scale blocks along K)."""
+    announce("gemm fp8 w8a8 M=%d N=%d K=%d" % (M, N, Kd))
+    y, ref = run_w8a8(M, N, Kd, seed=M * 13 + N)
+    e = relerr(host64(y), ref)
+    print("  err %.2e" % e, flush=True)
+    assert e < (TOL_W8A8_GEMV if M <= 8 else TOL_W8A8_MFMA)
+
+
+def test_gemm_fp8_w8a8_strided_and_bf16():
+    for M in (5, 200):
+        announce("gemm fp8 w8a8 strided/bf16 M=%d" % M)
+        y, ref = run_w8a8(M, 300, 1024, seed=90 + M, pad=48)
+        assert relerr(host64(y), ref) < (TOL_W8A8_GEMV if M <= 8 else TOL_W8A8_MFMA)
+        y, ref = run_w8a8(M, 300, 1024, out_dtype=torch.bfloat16, seed=91 + M, pad=16)
+        assert relerr(host64(y), ref) < 5e-3
+
+
+@pytest.mark.parametrize("M,N,Kd", [(8192, 5 * 8192 + 64, 4096), (8192, 4096, 8192), (1, 5 * 8192 + 64, 4096),
+                                    (6, 4096, 8192)])
+def test_gemm_fp8_w8a8_layer_shapes_full(M, N, Kd):
+    """The layer's projections in W8A8 at full size, every output: the input
+    projection (41,024 x 4,096) and the output projection (4,096 x 8,192) for
+    the 8,192-token prefill and for decode tokens."""
+    announce("gemm fp8 w8a8 full M=%d N=%d K=%d" % (M, N, Kd))
+    y, ref = run_w8a8(M, N, Kd, out_dtype=torch.bfloat16 if M > 8 else torch.float32, seed=N + M)
+    e = relerr(host64(y), ref)
+    print("  err %.2e" % e, flush=True)
+    assert e < (5e-3 if M > 8 else TOL_W8A8_GEMV)
+
+
+def test_epilogue_fp8_feeds_w8a8_projection():
+    """The output projection takes the quantized epilogue directly (codes
+    [T, H*128], one scale per (token, head) = per 128-column group): the GPU
+    chain against the oracle's own chain (float64 epilogue, its quantizer,
+    the W8A8 product). The two quantizers may round a value lying within
+    float32 rounding of a tie differently (about 1% of the codes; one code
+    step each), so the bound is 1% of the largest output."""
+    for T in (6, 300):
+        announce("epilogue fp8 -> w8a8 projection T=%d" % T)
+        rng = np.random.default_rng(95 + T)
+        H, N = 16, 1000
+        o = (rng.standard_normal((T, H, 128)) * rng.uniform(0.1, 3.0, (T, H, 1))).astype(np.float32)
+        gate = synth.normal(rng, (T, H * 128))
+        w = rng.uniform(0.5, 1.5, 128).astype(np.float32)
+        wc = fp8_codes(rng, (N, H * 128))
+        ws = rng.uniform(1e-3, 1e-2, ((N + 127) // 128, H)).astype(np.float32)
+        codes = torch.empty((T, H * 128), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((T, H), dtype=torch.float32, device="cuda")
+        K.kda_output_norm_gate_fp8(torch.from_numpy(o).cuda(), dev(gate), torch.from_numpy(w).cuda(), codes, scales)
+        y = torch.empty((T, N), dtype=torch.float32, device="cuda")
+        K.kda_gemm_fp8(codes, scales, torch.from_numpy(wc).cuda(), torch.from_numpy(ws).cuda(), y)
+        torch.cuda.synchronize()
+        yo = R.output_norm_gate(o, gate.vals, w).reshape(T, H * 128)
+        rc, rs = R.quantize_fp8_groups(yo)
+        ref = R.gemm_fp8_w8a8(rc, rs, wc, ws)
+        e = relerr(host64(y), ref)
+        print("  err %.2e" % e, flush=True)
+        assert e < 1e-2
