@@ -374,7 +374,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--skip-layer", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "seqpar", "varlen", "decode", "layer", "fp8", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "seqpar", "varlen", "decode", "decode_step", "layer", "fp8", "copy"],
+                    default=None,
                     help="time one path only (for profiler runs); 'copy' times the plain copy that calibrates byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -441,6 +442,15 @@ def main():
                          "ms_per_step": ms_v, "tokens/s/layer": T_v / (ms_v * 1e-3),
                          "algorithmic_GB/s": (T_v * (4 * 64 * 128 * 2 + 64 * 2 + 64 * 128 * 4)
                                               + 2 * 8 * 64 * 128 * 128 * 4) / (ms_v * 1e-3) / 1e9}
+    if args.only == "decode_step":
+        # the decode step and the conv update alone (a profile of this run
+        # holds no other decode_kernel instantiation)
+        log("decode step only, B=256 H=64")
+        ms, ms_conv, ms_ref = bench_decode(torch, K, args.steps, args.warmup)
+        out["decode"] = {"ms_per_step": ms, "GB/s": DECODE_BYTES / (ms * 1e-3) / 1e9,
+                         "frac_of_hbm_peak": DECODE_BYTES / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        out["conv_update"] = {"ms_per_step": ms_conv, "GB/s": CONV_BYTES / (ms_conv * 1e-3) / 1e9,
+                              "frac_of_hbm_peak": CONV_BYTES / (ms_conv * 1e-3) / 1e9 / HBM_PEAK_GBS}
     if args.only in (None, "decode"):
         log("decode B=256 H=64")
         ms, ms_conv, ms_ref = bench_decode(torch, K, args.steps, args.warmup)
@@ -453,7 +463,8 @@ def main():
                          "inplace_stream_reference_GB/s": ref_gbs,
                          "inplace_stream_reference": "torch mul_ in place on the 1 GiB state buffer (read + write)"}
         out["conv_update"] = {"workload": "x [256,8192] bf16, state [256,3,8192] bf16 in place",
-                              "ms_per_step": ms_conv, "GB/s": CONV_BYTES / (ms_conv * 1e-3) / 1e9}
+                              "ms_per_step": ms_conv, "GB/s": CONV_BYTES / (ms_conv * 1e-3) / 1e9,
+                              "frac_of_hbm_peak": CONV_BYTES / (ms_conv * 1e-3) / 1e9 / HBM_PEAK_GBS}
         log("decode B=256 H=64, bf16 state")
         ms_b, nb = bench_decode_bf16_state(torch, K, args.steps, args.warmup)
         out["decode_bf16_state"] = {"workload": "decode step B=256 H=64, bf16 inputs, state stored in bf16 "

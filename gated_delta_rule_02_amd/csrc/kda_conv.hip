@@ -91,6 +91,87 @@ __global__ __launch_bounds__(kWaves * 64) void conv_update_kernel(ConvUpdateArgs
         if (j < W - 1) st2(st + (size_t)j * a.C + c, win[j + 1].x, win[j + 1].y);
 }
 
+// Wide form (W fixed at compile time): a lane owns 8 consecutive channels, so
+// that every access is 16 bytes (the input, each state row, the output, the
+// lane's 8 x W weights); a 16-lane row of the wavefront covers one group of
+// 128 channels, whose L2 norm is a 16-lane reduction.
+// Two sequences per thread (the second B/2 rows on), so that the lane's
+// weights serve both; streamed data goes around the caches (non-temporal).
+template <typename T, int W>
+__global__ __launch_bounds__(kWaves * 64) void conv_update_wide_kernel(ConvUpdateArgs a)
+{
+    using V = Vec16<T>;
+    constexpr int NV = 8 / V::N;  // 16-byte vectors per 8 channels
+    const int half = (a.B + 1) / 2;
+    const int c = (blockIdx.y * kWaves + (threadIdx.x >> 6)) * 512 + 8 * (threadIdx.x & 63);
+    const bool in = c < a.C;  // C is a multiple of 128: whole 16-lane groups are in or out
+    float wv[8 * W], bv[8];
+    if (in) {
+        // weights of channels c .. c + 7: 8 W consecutive values
+        const T* wp = static_cast<const T*>(a.weight) + (size_t)c * W;
+#pragma unroll
+        for (int v = 0; v < 8 * W / V::N; ++v) V::unpack(ld16(wp + v * V::N), &wv[v * V::N]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bv[e] = 0.f;
+        if (a.bias) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) V::unpack(ld16(static_cast<const T*>(a.bias) + c + v * V::N), &bv[v * V::N]);
+        }
+    }
+#pragma unroll
+    for (int rep = 0; rep < 2; ++rep) {
+        const int b = blockIdx.x + rep * half;
+        if (b >= a.B) break;  // uniform over the workgroup
+        const T* x = static_cast<const T*>(a.x) + (size_t)b * a.x_ld + c;
+        T* st = static_cast<T*>(a.conv_state) + (size_t)b * (W - 1) * a.C + c;
+        float win[W][8], acc[8];
+        if (in) {
+#pragma unroll
+            for (int j = 0; j < W; ++j) {
+                const T* src = j < W - 1 ? st + (size_t)j * a.C : x;
+#pragma unroll
+                for (int v = 0; v < NV; ++v)
+                    V::unpack(__builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + v * V::N)),
+                              &win[j][v * V::N]);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                acc[e] = bv[e];
+#pragma unroll
+                for (int j = 0; j < W; ++j) acc[e] += wv[e * W + j] * win[j][e];
+            }
+            if (a.apply_silu) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] = siluf_(acc[e]);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+        }
+        if (a.l2_group) {
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += acc[e] * acc[e];
+            const float r = rsqrtf(group_sum<16>(ss) + a.l2_eps);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] *= r;
+        }
+        if (in) {
+            T* y = static_cast<T*>(a.y) + (size_t)b * a.C + c;
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+                __builtin_nontemporal_store(V::pack(&acc[v * V::N]), reinterpret_cast<u32x4_t*>(y + v * V::N));
+            // shift the window left by one and append the new input (bit copies)
+#pragma unroll
+            for (int j = 0; j < W - 1; ++j)
+#pragma unroll
+                for (int v = 0; v < NV; ++v)
+                    __builtin_nontemporal_store(V::pack(&win[j + 1][v * V::N]),
+                                                reinterpret_cast<u32x4_t*>(st + (size_t)j * a.C + v * V::N));
+        }
+    }
+}
+
 // ---------------------------------------------------------------- prefill
 __device__ __forceinline__ int find_seq(const int32_t* cu, int num_seqs, int64_t t)
 {
@@ -260,6 +341,22 @@ __global__ void conv_state_out_kernel(ConvPrefillArgs a)
 
 hipError_t launch_conv_update(const ConvUpdateArgs& a, hipStream_t s)
 {
+    // the wide form: 8 channels per lane, 16-byte accesses (C is a multiple
+    // of 128 and every row 16-byte aligned)
+    {
+        const dim3 grid((unsigned)((a.B + 1) / 2), (unsigned)((a.C + 512 * kWaves - 1) / (512 * kWaves))),
+            block(kWaves * 64);
+        switch (a.W) {
+#define KDA_CONVU_W(WW)                                                                                    \
+    case WW:                                                                                               \
+        if (a.dtype == F32) hipLaunchKernelGGL((conv_update_wide_kernel<float, WW>), grid, block, 0, s, a); \
+        else hipLaunchKernelGGL((conv_update_wide_kernel<bf16_t, WW>), grid, block, 0, s, a);            \
+        return hipGetLastError();
+            KDA_CONVU_W(2) KDA_CONVU_W(3) KDA_CONVU_W(4) KDA_CONVU_W(5) KDA_CONVU_W(6) KDA_CONVU_W(7) KDA_CONVU_W(8)
+#undef KDA_CONVU_W
+            default: break;
+        }
+    }
     dim3 grid((unsigned)a.B, (unsigned)((a.C + kGroup * kWaves - 1) / (kGroup * kWaves))), block(kWaves * 64);
     if (a.dtype == F32)
         hipLaunchKernelGGL(conv_update_kernel<float>, grid, block, 0, s, a);
