@@ -638,7 +638,7 @@ int kda_prefill_segment_maps(const void* k, const void* v, const void* g, const 
         REQUIRE(!overlap(r, rws), KDA_ERR_INVALID_ARG, "kda_prefill_segment_maps: workspace overlaps an input");
 
     PrefillArgs a{};
-    a.q = k;  // the intra pass also forms the read-side products from a query array; they go unused here
+    a.q = k;  // never read: the map pass forms no query side
     a.k = k; a.v = v; a.g = g; a.beta = beta;
     a.cu_seqlens = cu_seqlens_dev; a.seq_len = seq_len;
     a.sT = N_out; a.map_M = M_out;

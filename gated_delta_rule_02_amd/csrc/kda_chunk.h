@@ -305,13 +305,15 @@ struct __attribute__((aligned(16))) Smem {
 // group hh of block R); the next chunk's k, q, g of those tokens and beta
 // stream into registers while the current chunk computes. The caller
 // separates the phases with barriers.
+// NoQ: no query side (the segment maps of the sequence-parallel prefill form
+// no output): q is not loaded and neither P nor q o 2^b is formed.
 // Lean: the two-pass intra pass. The kernel holds no state in registers
 // here, so P2 can afford more live registers: the diagonal-block inverses by
 // repeated squaring instead of the Horner form (fewer dependent products) and
 // the off-diagonal pairs split evenly over the SIMDs. The producers also load
 // v and, in P2b, stage the right-hand sides -diag(beta)(K o 2^B) and
 // diag(beta) V of the products with T, transposed and rounded once.
-template <bool F32P, typename TIN, int NQ = 2, bool Lean = false, int LoadPol = 0>
+template <bool F32P, typename TIN, int NQ = 2, bool Lean = false, int LoadPol = 0, bool NoQ = false>
 struct Front {
     using O = Ops<F32P>;
     using OT = typename O::OT;
@@ -372,7 +374,7 @@ struct Front {
                     rk[t] = IN::template ld_pair<Pol>(rk_, voff, soff);
                 }
             }
-            if constexpr (Parts & 2) {
+            if constexpr ((Parts & 2) && !NoQ) {
                 const rsrc_t rq_ = make_rsrc(qg + c_s * ts, bytes);
 #pragma unroll
                 for (int t = 0; t < RP; ++t) rq[t] = IN::template ld_pair<Pol>(rq_, voff, (rbase + t) * ts * ES);
@@ -466,10 +468,10 @@ struct Front {
 #pragma unroll
         for (int t = 0; t < RP; ++t) {
             el *= al[t];
-            const f32x2 kv = IN::unpack(rk[t]), qv = IN::unpack(rq[t]);
+            const f32x2 kv = IN::unpack(rk[t]), qv = NoQ ? f32x2{0.f, 0.f} : IN::unpack(rq[t]);
             const f32x2 klv = kv * el, qlv = qv * el;
             *reinterpret_cast<f32x2*>(&sm.key.f.KL[rbase + t][c0]) = klv;
-            *reinterpret_cast<f32x2*>(&sm.key.f.QL[rbase + t][c0]) = qlv;
+            if constexpr (!NoQ) *reinterpret_cast<f32x2*>(&sm.key.f.QL[rbase + t][c0]) = qlv;
             if constexpr (Lean) {
                 kt2[t] = O::pack2(klv.x * (DR.x * nb[t]), klv.y * (DR.y * nb[t]));
                 const f32x2 vv = IN::unpack(rvv[t]);  // the next chunk's loads reuse rvv after P1
@@ -507,7 +509,7 @@ struct Front {
             const f32x4 x0 = ld4f(ks) * ld4f(&sm.Fd[Rd][c]);
             const f32x4 x1 = ld4f(ks + 16) * ld4f(&sm.Fd[Rd][c + 16]);
             accA = O::diagA(ld4f(kl), ld4f(kl + 16), x0, x1, accA);
-            accP = O::diagP(ld4f(ql), ld4f(ql + 16), x0, x1, accP);
+            if constexpr (!NoQ) accP = O::diagP(ld4f(ql), ld4f(ql + 16), x0, x1, accP);
             if constexpr (!Lean) __builtin_amdgcn_sched_barrier(0);  // one K step at a time (register pressure)
         }
 #pragma unroll
@@ -515,7 +517,7 @@ struct Front {
             const int row = 4 * q4 + i;  // row in block, column m16
             const float b = sm.beta[16 * Rd + row];
             sm.Nd[Rd][row][m16] = (OT)(row > m16 ? -accA[i] * b : 0.0f);
-            sm.Pb[tri_id(Rd, Rd)][row][m16] = (OT)(row >= m16 ? accP[i] : 0.0f);
+            if constexpr (!NoQ) sm.Pb[tri_id(Rd, Rd)][row][m16] = (OT)(row >= m16 ? accP[i] : 0.0f);
         }
         // wavefront-local: the inverse below reads what this wavefront wrote
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -561,9 +563,10 @@ struct Front {
     }
 
     // Off-diagonal block (Rr, I), I < Rr: -A (beta-scaled) and / or P
-    template <bool DoA, bool DoP>
+    template <bool DoA, bool DoP_>
     __device__ __forceinline__ void p2_pair(int Rr, int I)
     {
+        constexpr bool DoP = DoP_ && !NoQ;
         const int pid = pair_id(Rr, I);
         f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -633,7 +636,7 @@ struct Front {
             h8 w0, w1, u0, u1;
 #pragma unroll
             for (int t = 0; t < RP; ++t) {
-                *reinterpret_cast<typename O::P2*>(&sm.key.x.Qt[rbase + t][c0]) = qt2[t];
+                if constexpr (!NoQ) *reinterpret_cast<typename O::P2*>(&sm.key.x.Qt[rbase + t][c0]) = qt2[t];
                 w0[t] = kt2[t].x;
                 w1[t] = kt2[t].y;
                 u0[t] = xu2[t].x;

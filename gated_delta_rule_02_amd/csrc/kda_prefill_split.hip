@@ -111,8 +111,9 @@ __device__ __forceinline__ void inverse_column(SM& sm, _Float16 (*Tm)[16][BLD], 
     }
 }
 
-// POL: cache policy of the input loads (0 or kStream)
-template <typename TIN, int POL>
+// POL: cache policy of the input loads (0 or kStream); NOQ: segment maps
+// (no query side: Q~ and P are neither formed nor stored)
+template <typename TIN, int POL, bool NOQ = false>
 __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
 {
     using O = Ops<false>;
@@ -148,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
     const TIN* vg = static_cast<const TIN*>(a.v);
     uint8_t* slots = sa.ws + (size_t)u * sa.nwin * kSlot;
 
-    Front<false, TIN, 2, true, POL> fr(sm, a, h);
+    Front<false, TIN, 2, true, POL, NOQ> fr(sm, a, h);
     {
         const int64_t cs = seq_s + c_first * C;
         fr.load(cs, (int)min<int64_t>(C, seq_e - cs), vg);
@@ -247,9 +248,10 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
         // ---- the operand matrices in the A-operand layout, 16 bytes per lane
         // (every LDS read is issued before the first store, so that they are
         // in flight together)
-        h8 cq[2], ck[2], cp = {};
+        h8 cq[2] = {}, ck[2], cp = {};
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
+            if constexpr (NOQ) break;
             const int idx = tid + kThreads * k2;  // [t 4][s 4][lane 64]
             const int t = idx >> 8, s = (idx >> 6) & 3, l = idx & 63;
             const int row = 16 * t + (l & 15), col = 32 * s + 4 * (l >> 4);
@@ -264,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
             ck[k2] = cat(*reinterpret_cast<const h4*>(&sm.KbT[row][col]),
                          *reinterpret_cast<const h4*>(&sm.KbT[row][col + 16]));
         }
-        if (tid < 6 * 64) {
+        if (!NOQ && tid < 6 * 64) {
             const int i = tid >> 6, l = tid & 63;  // fragment i = (t, s) with 2s <= t
             const int t = i < 2 ? i : 2 + (i - 2) / 2, s = i < 2 ? 0 : (i - 2) % 2;
             const int m = l & 15, cq4 = 4 * (l >> 4);
@@ -278,10 +280,10 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             const int idx = tid + kThreads * k2;
-            *reinterpret_cast<h8*>(slot + kQt + idx * 16) = cq[k2];
+            if constexpr (!NOQ) *reinterpret_cast<h8*>(slot + kQt + idx * 16) = cq[k2];
             *reinterpret_cast<h8*>(slot + kKbT + idx * 16) = ck[k2];
         }
-        if (tid < 6 * 64) *reinterpret_cast<h8*>(slot + kPm + tid * 16) = cp;
+        if (!NOQ && tid < 6 * 64) *reinterpret_cast<h8*>(slot + kPm + tid * 16) = cp;
         if (tid < D / 4) *reinterpret_cast<f32x4*>(slot + kDc + tid * 16) = cdc;
         // the next P0 writes only Gp and beta, which nothing above reads; its
         // barrier orders these LDS reads before P1 reuses the region
@@ -392,9 +394,12 @@ void state_kernel(SplitArgs sa)
     auto dma = [&](int c, int b) {
         const uint32_t st = lds0 + b * kStage;
 #pragma unroll
-        for (int i = 0; i < kDma / 1024; ++i)
+        for (int i = 0; i < kDma / 1024; ++i) {
+            // segment maps read neither Q~ nor P
+            if (MAP && ((i >= kQt / 1024 && i < kKbT / 1024) || i >= kPm / 1024)) continue;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(uintptr_t)(st + i * 1024), 16, lane * 16,
                                                      c * kSlot + i * 1024, 0, 0);
+        }
 #pragma unroll
         for (int i = 0; i < 2 * kTiles; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(uintptr_t)(st + kStUp + i * 1024), 16, lane * 16,
@@ -695,7 +700,11 @@ hipError_t launch_prefill_split(const PrefillArgs& a, void* ws, size_t ws_bytes,
         const int64_t chains = active * (a.map_M ? 2 : 1);
         const bool narrow = chains * 4 <= 256;
         if (max_chunks > 0) {
-            if (stream)
+            if (a.map_M && stream)
+                hipLaunchKernelGGL((intra_kernel<bf16_t, kStream, true>), gi, bi, 0, s, sa);
+            else if (a.map_M)
+                hipLaunchKernelGGL((intra_kernel<bf16_t, 0, true>), gi, bi, 0, s, sa);
+            else if (stream)
                 hipLaunchKernelGGL((intra_kernel<bf16_t, kStream>), gi, bi, 0, s, sa);
             else
                 hipLaunchKernelGGL((intra_kernel<bf16_t, 0>), gi, bi, 0, s, sa);
