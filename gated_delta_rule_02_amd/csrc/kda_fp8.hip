@@ -339,12 +339,21 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(QuantFp8Args a)
 // through each lane's source address), so that the rows of an operand read
 // spread over the banks. As in the bf16 GEMM, the product is formed
 // transposed, so that a lane holds four consecutive columns of one row of Y.
+// Per block a wavefront issues the eight products of two W tiles and its four
+// X tiles into separate registers before scaling them in, so that the matrix
+// unit runs while the vector unit adds (one shared result register left every
+// product's latency exposed).
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 constexpr int kF8Tile = 256;                  // rows of X and of W per workgroup
 constexpr int kF8Stage = 2 * kF8Tile * 128;   // one K step: X rows, then W rows
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-__device__ __forceinline__ int swz8(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+// 16-byte chunk c (0..7) of row r: slot c ^ ((r / 2) mod 8). A fragment read
+// takes one chunk of 16 consecutive rows; rows r and r + 1 fall in different
+// halves of the 64 banks and the even (odd) rows of the 16 get distinct slots,
+// so the read is free of bank conflicts (with slot c ^ (r mod 8), rows r and
+// r + 8 collided: 2-way conflicts on every read).
+__device__ __forceinline__ int swz8(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
 template <typename TC, bool VEC>
 __global__ __launch_bounds__(512) void gemm_fp8_kernel(Fp8GemvArgs a)
@@ -371,13 +380,13 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(Fp8GemvArgs a)
     // after), lane l row 8 i' + l / 8 and LDS chunk slot l % 8, which holds
     // K chunk slot ^ (row mod 8)
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t*)&smem[0][0];
-    const int crow = lane >> 3, cchunk = (lane & 7) ^ (lane >> 3);
+    const int crow = lane >> 3;
     auto copy = [&](int kb, int st) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int i = wave * 8 + j;  // wave-uniform: X for waves 0-3, W for 4-7
             const int r = 8 * (i & 31) + crow;
-            const int koff = kb * 128 + 16 * cchunk;
+            const int koff = kb * 128 + 16 * ((lane & 7) ^ ((r >> 1) & 7));
             const uint32_t dst = lds0 + st * kF8Stage + i * 1024;
             if (i < 32)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(uintptr_t)dst, 16, (int)(r * a.ldx) + koff, 0, 0, 0);
@@ -424,24 +433,32 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(Fp8GemvArgs a)
             fa[i] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         }
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            i32x8_t fb[4];
+        for (int h = 0; h < 4; ++h) {
+            i32x8_t fb[2];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = wn + 16 * (4 * h + j) + m16;
+            for (int j = 0; j < 2; ++j) {
+                const int r = wn + 16 * (2 * h + j) + m16;
                 const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(sb + swz8(r, 2 * q4));
                 const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(sb + swz8(r, 2 * q4 + 1));
                 fb[j] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
             }
+            f32x4 p[4][2];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < 2; ++j)
                     // formats 0 / 0: E4M3 operands; block scales 127 (E8M0 1.0)
-                    const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[j], fa[i], zero, 0, 0, 0, 127, 0, 127);
-                    f32x4& c = acc[i][4 * h + j];
+                    p[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[j], fa[i], zero, 0, 0, 0, 127, 0, 127);
+            // the eight products first, then the 32 scale-adds
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) c[e] = fmaf(p[e], s[i], c[e]);
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    f32x4& c = acc[i][2 * h + j];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) c[e] = fmaf(p[i][j][e], s[i], c[e]);
                 }
         }
         __syncthreads();  // the copy of step kb + 1 has landed and every read of stage st is done
