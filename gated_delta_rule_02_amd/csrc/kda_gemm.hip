@@ -9,18 +9,19 @@
 //
 // Two kernels. The main one (K a multiple of 64): a 256 x 256 tile of C per
 // workgroup of 4 wavefronts, each owning 128 x 128 (8 x 8 MFMA tiles, 256
-// accumulator registers: one wavefront per SIMD), K steps of 32 in four LDS
-// stages filled by buffer-to-LDS copies that the wavefronts issue three steps
-// ahead, and operand fragments read one step ahead. Per K step a wavefront
-// reads 16 KiB of operands from LDS for 64 MFMAs, half the LDS rate the MFMAs
-// could use. The stage
-// layout is row major with the 16-byte K chunks of each row XOR-swizzled by
-// (row / 4) mod 4, so that the 16 rows an MFMA operand read touches fall in
-// distinct banks; the swizzle is applied by choosing each lane's global
-// source address (a buffer-to-LDS copy writes lane l to byte 16 l of its
-// 1 KiB destination). The products are formed transposed
-// (B tile x A tile^T): each lane then holds four consecutive columns of one
-// row of C, stored with one 16-byte (float32) or 8-byte (bfloat16) access.
+// accumulator registers: one wavefront per SIMD), K steps of 64 in two LDS
+// stages filled by buffer-to-LDS copies of whole 128-byte operand rows (the
+// copy of step k + 1 runs during step k). With K steps of 32 every copy
+// request covered half a cache line, and the kernel issued twice the L2 read
+// requests of the vendor BLAS for the same product; at the per-compute-unit
+// limit on requests in flight that halved its operand bandwidth. The stage
+// rows are 128 bytes with their 16-byte chunks XOR-swizzled by (row / 2) mod
+// 8 (applied by choosing each lane's global source address: a buffer-to-LDS
+// copy writes lane l to byte 16 l of its 1 KiB destination), so that the 16
+// rows an MFMA operand read touches fall in distinct banks. The products are
+// formed transposed (B tile x A tile^T): each lane then holds four
+// consecutive columns of one row of C, stored with one 16-byte (float32) or
+// 8-byte (bfloat16) access.
 // The fallback (any K multiple of 8): 128 x 128 tiles, 2 x 2 wavefronts of
 // 64 x 64, K steps of 32 through double-buffered LDS.
 #include "kda_device.h"
@@ -117,15 +118,16 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a)
 }
 
 // ------------------------------------------------------------ main kernel
-constexpr int TM = 256, TN = 256, TK = 32;   // workgroup tile and K step
-constexpr int kStages = 4;                   // K steps in LDS: the copies run 3 steps ahead
-constexpr int kStageBytes = TM * TK * 2;      // one operand's stage: 256 rows x 64 B
+constexpr int TM = 256, TN = 256, TK = 64;  // workgroup tile and K step (128 bytes of each operand row)
+constexpr int kStageBytes = TM * TK * 2;     // one operand's stage: 256 rows x 128 B
 typedef __attribute__((address_space(3))) void lds_void;
 
-// LDS byte offset of 16-byte chunk c (0..3) of row r of a stage: the chunks
-// are XOR-swizzled by (r / 4) mod 4, so the 16 rows of an operand read cover
-// all 64 banks
-__device__ __forceinline__ int swz(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+// LDS byte offset of 16-byte chunk c (0..7) of row r of a stage: the chunks are
+// XOR-swizzled by (r / 2) mod 8. An operand read takes one chunk of 16
+// consecutive rows; rows r and r + 1 lie in different halves of the 64
+// banks and the 8 even (odd) rows get distinct slots, so the read touches
+// every bank once.
+__device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
 // NJ: 16-column MFMA tiles per wavefront in N (8: the 256 x 256 tile; 2 or 4:
 // a 256 x 64 or 256 x 128 tile for the last N mod 256 columns, so that they
@@ -134,11 +136,10 @@ template <typename TC, int NJ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm256_kernel(GemmArgs a)
 {
     constexpr int TNW = 32 * NJ;         // columns of C per workgroup
-    constexpr int kBCopy = TNW / 64;     // B copy instructions per wavefront and K step
-    constexpr int kCopyInstr = 4 + kBCopy;
-    constexpr int kWaitOneCopy = 0x0f70 | kCopyInstr;  // s_waitcnt vmcnt(kCopyInstr)
+    constexpr int kACopy = TM / 32;      // A copy instructions per wavefront and K step (8 rows each)
+    constexpr int kBCopy = TNW / 32;     // B copy instructions per wavefront and K step
     static_assert(NJ == 2 || NJ == 4 || NJ == 8, "64, 128 or 256 columns");
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kStages][2][kStageBytes];  // [stage][A, B]
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2][2][kStageBytes];  // [stage][A, B]
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -158,32 +159,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const rsrc_t ra = make_rsrc(A, ((rows_a - 1) * a.lda + a.K) * 2);
     const rsrc_t rb = make_rsrc(B, ((rows_b - 1) * a.ldb + a.K) * 2);
 
-    // copy of K step kt into stage st: 16 instructions for A (4 per
-    // wavefront) and TNW / 16 for B (kBCopy per wavefront); instruction i
-    // covers rows 16i .. 16i+15, lane l row 16i + l/4 and LDS chunk slot l%4,
-    // which holds K chunk slot ^ ((row/4) mod 4)
+    // copy of K step kt into stage st: whole 128-byte rows, 8 rows per 1 KiB
+    // instruction (lane l: row 8i + l/8, LDS chunk slot l%8, which holds the
+    // row's K chunk slot ^ ((row / 2) mod 8))
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)&smem[0][0][0];
-    const int lrow = lane >> 2, lslot = lane & 3;
-    auto copy_part = [&](int kt, int st, int j) {
-        const int i = wave * 4 + j;
-        const int row = 16 * i + lrow;
-        const int chunk = lslot ^ ((row >> 2) & 3);
-        const int koff = (kt * TK + chunk * 8) * 2;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(uintptr_t)(lds0 + (st * 2 + 0) * kStageBytes + i * 1024),
-                                                 16, (int)(row * a.lda * 2) + koff, 0, 0, 0);
-        if (j < kBCopy) {
-            // B has TNW rows: instruction ib = wave * kBCopy + j covers rows 16 ib .. 16 ib + 15
-            const int ib = wave * kBCopy + j;
-            const int rowb = 16 * ib + lrow;
-            const int chunkb = lslot ^ ((rowb >> 2) & 3);
-            const int koffb = (kt * TK + chunkb * 8) * 2;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(uintptr_t)(lds0 + (st * 2 + 1) * kStageBytes + ib * 1024),
-                                                     16, (int)(rowb * a.ldb * 2) + koffb, 0, 0, 0);
-        }
-    };
+    const int lrow = lane >> 3, lslot = lane & 7;
     auto copy = [&](int kt, int st) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) copy_part(kt, st, j);
+        for (int j = 0; j < kACopy; ++j) {
+            const int i = wave * kACopy + j;
+            const int row = 8 * i + lrow;
+            const int koff = (kt * TK + (lslot ^ ((row >> 1) & 7)) * 8) * 2;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(uintptr_t)(lds0 + (st * 2 + 0) * kStageBytes + i * 1024),
+                                                     16, (int)(row * a.lda * 2) + koff, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < kBCopy; ++j) {
+            const int i = wave * kBCopy + j;
+            const int row = 8 * i + lrow;
+            const int koff = (kt * TK + (lslot ^ ((row >> 1) & 7)) * 8) * 2;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(uintptr_t)(lds0 + (st * 2 + 1) * kStageBytes + i * 1024),
+                                                     16, (int)(row * a.ldb * 2) + koff, 0, 0, 0);
+        }
     };
 
     f32x4 acc[8][NJ];
@@ -192,54 +189,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Pipeline: step kt computes on stage kt % 4 with operand fragments read
-    // during step kt - 1. Between its MFMAs it issues the copy of step kt + 3
-    // (each copy instruction waits for the compute unit's address unit, 1 KiB
-    // at 64 B per clock shared by the four wavefronts, which the matrix unit's
-    // work hides; issued up front they delayed every step's MFMAs) and reloads
-    // each A fragment for step kt + 1 as soon as its last MFMA is issued (the
-    // B fragments, used by every row, after the last row). At its end it waits
-    // for the copy of step kt + 2, so that after the barrier stage kt + 2 is
-    // complete for the next step's early reads. The compiler does not track
-    // the copies: the waits are explicit. A copy is kCopyInstr instructions
-    // per wavefront (4 of A, kBCopy of B) and copies complete in order, so
-    // "copy c has landed" is vmcnt(kCopyInstr x the copies issued after it).
+    // Pipeline: two stages of 64 K. Step kt computes on stage kt % 2 (two K32
+    // halves) while the copy of step kt + 1, issued at its start, fills the
+    // other stage; the second half's fragments are read while the first half's
+    // MFMAs run. At its end every wavefront waits for its copy (the compiler
+    // does not track these copies: the wait is explicit) and the barrier
+    // hands the stage over.
     const int nk = (int)(a.K / TK);
     u32x4_t fa[8], fb[NJ];
-    auto read_a = [&](int kt, int i) {
-        fa[i] = *reinterpret_cast<const u32x4_t*>(&smem[kt % kStages][0][0] + swz(wm + 16 * i + m16, q4));
+    auto read_a = [&](int st, int h, int i) {
+        fa[i] = *reinterpret_cast<const u32x4_t*>(&smem[st][0][0] + swz(wm + 16 * i + m16, 4 * h + q4));
     };
-    auto read_b = [&](int kt, int j) {
-        fb[j] = *reinterpret_cast<const u32x4_t*>(&smem[kt % kStages][1][0] + swz(wn + 16 * j + m16, q4));
+    auto read_b = [&](int st, int h, int j) {
+        fb[j] = *reinterpret_cast<const u32x4_t*>(&smem[st][1][0] + swz(wn + 16 * j + m16, 4 * h + q4));
     };
-    for (int p = 0; p < kStages - 1 && p < nk; ++p) copy(p, p);
-    if (nk > 2) __builtin_amdgcn_s_waitcnt(kWaitOneCopy);  // steps 0 and 1 landed (step 2 in flight)
-    else __builtin_amdgcn_s_waitcnt(0x0f70);               // vmcnt(0)
+    copy(0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     lds_barrier();
-#pragma unroll
-    for (int i = 0; i < 8; ++i) read_a(0, i);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) read_b(0, j);
     for (int kt = 0; kt < nk; ++kt) {
-        const bool cp = kt + kStages - 1 < nk, nx = kt + 1 < nk;
+        const int st = kt & 1;
+        if (kt + 1 < nk) copy(kt + 1, st ^ 1);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 8; ++i) read_a(st, 0, i);
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb[j]),
-                                                                    __builtin_bit_cast(bf16x8, fa[i]), acc[i][j], 0, 0, 0);
-            if (i < 4 && cp) copy_part(kt + kStages - 1, (kt + kStages - 1) % kStages, i);
-            if (nx) read_a(kt + 1, i);
-            __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < NJ; ++j) read_b(st, 0, j);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb[j]),
+                                                                        __builtin_bit_cast(bf16x8, fa[i]), acc[i][j], 0, 0, 0);
+                if (h == 0) read_a(st, 1, i);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (h == 0) {
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) read_b(st, 1, j);
+            }
         }
-        if (nx) {
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) read_b(kt + 1, j);
-        }
-        // the copy of step kt + 2 has landed (this wavefront's part) ...
-        if (cp) __builtin_amdgcn_s_waitcnt(kWaitOneCopy);  // vmcnt(kCopyInstr)
-        else __builtin_amdgcn_s_waitcnt(0x0f70);           // vmcnt(0)
-        lds_barrier();  // ... and everyone's; every read of stage kt % 4 is done
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wavefront's copy has landed ...
+        lds_barrier();                        // ... and everyone's; every read of stage st is done
     }
 
     // acc[i][j] holds C^T of tile (i, j): lane (m16, q4) element e is
