@@ -98,6 +98,34 @@ def timed(torch, fn, steps, warmup):
     return start.elapsed_time(end) / steps, wall
 
 
+def graph_ms(torch, fn, n):
+    """Per-call ms of `n` calls captured in one HIP graph and replayed: for a
+    kernel of a few microseconds, back-to-back launches from the host time the
+    dispatch gap as much as the kernel; a graph replays them without it. The
+    graph is replayed several times with synchronizations between (an eager
+    call first, as a warm-up)."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(n):
+                fn()
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b) / n
+        best = t if best is None else min(best, t)
+    return best
+
+
 def timed_cold(torch, fn, steps, warmup, flush_bytes=512 << 20):
     """Per-call ms when, before every call, a 512 MiB buffer is written so that
     the 256 MB last-level cache (MALL) and L2 hold none of the call's inputs.
@@ -231,10 +259,11 @@ def bench_decode(torch, K, steps, warmup):
     x, cst, w = dev(d["conv_x"], torch), dev(d["conv_state"], torch), dev(d["conv_w"], torch)
     y = torch.empty_like(x)
     ms_conv, _ = timed(torch, lambda: K.kda_conv_state_update(x, cst, w, y), steps, warmup)
+    ms_conv_graph = graph_ms(torch, lambda: K.kda_conv_state_update(x, cst, w, y), steps)
     # reference: a plain in-place read-modify-write of a buffer the size of the
     # state (torch's elementwise kernel), the access pattern decode cannot avoid
     ms_ref, _ = timed(torch, lambda: st.mul_(1.0), max(5, steps // 2), 2)
-    return ms, ms_conv, ms_ref
+    return ms, (ms_conv, ms_conv_graph), ms_ref
 
 
 def bench_decode_multi(torch, K, steps, warmup):
@@ -446,15 +475,15 @@ def main():
         # the decode step and the conv update alone (a profile of this run
         # holds no other decode_kernel instantiation)
         log("decode step only, B=256 H=64")
-        ms, ms_conv, ms_ref = bench_decode(torch, K, args.steps, args.warmup)
+        ms, (ms_conv, ms_cg), ms_ref = bench_decode(torch, K, args.steps, args.warmup)
         out["decode"] = {"ms_per_step": ms, "GB/s": DECODE_BYTES / (ms * 1e-3) / 1e9,
                          "frac_of_hbm_peak": DECODE_BYTES / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
         out["conv_update"] = {"ms_per_step": ms_conv, "GB/s": CONV_BYTES / (ms_conv * 1e-3) / 1e9,
-                              "frac_of_hbm_peak": CONV_BYTES / (ms_conv * 1e-3) / 1e9 / HBM_PEAK_GBS}
+                              "graph_ms_per_step": ms_cg, "graph_frac_of_hbm_peak": CONV_BYTES / (ms_cg * 1e-3) / 1e9 / HBM_PEAK_GBS}
     if args.only in (None, "decode"):
         log("decode B=256 H=64")
-        ms, ms_conv, ms_ref = bench_decode(torch, K, args.steps, args.warmup)
-        log("decode %.3f ms/step, conv %.3f ms, in-place stream %.3f ms" % (ms, ms_conv, ms_ref))
+        ms, (ms_conv, ms_cg), ms_ref = bench_decode(torch, K, args.steps, args.warmup)
+        log("decode %.3f ms/step, conv %.4f ms (%.4f ms in a graph), in-place stream %.3f ms" % (ms, ms_conv, ms_cg, ms_ref))
         ref_gbs = 2 * 2 ** 30 / (ms_ref * 1e-3) / 1e9
         out["decode"] = {"workload": "decode step B=256 H=64 dk=dv=128, bf16 inputs, fp32 state [256,64,128,128] in place, fp32 o",
                          "ms_per_step": ms, "GB/s": DECODE_BYTES / (ms * 1e-3) / 1e9,
@@ -464,7 +493,11 @@ def main():
                          "inplace_stream_reference": "torch mul_ in place on the 1 GiB state buffer (read + write)"}
         out["conv_update"] = {"workload": "x [256,8192] bf16, state [256,3,8192] bf16 in place",
                               "ms_per_step": ms_conv, "GB/s": CONV_BYTES / (ms_conv * 1e-3) / 1e9,
-                              "frac_of_hbm_peak": CONV_BYTES / (ms_conv * 1e-3) / 1e9 / HBM_PEAK_GBS}
+                              "frac_of_hbm_peak": CONV_BYTES / (ms_conv * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                              "graph_ms_per_step": ms_cg,
+                              "graph_frac_of_hbm_peak": CONV_BYTES / (ms_cg * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                              "note": "ms_per_step: back-to-back launches, which for a kernel of a few microseconds "
+                                      "include the dispatch gap; graph_ms_per_step: 20 calls replayed from one HIP graph"}
         log("decode B=256 H=64, bf16 state")
         ms_b, nb = bench_decode_bf16_state(torch, K, args.steps, args.warmup)
         out["decode_bf16_state"] = {"workload": "decode step B=256 H=64, bf16 inputs, state stored in bf16 "

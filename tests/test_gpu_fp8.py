@@ -42,17 +42,21 @@ def test_gemv_fp8_small(M, N, Kd):
 
 
 def test_gemv_fp8_strided_rows():
-    """x and y as row-strided views of wider buffers (ldx > K, ldy > N), for
-    one token and for four."""
-    for M, N, Kd in ((1, 777, 2048), (4, 300, 1024)):
+    """x, y and the weight codes as row-strided views of wider buffers (ldx > K,
+    ldy > N, ldw > K), for one token, for four (row form) and for six (the
+    matrix-core form)."""
+    for M, N, Kd in ((1, 777, 2048), (4, 300, 1024), (6, 333, 1536)):
         announce("gemv fp8 strided M=%d N=%d K=%d" % (M, N, Kd))
         rng = np.random.default_rng(40 + M)
         codes, scales = fp8_weights(rng, N, Kd)
         x = synth.normal(rng, (M, Kd))
         xb = torch.zeros((M, Kd + 64), dtype=torch.bfloat16, device="cuda")
         xb[:, :Kd] = dev(x)
+        wb = torch.full((N, Kd + 48), 0x7F, dtype=torch.uint8)  # NaN codes in the padding: never read
+        wb[:, :Kd] = torch.from_numpy(codes)
+        wb = wb.cuda()
         yb = torch.full((M, N + 5), float("nan"), dtype=torch.float32, device="cuda")
-        K.kda_gemv_fp8(xb[:, :Kd], torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(), yb[:, :N])
+        K.kda_gemv_fp8(xb[:, :Kd], wb[:, :Kd], torch.from_numpy(scales).cuda(), yb[:, :N])
         torch.cuda.synchronize()
         assert relerr(host64(yb[:, :N]), R.gemv_fp8_blocks(x.vals, codes, scales)) < 2e-5
         assert torch.isnan(yb[:, N:]).all()
