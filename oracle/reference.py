@@ -492,6 +492,45 @@ def quantize_fp8_groups(y, group=128):
     return codes, scale
 
 
+def layer_forward_fp8(x, Win_codes, Win_scales, Wo_codes, Wo_scales, conv_q, conv_k, conv_v, A_log, norm_w,
+                      H, d=128, scale=1.0, lower_bound=-5.0, l2_eps=1e-6, rms_eps=1e-6,
+                      nthreads=None, return_parts=False, initial_state=None):
+    """The token mixer with block-FP8 (W8A8) projections -- [flozi-KDA]
+    section "Production boundaries" (E4M3 weights in 128 x 128 blocks with
+    dynamic activation quantization): the input x is quantized per (token,
+    128 channels) with float32 decisions (as a float32 implementation takes
+    them), the packed input projection P = X W_in^T is the exact product of the
+    decoded codes, stored as bfloat16; convolution, gate, core and epilogue are
+    those of ``layer_forward``; the epilogue output y (float64, not rounded) is
+    quantized per (token, head) and the output projection is the exact
+    product with W_o's codes.
+
+    Win_codes: [5*H*d + H, hidden] uint8 (rows q | k | v | f | gate | b),
+    Win_scales: [ceil(rows/128), hidden/128]; Wo_codes: [hidden, H*d] uint8,
+    Wo_scales: [hidden/128, H*d/128]. Returns out [T, hidden] float64 (and the
+    intermediates if asked)."""
+    x = np.asarray(x, dtype=np.float64)
+    T = x.shape[0]
+    W = H * d
+    xq, xs = quantize_fp8_groups_f32(x)
+    P = round_bf16(gemm_fp8_w8a8(xq, xs, Win_codes, Win_scales))
+    q_pre, k_pre, v_pre, f_pre, g_pre = (P[:, i * W:(i + 1) * W] for i in range(5))
+    b_pre = P[:, 5 * W:5 * W + H]
+    q = round_bf16(l2norm_groups(conv_causal(q_pre, conv_q)[0], d, l2_eps))
+    k = round_bf16(l2norm_groups(conv_causal(k_pre, conv_k)[0], d, l2_eps))
+    v = round_bf16(conv_causal(v_pre, conv_v)[0])
+    g, beta = gate_prologue(f_pre.reshape(T, H, d), b_pre, A_log, lower_bound)
+    g, beta = round_bf16(g), round_bf16(beta)
+    o, S = kda_serial(q.reshape(T, H, d), k.reshape(T, H, d), v.reshape(T, H, d), g, beta,
+                      initial_state=initial_state, scale=scale, lower_bound=lower_bound, nthreads=nthreads)
+    y = output_norm_gate(o, g_pre, norm_w, rms_eps).reshape(T, W)
+    yq, ys = quantize_fp8_groups(y)
+    out = gemm_fp8_w8a8(yq, ys, Wo_codes, Wo_scales)
+    if return_parts:
+        return out, dict(P=P, q=q, k=k, v=v, g=g, beta=beta, o=o, S=S, y=y, yq=yq, ys=ys)
+    return out
+
+
 def quantize_fp8_groups_f32(x, group=128):
     """The dynamic activation quantization of ``quantize_fp8_groups`` with
     every rounding decision taken in float32, as a float32 implementation

@@ -868,3 +868,80 @@ def test_e4m3_sign_of_zero():
     x = np.array([-1e-4, 1e-4, -0.0, 0.0, -2.0 ** -10, -2.0 ** -9])
     assert list(R.e4m3_encode(x)) == [0x80, 0x00, 0x80, 0x00, 0x80, 0x81]
     assert list(R.e4m3_encode_brute(x)) == [0x80, 0x00, 0x80, 0x00, 0x80, 0x81]
+
+
+def _fp8_layer_case(seed, T=9, hidden=256, H=2, d=128):
+    """Block-FP8 weights (E4M3 codes + 128 x 128 scales) and an input whose
+    per-(token, 128) quantization is lossless: on the E4M3 grid times a
+    power-of-two group scale, each group's maximum exactly 448 x scale."""
+    rng = np.random.default_rng(seed)
+    W = H * d
+    rows = 5 * W + H
+    def codes(n, k, lo=3, hi=9):
+        e = rng.integers(lo, hi + 1, (n, k))
+        m = rng.integers(0, 8, (n, k))
+        return ((rng.integers(0, 2, (n, k)) << 7) | (e << 3) | m).astype(np.uint8)
+    Wc = codes(rows, hidden)
+    Ws = rng.uniform(0.01, 0.02, ((rows + 127) // 128, hidden // 128))
+    Woc = codes(hidden, W)
+    Wos = rng.uniform(0.002, 0.004, (hidden // 128, W // 128))
+    xc = codes(T, hidden, 1, 14)
+    for t in range(T):
+        for gi in range(hidden // 128):
+            xc[t, 128 * gi + rng.integers(0, 128)] = 0x7E
+    xsc = np.exp2(rng.integers(-9, -5, (T, hidden // 128))).astype(np.float64)
+    x = R.e4m3_decode(xc) * np.repeat(xsc, 128, axis=1)
+    r = lambda shape, sd: R.round_bf16(rng.standard_normal(shape) * sd)
+    return dict(x=x, Wc=Wc, Ws=Ws, Woc=Woc, Wos=Wos, cq=r((W, 4), 0.5), ck=r((W, 4), 0.5), cv=r((W, 4), 0.5),
+                A_log=np.zeros(H), norm_w=np.ones(d), H=H, d=d)
+
+
+def _dequant(codes, scales):
+    s = np.repeat(np.repeat(np.asarray(scales, dtype=np.float64), 128, axis=0), 128, axis=1)
+    return R.e4m3_decode(codes) * s[:codes.shape[0], :codes.shape[1]]
+
+
+def test_layer_fp8_matches_layer_on_dequantized_weights():
+    """W8A8 layer wiring, input side: with a losslessly quantized input, the
+    W8A8 layer's q, k, v, g, beta, core output and final state equal those of
+    the bf16 layer run on the dequantized weights (its rows split as q | k | v
+    | f | gate | b), up to the rare bf16 rounding flip that a different
+    summation order of the same float64 products can cause. Output side: a
+    W_o that selects one column of y per output (code 1.0, scale 1) returns
+    the dequantized epilogue codes exactly, within half an E4M3 step of y."""
+    c = _fp8_layer_case(71)
+    H, d = c["H"], c["d"]
+    W = H * d
+    T = c["x"].shape[0]
+    xq, xs = R.quantize_fp8_groups_f32(c["x"])
+    np.testing.assert_array_equal(R.e4m3_decode(xq) * np.repeat(xs.astype(np.float64), 128, axis=1), c["x"])
+    Wd = _dequant(c["Wc"], c["Ws"])
+    Wq, Wk, Wv, Wf, Wg = (Wd[i * W:(i + 1) * W] for i in range(5))
+    Wb = Wd[5 * W:5 * W + H]
+    Wod = _dequant(c["Woc"], c["Wos"])
+    _, ref = R.layer_forward(c["x"], Wq, Wk, Wv, Wf, Wg, Wb, Wod, c["cq"], c["ck"], c["cv"], c["A_log"],
+                             c["norm_w"], H, d, return_parts=True)
+    out, p = R.layer_forward_fp8(c["x"], c["Wc"], c["Ws"], c["Woc"], c["Wos"], c["cq"], c["ck"], c["cv"],
+                                 c["A_log"], c["norm_w"], H, d, return_parts=True)
+    for n in ("q", "k", "v", "g", "beta"):
+        a, b = np.asarray(p[n]), np.asarray(ref[n])
+        assert np.mean(a != b) < 1e-3, n
+        assert np.max(np.abs(a - b)) <= 2.0 ** -7 * np.max(np.abs(b)), n
+    np.testing.assert_allclose(p["o"], ref["o"], rtol=0, atol=2e-2 * np.max(np.abs(ref["o"])))
+    np.testing.assert_allclose(p["S"], ref["S"], rtol=0, atol=2e-2 * np.max(np.abs(ref["S"])))
+    # output side: W_o = selection of column sel[n] of y
+    hidden = c["x"].shape[1]
+    sel = np.random.default_rng(72).integers(0, W, hidden)
+    Woc = np.zeros((hidden, W), np.uint8)
+    Woc[np.arange(hidden), sel] = 0x38          # 1.0
+    out2, p2 = R.layer_forward_fp8(c["x"], c["Wc"], c["Ws"], Woc, np.ones((hidden // 128, W // 128)), c["cq"],
+                                   c["ck"], c["cv"], c["A_log"], c["norm_w"], H, d, return_parts=True)
+    deq = R.e4m3_decode(p2["yq"]) * np.repeat(p2["ys"], 128, axis=1)
+    np.testing.assert_array_equal(out2, deq[:, sel])
+    y = p2["y"]
+    bound = np.maximum(2.0 ** -4 * np.abs(y), 2.0 ** -10 * np.repeat(p2["ys"], 128, axis=1)) * (1 + 1e-12)
+    assert np.all(np.abs(deq - y) <= bound)
+    # zero output weights give zero output
+    out3 = R.layer_forward_fp8(c["x"], c["Wc"], c["Ws"], np.zeros_like(c["Woc"]), c["Wos"], c["cq"], c["ck"],
+                               c["cv"], c["A_log"], c["norm_w"], H, d)
+    assert np.all(out3 == 0.0)
