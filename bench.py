@@ -347,6 +347,16 @@ def bench_layer(torch, steps, warmup):
     return ms, mixer.flops_per_token() * x.shape[0]
 
 
+def bench_layer_fp8(torch, steps, warmup):
+    """The same layer with block-FP8 (W8A8) projections."""
+    from gated_delta_rule_02_amd import layer, synth
+    d = synth.workload_layer_fp8()
+    mixer = layer.KDAMixerFP8.from_host(d)
+    x = dev(d["x"], torch)
+    ms, _ = timed(torch, lambda: mixer.forward(x), max(1, steps // 4), max(1, warmup // 2))
+    return ms, mixer.flops_per_token() * x.shape[0]
+
+
 def bench_gemm(torch, K, steps, warmup):
     """The layer's input projection alone (M = 8192 tokens, K = 4096,
     N = 5 x 8192 + 64, bf16 in and out) with the library's GEMM, and the same
@@ -525,6 +535,14 @@ def main():
         out["layer"] = {"workload": "full token-mixer layer T=8192 hidden=4096 H=64: projections, conv, gate, "
                                     "KDA core, norm x gate, output projection",
                         "ms_per_step": ms, "tokens/s": 8192 / (ms * 1e-3), "TFLOP/s": flops / (ms * 1e-3) / 1e12}
+        log("layer T=8192 hidden=4096, block-FP8 W8A8 projections")
+        ms8, flops8 = bench_layer_fp8(torch, args.steps, args.warmup)
+        log("layer fp8 %.3f ms/step" % ms8)
+        out["layer_fp8"] = {"workload": "the same layer with E4M3 weights in 128x128 blocks (fp32 block scales) and "
+                                        "activations quantized per (token, 128 channels): kda_quantize_fp8, "
+                                        "kda_gemm_fp8, kda_output_norm_gate_fp8",
+                            "ms_per_step": ms8, "tokens/s": 8192 / (ms8 * 1e-3), "TFLOP/s": flops8 / (ms8 * 1e-3) / 1e12,
+                            "speedup_vs_bf16_layer": ms / ms8}
         log("input projection GEMM 8192 x 41024 x 4096")
         ms_g, ms_r, fl = bench_gemm(torch, K, args.steps, args.warmup)
         out["gemm"] = {"workload": "input projection 8192 x 41024 x 4096, bf16 in and out, fp32 accumulate",

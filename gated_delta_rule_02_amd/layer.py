@@ -73,6 +73,15 @@ class KDAMixer:
         W = self.W
         return P, [P[:, i * W:(i + 1) * W] for i in range(5)] + [P[:, 5 * W:5 * W + self.H]]
 
+    def output(self, o, gp, tag=""):
+        """y = RMSNorm(o) x w x sigmoid(gate) (bf16), out = y W_o^T (float32)."""
+        T = o.shape[0]
+        y = self._buf(tag + "y", (T, self.W), torch.bfloat16)
+        K.kda_output_norm_gate(o, gp, self.norm_w, y, eps=self.rms_eps)
+        out = self._buf(tag + "out", (T, self.hidden), torch.float32)
+        K.kda_gemm(y, self.Wo, out)
+        return out, y
+
     def forward(self, x, cu_seqlens=None, cu_seqlens_host=None, initial_state=None, final_state=None,
                 conv_state_in=None, conv_state_out=None, return_parts=False):
         """x [T, hidden] bf16 (packed sequences if cu_seqlens is given) ->
@@ -95,10 +104,7 @@ class KDAMixer:
         K.kda_prefill(qkv[0], qkv[1], qkv[2], g, beta, o, cu_seqlens=cu_seqlens,
                       cu_seqlens_host=cu_seqlens_host, initial_state=initial_state,
                       final_state=final_state, scale=self.scale, lower_bound=self.lower_bound)
-        y = self._buf("y", (T, W), torch.bfloat16)
-        K.kda_output_norm_gate(o, gp, self.norm_w, y, eps=self.rms_eps)
-        out = self._buf("out", (T, self.hidden), torch.float32)
-        K.kda_gemm(y, self.Wo, out)
+        out, y = self.output(o, gp)
         if return_parts:
             return out, dict(q=qkv[0], k=qkv[1], v=qkv[2], g=g, beta=beta, o=o, y=y, P=P)
         return out
@@ -122,8 +128,59 @@ class KDAMixer:
         o = self._buf("do", (B, H, D), torch.float32)
         K.kda_decode_step(qkv[0], qkv[1], qkv[2], g, beta, state, o, scale=self.scale,
                           lower_bound=self.lower_bound)
-        y = self._buf("dy", (B, W), torch.bfloat16)
-        K.kda_output_norm_gate(o, gp, self.norm_w, y, eps=self.rms_eps)
-        out = self._buf("dout", (B, self.hidden), torch.float32)
-        K.kda_gemm(y, self.Wo, out)
+        out, _ = self.output(o, gp, tag="d")
         return out
+
+
+class KDAMixerFP8(KDAMixer):
+    """The same mixer with its projections in block FP8 (W8A8): E4M3 weights
+    in 128 x 128 blocks with float32 block scales, as the release stores them,
+    and activations quantized dynamically ("Ling-3.1-flash: Grouped Routing
+    and Two Different MLA Caches", section "Production boundaries"). The input
+    x is quantized per (token, 128 channels) by kda_quantize_fp8 and the
+    epilogue writes its output quantized per (token, head)
+    (kda_output_norm_gate_fp8); both projections run kda_gemm_fp8 (weight
+    streaming up to 8 tokens, the FP8 matrix cores beyond)."""
+
+    def __init__(self, Win_codes, Win_scales, Wo_codes, Wo_scales, conv_q, conv_k, conv_v, A_log, norm_w, H,
+                 **kw):
+        super().__init__(Win_codes, conv_q, conv_k, conv_v, A_log, norm_w, Wo_codes, H, **kw)
+        self.W_in_s, self.Wo_s = Win_scales, Wo_scales
+
+    @classmethod
+    def from_host(cls, d):
+        """Build from the seeded host weights of ``synth.workload_layer_fp8``."""
+        u8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        # packed rows padded with zero codes to a multiple of 8 (16-byte aligned
+        # column slices of the projection output), with block scales to match
+        codes, scales = d["Win_codes"], d["Win_scales"]
+        pad = (-codes.shape[0]) % 8
+        if pad:
+            codes = np.concatenate([codes, np.zeros((pad, codes.shape[1]), np.uint8)])
+        need = (codes.shape[0] + 127) // 128
+        if scales.shape[0] < need:
+            scales = np.concatenate([scales, np.ones((need - scales.shape[0], scales.shape[1]), np.float32)])
+        return cls(u8(codes), u8(scales), u8(d["Wo_codes"]), u8(d["Wo_scales"]),
+                   _dev_bf16(d["conv_q"]), _dev_bf16(d["conv_k"]), _dev_bf16(d["conv_v"]),
+                   torch.from_numpy(d["A_log"]).cuda(), torch.from_numpy(d["norm_w"]).cuda(), d["H"])
+
+    def projections(self, x):
+        """x quantized per (token, 128 channels), then P = X W_in^T (bf16)."""
+        T, hidden = x.shape
+        xq = self._buf("xq", (T, hidden), torch.uint8)
+        xs = self._buf("xs", (T, hidden // 128), torch.float32)
+        K.kda_quantize_fp8(x, xq, xs)
+        P = self._buf("P", (T, self.W_in.shape[0]), torch.bfloat16)
+        K.kda_gemm_fp8(xq, xs, self.W_in, self.W_in_s, P)
+        W = self.W
+        return P, [P[:, i * W:(i + 1) * W] for i in range(5)] + [P[:, 5 * W:5 * W + self.H]]
+
+    def output(self, o, gp, tag=""):
+        """The epilogue quantized per (token, head), then out = Y W_o^T (float32)."""
+        T = o.shape[0]
+        yq = self._buf(tag + "yq", (T, self.W), torch.uint8)
+        ys = self._buf(tag + "ys", (T, self.H), torch.float32)
+        K.kda_output_norm_gate_fp8(o, gp, self.norm_w, yq, ys, eps=self.rms_eps)
+        out = self._buf(tag + "out", (T, self.hidden), torch.float32)
+        K.kda_gemm_fp8(yq, ys, self.Wo, self.Wo_s, out)
+        return out, (yq, ys)

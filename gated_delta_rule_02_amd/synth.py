@@ -184,3 +184,35 @@ def workload_layer(T=8192, hidden=4096, H=64, seed=1004):
     d["norm_w"] = np.ones(CORE_D, dtype=np.float32)
     d["H"] = H
     return d
+
+
+def fp8_codes(rng, shape, exp_lo=3, exp_hi=9):
+    """Random E4M3 bit patterns: uniform sign, exponent field uniform in
+    [exp_lo, exp_hi] (never the NaN pattern), uniform 3-bit mantissa."""
+    e = rng.integers(exp_lo, exp_hi + 1, shape)
+    m = rng.integers(0, 8, shape)
+    s = rng.integers(0, 2, shape)
+    return ((s << 7) | (e << 3) | m).astype(np.uint8)
+
+
+def workload_layer_fp8(T=8192, hidden=4096, H=64, seed=1006):
+    """The token-mixer layer with its weights in the release's block-FP8
+    storage: E4M3 codes (``fp8_codes``: magnitudes 2^-4 .. 7.5) with one
+    float32 scale per 128 x 128 block drawn U(0.006, 0.010), so that the
+    weights' RMS is about 0.02 as in the bf16 layer. The packed input
+    projection has rows q | k | v | f | gate (H*128 each) | b (H). Input x, conv
+    weights, A_log and the norm weight as ``workload_layer``."""
+    rng = np.random.default_rng(seed)
+    W = H * CORE_D
+    rows = 5 * W + H
+    d = dict(x=normal(rng, (T, hidden)))
+    d["Win_codes"] = fp8_codes(rng, (rows, hidden))
+    d["Win_scales"] = rng.uniform(0.006, 0.010, ((rows + 127) // 128, hidden // 128)).astype(np.float32)
+    d["Wo_codes"] = fp8_codes(rng, (hidden, W))
+    d["Wo_scales"] = rng.uniform(0.006, 0.010, (hidden // 128, W // 128)).astype(np.float32)
+    for name in ("conv_q", "conv_k", "conv_v"):
+        d[name] = normal(rng, (W, 4), std=0.5)
+    d["A_log"] = np.zeros(H, dtype=np.float32)
+    d["norm_w"] = np.ones(CORE_D, dtype=np.float32)
+    d["H"] = H
+    return d
