@@ -357,6 +357,23 @@ def bench_layer_fp8(torch, steps, warmup):
     return ms, mixer.flops_per_token() * x.shape[0]
 
 
+def bench_decode_layer_fp8(torch, steps, warmup, B=1):
+    """One decode step of the W8A8 layer for B sequences (hidden 4096, H=64):
+    launched eagerly from the host, and replayed from one HIP graph."""
+    from gated_delta_rule_02_amd import layer, synth
+    d = synth.workload_layer_fp8(T=8)
+    mixer = layer.KDAMixerFP8.from_host(d)
+    H, W = d["H"], d["H"] * 128
+    x = dev(d["x"], torch)[:1].repeat(B, 1).contiguous()
+    st = torch.zeros((B, H, 128, 128), device="cuda")
+    cs = torch.zeros((3, B, 3, W), dtype=torch.bfloat16, device="cuda")
+    ms_e, _ = timed(torch, lambda: mixer.decode(x, st, cs), steps, warmup)
+    g = layer.DecodeGraph(mixer, B, st, cs)
+    ms_g, _ = timed(torch, lambda: g.step(x), steps, warmup)
+    wbytes = mixer.W_in.numel() + mixer.Wo.numel()
+    return ms_e, ms_g, wbytes
+
+
 def bench_gemm(torch, K, steps, warmup):
     """The layer's input projection alone (M = 8192 tokens, K = 4096,
     N = 5 x 8192 + 64, bf16 in and out) with the library's GEMM, and the same
@@ -543,6 +560,15 @@ def main():
                                         "kda_gemm_fp8, kda_output_norm_gate_fp8",
                             "ms_per_step": ms8, "tokens/s": 8192 / (ms8 * 1e-3), "TFLOP/s": flops8 / (ms8 * 1e-3) / 1e12,
                             "speedup_vs_bf16_layer": ms / ms8}
+        for Bd in (1, 8):
+            log("W8A8 layer decode step B=%d: eager and HIP graph" % Bd)
+            ms_e, ms_g, wb = bench_decode_layer_fp8(torch, args.steps, args.warmup, B=Bd)
+            log("decode B=%d eager %.4f ms, graph %.4f ms" % (Bd, ms_e, ms_g))
+            out["layer_fp8_decode_b%d" % Bd] = {
+                "workload": "one decode token for %d sequence(s) through the W8A8 layer (hidden 4096, H=64): "
+                            "quantize, FP8 GEMV, 3 conv updates, gate, decode step, quantized epilogue, FP8 GEMV" % Bd,
+                "ms_eager": ms_e, "ms_graph": ms_g, "weight_bytes": wb,
+                "weight_GB/s_graph": wb / (ms_g * 1e-3) / 1e9}
         log("input projection GEMM 8192 x 41024 x 4096")
         ms_g, ms_r, fl = bench_gemm(torch, K, args.steps, args.warmup)
         out["gemm"] = {"workload": "input projection 8192 x 41024 x 4096, bf16 in and out, fp32 accumulate",

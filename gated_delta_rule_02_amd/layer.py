@@ -132,6 +132,38 @@ class KDAMixer:
         return out
 
 
+class DecodeGraph:
+    """One decode step of a mixer captured as a HIP graph: the step's kernels
+    (projections, the three conv updates, gate, decode step, epilogue, output
+    projection) are replayed without a host launch each, which at a few
+    sequences is a large part of the step. The graph reads x from, and writes
+    out to, its own buffers and updates the given state and conv states in
+    place, so each replay advances those sequences by one token. Every call
+    it makes allocates nothing and enqueues no memset (the library never
+    does), and the mixer's buffers are allocated by an eager step before the
+    capture."""
+
+    def __init__(self, mixer, B, state, conv_states):
+        self.x = torch.zeros((B, mixer.hidden), dtype=torch.bfloat16, device="cuda")
+        self.state, self.conv_states = state, conv_states
+        # an eager step on copies allocates every buffer the step uses
+        mixer.decode(self.x, state.clone(), conv_states.clone())
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(self.graph, stream=s):
+                self.out = mixer.decode(self.x, state, conv_states)
+        torch.cuda.current_stream().wait_stream(s)
+
+    def step(self, x):
+        """Copy x [B, hidden] in, replay, return the output buffer."""
+        self.x.copy_(x)
+        self.graph.replay()
+        return self.out
+
+
 class KDAMixerFP8(KDAMixer):
     """The same mixer with its projections in block FP8 (W8A8): E4M3 weights
     in 128 x 128 blocks with float32 block scales, as the release stores them,

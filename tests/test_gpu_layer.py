@@ -218,3 +218,42 @@ def test_layer_fp8_workload_full_size():
     print("  P ratio %.3f  out %.2e (bound ratio %.3f)  core o %.2e  state %.2e" % (r_p, e_out, r_out, e_o, e_s),
           flush=True)
     assert r_p <= 1.0 and e_o < TOL_W8A8_LAYER and e_s < TOL_W8A8_LAYER and r_out <= 1.0
+
+
+def test_decode_graph_replays_match_eager():
+    """The W8A8 layer's decode step captured as one HIP graph: six replays in a
+    row (each advancing state and conv state by a token, with eager work and
+    synchronizations between them) against six eager decode steps from the
+    same starting state, bit for bit (same kernels, same order), for one
+    sequence and for four; and the first replay against the oracle's chain."""
+    announce("decode graph replays")
+    d = synth.workload_layer_fp8(T=70, hidden=256, H=2, seed=23)
+    mixer = layer.KDAMixerFP8.from_host(d)
+    x = dev(d["x"])
+    H, W = 2, 256
+    for B in (1, 4):
+        st0 = torch.zeros((B, H, 128, 128), device="cuda")
+        cs0 = torch.zeros((3, B, 3, W), dtype=torch.bfloat16, device="cuda")
+        for b in range(B):
+            stb = torch.zeros((1, H, 128, 128), device="cuda")
+            csb = torch.zeros((3, 1, 3, W), dtype=torch.bfloat16, device="cuda")
+            mixer.forward(x[:64].contiguous(), final_state=stb, conv_state_out=csb)
+            st0[b] = stb[0]
+            cs0[:, b] = csb[:, 0]
+        torch.cuda.synchronize()
+        st_e, cs_e = st0.clone(), cs0.clone()
+        st_g, cs_g = st0.clone(), cs0.clone()
+        eager = []
+        for t in range(6):
+            eager.append(mixer.decode(x[64 + t:65 + t].repeat(B, 1).contiguous(), st_e, cs_e).clone())
+        g = layer.DecodeGraph(mixer, B, st_g, cs_g)
+        for t in range(6):
+            o = g.step(x[64 + t:65 + t].repeat(B, 1)).clone()
+            torch.cuda.synchronize()
+            _ = (st_e * 2).sum().item()      # eager work between replays
+            assert torch.equal(o, eager[t]), (B, t)
+        assert torch.equal(st_g, st_e) and torch.equal(cs_g, cs_e)
+    ref, rp = oracle_layer_fp8(d)
+    r = w8a8_output_check(host64(eager[0][:1]), rp["y"][64:65], d["Wo_codes"], d["Wo_scales"])
+    print("  first step bound ratio %.3f" % r, flush=True)
+    assert r <= 1.0
