@@ -292,8 +292,10 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
 }
 
 // ------------------------------------------------------------- state pass
-// Three wavefronts: two compute wavefronts (one 16-column tile of the state
-// each) and a loader that copies each chunk's operands into an LDS stage with
+// The form for 64-column workgroups and segment maps (32-column workgroups
+// take the role-split form below). Three wavefronts: two compute wavefronts
+// (one or two 16-column tiles of the state each) and a loader that copies each
+// chunk's operands into an LDS stage with
 // buffer-to-LDS loads (two stages, one chunk ahead). Each role waits only on
 // its own memory counter; one barrier per chunk hands a stage from the loader
 // to the compute wavefronts. (A fourth wavefront that touched the chunks two
@@ -579,12 +581,285 @@ void state_kernel(SplitArgs sa)
     }
 }
 
+// ------------------------------------------------------- role-split state pass
+// The same recurrence with the work of each 16-column tile shared by two
+// compute wavefronts that run side by side on their own SIMDs:
+//   A (the chain): U = U' + (-W) S, then S <- Diag(2^b_C) S + Kbar^T U;
+//   B (the output): O^T = S^T Q~^T + U^T P^T and its stores.
+// A hands S (for the next chunk) and U (after its first product) to B through
+// LDS, as float16 B operands, double-buffered by chunk parity. The chain of a
+// chunk is then two products of 16 MFMAs instead of all four products in one
+// wavefront; with one wavefront per tile the pass was bound by that
+// wavefront's chain, not by its loads. One barrier per chunk (the stage holds
+// the chunk; S is published); U's hand-over is a per-tile LDS counter that B
+// polls, so that the loader, which spends most of a chunk issuing the next
+// one's copies, is not waited for in the middle of the chunk. Waves: 0 B,
+// 1 A of tile 0; 2 B, 3 A of tile 1; 4 loader (on SIMD 0 with the lighter B
+// wavefront).
+constexpr int kRoleTiles = 2;                       // 16-column tiles per workgroup
+constexpr int kRoleThreads = 64 * (2 * kRoleTiles + 1);
+constexpr int kRoleStage = state_stage_bytes(kRoleTiles);
+
+template <typename TOUT, int POL>
+__global__ __launch_bounds__(kRoleThreads) void state_roles_kernel(SplitArgs sa)
+{
+    constexpr int kColGroups = D / (16 * kRoleTiles);  // workgroups per (sequence, head)
+    constexpr int kStDc = kStUp + kRoleTiles * 2048;    // offset of 2^b_C in a stage
+    __shared__ __attribute__((aligned(16))) uint8_t buf[2][kRoleStage];
+    __shared__ h8 sbx[2][kRoleTiles][4][64];  // S before chunk c in [c & 1], B-operand layout
+    __shared__ h8 ubx[2][kRoleTiles][2][64];  // U of chunk c in [c & 1], B-operand layout
+    __shared__ int uflag[kRoleTiles];         // chunks whose U wavefront A has published
+    const PrefillArgs& a = sa.p;
+    constexpr int C = 64;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int m16 = lane & 15;
+    const int q4 = lane >> 4;
+    const bool loader = wave == 2 * kRoleTiles;
+    const bool roleA = !loader && (wave & 1);
+    const bool roleB = !loader && !(wave & 1);
+    const int p = loader ? 0 : wave >> 1;  // this wavefront's tile within the workgroup
+
+    // workgroups of one (sequence, head) get ids congruent mod 8 (one XCD)
+    const int bid = (int)blockIdx.x;
+    const int jq = (bid >> 3) % kColGroups;
+    const int u = (bid & 7) + 8 * ((bid >> 3) / kColGroups);  // n * H + h
+    if (u >= a.num_seqs * a.H) return;
+    const int h = u % a.H;
+    const int n = u / a.H;
+    int64_t seq_s, seq_e;
+    seq_bounds(a, n, seq_s, seq_e);
+    const int64_t nchunks = (seq_e - seq_s + C - 1) / C;
+    const int64_t c_end = min<int64_t>(nchunks, sa.chunk0 + sa.nwin);
+    const int nch = (int)max<int64_t>(0, c_end - sa.chunk0);
+    const int j = kRoleTiles * jq + p;  // this wavefront's 16-column tile
+    const size_t sbase = (size_t)u * D * D;
+
+    if (nch == 0) {
+        // an empty sequence still has a final state: the initial one
+        if (roleA && sa.chunk0 == 0 && a.sT) {
+            int off = 4 * q4 * D + 16 * j + m16;
+            asm volatile("" : "+v"(off));
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const size_t e = sbase + off + (size_t)(16 * t + i) * D;
+                    a.sT[e] = a.s0 ? a.s0[e] : 0.0f;
+                }
+        }
+        return;
+    }
+    const float* sin = sa.chunk0 == 0 ? a.s0 : sa.carry;
+    float* sout = c_end >= nchunks ? a.sT : sa.carry;
+
+    const uint8_t* slots = sa.ws + (size_t)u * sa.nwin * kSlot;
+    const rsrc_t rs = make_rsrc(slots, (int64_t)nch * kSlot);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)&buf[0][0];
+    // loader: chunk c into stage b, 1 KiB per instruction: the operand block,
+    // U' of this workgroup's tiles, 2^b_C (the tail of its KiB is padding)
+    auto dma = [&](int c, int b) {
+        const uint32_t st = lds0 + b * kRoleStage;
+#pragma unroll
+        for (int i = 0; i < kDma / 1024; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(uintptr_t)(st + i * 1024), 16, lane * 16,
+                                                     c * kSlot + i * 1024, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * kRoleTiles; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(uintptr_t)(st + kStUp + i * 1024), 16, lane * 16,
+                                                     c * kSlot + kUp + jq * kRoleTiles * 2048 + i * 1024, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(uintptr_t)(st + kStDc), 16, lane * 16,
+                                                 c * kSlot + kDc, 0, 0);
+    };
+
+    // S[t][i] = S[16t + 4q + i][16 j + m16] (wavefront A only)
+    f32x4 S[8];
+    auto publish_s = [&](int b) {
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) sbx[b][p][s2][lane] = cat(to_h4(S[2 * s2]), to_h4(S[2 * s2 + 1]));
+    };
+    if (roleA) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                S[t][i] = sin ? sin[sbase + (size_t)(16 * t + 4 * q4 + i) * D + 16 * j + m16] : 0.0f;
+        publish_s(0);
+        if (lane == 0) uflag[p] = 0;
+    }
+    if (loader) {
+        dma(0, 0);
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    }
+
+    const int ts = a.H * D;
+    TOUT* og = static_cast<TOUT*>(a.o);
+    const int snap_ic = a.snap ? (int)(a.snap_interval / C) : 1;
+    int snap_left = snap_ic - (int)(sa.chunk0 % snap_ic);
+    int snap_j = (int)(sa.chunk0 / snap_ic);
+    for (int c = 0; c < nch; ++c) {
+        __syncthreads();  // stage c & 1 holds chunk c, sbx[c & 1] its S
+        if (loader) {
+            if (c + 1 < nch) dma(c + 1, (c + 1) & 1);
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the stage is complete before the next barrier
+            continue;
+        }
+        const uint8_t* st = &buf[c & 1][0];
+        const h8* nw = reinterpret_cast<const h8*>(st + kNegW);
+        const h8* qt = reinterpret_cast<const h8*>(st + kQt);
+        const h8* kb = reinterpret_cast<const h8*>(st + kKbT);
+        const h8* pm = reinterpret_cast<const h8*>(st + kPm);
+        if (roleA) {
+            h8 sb[4];
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) sb[s2] = cat(to_h4(S[2 * s2]), to_h4(S[2 * s2 + 1]));
+            f32x4 U[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const h4 up = *reinterpret_cast<const h4*>(st + kStUp + ((p * 4 + t) * 64 + lane) * 8);
+                U[t] = f32x4{(float)up[0], (float)up[1], (float)up[2], (float)up[3]};
+            }
+            // U = U' + (-W) S, the operand reads one K step ahead
+            h8 an[2][4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) an[0][t] = nw[(t * 4 + 0) * 64 + lane];
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                const int cur = s2 & 1, nxt = cur ^ 1;
+                if (s2 < 3) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) an[nxt][t] = nw[(t * 4 + s2 + 1) * 64 + lane];
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    U[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(an[cur][t], sb[s2], U[t], 0, 0, 0);
+            }
+            h8 ak[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) ak[i] = kb[i * 64 + lane];  // [t][s] = index t * 2 + s
+            h8 ub[2];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                ub[s2] = cat(to_h4(U[2 * s2]), to_h4(U[2 * s2 + 1]));
+                ubx[c & 1][p][s2][lane] = ub[s2];
+            }
+            // U is in LDS before the counter says so
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            if (lane == 0) __hip_atomic_store(&uflag[p], c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            // S <- Diag(2^b_C) S + Kbar^T U
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const f32x4 dc = *reinterpret_cast<const f32x4*>(st + kStDc + (16 * t + 4 * q4) * 4);
+                f32x4 acc = S[t] * dc;
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak[t * 2 + s2], ub[s2], acc, 0, 0, 0);
+                S[t] = acc;
+            }
+            const int64_t cs = seq_s + (sa.chunk0 + c) * C;
+            if (a.snap && --snap_left == 0) {
+                if (seq_e - cs >= C)
+                    store_state_slice(a.snap + (((size_t)n * a.snap_slots + snap_j) * a.H + h) * D * D, S, q4,
+                                      16 * j + m16);
+                snap_left = snap_ic;
+                ++snap_j;
+            }
+            // S for the next chunk (B read the previous user of this buffer
+            // before this chunk's barrier)
+            publish_s((c + 1) & 1);
+        } else {
+            // O^T = S^T Q~^T + U^T P^T: S and U as A operands (the registers of
+            // a B operand hold its transpose as an A operand)
+            h8 sb[4], aq[2][4], ap[6];
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) sb[s2] = sbx[c & 1][p][s2][lane];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) aq[0][t] = qt[(t * 4 + 0) * 64 + lane];
+            f32x4 Ot[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) Ot[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                const int cur = s2 & 1, nxt = cur ^ 1;
+                if (s2 < 3) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) aq[nxt][t] = qt[(t * 4 + s2 + 1) * 64 + lane];
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 6; ++i) ap[i] = pm[i * 64 + lane];  // (t, s) with 2s <= t
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    Ot[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sb[s2], aq[cur][t], Ot[t], 0, 0, 0);
+            }
+            // wait for A's U of this chunk (bounded: a wavefront that never
+            // saw it would leave with a wrong output rather than hang)
+            for (int spin = 0; spin < (1 << 22); ++spin) {
+                if (__hip_atomic_load(&uflag[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) > c) break;
+                __builtin_amdgcn_s_sleep(1);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            h8 ub[2];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) ub[s2] = ubx[c & 1][p][s2][lane];
+#pragma unroll
+            for (int i = 0; i < 6; ++i) {
+                const int t = i < 2 ? i : 2 + (i - 2) / 2, s2 = i < 2 ? 0 : (i - 2) % 2;
+                Ot[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ub[s2], ap[i], Ot[t], 0, 0, 0);
+            }
+            // lane (token m16 of tile t, q4) holds columns 16j + 4 q4 .. +3;
+            // rows past the sequence are dropped by the descriptor range
+            const int64_t cs = seq_s + (sa.chunk0 + c) * C;
+            const int ntok = (int)min<int64_t>(C, seq_e - cs);
+            const rsrc_t ro_ = make_rsrc(og + cs * ts, (int64_t)ntok * ts * (int64_t)sizeof(TOUT));
+            const int voff = (m16 * ts + h * D + 16 * j + 4 * q4) * (int)sizeof(TOUT);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const f32x4 v = a.scale * Ot[t];
+                if constexpr (sizeof(TOUT) == 4) {
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), ro_, voff, 16 * t * ts * 4,
+                                                           POL);
+                } else {
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, to_b4(v)), ro_, voff,
+                                                          16 * t * ts * 2, POL);
+                }
+            }
+        }
+    }
+    if (loader) {
+        // no load may still be writing LDS when the workgroup ends
+        __builtin_amdgcn_s_waitcnt(0x0f70);
+        return;
+    }
+    if (roleA && sout) {
+        int off = 4 * q4 * D + 16 * j + m16;
+        asm volatile("" : "+v"(off));
+        float* so = sout + sbase + off;
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) so[(16 * t + i) * D] = S[t][i];
+    }
+}
+
 template <typename TOUT, int TPW>
 void launch_state(SplitArgs sa, int64_t U, bool stream, hipStream_t s)
 {
     constexpr int kColGroups = D / (16 * kStateWaves * TPW);
     sa.map_half = (int)(kColGroups * 8 * ((U + 7) / 8));
     const dim3 gs((unsigned)(sa.map_half * (sa.p.map_M ? 2 : 1))), bs(kStateThreads);
+    if (TPW == 1 && !sa.p.map_M) {
+        // the role-split form: two compute wavefronts per tile
+        static_assert(kStateWaves == kRoleTiles, "the role-split form keeps the 32-column workgroups");
+        const dim3 br(kRoleThreads);
+        if (stream)
+            hipLaunchKernelGGL((state_roles_kernel<TOUT, kStream>), gs, br, 0, s, sa);
+        else
+            hipLaunchKernelGGL((state_roles_kernel<TOUT, 0>), gs, br, 0, s, sa);
+        return;
+    }
     if (sa.p.map_M)
         hipLaunchKernelGGL((state_kernel<TOUT, TPW, 0, true>), gs, bs, 0, s, sa);
     else if (stream)
@@ -691,9 +966,10 @@ hipError_t launch_prefill_split(const PrefillArgs& a, void* ws, size_t ws_bytes,
         sa.groups = intra_groups(active, sa.nwin);
         const dim3 gi((unsigned)(U * sa.groups)), bi(kThreads);
         // state pass: 4 workgroups of 32 columns per state chain while they
-        // all fit on the chip at once (one per compute unit), else 2 of 64
-        // columns (each wavefront then carries two tiles through every
-        // operand read); segment maps run two chains per unit. Measured: a
+        // all fit on the chip at once (one per compute unit; the role-split
+        // form, two compute wavefronts per tile), else 2 of 64 columns (each
+        // wavefront then carries two tiles through every operand read);
+        // segment maps run two chains per unit. Measured: a
         // second round of 32-column workgroups costs more than the wider
         // ones (packed varlen 6.66 against 6.47 ms; one segment's maps, 64
         // heads, 0.070 against 0.064 ms). The two give identical results.
