@@ -454,14 +454,39 @@ size_t kda_prefill_workspace_bytes(int64_t num_tokens, int num_seqs, int H, int 
     return bytes;
 }
 
+// the gate inputs of kda_prefill_gated
+struct GateIn {
+    const void* f;
+    int64_t f_ld;
+    const void* b;
+    int64_t b_ld;
+    const float* A_log;
+};
+
 static int prefill_impl(const void* q, const void* k, const void* v, const void* g, const void* beta,
                         kda_dtype in_dtype, int64_t num_tokens, int H, int dk, int dv,
                         const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int num_seqs,
                         float scale, float lower_bound, const float* initial_state, float* final_state,
                         void* o, kda_dtype out_dtype, void* workspace, size_t workspace_bytes,
                         int64_t snap_interval, int64_t snap_slots, float* snapshots, void* hip_stream,
-                        bool static_ws = false)
+                        bool static_ws = false, const GateIn* gate = nullptr)
 {
+    const char* fn = gate ? "kda_prefill_gated" : "kda_prefill";
+    if (gate) {
+        REQUIRE(in_dtype == KDA_BF16, KDA_ERR_UNSUPPORTED, "%s: bfloat16 inputs only", fn);
+        REQUIRE(workspace != nullptr, KDA_ERR_WORKSPACE, "%s: a workspace is required (two-pass form)", fn);
+        REQUIRE(num_tokens == 0 || (gate->f && gate->b && gate->A_log), KDA_ERR_INVALID_ARG,
+                "%s: null f, b or A_log", fn);
+        REQUIRE(gate->f_ld >= (int64_t)H * 128 && gate->f_ld % 8 == 0 && gate->f_ld < ((int64_t)1 << 24),
+                KDA_ERR_INVALID_ARG, "%s: f_ld must be a multiple of 8 in [H*128, 2^24) (got %lld)", fn,
+                (long long)gate->f_ld);
+        REQUIRE(gate->b_ld >= H && gate->b_ld < ((int64_t)1 << 24), KDA_ERR_INVALID_ARG,
+                "%s: b_ld must lie in [H, 2^24) (got %lld)", fn, (long long)gate->b_ld);
+        REQUIRE(aligned16(gate->f) && ((uintptr_t)gate->b & 1) == 0, KDA_ERR_INVALID_ARG,
+                "%s: f must be 16-byte and b 2-byte aligned", fn);
+        g = gate->f;  // stand-ins for the pointer checks below; never read as g or beta
+        beta = gate->b;
+    }
     REQUIRE(valid_dtype(in_dtype) && valid_dtype(out_dtype), KDA_ERR_INVALID_ARG, "kda_prefill: bad dtype");
     REQUIRE(num_tokens >= 0 && H >= 1, KDA_ERR_INVALID_ARG, "kda_prefill: bad num_tokens or H");
     REQUIRE(dk == 128 && dv == 128, KDA_ERR_UNSUPPORTED,
@@ -469,8 +494,8 @@ static int prefill_impl(const void* q, const void* k, const void* v, const void*
     if (int rc = check_lower_bound("kda_prefill", lower_bound, true); rc != KDA_OK) return rc;
     REQUIRE(num_tokens == 0 || (q && k && v && g && beta && o), KDA_ERR_INVALID_ARG,
             "kda_prefill: null tensor pointer");
-    for (const void* p : {q, k, v, g, beta, (const void*)initial_state, (const void*)final_state, (const void*)o,
-                          (const void*)workspace, (const void*)snapshots})
+    for (const void* p : {q, k, v, g, gate ? nullptr : beta, (const void*)initial_state, (const void*)final_state,
+                          (const void*)o, (const void*)workspace, (const void*)snapshots})
         REQUIRE(!p || aligned16(p), KDA_ERR_INVALID_ARG, "kda_prefill: pointers must be 16-byte aligned");
     int64_t seq_len = 0;
     int rc = check_cu(cu_seqlens_dev, cu_seqlens_host, num_seqs, num_tokens, &seq_len);
@@ -525,11 +550,13 @@ static int prefill_impl(const void* q, const void* k, const void* v, const void*
     const Range rs0 = rng(initial_state, initial_state ? sbytes : 0), rsT = rng(final_state, final_state ? sbytes : 0);
     const Range rws = rng(workspace, split ? workspace_bytes : 0);
     const Range rsn = rng(snapshots, snapshots ? (size_t)num_seqs * snap_slots * H * 128 * 128 * 4 : 0);
+    const Range rg = gate ? rng(g, T ? ((T - 1) * (size_t)gate->f_ld + H * 128) * ei : 0) : rng(g, T * H * 128 * ei);
+    const Range rb = gate ? rng(beta, T ? ((T - 1) * (size_t)gate->b_ld + H) * ei : 0) : rng(beta, T * H * ei);
     for (const Range& r : {rng(q, T * H * 128 * ei), rng(k, T * H * 128 * ei), rng(v, T * H * 128 * ei),
-                           rng(g, T * H * 128 * ei), rng(beta, T * H * ei), rs0, ro, rsT, rws})
+                           rg, rb, rs0, ro, rsT, rws})
         REQUIRE(!overlap(r, rsn), KDA_ERR_INVALID_ARG, "kda_prefill_snapshots: snapshots overlap another tensor");
     const Range ins[] = {rng(q, T * H * 128 * ei), rng(k, T * H * 128 * ei), rng(v, T * H * 128 * ei),
-                         rng(g, T * H * 128 * ei), rng(beta, T * H * ei), rs0};
+                         rg, rb, rs0};
     for (const Range& r : ins) {
         REQUIRE(!overlap(r, ro), KDA_ERR_INVALID_ARG, "kda_prefill: o overlaps an input");
         if (r.p != rs0.p) REQUIRE(!overlap(r, rsT), KDA_ERR_INVALID_ARG, "kda_prefill: final_state overlaps an input");
@@ -548,6 +575,12 @@ static int prefill_impl(const void* q, const void* k, const void* v, const void*
     a.num_seqs = num_seqs; a.H = H; a.scale = scale; a.lower_bound = lower_bound;
     a.in_dtype = (DType)in_dtype; a.out_dtype = (DType)out_dtype;
     a.snap = snapshots; a.snap_interval = snapshots ? snap_interval : 0; a.snap_slots = snapshots ? snap_slots : 0;
+    if (gate) {
+        a.g = a.beta = nullptr;
+        a.gate_f = gate->f; a.gate_f_ld = gate->f_ld;
+        a.gate_b = gate->b; a.gate_b_ld = gate->b_ld;
+        a.A_log = gate->A_log;
+    }
     const hipStream_t st = static_cast<hipStream_t>(hip_stream);
     if (split)
         return hip_status(launch_prefill_split(a, workspace, workspace_bytes, max_chunks, cu_seqlens_host, st), "kda_prefill");
@@ -591,6 +624,18 @@ int kda_prefill_noalloc(const void* q, const void* k, const void* v, const void*
 }
 
 size_t kda_prefill_noalloc_scratch_bytes(void) { return kStaticScratchBytes; }
+
+int kda_prefill_gated(const void* q, const void* k, const void* v, const void* f, int64_t f_ld, const void* b,
+                      int64_t b_ld, const float* A_log, kda_dtype in_dtype, int64_t num_tokens, int H, int dk, int dv,
+                      const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int num_seqs,
+                      float scale, float lower_bound, const float* initial_state, float* final_state,
+                      void* o, kda_dtype out_dtype, void* workspace, size_t workspace_bytes, void* hip_stream)
+{
+    const GateIn gate{f, f_ld, b, b_ld, A_log};
+    return prefill_impl(q, k, v, nullptr, nullptr, in_dtype, num_tokens, H, dk, dv, cu_seqlens_dev, cu_seqlens_host,
+                        num_seqs, scale, lower_bound, initial_state, final_state, o, out_dtype, workspace,
+                        workspace_bytes, 0, 0, nullptr, hip_stream, false, &gate);
+}
 
 // ---------------------------------------------------------------- segment maps
 int kda_prefill_segment_maps(const void* k, const void* v, const void* g, const void* beta, kda_dtype in_dtype,

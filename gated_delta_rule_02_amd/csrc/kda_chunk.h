@@ -307,13 +307,18 @@ struct __attribute__((aligned(16))) Smem {
 // separates the phases with barriers.
 // NoQ: no query side (the segment maps of the sequence-parallel prefill form
 // no output): q is not loaded and neither P nor q o 2^b is formed.
+// Gate: the gate prologue runs here (PrefillArgs::gate_f): the g and beta
+// loads read the projection rows f and b, and P0 forms g and beta from them,
+// rounded to bfloat16 exactly as the gate prologue stores them, so the results
+// equal those of the prologue followed by the prefill.
 // Lean: the two-pass intra pass. The kernel holds no state in registers
 // here, so P2 can afford more live registers: the diagonal-block inverses by
 // repeated squaring instead of the Horner form (fewer dependent products) and
 // the off-diagonal pairs split evenly over the SIMDs. The producers also load
 // v and, in P2b, stage the right-hand sides -diag(beta)(K o 2^B) and
 // diag(beta) V of the products with T, transposed and rounded once.
-template <bool F32P, typename TIN, int NQ = 2, bool Lean = false, int LoadPol = 0, bool NoQ = false>
+template <bool F32P, typename TIN, int NQ = 2, bool Lean = false, int LoadPol = 0, bool NoQ = false,
+          bool Gate = false>
 struct Front {
     using O = Ops<F32P>;
     using OT = typename O::OT;
@@ -334,6 +339,9 @@ struct Front {
     const int h, H, ts;
     const float lbl;
     const TIN *qg, *kg, *gg, *bg;
+    const int64_t gts, bts;   // row strides (elements) of the g and beta sources
+    const float lb, rate;     // Gate: lower bound, exp(A_log[h])
+    int ntl = 0;              // Gate: tokens of the loaded chunk (rows past it get g = 0)
 
     PT rk[RP], rq[RP], rg[RP];  // k, q, g of this producer's tokens
     PT rvv[Lean ? RP : 1];      // v of this producer's tokens (Lean)
@@ -350,7 +358,9 @@ struct Front {
           m16(threadIdx.x & 15), q4((threadIdx.x & 63) >> 4), prod(wave < NQ * NB), R(wave % NB), hh(wave / NB),
           c0(2 * (threadIdx.x & 63)), rbase(16 * (wave % NB) + RP * (wave / NB)), h(head), H(a.H), ts(a.H * D),
           lbl(a.lower_bound * kLog2e), qg(static_cast<const TIN*>(a.q)), kg(static_cast<const TIN*>(a.k)),
-          gg(static_cast<const TIN*>(a.g)), bg(static_cast<const TIN*>(a.beta))
+          gg(static_cast<const TIN*>(Gate ? a.gate_f : a.g)), bg(static_cast<const TIN*>(Gate ? a.gate_b : a.beta)),
+          gts(Gate ? a.gate_f_ld : (int64_t)a.H * D), bts(Gate ? a.gate_b_ld : a.H), lb(a.lower_bound),
+          rate(Gate ? __expf(a.A_log[head]) : 0.0f)
     {
     }
 
@@ -366,11 +376,12 @@ struct Front {
         if (prod) {
             const int voff = (c0 + h * D) * ES;  // per lane
             if constexpr (Parts & 1) {
-                const rsrc_t rk_ = make_rsrc(kg + c_s * ts, bytes), rg_ = make_rsrc(gg + c_s * ts, bytes);
+                const rsrc_t rk_ = make_rsrc(kg + c_s * ts, bytes);
+                const rsrc_t rg_ = make_rsrc(gg + c_s * gts, (int64_t)nt * gts * ES);
 #pragma unroll
                 for (int t = 0; t < RP; ++t) {
                     const int soff = (rbase + t) * ts * ES;  // wave-uniform row term
-                    rg[t] = IN::template ld_pair<Pol>(rg_, voff, soff);
+                    rg[t] = IN::template ld_pair<Pol>(rg_, voff, Gate ? (int)((rbase + t) * gts * ES) : soff);
                     rk[t] = IN::template ld_pair<Pol>(rk_, voff, soff);
                 }
             }
@@ -386,8 +397,9 @@ struct Front {
             }
         }
         if constexpr (Parts & 1) {
-            const rsrc_t rb_ = make_rsrc(bg + c_s * H, (int64_t)nt * H * ES);  // uniform: built outside the branch
-            if (tid < C) rb = IN::template ld_one<Pol>(rb_, (tid * H + h) * ES, 0);
+            const rsrc_t rb_ = make_rsrc(bg + c_s * bts, (int64_t)nt * bts * ES);  // uniform: built outside the branch
+            if (tid < C) rb = IN::template ld_one<Pol>(rb_, (int)((tid * bts + h) * ES), 0);
+            if constexpr (Gate) ntl = nt;
         }
     }
 
@@ -398,13 +410,24 @@ struct Front {
             f32x2 G = {0.f, 0.f};
 #pragma unroll
             for (int t = 0; t < RP; ++t) {
-                const f32x2 gv = IN::unpack(rg[t]);  // rows past the chunk read as 0
+                f32x2 gv = IN::unpack(rg[t]);  // rows past the chunk read as 0
+                if constexpr (Gate) {
+                    // the gate prologue's g (stored as bfloat16); rows past the chunk 0
+                    const bool live = rbase + t < ntl;
+                    gv.x = live ? (float)(__bf16)fmaxf(-rate * softplus_hw(gv.x), lb) : 0.0f;
+                    gv.y = live ? (float)(__bf16)fmaxf(-rate * softplus_hw(gv.y), lb) : 0.0f;
+                }
                 g2[t] = f32x2{fmaxf(gv.x * kLog2e, lbl), fmaxf(gv.y * kLog2e, lbl)};
                 G += g2[t];
             }
             *reinterpret_cast<f32x2*>(&sm.Gp[R][hh][c0]) = G;
         }
-        if (tid < C) sm.beta[tid] = IN::one(rb);
+        if (tid < C) {
+            if constexpr (Gate)
+                sm.beta[tid] = tid < ntl ? (float)(__bf16)sigmoidf_(IN::one(rb)) : 0.0f;
+            else
+                sm.beta[tid] = IN::one(rb);
+        }
     }
 
     __device__ __forceinline__ f32x2 block_sum(int J) const

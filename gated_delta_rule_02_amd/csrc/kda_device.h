@@ -117,6 +117,22 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // be bound by full-precision division and log1p sequences.
 __device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 __device__ __forceinline__ float siluf_(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+
+// softplus(x) = max(x, 0) + ln(1 + e^-|x|) on the hardware base-2 exponential
+// and logarithm: e^-|x| lies in (0, 1], so the logarithm sees [1, 2] and
+// needs no denormal handling, and an exponential below the float32 normal
+// range flushes to 0, which the formula absorbs; ln(1 + e) by e - e^2/2 where
+// 1 + e would drop e's low bits (relative error < e^2/3). About half the
+// instructions of the library forms, which handle denormal arguments: this
+// kernel was bound by them.
+constexpr float kLn2 = 0.69314718055994531f;
+__device__ __forceinline__ float softplus_hw(float x)
+{
+    const float e = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
+    const float l = e < 0x1p-10f ? e * (1.0f - 0.5f * e) : kLn2 * __builtin_amdgcn_logf(1.0f + e);
+    return fmaxf(x, 0.0f) + l;
+}
+
 // softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^{-|x|}); log1p(e) by its
 // series e - e^2/2 where 1 + e would drop e's low bits (relative error < e^2/3)
 __device__ __forceinline__ float softplusf_(float x)

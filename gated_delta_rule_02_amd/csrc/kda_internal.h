@@ -93,6 +93,14 @@ struct PrefillArgs {
     // sequence the affine map S_out = M S_in + N of its tokens, M into map_M
     // [N, H, 128, 128] and N into sT, and writes no output (s0, o and snap unused)
     float* map_M;
+    // gate prologue inside the prefill (two-pass form only): when gate_f is
+    // set, g = max(-exp(A_log[h]) softplus(f), lower_bound) and beta =
+    // sigmoid(b) are formed from the projection rows f [T, >= H*128] (row
+    // stride gate_f_ld) and b [T, >= H] (gate_b_ld), each rounded to bfloat16
+    // as the gate prologue stores them, in place of the g and beta inputs
+    const void *gate_f, *gate_b;
+    int64_t gate_f_ld, gate_b_ld;
+    const float* A_log;
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 // Two-pass form (bfloat16 inputs): per-chunk products in `ws`, then the state

@@ -112,8 +112,9 @@ __device__ __forceinline__ void inverse_column(SM& sm, _Float16 (*Tm)[16][BLD], 
 }
 
 // POL: cache policy of the input loads (0 or kStream); NOQ: segment maps
-// (no query side: Q~ and P are neither formed nor stored)
-template <typename TIN, int POL, bool NOQ = false>
+// (no query side: Q~ and P are neither formed nor stored); GATE: g and beta
+// formed from the projection rows (the gate prologue inside the prefill)
+template <typename TIN, int POL, bool NOQ = false, bool GATE = false>
 __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
 {
     using O = Ops<false>;
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
     const TIN* vg = static_cast<const TIN*>(a.v);
     uint8_t* slots = sa.ws + (size_t)u * sa.nwin * kSlot;
 
-    Front<false, TIN, 2, true, POL, NOQ> fr(sm, a, h);
+    Front<false, TIN, 2, true, POL, NOQ, GATE> fr(sm, a, h);
     {
         const int64_t cs = seq_s + c_first * C;
         fr.load(cs, (int)min<int64_t>(C, seq_e - cs), vg);
@@ -980,6 +981,10 @@ hipError_t launch_prefill_split(const PrefillArgs& a, void* ws, size_t ws_bytes,
                 hipLaunchKernelGGL((intra_kernel<bf16_t, kStream, true>), gi, bi, 0, s, sa);
             else if (a.map_M)
                 hipLaunchKernelGGL((intra_kernel<bf16_t, 0, true>), gi, bi, 0, s, sa);
+            else if (a.gate_f && stream)
+                hipLaunchKernelGGL((intra_kernel<bf16_t, kStream, false, true>), gi, bi, 0, s, sa);
+            else if (a.gate_f)
+                hipLaunchKernelGGL((intra_kernel<bf16_t, 0, false, true>), gi, bi, 0, s, sa);
             else if (stream)
                 hipLaunchKernelGGL((intra_kernel<bf16_t, kStream>), gi, bi, 0, s, sa);
             else

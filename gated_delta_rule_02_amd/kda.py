@@ -29,6 +29,8 @@ _SIGS = {
     "kda_prefill": (_I, [_P] * 5 + [_I, _I64, _I, _I, _I, _P, _P, _I, _F, _F, _P, _P, _P, _I, _P, _SZ, _P]),
     "kda_prefill_workspace_bytes": (_SZ, [_I64, _I, _I, _I, _I, _I]),
     "kda_prefill_noalloc": (_I, [_P] * 5 + [_I, _I64, _I, _I, _I, _P, _P, _I, _F, _F, _P, _P, _P, _I, _P]),
+    "kda_prefill_gated": (_I, [_P] * 4 + [_I64, _P, _I64, _P, _I, _I64, _I, _I, _I, _P, _P, _I, _F, _F, _P, _P,
+                                          _P, _I, _P, _SZ, _P]),
     "kda_prefill_noalloc_scratch_bytes": (_SZ, []),
     "kda_prefill_snapshots": (_I, [_P] * 5 + [_I, _I64, _I, _I, _I, _P, _P, _I, _F, _F, _P, _P, _P, _I, _P, _SZ,
                                               _I64, _I64, _P, _P]),
@@ -178,6 +180,35 @@ def kda_prefill(q, k, v, g, beta, o, cu_seqlens=None, cu_seqlens_host=None, num_
               cu_dev, cu_host, num_seqs, scale, lower_bound, _ptr(initial_state), _ptr(final_state),
               _ptr(o), _dt(o), _ptr(workspace), ws_bytes, int(snapshot_interval), snapshots.shape[1],
               _ptr(snapshots), _stream(stream))
+    return o
+
+
+def kda_prefill_gated(q, k, v, f, b, A_log, o, cu_seqlens=None, cu_seqlens_host=None, num_seqs=None,
+                      initial_state=None, final_state=None, scale=1.0, lower_bound=-5.0, workspace="auto",
+                      stream=None):
+    """kda_prefill with the gate prologue inside it: f rows [T, >=H*128] and
+    b rows [T, >=H] (bfloat16, contiguous rows, any row stride), A_log float32
+    [H] in place of g and beta. Results equal kda_gate_prologue followed by
+    kda_prefill. bfloat16 q, k, v and a workspace ("auto" or a tensor)."""
+    for n_, t_ in (("q", q), ("k", k), ("v", v), ("A_log", A_log), ("o", o),
+                   ("initial_state", initial_state), ("final_state", final_state)):
+        _dense(t_, n_)
+    if f.stride(-1) != 1 or b.stride(-1) != 1:
+        raise ValueError("f and b rows must be contiguous")
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    cu_dev, cu_host, keep = _cu(cu_seqlens, cu_seqlens_host)
+    if num_seqs is None:
+        num_seqs = (keep.numel() - 1) if keep is not None else 1
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto' or a tensor")
+        need = lib().kda_prefill_workspace_bytes(T, num_seqs, H, dk, dv, _dt(q))
+        workspace = _workspace(q.device, need) if need else None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _call("kda_prefill_gated", _ptr(q), _ptr(k), _ptr(v), _ptr(f), f.stride(0), _ptr(b), b.stride(0),
+          _ptr(A_log), _dt(q), T, H, dk, dv, cu_dev, cu_host, num_seqs, scale, lower_bound,
+          _ptr(initial_state), _ptr(final_state), _ptr(o), _dt(o), _ptr(workspace), ws_bytes, _stream(stream))
     return o
 
 

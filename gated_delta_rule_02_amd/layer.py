@@ -97,16 +97,15 @@ class KDAMixer:
                                conv_state_out=None if conv_state_out is None else conv_state_out[i],
                                apply_silu=True, l2norm_group=l2, l2norm_eps=self.l2_eps)
             qkv.append(y.view(T, H, D))
-        g = self._buf("g", (T, H, D), torch.bfloat16)
-        beta = self._buf("beta", (T, H), torch.bfloat16)
-        K.kda_gate_prologue(fp, bp, self.A_log, g, beta, H, D, lower_bound=self.lower_bound)
+        # the gate prologue runs inside the prefill: g and beta are formed from
+        # the f and b columns of P in registers and never stored
         o = self._buf("o", (T, H, D), torch.float32)
-        K.kda_prefill(qkv[0], qkv[1], qkv[2], g, beta, o, cu_seqlens=cu_seqlens,
-                      cu_seqlens_host=cu_seqlens_host, initial_state=initial_state,
-                      final_state=final_state, scale=self.scale, lower_bound=self.lower_bound)
+        K.kda_prefill_gated(qkv[0], qkv[1], qkv[2], fp, bp, self.A_log, o, cu_seqlens=cu_seqlens,
+                            cu_seqlens_host=cu_seqlens_host, initial_state=initial_state,
+                            final_state=final_state, scale=self.scale, lower_bound=self.lower_bound)
         out, y = self.output(o, gp)
         if return_parts:
-            return out, dict(q=qkv[0], k=qkv[1], v=qkv[2], g=g, beta=beta, o=o, y=y, P=P)
+            return out, dict(q=qkv[0], k=qkv[1], v=qkv[2], o=o, y=y, P=P)
         return out
 
     def decode(self, x, state, conv_states):

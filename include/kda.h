@@ -152,6 +152,34 @@ int kda_prefill_noalloc(const void* q, const void* k, const void* v, const void*
 
 size_t kda_prefill_noalloc_scratch_bytes(void);
 
+/* ----------------------------------------------------------------------
+ * kda_prefill_gated -- kda_prefill with the gate prologue inside it.
+ *
+ * The decay and write strength come from the token mixer's projection rows,
+ * as kda_gate_prologue forms them ("Ling-3.1-flash: a 560B hybrid-attention
+ * MoE, counted from its safetensors headers", section "How KDA and MLA split
+ * the work"): g = max(-exp(A_log[h]) softplus(f), lower_bound) per channel and
+ * beta = sigmoid(b) per head, each rounded to bfloat16 as that prologue stores
+ * them, so o and final_state equal kda_gate_prologue followed by kda_prefill
+ * bit for bit. g and beta are formed in registers by the chunk-local pass and
+ * never stored.
+ *
+ * f          bfloat16 rows [num_tokens, >= H*dk], row stride f_ld elements (a
+ *            multiple of 8 below 2^24), 16-byte aligned; channel h*dk + c of a
+ *            row is channel c of head h.
+ * b          bfloat16 rows [num_tokens, >= H], row stride b_ld (below 2^24).
+ * A_log      float32 [H].
+ * Everything else as kda_prefill; in_dtype must be BF16 and a workspace is
+ * required (the two-pass form: KDA_ERR_UNSUPPORTED / KDA_ERR_WORKSPACE
+ * otherwise). f and b may overlap each other and q, k, v (they are read
+ * only), not o, final_state or the workspace.
+ * ---------------------------------------------------------------------- */
+int kda_prefill_gated(const void* q, const void* k, const void* v, const void* f, int64_t f_ld, const void* b,
+                      int64_t b_ld, const float* A_log, kda_dtype in_dtype, int64_t num_tokens, int H, int dk, int dv,
+                      const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int num_seqs,
+                      float scale, float lower_bound, const float* initial_state, float* final_state,
+                      void* o, kda_dtype out_dtype, void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* ------------------------------------------------------------------------
  * kda_prefill_snapshots -- kda_prefill that also saves the state at fixed
  * token positions of every sequence.

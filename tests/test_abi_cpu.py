@@ -389,3 +389,40 @@ def test_prefill_noalloc_validation():
     assert rc == K.KDA_ERR_UNSUPPORTED and "lower_bound" in msg
     assert f(q=None)[0] == K.KDA_ERR_INVALID_ARG
     assert f(q=fake(1) + 8)[0] == K.KDA_ERR_INVALID_ARG
+
+
+def prefill_gated(**over):
+    a = dict(q=fake(1), k=fake(2), v=fake(3), f=fake(4), f_ld=4 * 128, b=fake(5), b_ld=4, A_log=fake(7),
+             in_dtype=K.KDA_BF16, T=256, H=4, dk=128, dv=128, cu_dev=None, cu_host=None, N=1, scale=1.0,
+             lb=-5.0, s0=None, sT=None, o=fake(6), out_dtype=K.KDA_F32, ws=fake(8), ws_bytes=1 << 29,
+             stream=None)
+    a.update(over)
+    return call("kda_prefill_gated", a["q"], a["k"], a["v"], a["f"], a["f_ld"], a["b"], a["b_ld"], a["A_log"],
+                a["in_dtype"], a["T"], a["H"], a["dk"], a["dv"], a["cu_dev"], a["cu_host"], a["N"], a["scale"],
+                a["lb"], a["s0"], a["sT"], a["o"], a["out_dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_prefill_gated_validation():
+    """kda_prefill_gated: the two-pass form only, strided gate rows checked
+    for shape, alignment and overlap (every call below fails validation)."""
+    rc, msg = prefill_gated(in_dtype=K.KDA_F32)
+    assert rc == K.KDA_ERR_UNSUPPORTED and "bfloat16" in msg
+    rc, msg = prefill_gated(ws=None, ws_bytes=0)
+    assert rc == K.KDA_ERR_WORKSPACE
+    rc, msg = prefill_gated(f_ld=4 * 128 - 8)           # shorter than H * 128
+    assert rc == K.KDA_ERR_INVALID_ARG and "f_ld" in msg
+    assert prefill_gated(f_ld=4 * 128 + 4)[0] == K.KDA_ERR_INVALID_ARG   # not a multiple of 8
+    assert prefill_gated(f_ld=1 << 24)[0] == K.KDA_ERR_INVALID_ARG
+    rc, msg = prefill_gated(b_ld=3)
+    assert rc == K.KDA_ERR_INVALID_ARG and "b_ld" in msg
+    rc, msg = prefill_gated(A_log=None)
+    assert rc == K.KDA_ERR_INVALID_ARG and "A_log" in msg
+    assert prefill_gated(f=fake(4) + 2)[0] == K.KDA_ERR_INVALID_ARG    # f misaligned
+    assert prefill_gated(b=fake(5) + 1)[0] == K.KDA_ERR_INVALID_ARG    # b misaligned
+    # the strided f rows reach into o; b rows into the workspace
+    rc, msg = prefill_gated(f=fake(6) - 255 * 4 * 128 * 2, f_ld=4 * 128 + 8)
+    assert rc == K.KDA_ERR_INVALID_ARG and "o overlaps" in msg
+    rc, msg = prefill_gated(b=fake(8) - 1024, b_ld=64)
+    assert rc == K.KDA_ERR_INVALID_ARG and "workspace overlaps" in msg
+    assert prefill_gated(lb=-6.0)[0] == K.KDA_ERR_UNSUPPORTED
+    assert prefill_gated(dk=64)[0] == K.KDA_ERR_UNSUPPORTED
