@@ -852,7 +852,10 @@ void launch_state(SplitArgs sa, int64_t U, bool stream, hipStream_t s)
     sa.map_half = (int)(kColGroups * 8 * ((U + 7) / 8));
     const dim3 gs((unsigned)(sa.map_half * (sa.p.map_M ? 2 : 1))), bs(kStateThreads);
     if (TPW == 1 && !sa.p.map_M) {
-        // the role-split form: two compute wavefronts per tile
+        // the role-split form: two compute wavefronts per tile. (For the
+        // 64-column workgroups a role-split form with four tiles, nine
+        // wavefronts and single-buffered hand-overs measured no faster than
+        // the two-wavefront form: packed varlen 6.59 against 6.56 ms.)
         static_assert(kStateWaves == kRoleTiles, "the role-split form keeps the 32-column workgroups");
         const dim3 br(kRoleThreads);
         if (stream)
