@@ -470,7 +470,7 @@ def main():
                        "global_batch": 1, "seq_len": T, "heads": 64, "head_dim": 128, "chunk": 64},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                         "kernel": "kda_prefill call (two-pass form: intra_kernel + state_kernel per window, 2 windows of 32 chunks)",
+                         "kernel": "kda_prefill call (two-pass form: intra_kernel + state_roles_kernel per window, 2 windows of 32 chunks)",
                          "algorithmic_bytes_per_launch": PREFILL_BYTES_PER_TOKEN * T,
                          "mfma_tflops": PREFILL_FLOPS_PER_TOKEN * T / (ms * 1e-3) / 1e12,
                          "mfma_frac_of_bf16_peak": PREFILL_FLOPS_PER_TOKEN * T / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
