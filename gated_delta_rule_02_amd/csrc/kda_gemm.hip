@@ -262,6 +262,100 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 }
 
+// ------------------------------------------------------------ narrow kernel
+// C[M, N <= 64] (the last N mod 256 columns of a wide product, such as the 64
+// beta columns of the input projection): a 256 x 64 tile per workgroup leaves
+// M / 256 workgroups, each walking all of K in latency-bound steps. Here a
+// workgroup takes 32 rows and the four wavefronts split K four ways, each
+// loading its operand fragments straight from memory into registers (a row's
+// 128-byte line per 64-wide K step, the next step's fragments in flight during
+// this step's products); the four partial tiles are summed through LDS.
+constexpr int kNarrowRows = 32;
+
+template <typename TC>
+__global__ __launch_bounds__(256) void gemm_narrow_kernel(GemmArgs a)
+{
+    __shared__ f32x4 part[3][2][4][64];  // the partial tiles of wavefronts 1 .. 3
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int m16 = lane & 15, q4 = lane >> 4;
+    const int64_t m0 = (int64_t)blockIdx.x * kNarrowRows;
+    const int64_t rows_a = min<int64_t>(kNarrowRows, a.M - m0);
+    const rsrc_t ra = make_rsrc(static_cast<const bf16_t*>(a.A) + m0 * a.lda, ((rows_a - 1) * a.lda + a.K) * 2);
+    const rsrc_t rb = make_rsrc(a.B, ((a.N - 1) * a.ldb + a.K) * 2);
+    const int kq = (int)(a.K / 4);                  // this wavefront's K range: [wave kq, (wave + 1) kq)
+    const int nk = kq / 64;
+    // lane (m16, q4): row 16 i + m16, K elements 8 q4 .. +7 of each 32-wide half
+    int offa[2], offb[4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) offa[i] = (int)((16 * i + m16) * a.lda * 2) + (wave * kq + 8 * q4) * 2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) offb[j] = (int)((16 * j + m16) * a.ldb * 2) + (wave * kq + 8 * q4) * 2;
+    u32x4_t fa[2][2][2], fb[2][4][2];  // [buffer][tile][K half]
+    auto load = [&](int kt, int buf) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                fa[buf][i][h] = __builtin_amdgcn_raw_buffer_load_b128(ra, offa[i], (kt * 64 + 32 * h) * 2, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                fb[buf][j][h] = __builtin_amdgcn_raw_buffer_load_b128(rb, offb[j], (kt * 64 + 32 * h) * 2, 0);
+        }
+    };
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    load(0, 0);
+    for (int kt = 0; kt < nk; kt += 2) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            if (kt + b >= nk) break;
+            if (kt + b + 1 < nk) load(kt + b + 1, b ^ 1);
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, fb[b][j][h]), __builtin_bit_cast(bf16x8, fa[b][i][h]), acc[i][j],
+                            0, 0, 0);
+        }
+    }
+    // acc[i][j] holds C^T of tile (i, j): lane (m16, q4) element e is
+    // C[row 16i + m16][column 16j + 4q4 + e]; wavefronts 1 .. 3 hand theirs to 0
+    if (wave > 0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) part[wave - 1][i][j][lane] = acc[i][j];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < 3; ++w)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] += part[w][i][j][lane];
+    TC* Cp = static_cast<TC*>(a.C);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int64_t row = m0 + 16 * i + m16;
+        if (row >= a.M) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t col = 16 * j + 4 * q4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (col + e < a.N) st(Cp + row * a.ldc + col + e, acc[i][j][e]);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s)
@@ -283,7 +377,14 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s)
         }
         GemmArgs r = a;
         r.N = a.N - m.N;
-        if (r.N > 0) {
+        if (r.N > 0 && r.N <= 64 && a.K % 256 == 0) {
+            // up to 64 columns left: 32-row workgroups with K split four ways
+            r.B = static_cast<const bf16_t*>(a.B) + m.N * a.ldb;
+            r.C = static_cast<uint8_t*>(a.C) + m.N * (a.c_dtype == F32 ? 4 : 2);
+            const dim3 grid((unsigned)((a.M + kNarrowRows - 1) / kNarrowRows)), block(256);
+            if (a.c_dtype == F32) hipLaunchKernelGGL((gemm_narrow_kernel<float>), grid, block, 0, s, r);
+            else hipLaunchKernelGGL((gemm_narrow_kernel<bf16_t>), grid, block, 0, s, r);
+        } else if (r.N > 0) {
             r.B = static_cast<const bf16_t*>(a.B) + m.N * a.ldb;
             r.C = static_cast<uint8_t*>(a.C) + m.N * (a.c_dtype == F32 ? 4 : 2);
             const int nj = r.N <= 64 ? 2 : (r.N <= 128 ? 4 : 8);

@@ -45,6 +45,21 @@ def test_gemm_fallback_path(M, N, Kd):
     assert relerr(host64(C[:, :N]), ref) < 2e-5
 
 
+@pytest.mark.parametrize("M,N,Kd,out", [(77, 256 + 37, 1024, torch.float32), (1000, 64, 256, torch.bfloat16),
+                                         (33, 512 + 64, 768, torch.float32), (300, 520, 512, torch.bfloat16)])
+def test_gemm_narrow_tail(M, N, Kd, out):
+    """Up to 64 columns past the 256-column tiles with K a multiple of 256: the
+    narrow kernel (32-row workgroups, K split over four wavefronts, partial tiles
+    summed in LDS); ragged M, N mod 256 from 8 to 64, a padded row stride of C."""
+    announce("gemm narrow tail M=%d N=%d K=%d %s" % (M, N, Kd, out))
+    ldc = (N + 7) // 8 * 8 + 8
+    C, ref = run(M, N, Kd, out_dtype=out, ldc=ldc, seed=M + Kd)
+    e = relerr(host64(C[:, :N]), ref)
+    print("  err %.2e" % e, flush=True)
+    assert e < (2e-5 if out == torch.float32 else 5e-3)
+    assert torch.isnan(C[:, N:].float()).all()
+
+
 def test_gemm_tail_tiles_bf16_output():
     """The 128-column tail tiles (N mod 256 = 100) with a bfloat16 output."""
     announce("gemm tail tiles bf16 out")
