@@ -82,6 +82,23 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a)
     }
 }
 
+// The epilogue reads o and the gate columns once: non-temporal, so that y,
+// which the output projection reads next, stays in the last-level cache
+// (measured at T = 8192: the epilogue and the output projection after it
+// 625-634 -> 588-590 us; the epilogue alone unchanged)
+template <typename T> __device__ __forceinline__ f32x4 ld4_nt(const T* p);
+template <> __device__ __forceinline__ f32x4 ld4_nt<float>(const float* p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+template <> __device__ __forceinline__ f32x4 ld4_nt<bf16_t>(const bf16_t* p)
+{
+    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+    const u2 u = __builtin_nontemporal_load(reinterpret_cast<const u2*>(p));
+    return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                 __uint_as_float(u.y & 0xffff0000u)};
+}
+
 // Epilogue: a lane owns 4 consecutive channels; 32 lanes cover one (token,
 // head) row, so a wavefront handles two rows and the RMS is a 32-lane sum.
 constexpr int kNormRowsPerBlock = 8;
@@ -94,8 +111,8 @@ __global__ __launch_bounds__(256) void norm_gate_kernel(NormGateArgs a)
     const int c = 4 * (threadIdx.x & 31);   // dv == 128
     const int64_t t = row / a.H;
     const int h = (int)(row % a.H);
-    const f32x4 ov = ld4(static_cast<const TO_*>(a.o) + row * a.dv + c);
-    const f32x4 gv = ld4(static_cast<const TY*>(a.gate) + t * a.gate_ld + (int64_t)h * a.dv + c);
+    const f32x4 ov = ld4_nt(static_cast<const TO_*>(a.o) + row * a.dv + c);
+    const f32x4 gv = ld4_nt(static_cast<const TY*>(a.gate) + t * a.gate_ld + (int64_t)h * a.dv + c);
     const f32x4 wv = ld4(a.w + c);
     const float ms = group_sum<32>(ov.x * ov.x + ov.y * ov.y + ov.z * ov.z + ov.w * ov.w) * (1.0f / 128.0f);
     const float r = rsqrtf(ms + a.eps);

@@ -251,6 +251,17 @@ __global__ __launch_bounds__(KS * 64) void gemv_fp8_mfma_kernel(Fp8GemvArgs a)
     }
 }
 
+template <typename T> __device__ __forceinline__ f32x2 ld2_nt(const T* p);
+template <> __device__ __forceinline__ f32x2 ld2_nt<float>(const float* p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(p));
+}
+template <> __device__ __forceinline__ f32x2 ld2_nt<bf16_t>(const bf16_t* p)
+{
+    const uint32_t u = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+    return f32x2{__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u)};
+}
+
 constexpr int kNormRows = 4;  // (token, head) rows per workgroup, one wavefront each
 
 template <typename TO, typename TG>
@@ -262,10 +273,12 @@ __global__ __launch_bounds__(kNormRows * 64) void norm_gate_fp8_kernel(NormGateF
     const int64_t t = row / a.H;
     const int h = (int)(row % a.H);
     const int c = 2 * lane;  // dv == 128
-    const f32x2 ov = ld2(static_cast<const TO*>(a.o) + row * 128 + c);
+    // o and the gate columns are read once: non-temporal, as in the bf16
+    // epilogue, so that the codes the output projection reads next stay cached
+    const f32x2 ov = ld2_nt(static_cast<const TO*>(a.o) + row * 128 + c);
     const float ms = wave_sum(ov.x * ov.x + ov.y * ov.y) * (1.0f / 128.0f);
     const float r = rsqrtf(ms + a.eps);
-    const f32x2 gv = ld2(static_cast<const TG*>(a.gate) + t * a.gate_ld + (int64_t)h * 128 + c);
+    const f32x2 gv = ld2_nt(static_cast<const TG*>(a.gate) + t * a.gate_ld + (int64_t)h * 128 + c);
     const float y0 = ov.x * r * a.w[c] * sigmoidf_(gv.x);
     const float y1 = ov.y * r * a.w[c + 1] * sigmoidf_(gv.y);
     const float amax = wave_max(fmaxf(fabsf(y0), fabsf(y1)));
