@@ -294,9 +294,9 @@ __global__ __launch_bounds__(kThreads) void intra_kernel(SplitArgs sa)
 
 // ------------------------------------------------------------- state pass
 // The form for 64-column workgroups and segment maps (32-column workgroups
-// take the role-split form below). Three wavefronts: two compute wavefronts
-// (one or two 16-column tiles of the state each) and a loader that copies each
-// chunk's operands into an LDS stage with
+// of an ordinary prefill take the role-split form below). Three wavefronts:
+// two compute wavefronts (one or two 16-column tiles of the state each) and a
+// loader that copies each chunk's operands into an LDS stage with
 // buffer-to-LDS loads (two stages, one chunk ahead). Each role waits only on
 // its own memory counter; one barrier per chunk hands a stage from the loader
 // to the compute wavefronts. (A fourth wavefront that touched the chunks two
@@ -851,7 +851,9 @@ void launch_state(SplitArgs sa, int64_t U, bool stream, hipStream_t s)
     constexpr int kColGroups = D / (16 * kStateWaves * TPW);
     sa.map_half = (int)(kColGroups * 8 * ((U + 7) / 8));
     const dim3 gs((unsigned)(sa.map_half * (sa.p.map_M ? 2 : 1))), bs(kStateThreads);
-    if (TPW == 1 && !sa.p.map_M) {
+    if (sa.p.map_M) {
+        hipLaunchKernelGGL((state_kernel<TOUT, TPW, 0, true>), gs, bs, 0, s, sa);
+    } else if constexpr (TPW == 1) {
         // the role-split form: two compute wavefronts per tile. (For the
         // 64-column workgroups a role-split form with four tiles, nine
         // wavefronts and single-buffered hand-overs measured no faster than
@@ -862,14 +864,11 @@ void launch_state(SplitArgs sa, int64_t U, bool stream, hipStream_t s)
             hipLaunchKernelGGL((state_roles_kernel<TOUT, kStream>), gs, br, 0, s, sa);
         else
             hipLaunchKernelGGL((state_roles_kernel<TOUT, 0>), gs, br, 0, s, sa);
-        return;
-    }
-    if (sa.p.map_M)
-        hipLaunchKernelGGL((state_kernel<TOUT, TPW, 0, true>), gs, bs, 0, s, sa);
-    else if (stream)
+    } else if (stream) {
         hipLaunchKernelGGL((state_kernel<TOUT, TPW, kStream, false>), gs, bs, 0, s, sa);
-    else
+    } else {
         hipLaunchKernelGGL((state_kernel<TOUT, TPW, 0, false>), gs, bs, 0, s, sa);
+    }
 }
 
 // A window's workspace up to this size is left to the last-level cache (256
