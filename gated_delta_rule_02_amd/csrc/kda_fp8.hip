@@ -389,22 +389,24 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(Fp8GemvArgs a)
     const rsrc_t rw = make_rsrc(Wr, (rows_w - 1) * a.ldw + a.K);
 
     // copy of K step kb into stage st: 64 instructions of 1 KiB, 8 per
-    // wavefront; instruction i covers 8 rows (X rows for i < 32, W rows
-    // after), lane l row 8 i' + l / 8 and LDS chunk slot l % 8, which holds
-    // K chunk slot ^ (row mod 8)
+    // wavefront (X rows for waves 0-3, W rows for 4-7); instruction j of a
+    // wavefront covers rows 64 (wave mod 4) + 8 j + l / 8 (lane l) into LDS
+    // chunk slot l % 8, which holds K chunk slot ^ ((row / 2) mod 8). That
+    // swizzle depends on j only through its parity, so two lane offsets serve
+    // all eight instructions and the row step 8 j ld goes into the scalar offset
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t*)&smem[0][0];
-    const int crow = lane >> 3;
-    auto copy = [&](int kb, int st) {
+    const bool cw = wave >= 4;
+    const rsrc_t rc = cw ? rw : rx;
+    const int ldc = (int)(cw ? a.ldw : a.ldx);
+    const int rb = 64 * (wave & 3) + (lane >> 3);
+    int voff[2];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int i = wave * 8 + j;  // wave-uniform: X for waves 0-3, W for 4-7
-            const int r = 8 * (i & 31) + crow;
-            const int koff = kb * 128 + 16 * ((lane & 7) ^ ((r >> 1) & 7));
-            const uint32_t dst = lds0 + st * kF8Stage + i * 1024;
-            if (i < 32)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(uintptr_t)dst, 16, (int)(r * a.ldx) + koff, 0, 0, 0);
-            else
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t*)(uintptr_t)dst, 16, (int)(r * a.ldw) + koff, 0, 0, 0);
+    for (int par = 0; par < 2; ++par) voff[par] = rb * ldc + 16 * ((lane & 7) ^ (((rb >> 1) + 4 * par) & 7));
+    auto copy = [&](int kb, int st, int j0, int j1) {
+#pragma unroll
+        for (int j = j0; j < j1; ++j) {
+            const uint32_t dst = lds0 + st * kF8Stage + (wave * 8 + j) * 1024;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_void_t*)(uintptr_t)dst, 16, voff[j & 1], 8 * j * ldc + kb * 128, 0, 0);
         }
     };
 
@@ -424,17 +426,31 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(Fp8GemvArgs a)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // the scales of step kb + 1 are loaded one step ahead, before that step's
+    // copy: a load issued after the copy would make its first use wait for
+    // the copy as well (the vector memory counter drains in order), which
+    // stalled every step on the next step's copy
+    float sxv[4], swv;
+    auto load_scales = [&](int kb) {
+        swv = swp[kb];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sxv[i] = sxp[i][kb];
+    };
     const int nk = (int)(a.K >> 7);
-    copy(0, 0);
+    load_scales(0);
+    copy(0, 0, 0, 8);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wavefront's copy has landed
     __syncthreads();
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     for (int kb = 0; kb < nk; ++kb) {
         const int st = kb & 1;
-        if (kb + 1 < nk) copy(kb + 1, st ^ 1);
-        const float sw = swp[kb];
         float s[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[i] = sxp[i][kb] * sw;
+        for (int i = 0; i < 4; ++i) s[i] = sxv[i] * swv;
+        if (kb + 1 < nk) {
+            load_scales(kb + 1);
+            copy(kb + 1, st ^ 1, 0, 8);
+        }
         const uint8_t* sa = &smem[st][0];
         const uint8_t* sb = &smem[st][kF8Tile * 128];
         i32x8_t fa[4];
@@ -474,7 +490,8 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(Fp8GemvArgs a)
                     for (int e = 0; e < 4; ++e) c[e] = fmaf(p[i][j][e], s[i], c[e]);
                 }
         }
-        __syncthreads();  // the copy of step kb + 1 has landed and every read of stage st is done
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wavefront's copy of step kb + 1 has landed
+        __syncthreads();  // every copy of step kb + 1 has landed and every read of stage st is done
     }
 
     // acc[i][j]: lane (m16, q4) element e is Y[row 16i + m16][column 16j + 4q4 + e]
