@@ -32,7 +32,7 @@ __device__ __forceinline__ void st2<float>(float* p, float a, float b)
 template <>
 __device__ __forceinline__ void st2<bf16_t>(bf16_t* p, float a, float b)
 {
-    *reinterpret_cast<uint32_t*>(p) = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+    *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(a, b);
 }
 
 // Finish one output pair: activation, optional L2 over the wavefront's group.

@@ -76,8 +76,8 @@ __device__ __forceinline__ void st_state(bf16_t* p, const f32x4* v)
     u32x4_t u;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        u[2 * h] = (uint32_t)f32_to_bf16(v[h].x) | ((uint32_t)f32_to_bf16(v[h].y) << 16);
-        u[2 * h + 1] = (uint32_t)f32_to_bf16(v[h].z) | ((uint32_t)f32_to_bf16(v[h].w) << 16);
+        u[2 * h] = pack_bf16x2(v[h].x, v[h].y);
+        u[2 * h + 1] = pack_bf16x2(v[h].z, v[h].w);
     }
     KDA_NT_STORE(u, reinterpret_cast<u32x4_t*>(p));
 }

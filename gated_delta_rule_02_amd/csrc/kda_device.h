@@ -18,12 +18,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 // ---- bfloat16 conversion (round to nearest, ties to even) ----------------
 __device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-__device__ __forceinline__ bf16_t f32_to_bf16(float f)
+// by the hardware conversion (a NaN stays a quiet NaN); two values at a time
+// pack into one 32-bit word with a single instruction
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);  // quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (bf16_t)(u >> 16);
+    typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, b2_t{(__bf16)a, (__bf16)b});
 }
 
 // ---- typed scalar load/store for the two storage types -------------------
@@ -75,8 +76,8 @@ template <> __device__ __forceinline__ void st4<float>(float* p, f32x4 v)
 template <> __device__ __forceinline__ void st4<bf16_t>(bf16_t* p, f32x4 v)
 {
     uint2 u;
-    u.x = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
-    u.y = (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16);
+    u.x = pack_bf16x2(v.x, v.y);
+    u.y = pack_bf16x2(v.z, v.w);
     *reinterpret_cast<uint2*>(p) = u;
 }
 
