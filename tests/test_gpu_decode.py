@@ -296,6 +296,30 @@ def test_state_convert_round_trip():
     assert np.array_equal(z.cpu().numpy(), bf16_round(x))
 
 
+def test_state_convert_special_values():
+    """float32 -> bfloat16 on the cases a rounding rule can get wrong: exact
+    ties with an even and an odd kept bit, one unit either side of a tie,
+    subnormals (a tie among them, and the largest rounding up to the smallest
+    normal), signed zeros, infinities, the largest finite value (rounds to
+    infinity) and NaN; bit for bit against round-to-nearest-even written on
+    the bit patterns."""
+    announce("state convert special values")
+    pats = [0x3F808000, 0x3F818000, 0x3F807FFF, 0x3F808001, 0x00000001, 0x00008000, 0x00018000, 0x007FFFFF,
+            0x00000000, 0x7F800000, 0x7F7FFFFF, 0x7F7F7FFF, 0x477FE000, 0x477FF000]
+    pats = pats + [p | 0x80000000 for p in pats]
+    x = np.array(pats, dtype=np.uint32).view(np.float32)
+    x = np.concatenate([x, np.array([0x7FC00000, 0xFFC00001], dtype=np.uint32).view(np.float32)])
+    y = torch.empty(x.shape, dtype=torch.bfloat16, device="cuda")
+    K.kda_state_convert(torch.from_numpy(x).cuda(), y)
+    torch.cuda.synchronize()
+    got = y.cpu().view(torch.int16).numpy().view(np.uint16)
+    n = len(pats)
+    want = (bf16_round(x[:n]).view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(got[:n], want), [(hex(p), hex(g), hex(w)) for p, g, w in zip(pats, got[:n], want) if g != w]
+    # NaN stays NaN (exponent all ones, non-zero fraction)
+    assert all((g & 0x7F80) == 0x7F80 and (g & 0x007F) != 0 for g in got[n:]), [hex(g) for g in got[n:]]
+
+
 def test_decode_bf16_state_error_study():
     """64 decode steps, the state stored after every step in bf16 or in fp32,
     against the FP64 oracle, for the workload's decay (g = -softplus(z)) and a
